@@ -1,0 +1,166 @@
+/*
+ * gdn_oracle.c -- plain fp64 CPU oracle for the gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is used by the tests, by the smoke
+ * check and by the benchmark's CPU-baseline leg; the product path never
+ * links, loads or calls it.  It shares no code, header or constant with the
+ * HIP library.
+ *
+ * What it computes (per independent (b, h) head, tokens t = 0..T-1):
+ *
+ *   Gated DeltaNet (GatedDeltaNet walkthrough, yfxerp.com, section "Delta
+ *   Rule: predict first, then correct"; the recurrence and the per-token
+ *   reference loop there):
+ *       S <- exp(g_t) * S                       (gated forgetting of the whole state)
+ *       u <- beta_t * (v_t - S^T k_t)           (prediction error, scaled by write strength)
+ *       S <- S + k_t u^T                        (write only the correction)
+ *       o_t <- scale * S^T q_t                  (read-out with the query, after the update)
+ *   S is d_k x d_v (key rows, value columns).  The matrix form on that page,
+ *   S_t = (I - beta k k^T) exp(g) S_{t-1} + beta k v^T, is the same map.
+ *
+ *   Gated DeltaNet-2 (NVIDIA AI lanza Gated DeltaNet-2, 7minutos.es, section
+ *   "Regla-2 del Delta cerrado"):
+ *       S_t = (I - k_t (b_t . k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T
+ *   evaluated as: decay rows by alpha (before the edit), predict with the
+ *   erase-gated key, write the write-gated value minus the prediction:
+ *       S <- Diag(exp(log_alpha_t)) S
+ *       u <- w_t . v_t - S^T (b_t . k_t)
+ *       S <- S + k_t u^T ;   o_t <- scale * S^T q_t
+ *
+ *   Decode step: the Gated DeltaNet body above once, with S given, S updated
+ *   in place.
+ *
+ * Layouts (row-major, contiguous): q,k [B,T,H,Dk]; v [B,T,H,Dv];
+ * g, beta [B,T,H]; log_alpha, b [B,T,H,Dk]; w [B,T,H,Dv];
+ * h0, S [B,H,Dk,Dv]; o [B,T,H,Dv].  h0 may be NULL (zero initial state).
+ * S_out may be NULL.  Heads run in parallel with OpenMP, one head per
+ * iteration; within a head everything is sequential.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int gdn_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* One Gated DeltaNet token on one head's state S[Dk*Dv]. */
+static void gdn_token(double *S, const double *q, const double *k, const double *v,
+                      double g, double beta, double *u, double *o,
+                      int Dk, int Dv, double scale) {
+    const double decay = exp(g);
+    for (int i = 0; i < Dk * Dv; ++i) S[i] *= decay;
+    for (int j = 0; j < Dv; ++j) {
+        double pred = 0.0;
+        for (int i = 0; i < Dk; ++i) pred += S[i * Dv + j] * k[i];
+        u[j] = beta * (v[j] - pred);
+    }
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j) S[i * Dv + j] += k[i] * u[j];
+    if (o) {
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < Dk; ++i) acc += S[i * Dv + j] * q[i];
+            o[j] = scale * acc;
+        }
+    }
+}
+
+void gdn_oracle_fwd(const double *q, const double *k, const double *v,
+                    const double *g, const double *beta, const double *h0,
+                    double *o, double *S_out,
+                    int B, int T, int H, int Dk, int Dv, double scale, int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        const long b = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        double *u = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (h0) memcpy(S, h0 + unit * (long)Dk * Dv, sizeof(double) * (size_t)Dk * Dv);
+        else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
+        for (long t = 0; t < T; ++t) {
+            const long th = (b * T + t) * H + h;        /* token-head index */
+            gdn_token(S, q + th * Dk, k + th * Dk, v + th * Dv, g[th], beta[th], u,
+                      o + th * Dv, Dk, Dv, scale);
+        }
+        if (S_out) memcpy(S_out + unit * (long)Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
+        free(S);
+        free(u);
+    }
+}
+
+void gdn2_oracle_fwd(const double *q, const double *k, const double *v,
+                     const double *log_alpha, const double *bgate, const double *wgate,
+                     const double *h0, double *o, double *S_out,
+                     int B, int T, int H, int Dk, int Dv, double scale, int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        const long b = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        double *u = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (h0) memcpy(S, h0 + unit * (long)Dk * Dv, sizeof(double) * (size_t)Dk * Dv);
+        else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
+        for (long t = 0; t < T; ++t) {
+            const long th = (b * T + t) * H + h;
+            const double *qt = q + th * Dk, *kt = k + th * Dk, *vt = v + th * Dv;
+            const double *la = log_alpha + th * Dk, *bt = bgate + th * Dk, *wt = wgate + th * Dv;
+            /* decay each key row by its own channel rate, before the edit */
+            for (int i = 0; i < Dk; ++i) {
+                const double a = exp(la[i]);
+                for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a;
+                e[i] = bt[i] * kt[i];
+            }
+            for (int j = 0; j < Dv; ++j) {
+                double pred = 0.0;
+                for (int i = 0; i < Dk; ++i) pred += S[i * Dv + j] * e[i];
+                u[j] = wt[j] * vt[j] - pred;
+            }
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * u[j];
+            double *ot = o + th * Dv;
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < Dk; ++i) acc += S[i * Dv + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        if (S_out) memcpy(S_out + unit * (long)Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
+        free(S);
+        free(u);
+        free(e);
+    }
+}
+
+/* Single-token decode step: q,k [B,H,Dk], v [B,H,Dv], g,beta [B,H], S [B,H,Dk,Dv] in/out. */
+void gdn_oracle_step(const double *q, const double *k, const double *v,
+                     const double *g, const double *beta, double *S, double *o,
+                     int B, int H, int Dk, int Dv, double scale, int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        double *u = (double *)malloc(sizeof(double) * (size_t)Dv);
+        gdn_token(S + unit * (long)Dk * Dv, q + unit * Dk, k + unit * Dk, v + unit * Dv,
+                  g[unit], beta[unit], u, o + unit * Dv, Dk, Dv, scale);
+        free(u);
+    }
+}

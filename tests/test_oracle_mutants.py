@@ -1,0 +1,78 @@
+"""The pins must be able to fail: plant plausible mistakes in a copy of the C
+oracle (on the CPU, in a temporary directory), load the mutant in place of
+the oracle, and require that at least one pin rejects each mutant."""
+import ctypes
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
+
+# (name, original text, planted mistake).  Every mutant keeps all memory
+# accesses in bounds.
+MUTANTS = [
+    ("error_sign", "u[j] = beta * (v[j] - pred);", "u[j] = beta * (v[j] + pred);"),
+    ("beta_dropped", "u[j] = beta * (v[j] - pred);", "u[j] = (v[j] - pred);"),
+    ("no_decay", "for (int i = 0; i < Dk * Dv; ++i) S[i] *= decay;", ";"),
+    ("decay_sign", "const double decay = exp(g);", "const double decay = exp(-g);"),
+    ("write_with_query", "for (int j = 0; j < Dv; ++j) S[i * Dv + j] += k[i] * u[j];\n    if (o)",
+     "for (int j = 0; j < Dv; ++j) S[i * Dv + j] += q[i] * u[j];\n    if (o)"),
+    ("scale_dropped", "o[j] = scale * acc;", "o[j] = acc;"),
+    ("predict_with_query", "pred += S[i * Dv + j] * k[i];", "pred += S[i * Dv + j] * q[i];"),
+    ("gdn2_erase_gate_dropped", "e[i] = bt[i] * kt[i];", "e[i] = kt[i];"),
+    ("gdn2_write_gate_dropped", "u[j] = wt[j] * vt[j] - pred;", "u[j] = vt[j] - pred;"),
+    ("gdn2_write_gate_on_error", "u[j] = wt[j] * vt[j] - pred;", "u[j] = wt[j] * (vt[j] - pred);"),
+    ("gdn2_decay_uniform", "const double a = exp(la[i]);", "const double a = exp(la[0]);"),
+    ("gdn2_readout_scale", "ot[j] = scale * acc;", "ot[j] = acc;"),
+]
+
+PIN_FUNCS = [
+    pins.test_hand_worked_gdn,
+    pins.test_hand_worked_gdn2,
+    pins.test_matrix_form_gdn,
+    pins.test_matrix_form_gdn2,
+    pins.test_beta0_pure_decay_closed_form,
+    pins.test_beta1_unit_key_writes_exactly,
+    pins.test_gdn2_b1_unit_key_writes_gated_value,
+    pins.test_single_token_closed_form,
+    pins.test_two_token_hand_expansion,
+    pins.test_one_hot_keys_are_scalar_emas,
+    pins.test_gdn2_one_hot_keys_are_channel_emas,
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / f"{name}.c"
+    path.write_text(text.replace(old, new))
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(path), "-o", str(so), "-lm"],
+                   check=True)
+    return str(so)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, monkeypatch, name, old, new):
+    so = _build_mutant(tmp_path, name, old, new)
+    lib = ctypes.CDLL(so)
+    i, d, dp = ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double)
+    lib.gdn_oracle_fwd.argtypes = [dp] * 8 + [i] * 5 + [d, i]
+    lib.gdn2_oracle_fwd.argtypes = [dp] * 9 + [i] * 5 + [d, i]
+    lib.gdn_oracle_step.argtypes = [dp] * 7 + [i] * 4 + [d, i]
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = []
+    for f in PIN_FUNCS:
+        kwargs = {}
+        if "gp" in inspect.signature(f).parameters:
+            kwargs["gp"] = -800.0
+        try:
+            f(**kwargs)
+        except AssertionError:
+            caught.append(f.__name__)
+    assert caught, f"no pin rejects mutant {name}"
