@@ -1,0 +1,237 @@
+"""Python binding of the gfx950 gated delta rule library (``libgdn.so``).
+
+Argument marshalling only: each function checks tensor dtypes, shapes and
+devices, allocates outputs and workspace with torch (device memory is torch's
+business), and calls the C entry point of the same name on torch's current
+stream.  All computation happens in the HIP kernels; there is no fallback.
+If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "lib_path", "load", "status_string",
+    "gdn_chunk_fwd", "gdn_chunk_intra", "gdn2_chunk_fwd", "gdn_recurrent_step",
+    "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
+    "GDN_F32", "GDN_BF16", "BT",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+BT = 64
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def load():
+    """Load libgdn.so and declare its C signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is not built; run `python gated_delta_rule_34_amd/build.py`")
+    lib = ctypes.CDLL(lib_path)
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [_i]
+    lib.gdn_chunk_fwd_workspace.restype = _sz
+    lib.gdn_chunk_fwd_workspace.argtypes = [_i] * 6
+    lib.gdn2_chunk_fwd_workspace.restype = _sz
+    lib.gdn2_chunk_fwd_workspace.argtypes = [_i] * 6
+    lib.gdn_chunk_fwd.restype = _i
+    lib.gdn_chunk_fwd.argtypes = [_vp] * 8 + [_i] * 6 + [_f, _vp, _sz, _vp]
+    lib.gdn_chunk_intra.restype = _i
+    lib.gdn_chunk_intra.argtypes = [_vp] * 5 + [_i] * 5 + [_vp]
+    lib.gdn2_chunk_fwd.restype = _i
+    lib.gdn2_chunk_fwd.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
+    lib.gdn_recurrent_step.restype = _i
+    lib.gdn_recurrent_step.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _vp]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().gdn_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise RuntimeError(f"{what} failed: {status_string(code)} (status {code})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    ws = torch.empty(max(int(nbytes), 256) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws, ws[off:off + max(int(nbytes), 256)]
+
+
+def gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype_code):
+    return int(load().gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype_code))
+
+
+def gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype_code):
+    return int(load().gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype_code))
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=None, output_final_state=True, workspace=None,
+                  out=None, final_state=None):
+    """Chunked Gated DeltaNet forward.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or fp32),
+    g, beta [B,T,H] fp32, h0 [B,H,Dk,Dv] fp32 or None.  Returns (o fp32, ht or None)."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, T, H, Dv), torch.float32, dev)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                                                                     device=dev)
+        _need(ht, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    lib = load()
+    need = lib.gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, dt)
+    if need == 0:
+        _check(2, "gdn_chunk_fwd_workspace")
+    if workspace is None:
+        _, ws = _workspace(need, dev)
+    else:
+        ws = workspace
+    _check(lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+                             B, T, H, Dk, Dv, dt, float(scale), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(dev)), "gdn_chunk_fwd")
+    return o, ht
+
+
+def gdn_chunk_intra(k, g, beta):
+    """State-independent chunk stage: returns (G2 [B,H,NT,64], Tinv [B,H,NT,64,64]) fp32,
+    Tinv = (I + A)^-1 - I per chunk."""
+    torch = _torch()
+    B, T, H, Dk = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(k, "k", (B, T, H, Dk), k.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    NT = (T + BT - 1) // BT
+    G2 = torch.empty((B, H, NT, BT), dtype=torch.float32, device=dev)
+    Tinv = torch.empty((B, H, NT, BT, BT), dtype=torch.float32, device=dev)
+    _check(load().gdn_chunk_intra(_ptr(k), _ptr(g), _ptr(beta), _ptr(G2), _ptr(Tinv), B, T, H, Dk, dt,
+                                  _stream(dev)), "gdn_chunk_intra")
+    return G2, Tinv
+
+
+def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, h0=None, scale=None, output_final_state=True, workspace=None,
+                   out=None, final_state=None):
+    """Chunked Gated DeltaNet-2 forward.  log_alpha [B,T,H,Dk] fp32; b [B,T,H,Dk] and
+    w [B,T,H,Dv] in the dtype of q.  Returns (o fp32, ht or None)."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (B, T, H, Dk), torch.float32, dev)
+    _need(b, "b", (B, T, H, Dk), q.dtype, dev)
+    _need(w, "w", (B, T, H, Dv), q.dtype, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, T, H, Dv), torch.float32, dev)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                                                                     device=dev)
+        _need(ht, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    lib = load()
+    need = lib.gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, dt)
+    if need == 0:
+        _check(2, "gdn2_chunk_fwd_workspace")
+    if workspace is None:
+        _, ws = _workspace(need, dev)
+    else:
+        ws = workspace
+    _check(lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(h0), _ptr(o),
+                              _ptr(ht), B, T, H, Dk, Dv, dt, float(scale), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(dev)), "gdn2_chunk_fwd")
+    return o, ht
+
+
+def gdn_recurrent_step(q, k, v, g, beta, S, scale=None, out=None):
+    """One decode token: q, k [B,H,Dk], v [B,H,Dv], g, beta [B,H] fp32, S [B,H,Dk,Dv] fp32
+    updated in place.  Returns o [B,H,Dv] fp32."""
+    torch = _torch()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, H, Dv), q.dtype, dev)
+    _need(g, "g", (B, H), torch.float32, dev)
+    _need(beta, "beta", (B, H), torch.float32, dev)
+    _need(S, "S", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, H, Dv), torch.float32, dev)
+    _check(load().gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                                     B, H, Dk, Dv, dt, float(scale), _stream(dev)), "gdn_recurrent_step")
+    return o

@@ -1,0 +1,152 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: argument validation,
+// workspace layout and kernel sequencing on the caller's stream.  No device
+// memory is allocated here; every buffer belongs to the caller.
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+constexpr int kBT = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(gdn_dtype dt) { return dt == GDN_F32 || dt == GDN_BF16; }
+size_t esize(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Workspace of the chunked forward: G2 [B,H,NT,64] fp32, then (T - I)
+// [B,H,NT,64,64] fp32, each section 256-byte aligned.
+struct ChunkWs {
+    size_t g2_off, t_off, total;
+};
+
+ChunkWs chunk_ws(int B, int T, int H) {
+    const size_t NT = (size_t)(T + kBT - 1) / kBT;
+    const size_t chunks = (size_t)B * H * NT;
+    ChunkWs w;
+    w.g2_off = 0;
+    w.t_off = align_up(chunks * kBT * sizeof(float));
+    w.total = w.t_off + align_up(chunks * kBT * kBT * sizeof(float));
+    return w;
+}
+
+bool sizes_ok(int B, int T, int H) {
+    if (B < 1 || T < 1 || H < 1) return false;
+    const long long NT = (T + kBT - 1) / kBT;
+    return (long long)B * H * NT < (1LL << 31);
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head size or dtype";
+        case GDN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case GDN_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
+    if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
+    return chunk_ws(B, T, H).total;
+}
+
+gdn_status gdn_chunk_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
+                           int T, int H, int Dk, gdn_dtype dtype, void *stream) {
+    if (!k || !g || !beta || !G2 || !Tinv) return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    return from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, dtype == GDN_BF16,
+                                      (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
+                         gdn_dtype dtype, float scale, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
+    const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es};
+    const Range rg{g, ntok * 4}, rb{beta, ntok * 4}, rh0{h0, h0 ? nstate : 0};
+    const Range ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0};
+    const ChunkWs lay = chunk_ws(B, T, H);
+    const Range rws{ws, lay.total};
+    // Outputs may not overlap inputs, each other or the workspace; ht may be exactly h0.
+    for (Range in : {rq, rk, rv, rg, rb, rh0, rws})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    if (ht) {
+        if (overlap(rht, rh0) && ht != h0) return GDN_ERR_INVALID_ARG;
+        for (Range in : {rq, rk, rv, rg, rb, ro, rws})
+            if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
+    }
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    for (Range in : {rq, rk, rv, rg, rb, rh0})
+        if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
+
+    hipStream_t st = (hipStream_t)stream;
+    float *G2 = (float *)((char *)ws + lay.g2_off);
+    float *Tinv = (float *)((char *)ws + lay.t_off);
+    gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, dtype == GDN_BF16, st));
+    if (s != GDN_OK) return s;
+    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, Dk, Dv, dtype == GDN_BF16,
+                                     scale, st));
+}
+
+size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
+    (void)B; (void)T; (void)H; (void)Dk; (void)Dv; (void)dtype;
+    return 0;
+}
+
+gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                          const void *w, const float *h0, float *o, float *ht, int B, int T, int H, int Dk,
+                          int Dv, gdn_dtype dtype, float scale, void *ws, size_t ws_bytes, void *stream) {
+    (void)q; (void)k; (void)v; (void)log_alpha; (void)b; (void)w; (void)h0; (void)o; (void)ht;
+    (void)B; (void)T; (void)H; (void)Dk; (void)Dv; (void)dtype; (void)scale; (void)ws; (void)ws_bytes;
+    (void)stream;
+    return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              float *S, float *o, int B, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
+                              void *stream) {
+    if (!q || !k || !v || !g || !beta || !S || !o) return GDN_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || (long long)B * H * (Dv / 64 > 0 ? Dv / 64 : 1) >= (1LL << 31))
+        return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t nh = (size_t)B * H;
+    const Range rS{S, nh * Dk * Dv * 4}, ro{o, nh * Dv * 4};
+    const Range rq{q, nh * Dk * es}, rk{k, nh * Dk * es}, rv{v, nh * Dv * es}, rg{g, nh * 4}, rb{beta, nh * 4};
+    for (Range in : {rq, rk, rv, rg, rb, ro})
+        if (overlap(rS, in)) return GDN_ERR_INVALID_ARG;
+    for (Range in : {rq, rk, rv, rg, rb})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_step(q, k, v, g, beta, S, o, B, H, Dk, Dv, dtype == GDN_BF16, scale,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

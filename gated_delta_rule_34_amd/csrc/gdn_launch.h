@@ -1,0 +1,20 @@
+// gdn_launch.h -- host-side launch functions of the gfx950 kernels (internal;
+// the public boundary is include/gdn.h).  Each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gdn {
+
+hipError_t launch_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
+                        int T, int H, int Dk, bool bf16, hipStream_t st);
+
+hipError_t launch_walk(const void *q, const void *k, const void *v, const float *beta, const float *G2,
+                       const float *Tinv, const float *h0, float *o, float *ht, int B, int T, int H,
+                       int Dk, int Dv, bool bf16, float scale, hipStream_t st);
+
+hipError_t launch_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                       float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
+                       hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,136 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library.
+ *
+ * The operation (per independent (batch b, head h) pair, tokens t = 0..T-1):
+ *
+ *   Gated DeltaNet ("GatedDeltaNet walkthrough", yfxerp.com, section
+ *   "Delta Rule: predict first, then correct" -- the recurrence and the
+ *   per-token reference loop):
+ *       S_t = (I - beta_t k_t k_t^T) exp(g_t) S_{t-1} + beta_t k_t v_t^T
+ *       o_t = scale * S_t^T q_t          (read-out after the update)
+ *   S_t is d_k x d_v (key rows, value columns).  The forward is evaluated in
+ *   64-token chunks through the WY form (same article, section on the
+ *   chunked Triton kernels: block size 64, one state matrix carried between
+ *   blocks, the gate cumsum scaled by log2(e) for exp2).
+ *
+ *   Gated DeltaNet-2 ("NVIDIA AI lanza Gated DeltaNet-2", 7minutos.es,
+ *   section "Regla-2 del Delta cerrado"):
+ *       S_t = (I - k_t (b_t . k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T
+ *   with per-key-channel decay alpha_t = exp(log_alpha_t), erase gate b_t
+ *   (key channels) and write gate w_t (value channels); same read-out.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *     row-major and densely packed in the layouts stated per argument.
+ *     The caller owns every buffer (inputs, outputs, workspace); the library
+ *     never allocates device memory and keeps no per-call state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  Inputs must stay valid
+ *     until the stream has executed the work.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call returns a status and touches no memory.  A failed
+ *     launch returns GDN_ERR_HIP.  Nothing is thrown across the ABI.
+ *   - `dtype` is the element type of q, k, v (and GDN-2's b, w):
+ *     GDN_F32 (fp32) or GDN_BF16 (bf16).  Gates (g, beta, log_alpha), the
+ *     state (h0, ht, S) and the output o are always fp32.
+ *   - Supported head sizes: Dk, Dv in {64, 128}.  B, T, H >= 1.  Any T
+ *     (the last chunk may be partial).  Offsets are 64-bit.
+ *   - g and log_alpha are log-decays and must be finite and <= 0; positive
+ *     values are accepted but not guaranteed (exp2 of a positive difference
+ *     may overflow).  beta, b, w are expected in [0, 1].
+ *   - Results are bitwise reproducible for identical inputs, sizes and device.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad alias */
+    GDN_ERR_UNSUPPORTED = 2,  /* head size or dtype not built */
+    GDN_ERR_WORKSPACE = 3,    /* workspace null, misaligned or too small */
+    GDN_ERR_HIP = 4           /* a HIP launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *gdn_status_string(gdn_status s);
+
+/* Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 only if
+ * the sizes are invalid).  The workspace must be 256-byte aligned. */
+size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
+
+/*
+ * gdn_chunk_fwd -- chunked Gated DeltaNet forward.
+ *   q, k   [B, T, H, Dk]  dtype          queries / keys (the pages L2-normalise them
+ *                                         upstream; not required here)
+ *   v      [B, T, H, Dv]  dtype          values
+ *   g      [B, T, H]      fp32           log-decay per token-head (exp(g) in (0, 1])
+ *   beta   [B, T, H]      fp32           write strength
+ *   h0     [B, H, Dk, Dv] fp32, nullable initial state (NULL = zeros)
+ *   o      [B, T, H, Dv]  fp32           output, fully overwritten
+ *   ht     [B, H, Dk, Dv] fp32, nullable final state; may alias h0 exactly
+ *   scale  read-out scale (1/sqrt(Dk) in the pages' layer)
+ *   ws, ws_bytes  device workspace of at least gdn_chunk_fwd_workspace(...) bytes
+ * No other aliasing between arguments is allowed.
+ */
+gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0,
+                         float *o, float *ht,
+                         int B, int T, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_chunk_intra -- the per-chunk, state-independent stage of gdn_chunk_fwd,
+ * exposed for stage-wise checks.  For chunk c = 0..NT-1 (NT = ceil(T/64)) of
+ * head (b, h), with tokens past T treated as k = 0, g = 0, beta = 0:
+ *   G2    [B, H, NT, 64]      fp32  log2(e) * chunk-local cumsum of g
+ *   Tinv  [B, H, NT, 64, 64]  fp32  (I + A)^-1 - I, A_ij = beta_i (k_i . k_j)
+ *                                   2^(G2_i - G2_j) for i > j, else 0
+ *                                   (strictly lower triangular; upper part 0)
+ */
+gdn_status gdn_chunk_intra(const void *k, const float *g, const float *beta,
+                           float *G2, float *Tinv,
+                           int B, int T, int H, int Dk, gdn_dtype dtype, void *stream);
+
+/* Bytes of workspace gdn2_chunk_fwd needs (256-byte aligned buffer). */
+size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
+
+/*
+ * gdn2_chunk_fwd -- chunked Gated DeltaNet-2 forward.
+ *   q, k       [B, T, H, Dk] dtype;  v [B, T, H, Dv] dtype
+ *   log_alpha  [B, T, H, Dk] fp32    per-key-channel log-decay (alpha = exp(log_alpha))
+ *   b          [B, T, H, Dk] dtype   erase gate (key channels)
+ *   w          [B, T, H, Dv] dtype   write gate (value channels)
+ *   h0, o, ht, scale, ws, ws_bytes, stream: as gdn_chunk_fwd.
+ */
+gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
+                          const float *log_alpha, const void *b, const void *w,
+                          const float *h0, float *o, float *ht,
+                          int B, int T, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_recurrent_step -- one decode token of Gated DeltaNet, state updated in
+ * place (the per-token loop of the walkthrough's "Delta Rule" section):
+ *   S <- exp(g) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = scale S^T q
+ *   q, k [B, H, Dk] dtype;  v [B, H, Dv] dtype;  g, beta [B, H] fp32
+ *   S    [B, H, Dk, Dv] fp32, read and written in place
+ *   o    [B, H, Dv] fp32
+ */
+gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, float *S, float *o,
+                              int B, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every function include/gdn.h declares, and
+rejects bad arguments on the host before touching the GPU (these calls pass
+fake, never-dereferenced device addresses and need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_34_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdn.lib_path), reason="libgdn.so not built")
+
+FAKE = 0x7F0000000000  # 256-aligned, never dereferenced by the validation paths
+NULL = None
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn\w*)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_intra",
+              "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gdn.lib_path)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings():
+    assert gdn.status_string(0) == "ok"
+    for c in range(1, 5):
+        assert gdn.status_string(c) not in ("ok", "unknown status")
+
+
+def _p(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def _chunk(lib, q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), g=FAKE + (3 << 32), beta=FAKE + (4 << 32),
+           h0=None, o=FAKE + (5 << 32), ht=FAKE + (6 << 32), B=2, T=100, H=3, Dk=128, Dv=128, dt=1,
+           ws=FAKE + (7 << 32), ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, dt)
+    return lib.gdn_chunk_fwd(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(o), _p(ht), B, T, H, Dk, Dv, dt,
+                             0.1, _p(ws), ws_bytes, None)
+
+
+def test_workspace_size():
+    lib = gdn.load()
+    n = lib.gdn_chunk_fwd_workspace(2, 100, 3, 128, 128, 1)
+    NT = 2
+    assert n >= 2 * 3 * NT * 64 * 4 + 2 * 3 * NT * 64 * 64 * 4
+    assert n % 256 == 0
+    assert lib.gdn_chunk_fwd_workspace(0, 100, 3, 128, 128, 1) == 0
+    assert lib.gdn_chunk_fwd_workspace(2, 100, 3, 96, 128, 1) == 0
+
+
+def test_chunk_fwd_rejects_bad_arguments():
+    lib = gdn.load()
+    assert _chunk(lib, q=NULL) == 1
+    assert _chunk(lib, o=NULL) == 1
+    assert _chunk(lib, B=0) == 1
+    assert _chunk(lib, T=0) == 1
+    assert _chunk(lib, H=-1) == 1
+    assert _chunk(lib, Dk=96, ws_bytes=1 << 30) == 2
+    assert _chunk(lib, Dv=32, ws_bytes=1 << 30) == 2
+    assert _chunk(lib, dt=7, ws_bytes=1 << 30) == 2
+    assert _chunk(lib, ws=NULL) == 3
+    assert _chunk(lib, ws=FAKE + (7 << 32) + 4) == 3                 # misaligned
+    assert _chunk(lib, ws_bytes=1024) == 3                          # too small
+    assert _chunk(lib, o=FAKE) == 1                                  # o overlaps q
+    assert _chunk(lib, ht=FAKE + (5 << 32)) == 1                     # ht overlaps o
+    assert _chunk(lib, h0=FAKE + (8 << 32), ht=FAKE + (8 << 32) + 256) == 1   # partial alias
+
+
+def test_step_and_intra_reject_bad_arguments():
+    lib = gdn.load()
+    f = lambda *a: lib.gdn_recurrent_step(*[_p(x) for x in a[:7]], *a[7:], 0.1, None)
+    base = [FAKE + (i << 32) for i in range(7)]
+    assert f(*base[:6], None, 4, 2, 128, 128, 1) == 1
+    assert f(*base, 0, 2, 128, 128, 1) == 1
+    assert f(*base, 4, 2, 100, 128, 1) == 2
+    assert f(*base[:5], base[0], base[6], 4, 2, 128, 128, 1) == 1   # S overlaps q
+    assert lib.gdn_chunk_intra(None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 1, 64, 1, 128, 1, None) == 1
+    assert lib.gdn_chunk_intra(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 1, 64, 1, 48, 1, None) == 2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "lib_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.load()

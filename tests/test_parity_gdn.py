@@ -1,0 +1,203 @@
+"""GPU parity of the chunked Gated DeltaNet forward (gdn_chunk_fwd through the
+C ABI) against the fp64 oracle, element by element on the same seeded inputs.
+
+Tolerance (max|diff| / rms(oracle), for o and for the final state):
+1e-4 on the fp32-input path, 2e-2 on the bf16-input path."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_34_amd as gdn
+import gdn_inputs as gi
+import oracle
+from oracle import chunked
+from tests.gpu_util import TOL, dev, gdn_dev_args, gdn_ref_args, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, **kw):
+    o, ht = gdn.gdn_chunk_fwd(*gdn_dev_args(x), scale=x["scale"], **kw)
+    return host(o), host(ht)
+
+
+def _check(x, o, S, ref=None):
+    if ref is None:
+        ref = oracle.gdn_fwd(*gdn_ref_args(x), scale=x["scale"])
+    eo, es = rel_err(o, ref[0]), rel_err(S, ref[1])
+    tol = TOL[x["dtype"]]
+    assert eo <= tol and es <= tol, f"o err {eo:.3e}, S err {es:.3e}, tol {tol}"
+    return eo, es
+
+
+def test_tiny_fp32_workload():
+    """B=1 H=2 T=256 d=64, fp32 inputs (the small measured workload), full compare."""
+    x = gi.workload("tiny_fp32")
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_head_sizes_ragged(dtype, Dk, Dv):
+    x = gi.gdn_inputs(2, 200, 3, Dk, Dv, seed=31 + Dk + Dv, dtype=dtype, h0=True)
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129, 200])
+def test_sequence_lengths(T):
+    for dtype in ("fp32", "bf16"):
+        x = gi.gdn_inputs(1, T, 2, 128, 128, seed=100 + T, dtype=dtype, h0=True)
+        o, S = _run(x)
+        _check(x, o, S)
+
+
+def test_layer_shape_reduced_bf16():
+    """Layer-shaped bf16 case (d=128) at reduced batch and length: 5 chunks + tail."""
+    x = gi.gdn_inputs(2, 300, 4, 128, 128, seed=1001, dtype="bf16")
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_weak_decay_exercises_state_carry():
+    """A ~ U(0.001, 0.01): the state survives many chunks, so a wrong carry shows."""
+    x = gi.gdn_inputs(2, 640, 2, 128, 128, seed=55, dtype="bf16", h0=True, a_range=(0.001, 0.01))
+    o, S = _run(x)
+    _check(x, o, S)
+    x = gi.gdn_inputs(1, 320, 2, 64, 64, seed=56, dtype="fp32", h0=True, a_range=(0.001, 0.01))
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_no_decay_pure_delta_rule():
+    for dtype in ("fp32", "bf16"):
+        x = gi.gdn_inputs(1, 256, 2, 128, 128, seed=57, dtype=dtype, h0=True)
+        x["g"][:] = 0.0
+        x["g_f64"][:] = 0.0
+        o, S = _run(x)
+        _check(x, o, S)
+
+
+def test_beta0_g0_keeps_initial_state():
+    x = gi.gdn_inputs(1, 130, 2, 128, 128, seed=58, dtype="fp32", h0=True)
+    for n in ("g", "beta"):
+        x[n][:] = 0.0
+        x[n + "_f64"][:] = 0.0
+    o, S = _run(x)
+    np.testing.assert_array_equal(S, x["h0_f64"])
+    ref_o = x["scale"] * np.einsum("bthk,bhkv->bthv", x["q_f64"], x["h0_f64"])
+    assert rel_err(o, ref_o) < 1e-5
+
+
+def test_reset_token():
+    """g = -200 at one token wipes the state (exp2 underflows to 0 in fp32)."""
+    for dtype in ("fp32", "bf16"):
+        x = gi.gdn_inputs(1, 192, 2, 64, 64, seed=59, dtype=dtype, h0=True, a_range=(0.01, 0.1))
+        p = 100
+        x["g"][:, p] = -200.0
+        x["g_f64"][:, p] = -200.0
+        o, S = _run(x)
+        _check(x, o, S)
+        suffix = [x[n + "_f64"][:, p:] for n in ("q", "k", "v", "g", "beta")]
+        ref_o, ref_S = oracle.gdn_fwd(*suffix, None, scale=x["scale"])
+        assert rel_err(o[:, p:], ref_o) <= TOL[dtype]
+        assert rel_err(S, ref_S) <= TOL[dtype]
+
+
+def test_beta1_unit_keys_write_exactly():
+    """fp32 unit-norm keys and beta = 1: k_T^T S_T = v_T for the last token."""
+    x = gi.gdn_inputs(1, 100, 2, 64, 64, seed=60, dtype="fp32")
+    x["beta"][:] = 1.0
+    x["beta_f64"][:] = 1.0
+    o, S = _run(x)
+    kS = np.einsum("bhk,bhkv->bhv", x["k_f64"][:, -1], S)
+    assert np.abs(kS - x["v_f64"][:, -1]).max() < 1e-4
+    _check(x, o, S)
+
+
+def test_one_hot_keys():
+    rng = np.random.default_rng(61)
+    x = gi.gdn_inputs(1, 150, 2, 64, 64, seed=61, dtype="fp32", h0=True, a_range=(0.01, 0.5))
+    c = rng.integers(0, 64, size=(1, 150, 2))
+    k = np.zeros((1, 150, 2, 64))
+    np.put_along_axis(k, c[..., None], 1.0, axis=-1)
+    x["k"], x["k_f64"] = k.astype(np.float32), k
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_split_call_resumes():
+    """fwd(x[:T1]) -> S1, then fwd(x[T1:], h0=S1) equals fwd(x) (T1 mid-chunk)."""
+    import torch
+    x = gi.gdn_inputs(2, 300, 2, 128, 128, seed=62, dtype="bf16", h0=True)
+    q, k, v, g, beta, h0 = gdn_dev_args(x)
+    o, S = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0)
+    T1 = 100
+    oa, Sa = gdn.gdn_chunk_fwd(*[t[:, :T1].contiguous() for t in (q, k, v, g, beta)], h0)
+    ob, Sb = gdn.gdn_chunk_fwd(*[t[:, T1:].contiguous() for t in (q, k, v, g, beta)], Sa)
+    ref = oracle.gdn_fwd(*gdn_ref_args(x), scale=x["scale"])
+    assert rel_err(host(torch.cat([oa, ob], 1)), ref[0]) <= TOL["bf16"]
+    assert rel_err(host(Sb), ref[1]) <= TOL["bf16"]
+    assert rel_err(host(Sb), host(S)) <= TOL["bf16"]
+
+
+def test_final_state_may_alias_initial_state():
+    x = gi.gdn_inputs(1, 130, 2, 64, 64, seed=63, dtype="fp32", h0=True)
+    q, k, v, g, beta, h0 = gdn_dev_args(x)
+    o, S = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, scale=x["scale"], final_state=h0)
+    assert S.data_ptr() == h0.data_ptr()
+    _check(x, host(o), host(h0))
+
+
+def test_deterministic():
+    x = gi.gdn_inputs(2, 260, 4, 128, 128, seed=64, dtype="bf16", h0=True)
+    a = gdn_dev_args(x)
+    o1, S1 = gdn.gdn_chunk_fwd(*a)
+    o2, S2 = gdn.gdn_chunk_fwd(*a)
+    assert (o1 == o2).all().item() and (S1 == S2).all().item()
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_intra_stage_matches_chunk_form(dtype):
+    """gdn_chunk_intra: log2-scaled chunk cumsum and (I + A)^-1 - I per chunk,
+    against the intermediates of the fp64 chunked form."""
+    x = gi.gdn_inputs(1, 150, 2, 128, 128, seed=65, dtype=dtype, a_range=(0.05, 2.0))
+    G2, Tinv = gdn.gdn_chunk_intra(dev(x["k"]), dev(x["g"]), dev(x["beta"]))
+    G2, Tinv = host(G2), host(Tinv)
+    for h in range(2):
+        _, _, inter = chunked.gdn_chunk_head(x["q_f64"][0, :, h], x["k_f64"][0, :, h], x["v_f64"][0, :, h],
+                                             x["g_f64"][0, :, h], x["beta_f64"][0, :, h],
+                                             np.zeros((128, 128)), 1.0, keep=True)
+        for c, it in enumerate(inter):
+            n = it["T"].shape[0]
+            np.testing.assert_allclose(G2[0, h, c, :n], it["G2"], rtol=2e-6, atol=1e-5)
+            Tref = it["T"] - np.eye(n)
+            err = np.abs(Tinv[0, h, c, :n, :n] - Tref).max()
+            assert err < 1e-4 * max(1.0, np.abs(Tref).max()), err
+            assert np.abs(Tinv[0, h, c][np.triu_indices(64)]).max() == 0.0
+
+
+def test_layer_workload_full_size_sampled_heads():
+    """The measured layer workload at full size (B=8 H=8 T=4096 d=128 bf16), in
+    the launch configuration the benchmark times; the oracle checks 4 heads."""
+    x = gi.workload("layer_bf16")
+    o, S = _run(x)
+    heads = [(0, 0), (3, 5), (6, 2), (7, 7)]
+    errs = []
+    for b, h in heads:
+        sub = [None if a is None else a[b:b + 1, :, h:h + 1] for a in gdn_ref_args(x)[:5]]
+        ro, rS = oracle.gdn_fwd(*sub, None, scale=x["scale"])
+        errs.append((rel_err(o[b, :, h], ro[0, :, 0]), rel_err(S[b, h], rS[0, 0])))
+    assert max(e[0] for e in errs) <= TOL["bf16"], errs
+    assert max(e[1] for e in errs) <= TOL["bf16"], errs
+
+
+def test_long_context_full_size_sampled_heads():
+    """Long context (B=1 H=16 T=65536 d=128 bf16, h0 ~ N(0, 0.02)); oracle on 2 heads."""
+    x = gi.workload("long_bf16")
+    o, S = _run(x)
+    for h in (0, 11):
+        sub = [a[:, :, h:h + 1] for a in gdn_ref_args(x)[:5]]
+        ro, rS = oracle.gdn_fwd(*sub, x["h0_f64"][:, h:h + 1], scale=x["scale"])
+        assert rel_err(o[0, :, h], ro[0, :, 0]) <= TOL["bf16"]
+        assert rel_err(S[0, h], rS[0, 0]) <= TOL["bf16"]
