@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated delta rule forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+that is already resident in HBM: the intra-chunk stage (cumsum, A, (I+A)^-1)
+followed by the state walk (W/U applied, state carry, output) -- exactly the
+launches gdn_chunk_fwd makes, issued through the two stage entry points so
+each kernel can be timed with HIP events on the stream it runs on.
+
+Default workload: B=8, H=8, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates,
+fp32 output and state (the layer-shaped case).  Prints ONE JSON line on
+stdout; progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk_gated_delta_rule fwd tokens/s and % bf16 MFMA peak, T=4096 d=128"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA, published
+BT = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, or None when
+    no summary exists or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(a, dev):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gdn_flops_full_tile(B, T, H, Dk, Dv):
+    """Algorithmic MFMA flops of the chunked WY forward per the full-tile count:
+    2*BT*(3*Dk + 2*Dv) + 6*Dk*Dv per token-head (A, W, U, intra output products
+    and the three state products)."""
+    return float(B) * T * H * (2 * BT * (3 * Dk + 2 * Dv) + 6 * Dk * Dv)
+
+
+def walk_algorithmic_bytes(B, T, H, Dk, Dv, esz, h0):
+    """Bytes the state walk must move by definition: q, k, v (input dtype), beta,
+    o (fp32) once each, the final state (and h0) once.  The per-chunk intermediates
+    of the intra stage are not counted."""
+    per_tok = (2 * Dk + Dv) * esz + 4 + Dv * 4
+    state = B * H * Dk * Dv * 4
+    return float(B) * T * H * per_tok + state * (2 if h0 else 1)
+
+
+def cpu_baseline_gdn(x):
+    import oracle
+    names = ("q", "k", "v", "g", "beta", "h0")
+    args = [x[n + "_f64"] for n in names]
+    B, T, H = x["B"], x["T"], x["H"]
+    # sample: whole heads of the same workload, bounded to ~10-30 s of CPU work
+    t0 = time.perf_counter()
+    oracle.gdn_fwd(*[a[:1, :, :1] if a is not None else None for a in args[:5]], None)
+    per_head = max(time.perf_counter() - t0, 1e-3)
+    threads = oracle.max_threads()
+    heads = B * H
+    budget_heads = max(1, min(heads, int(20.0 * threads / per_head)))
+    nb = max(1, min(B, budget_heads // H))
+    sub = [a[:nb] if a is not None else None for a in args]
+    t0 = time.perf_counter()
+    oracle.gdn_fwd(*sub[:5], sub[5])
+    dt = time.perf_counter() - t0
+    return {"value": nb * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb} of {B} sequences x {H} heads x {T} tokens (fp64 per-token recurrence, "
+                      f"OpenMP over heads), {dt:.2f} s"}
+
+
+def bench_gdn(args, wl):
+    import numpy as np
+    import torch
+    import gated_delta_rule_34_amd as gdn
+    import gdn_inputs as gi
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    x = gi.workload(wl)
+    log(f"[bench] generated {wl} in {time.perf_counter() - t0:.1f}s")
+    B, T, H, Dk, Dv = x["B"], x["T"], x["H"], x["Dk"], x["Dv"]
+    NT = (T + BT - 1) // BT
+    base = {n: to_dev(x[n], dev) for n in ("q", "k", "v", "g", "beta", "h0")}
+    # Rotate independent buffer sets so the 256 MB Infinity Cache cannot serve
+    # a step from the previous one.
+    sets = []
+    for i in range(args.sets):
+        s = {n: (t.clone() if t is not None else None) for n, t in base.items()}
+        s["o"] = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+        s["ht"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        s["G2"] = torch.empty((B, H, NT, BT), dtype=torch.float32, device=dev)
+        s["Tinv"] = torch.empty((B, H, NT, BT, BT), dtype=torch.float32, device=dev)
+        sets.append(s)
+    scale = x["scale"]
+    fused = x["dtype"] == "bf16"   # bf16 inputs: one kernel; fp32: intra stage + walk
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, gdn.GDN_BF16 if fused else gdn.GDN_F32),
+                     dtype=torch.uint8, device=dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        if fused:
+            gdn.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], scale=scale, workspace=ws,
+                              out=s["o"], final_state=s["ht"])
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
+        gdn.gdn_chunk_intra(s["k"], s["g"], s["beta"], G2_out=s["G2"], Tinv_out=s["Tinv"])
+        if ev is not None:
+            ev[1].record()
+        gdn.gdn_chunk_walk(s["q"], s["k"], s["v"], s["beta"], s["G2"], s["Tinv"], s["h0"], scale=scale,
+                           out=s["o"], final_state=s["ht"])
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    k2_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms = wall * 1e3 / args.steps
+    if fused:
+        kernels = {"fused_kernel": k1_ms * 1e3}
+    else:
+        kernels = {"intra_kernel": k1_ms * 1e3, "walk_kernel": k2_ms * 1e3}
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step wall; per launch (HIP events): " +
+        ", ".join(f"{k} {v:.1f} us" for k, v in kernels.items()))
+
+    tokens = B * T
+    flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
+    esz = 2 if x["dtype"] == "bf16" else 4
+    has_h0 = x["h0"] is not None
+    if fused:
+        kname, kms = "fused_kernel", k1_ms
+        kbytes = walk_algorithmic_bytes(B, T, H, Dk, Dv, esz, has_h0) + 4.0 * B * T * H   # + g
+    elif k2_ms >= k1_ms:
+        kname, kms = "walk_kernel", k2_ms
+        kbytes = walk_algorithmic_bytes(B, T, H, Dk, Dv, esz, has_h0)
+    else:
+        kname, kms = "intra_kernel", k1_ms
+        kbytes = float(B) * T * H * (Dk * esz + 8 + 4) + B * H * NT * BT * BT * 4.0
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = read_traffic(kname, wl)
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if x["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
+                   "inputs": x["dtype"], "state_and_output": "fp32",
+                   "mfma": "f16 operands, fp32 accumulate" if x["dtype"] == "bf16" else "fp32",
+                   "h0": has_h0, "buffer_sets": args.sets, "parallelism": "single GPU",
+                   "kernels": "single fused kernel" if fused else "intra-chunk stage + state walk"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3,
+                     "traffic": traffic},
+        "mfma": {"algorithmic_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                 "flop_model": "full-tile 2*64*(3*Dk+2*Dv)+6*Dk*Dv per token-head"},
+        "kernels_us": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline_gdn(x)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def bench_step(args, wl):
+    import torch
+    import gated_delta_rule_34_amd as gdn
+    import gdn_inputs as gi
+    import oracle
+
+    dev = torch.device("cuda:0")
+    x = gi.workload(wl)
+    B, H, Dk, Dv = x["B"], x["H"], x["Dk"], x["Dv"]
+    base = {n: to_dev(x[n], dev) for n in ("q", "k", "v", "g", "beta", "S")}
+    sets = []
+    for i in range(args.sets):
+        s = {n: t.clone() for n, t in base.items()}
+        s["o"] = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+        sets.append(s)
+
+    def step(s):
+        gdn.gdn_recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], s["S"], scale=x["scale"], out=s["o"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = e0.elapsed_time(e1) / args.steps
+    esz = 2 if x["dtype"] == "bf16" else 4
+    kbytes = float(B) * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * esz + 8 + Dv * 4)
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    res = {
+        "metric": "gdn_recurrent_step decode tokens/s (HBM roofline), B=256 H=16 d=128",
+        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl, "B": B, "H": H, "Dk": Dk, "Dv": Dv, "inputs": x["dtype"],
+                   "state": "fp32 in place", "buffer_sets": args.sets, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "step_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": kbytes,
+                     "avg_launch_us": kms * 1e3, "traffic": read_traffic("step_kernel", wl)},
+    }
+    if not args.no_cpu_baseline:
+        args_f64 = [x[n + "_f64"] for n in ("q", "k", "v", "g", "beta", "S")]
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.gdn_step(*args_f64)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": B / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle", "sample": f"whole decode batch, {reps} repetitions in ~10 s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="layer_bf16",
+                    choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16"])
+    ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "decode_bf16":
+        res = bench_step(args, args.workload)
+    else:
+        res = bench_gdn(args, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

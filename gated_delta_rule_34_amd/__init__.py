@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "lib_path", "load", "status_string",
-    "gdn_chunk_fwd", "gdn_chunk_intra", "gdn2_chunk_fwd", "gdn_recurrent_step",
+    "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
     "GDN_F32", "GDN_BF16", "BT",
 ]
@@ -49,6 +49,8 @@ def load():
     lib.gdn_chunk_fwd.argtypes = [_vp] * 8 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_chunk_intra.restype = _i
     lib.gdn_chunk_intra.argtypes = [_vp] * 5 + [_i] * 5 + [_vp]
+    lib.gdn_chunk_walk.restype = _i
+    lib.gdn_chunk_walk.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
     lib.gdn2_chunk_fwd.restype = _i
     lib.gdn2_chunk_fwd.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_recurrent_step.restype = _i
@@ -156,9 +158,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=None, output_final_state=True
     return o, ht
 
 
-def gdn_chunk_intra(k, g, beta):
+def gdn_chunk_intra(k, g, beta, G2_out=None, Tinv_out=None):
     """State-independent chunk stage: returns (G2 [B,H,NT,64], Tinv [B,H,NT,64,64]) fp32,
-    Tinv = (I + A)^-1 - I per chunk."""
+    Tinv = (I + A)^-1 - I per chunk.  Preallocated outputs may be passed in."""
     torch = _torch()
     B, T, H, Dk = k.shape
     dev = k.device
@@ -167,11 +169,45 @@ def gdn_chunk_intra(k, g, beta):
     _need(g, "g", (B, T, H), torch.float32, dev)
     _need(beta, "beta", (B, T, H), torch.float32, dev)
     NT = (T + BT - 1) // BT
-    G2 = torch.empty((B, H, NT, BT), dtype=torch.float32, device=dev)
-    Tinv = torch.empty((B, H, NT, BT, BT), dtype=torch.float32, device=dev)
+    G2 = G2_out if G2_out is not None else torch.empty((B, H, NT, BT), dtype=torch.float32, device=dev)
+    Tinv = Tinv_out if Tinv_out is not None else torch.empty((B, H, NT, BT, BT), dtype=torch.float32, device=dev)
+    _need(G2, "G2_out", (B, H, NT, BT), torch.float32, dev)
+    _need(Tinv, "Tinv_out", (B, H, NT, BT, BT), torch.float32, dev)
     _check(load().gdn_chunk_intra(_ptr(k), _ptr(g), _ptr(beta), _ptr(G2), _ptr(Tinv), B, T, H, Dk, dt,
                                   _stream(dev)), "gdn_chunk_intra")
     return G2, Tinv
+
+
+def gdn_chunk_walk(q, k, v, beta, G2, Tinv, h0=None, scale=None, output_final_state=True, out=None,
+                   final_state=None):
+    """Sequential stage of the chunked forward on the outputs of gdn_chunk_intra.
+    Returns (o fp32, ht or None)."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    NT = (T + BT - 1) // BT
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(G2, "G2", (B, H, NT, BT), torch.float32, dev)
+    _need(Tinv, "Tinv", (B, H, NT, BT, BT), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, T, H, Dv), torch.float32, dev)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                                                                     device=dev)
+        _need(ht, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    _check(load().gdn_chunk_walk(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(G2), _ptr(Tinv), _ptr(h0), _ptr(o),
+                                 _ptr(ht), B, T, H, Dk, Dv, dt, float(scale), _stream(dev)), "gdn_chunk_walk")
+    return o, ht
 
 
 def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, h0=None, scale=None, output_final_state=True, workspace=None,

@@ -67,8 +67,11 @@ const char *gdn_status_string(gdn_status s) {
     return "unknown status";
 }
 
+// bf16 inputs take the single-kernel path, which needs no workspace; fp32
+// inputs take the two-stage path (intra-chunk stage, then the state walk).
 size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
     if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
+    if (dtype == GDN_BF16) return kAlign;
     return chunk_ws(B, T, H).total;
 }
 
@@ -93,8 +96,9 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es};
     const Range rg{g, ntok * 4}, rb{beta, ntok * 4}, rh0{h0, h0 ? nstate : 0};
     const Range ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0};
+    const bool fused = dtype == GDN_BF16;
     const ChunkWs lay = chunk_ws(B, T, H);
-    const Range rws{ws, lay.total};
+    const Range rws{fused ? nullptr : ws, lay.total};
     // Outputs may not overlap inputs, each other or the workspace; ht may be exactly h0.
     for (Range in : {rq, rk, rv, rg, rb, rh0, rws})
         if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
@@ -103,17 +107,43 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
         for (Range in : {rq, rk, rv, rg, rb, ro, rws})
             if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
     }
+    hipStream_t st = (hipStream_t)stream;
+    if (fused)
+        return from_hip(gdn::launch_fused_bf16(q, k, v, g, beta, h0, o, ht, B, T, H, Dk, Dv, scale, st));
     if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
     for (Range in : {rq, rk, rv, rg, rb, rh0})
         if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
 
-    hipStream_t st = (hipStream_t)stream;
     float *G2 = (float *)((char *)ws + lay.g2_off);
     float *Tinv = (float *)((char *)ws + lay.t_off);
     gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, dtype == GDN_BF16, st));
     if (s != GDN_OK) return s;
     return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, Dk, Dv, dtype == GDN_BF16,
                                      scale, st));
+}
+
+gdn_status gdn_chunk_walk(const void *q, const void *k, const void *v, const float *beta, const float *G2,
+                          const float *Tinv, const float *h0, float *o, float *ht, int B, int T, int H, int Dk,
+                          int Dv, gdn_dtype dtype, float scale, void *stream) {
+    if (!q || !k || !v || !beta || !G2 || !Tinv || !o) return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
+    const size_t nchunk = (size_t)B * H * ((T + kBT - 1) / kBT);
+    const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es}, rb{beta, ntok * 4};
+    const Range rg2{G2, nchunk * kBT * 4}, rt{Tinv, nchunk * kBT * kBT * 4}, rh0{h0, h0 ? nstate : 0};
+    const Range ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0};
+    for (Range in : {rq, rk, rv, rb, rg2, rt, rh0})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    if (ht) {
+        if (overlap(rht, rh0) && ht != h0) return GDN_ERR_INVALID_ARG;
+        for (Range in : {rq, rk, rv, rb, rg2, rt, ro})
+            if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
+    }
+    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, Dk, Dv, dtype == GDN_BF16,
+                                     scale, (hipStream_t)stream));
 }
 
 size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {

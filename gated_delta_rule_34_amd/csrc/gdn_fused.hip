@@ -1,0 +1,494 @@
+// gdn_fused.hip -- single-kernel chunked Gated DeltaNet forward for bf16
+// inputs on gfx950.
+//
+// One workgroup owns (batch b, head h, a 32-wide slice of value columns) and
+// walks the 64-token chunks of that head in order.  Its four waves split
+// into two roles that run concurrently on the four SIMDs of a CU:
+//
+//   consumers (waves 0, 1; 16 value columns each) -- the state chain of
+//     chunk c, with their d_k x 16 slice of the state S resident in MFMA
+//     accumulators:
+//       X = K S, Y = Q S
+//       R = diag(beta) (V - diag(gamma) X)
+//       Vnew = R + (T - I) R           (= U - W S of the WY form)
+//       O = scale (diag(gamma) Y + diag(q.k) Vnew + strict(P) Vnew)
+//       S = gamma_C S + (K . 2^(G2_C - G2))^T Vnew
+//   producers (waves 2, 3) -- everything of chunk c + 1 that does not depend
+//     on the state, written to the other half of double-buffered LDS:
+//       wave 2: the chunk-local cumsum G2 = log2(e) cumsum(g) (so each decay is
+//         one exp2 of a non-positive difference), A = strictly-lower(
+//         diag(beta) K K^T . 2^(G2_i - G2_j)) on bf16 MFMA straight from the
+//         raw inputs, and T = (I + A)^-1 -- diagonal 16x16 blocks by forward
+//         substitution (one lane per column), off-diagonal blocks by
+//         T_IJ = -T_II sum_K A_IK T_KJ on MFMA;
+//       wave 3: P = (Q K^T) . 2^(G2_i - G2_j) (causal, diagonal kept apart in
+//         fp32), the decayed keys K . 2^(G2_C - G2) transposed, V, gamma,
+//         beta, and the fp16 copies of K and Q the consumers read.
+//   Both producers keep the raw inputs of the next two chunks in registers
+//   (loads for chunk c + 2 are issued while chunk c + 1 is processed).
+//
+// Per chunk the workgroup synchronises twice: after phase 1 (consumer X, Y,
+// R, Vnew | producer A, P tiles) and after phase 2 (consumer output and
+// state carry | producer inverse and staging).  Buffers written by the
+// producers in a phase are never the ones the consumers read in it.
+//
+// Precision: products of exact bf16 inputs (K K^T, Q K^T) run on bf16 MFMA;
+// products with intermediate operands (state, new values, decayed keys,
+// T - I, P) use fp16 operands; every accumulation, the state, the diagonal
+// terms beta_i v_i and (q_i.k_i) vnew_i, and the output are fp32.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+__device__ __forceinline__ f32x4 mma_bf16_raw(f32x4 acc, const uint4 &a, const uint4 &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma_f16_block(f32x4 acc, const f16x4 &a, const f16x4 &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
+}
+
+// bf16 pair packed in a u32 -> two floats
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// The 10 lower-triangular 16x16 tiles (I >= J) of a 64x64 chunk matrix;
+// compile-time so that register arrays are indexed statically.
+__device__ constexpr int tileI(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__device__ constexpr int tileJ(int t) { return t - tileI(t) * (tileI(t) + 1) / 2; }
+
+template <int DK, int DV>
+struct FusedCfg {
+    static constexpr int BV = 32;
+    static constexpr int NS = DK / 32;   // 32-wide k slabs
+    static constexpr int NKB = DK / 16;  // 16-row blocks of the state
+    static constexpr int LDK = DK + 4;   // fp16 row stride of sK, sQ
+    static constexpr int LDKT = BT + 4;  // fp16 row stride of sKt
+    static constexpr int LDP = BT + 4;   // fp16 row stride of sP, sT, sA
+    static constexpr int LDV = BV + 8;   // bf16 row stride of sV
+};
+
+// Everything the consumers read for one chunk is double-buffered (index =
+// chunk parity), so producers fill chunk c + 1 while consumers read chunk c
+// and one barrier per chunk suffices.  A is private to the inverse producer.
+template <int DK, int DV>
+struct FusedSmem {
+    using C = FusedCfg<DK, DV>;
+    _Float16 K[2][BT * C::LDK], Q[2][BT * C::LDK];
+    _Float16 Kt[2][DK * C::LDKT];
+    _Float16 P[2][BT * C::LDP], Tm[2][BT * C::LDP];
+    uint16_t V[2][BT * C::LDV];
+    float gam[2][BT], beta[2][BT], diag[2][BT];
+    _Float16 A[BT * C::LDP];
+};
+
+// Raw inputs of one chunk held by a producer lane (lane = (g, r)):
+// k/q rows 16I + r, columns 32s + 8g .. +7 as 8 bf16 in a uint4.
+template <int NS>
+struct ChunkRegs {
+    uint4 k[4][NS];
+    uint4 q[4][NS];
+    uint4 v[4];   // V tile rows 16p + lane/4, 8 columns at (lane%4)*8
+    float g, beta;
+};
+
+struct HeadArgs {
+    const uint16_t *q, *k, *v;
+    const float *g, *beta;
+    long b;
+    int h, T, H, vcol0;
+};
+
+template <int DK>
+__device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16_t *__restrict__ src,
+                                          const HeadArgs &a, int chunk, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const int t = chunk * BT + 16 * I + r;
+        const long off = ((a.b * a.T + t) * a.H + a.h) * (long)DK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+            dst[I][s] = (t < a.T) ? *(const uint4 *)(src + off + 32 * s) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int DV>
+__device__ __forceinline__ void load_v(uint4 (&dst)[4], const HeadArgs &a, int chunk, int lane) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int t = chunk * BT + 16 * p + (lane >> 2);
+        dst[p] = (t < a.T) ? *(const uint4 *)(a.v + ((a.b * a.T + t) * a.H + a.h) * (long)DV + a.vcol0 +
+                                              (lane & 3) * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void load_gates(float &gv, float &bv, const HeadArgs &a, int chunk, int lane) {
+    const int t = chunk * BT + lane;
+    const long idx = (a.b * a.T + t) * a.H + a.h;
+    gv = (t < a.T) ? a.g[idx] : 0.f;
+    bv = (t < a.T) ? a.beta[idx] : 0.f;
+}
+
+// log2(e) * chunk-local inclusive cumsum of g, one token per lane (fp64 scan).
+__device__ __forceinline__ float chunk_g2(float gv, int lane) {
+    double x = gv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return (float)(x * 1.4426950408889634);
+}
+
+// ------------------------------------------------------- producer: A and T
+// Chunk `chunk` from registers into T - I of LDS half `buf`; issues the
+// loads of chunk `next` (if any) once the registers are free.
+template <int DK, int DV>
+__device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
+                                          const HeadArgs &ha, int lane) {
+    using C = FusedCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+    const float G2 = chunk_g2(R.g, lane);
+    // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j)), bf16 MFMA on raw inputs
+#pragma unroll
+    for (int tile = 0; tile < 10; ++tile) {
+        const int I = tileI(tile), J = tileJ(tile);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[I][s], R.k[J][s]);
+        const int j = 16 * J + r;
+        const float G2j = __shfl(G2, j, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            const float G2i = __shfl(G2, i, 64);
+            const float bi = __shfl(R.beta, i, 64);
+            sm.A[i * C::LDP + j] = (_Float16)((i > j) ? acc[e] * bi * exp2f(G2i - G2j) : 0.f);
+        }
+    }
+    if (next >= 0) {
+        load_rows<DK>(R.k, ha.k, ha, next, lane);
+        load_gates(R.g, R.beta, ha, next, lane);
+    }
+    _Float16 *Tm = sm.Tm[buf];
+    // Diagonal blocks: lane (block bb, column cc) solves its column of T_bb.
+    {
+        const int bb = lane >> 4, cc = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == cc) ? 1.f : 0.f;
+            const _Float16 *arow = &sm.A[(16 * bb + i) * C::LDP + 16 * bb];
+#pragma unroll
+            for (int j = 0; j < i; ++j) s -= (float)arow[j] * x[j];
+            x[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            Tm[(16 * bb + i) * C::LDP + 16 * bb + cc] = (_Float16)(x[i] - (i == cc ? 1.f : 0.f));
+    }
+    // Off-diagonal blocks, one sub-diagonal at a time:
+    //   T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ.
+#pragma unroll
+    for (int n = 0; n < 6; ++n) {
+        // sub-diagonal d = 1: (1,0) (2,1) (3,2); d = 2: (2,0) (3,1); d = 3: (3,0)
+        const int d = n < 3 ? 1 : n < 5 ? 2 : 3;
+        const int J = n < 3 ? n : n < 5 ? n - 3 : 0;
+        const int I = J + d;
+        f32x4 M;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) M[e] = (float)sm.A[(16 * I + 4 * g + e) * C::LDP + 16 * J + r];
+#pragma unroll
+        for (int K = J; K < I; ++K) {
+            f16x4 a, bq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = sm.A[(16 * I + r) * C::LDP + 16 * K + 4 * g + e];
+                bq[e] = Tm[(16 * K + 4 * g + e) * C::LDP + 16 * J + r];
+            }
+            M = mma_f16_block(M, a, bq);
+        }
+        f16x4 a, bq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = Tm[(16 * I + r) * C::LDP + 16 * I + 4 * g + e];
+            bq[e] = (_Float16)M[e];
+        }
+        const f32x4 res = mma_f16_block(M, a, bq);  // T_II M = M + strict(T_II) M
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * g + e) * C::LDP + 16 * J + r] = (_Float16)(-res[e]);
+    }
+}
+
+// ------------------------------------------- producer: P and consumer inputs
+template <int DK, int DV>
+__device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
+                                          const HeadArgs &ha, int lane) {
+    using C = FusedCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+    const float G2 = chunk_g2(R.g, lane);
+    const float G2L = __shfl(G2, BT - 1, 64);
+    // P tiles: lane gets P[16I + r][16J + 4g + e] = (q_i . k_j) 2^(G2_i - G2_j)
+    _Float16 *P = sm.P[buf];
+#pragma unroll
+    for (int tile = 0; tile < 10; ++tile) {
+        const int I = tileI(tile), J = tileJ(tile);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[J][s], R.q[I][s]);
+        const int i = 16 * I + r;
+        const float G2i = __shfl(G2, i, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 16 * J + 4 * g + e;
+            const float G2j = __shfl(G2, j, 64);
+            float val = 0.f;
+            if (i > j) val = acc[e] * exp2f(G2i - G2j);
+            if (i == j) sm.diag[buf][i] = acc[e];
+            P[i * C::LDP + j] = (_Float16)val;
+        }
+    }
+    // fp16 copy of Q for the consumers; then Q's registers are free
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const uint4 w = R.q[I][s];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            f16x8 hv;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                hv[2 * p] = (_Float16)bf_lo(u[p]);
+                hv[2 * p + 1] = (_Float16)bf_hi(u[p]);
+            }
+            *(f16x8 *)&sm.Q[buf][(16 * I + r) * C::LDK + 32 * s + 8 * g] = hv;
+        }
+    if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
+    // fp16 K and the decayed, transposed keys Kt[kc][j] = k_j[kc] 2^(G2_last - G2_j)
+    _Float16 *Kt = sm.Kt[buf];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const int j = 16 * I + r;
+        const float dj = exp2f(G2L - __shfl(G2, j, 64));
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const uint4 w = R.k[I][s];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            f16x8 hv;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float lo = bf_lo(u[p]), hi = bf_hi(u[p]);
+                hv[2 * p] = (_Float16)lo;
+                hv[2 * p + 1] = (_Float16)hi;
+                const int kc = 32 * s + 8 * g + 2 * p;
+                Kt[kc * C::LDKT + j] = (_Float16)(lo * dj);
+                Kt[(kc + 1) * C::LDKT + j] = (_Float16)(hi * dj);
+            }
+            *(f16x8 *)&sm.K[buf][j * C::LDK + 32 * s + 8 * g] = hv;
+        }
+    }
+    // V tile (raw bf16), gamma, beta
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
+        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
+    }
+    sm.gam[buf][lane] = exp2f(G2);
+    sm.beta[buf][lane] = R.beta;
+    if (next >= 0) {
+        load_rows<DK>(R.k, ha.k, ha, next, lane);
+        load_v<DV>(R.v, ha, next, lane);
+        load_gates(R.g, R.beta, ha, next, lane);
+    }
+}
+
+// ---------------------------------------------------------------- consumers
+template <int DK, int DV>
+__device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, float *__restrict__ o,
+                                        const HeadArgs &ha, int chunk, int wave, float scale, int lane) {
+    using C = FusedCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 X[4], Y[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        _Float16 sb[8];
+        frag_from_acc(sb, S[2 * s], S[2 * s + 1]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            _Float16 a[8];
+            frag_rows(a, sm.K[buf], C::LDK, 16 * I, 32 * s, lane);
+            X[I] = mma_slab(X[I], a, sb);
+            frag_rows(a, sm.Q[buf], C::LDK, 16 * I, 32 * s, lane);
+            Y[I] = mma_slab(Y[I], a, sb);
+        }
+    }
+    // R = beta (V - gamma X)
+    f32x4 Rr[4];
+    const int cl = wave * 16 + r;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            const float vv = __uint_as_float(((uint32_t)sm.V[buf][i * C::LDV + cl]) << 16);
+            Rr[I][e] = sm.beta[buf][i] * (vv - sm.gam[buf][i] * X[I][e]);
+        }
+    // Vnew = R + (T - I) R
+    _Float16 rf[2][8];
+    frag_from_acc(rf[0], Rr[0], Rr[1]);
+    frag_from_acc(rf[1], Rr[2], Rr[3]);
+    f32x4 Vn[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        Vn[I] = Rr[I];
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) {
+            _Float16 a[8];
+            frag_rows(a, sm.Tm[buf], C::LDP, 16 * I, 32 * s, lane);
+            Vn[I] = mma_slab(Vn[I], a, rf[s]);
+        }
+    }
+    // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew)
+    _Float16 vf[2][8];
+    frag_from_acc(vf[0], Vn[0], Vn[1]);
+    frag_from_acc(vf[1], Vn[2], Vn[3]);
+    const int t0 = chunk * BT;
+    const int col = ha.vcol0 + cl;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            acc[e] = sm.gam[buf][i] * Y[I][e] + sm.diag[buf][i] * Vn[I][e];
+        }
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) {
+            _Float16 a[8];
+            frag_rows(a, sm.P[buf], C::LDP, 16 * I, 32 * s, lane);
+            acc = mma_slab(acc, a, vf[s]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 16 * I + 4 * g + e;
+            if (t < ha.T) o[((ha.b * ha.T + t) * ha.H + ha.h) * (long)DV + col] = scale * acc[e];
+        }
+    }
+    // S = gamma_C S + Kdecayed^T Vnew
+    const float gl = sm.gam[buf][BT - 1];
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m) {
+        f32x4 acc = S[m] * gl;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            _Float16 a[8];
+            frag_rows(a, sm.Kt[buf], C::LDKT, 16 * m, 32 * s, lane);
+            acc = mma_slab(acc, a, vf[s]);
+        }
+        S[m] = acc;
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ k,
+                                                       const uint16_t *__restrict__ v,
+                                                       const float *__restrict__ gin,
+                                                       const float *__restrict__ betain,
+                                                       const float *__restrict__ h0, float *__restrict__ o,
+                                                       float *__restrict__ ht, int T, int H, int NT, float scale) {
+    using C = FusedCfg<DK, DV>;
+    static_assert(sizeof(FusedSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ FusedSmem<DK, DV> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    constexpr int NTILE = DV / C::BV;
+    // Workgroup n runs on XCD n % 8; give the slices of one head consecutive
+    // ids on one XCD so they share its L2 for K and Q.
+    const int n = blockIdx.x, nwg = gridDim.x;
+    const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
+    const int vt = L % NTILE;
+    const long bh = L / NTILE;
+    HeadArgs ha;
+    ha.q = q; ha.k = k; ha.v = v; ha.g = gin; ha.beta = betain;
+    ha.h = (int)(bh % H);
+    ha.b = bh / H;
+    ha.T = T; ha.H = H;
+    ha.vcol0 = vt * C::BV;
+
+    // The upper tiles (0,1) and (2,3) of P and T - I are read by the 32-wide
+    // slabs of the consumers but never written: zero them once.
+    for (int idx = tid; idx < 2 * BT * C::LDP; idx += 256) {
+        (&sm.P[0][0])[idx] = (_Float16)0.f;
+        (&sm.Tm[0][0])[idx] = (_Float16)0.f;
+    }
+
+    f32x4 S[C::NKB];
+    ChunkRegs<C::NS> R;
+    const long sbase = bh * (long)DK * DV;
+    if (wave < 2) {
+        const int col = ha.vcol0 + wave * 16 + r;
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
+    } else {
+        load_rows<DK>(R.k, k, ha, 0, lane);
+        load_gates(R.g, R.beta, ha, 0, lane);
+        if (wave == 3) {
+            load_rows<DK>(R.q, q, ha, 0, lane);
+            load_v<DV>(R.v, ha, 0, lane);
+        }
+    }
+    __syncthreads();
+    // Iteration c: consumers walk chunk c (LDS half c & 1); producers prepare
+    // chunk c + 1 (LDS half (c + 1) & 1) and fetch chunk c + 2.
+    for (int c = -1; c < NT; ++c) {
+        if (wave < 2) {
+            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, scale, lane);
+        } else if (c + 1 < NT) {
+            const int next = (c + 2 < NT) ? c + 2 : -1;
+            if (wave == 2) produce_T(sm, R, (c + 1) & 1, next, ha, lane);
+            else produce_P(sm, R, (c + 1) & 1, next, ha, lane);
+        }
+        __syncthreads();
+    }
+    if (wave < 2 && ht) {
+        const int col = ha.vcol0 + wave * 16 + r;
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_fused_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                 const float *h0, float *o, float *ht, int B, int T, int H, float scale,
+                                 hipStream_t st) {
+    const int NT = (T + BT - 1) / BT;
+    const long grid = (long)B * H * (DV / FusedCfg<DK, DV>::BV);
+    hipLaunchKernelGGL((fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, o, ht, T, H, NT, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
+                             float scale, hipStream_t st) {
+    if (Dk == 64 && Dv == 64) return launch_fused_t<64, 64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
+    if (Dk == 64 && Dv == 128) return launch_fused_t<64, 128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
+    if (Dk == 128 && Dv == 64) return launch_fused_t<128, 64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
+    if (Dk == 128 && Dv == 128) return launch_fused_t<128, 128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -13,6 +13,11 @@ hipError_t launch_walk(const void *q, const void *k, const void *v, const float 
                        const float *Tinv, const float *h0, float *o, float *ht, int B, int T, int H,
                        int Dk, int Dv, bool bf16, float scale, hipStream_t st);
 
+// Single-kernel chunked forward for bf16 inputs (no workspace).
+hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                             const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
+                             float scale, hipStream_t st);
+
 hipError_t launch_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                        hipStream_t st);

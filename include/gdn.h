@@ -63,7 +63,10 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 const char *gdn_status_string(gdn_status s);
 
 /* Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 only if
- * the sizes are invalid).  The workspace must be 256-byte aligned. */
+ * the sizes are invalid).  The workspace must be 256-byte aligned.  bf16
+ * inputs run as one kernel and use no workspace (ws may then be NULL);
+ * fp32 inputs run the two stages below and keep their per-chunk results
+ * (G2, Tinv) in the workspace. */
 size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
 
 /*
@@ -98,6 +101,20 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
 gdn_status gdn_chunk_intra(const void *k, const float *g, const float *beta,
                            float *G2, float *Tinv,
                            int B, int T, int H, int Dk, gdn_dtype dtype, void *stream);
+
+/*
+ * gdn_chunk_walk -- the sequential stage of gdn_chunk_fwd: given the
+ * per-chunk G2 and Tinv that gdn_chunk_intra produced for the same k, g,
+ * beta, walk the chunks in order carrying the state and write o and ht.
+ * gdn_chunk_intra followed by gdn_chunk_walk on one stream enqueues exactly
+ * the work of gdn_chunk_fwd.  Argument meanings as in gdn_chunk_fwd;
+ * G2 [B, H, NT, 64] and Tinv [B, H, NT, 64, 64] are read only.
+ */
+gdn_status gdn_chunk_walk(const void *q, const void *k, const void *v, const float *beta,
+                          const float *G2, const float *Tinv, const float *h0,
+                          float *o, float *ht,
+                          int B, int T, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
+                          void *stream);
 
 /* Bytes of workspace gdn2_chunk_fwd needs (256-byte aligned buffer). */
 size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);

@@ -58,7 +58,8 @@ def _chunk(lib, q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), g=FAKE + (3 << 3
 
 def test_workspace_size():
     lib = gdn.load()
-    n = lib.gdn_chunk_fwd_workspace(2, 100, 3, 128, 128, 1)
+    assert lib.gdn_chunk_fwd_workspace(2, 100, 3, 128, 128, 1) == 256   # bf16: single kernel
+    n = lib.gdn_chunk_fwd_workspace(2, 100, 3, 128, 128, 0)
     NT = 2
     assert n >= 2 * 3 * NT * 64 * 4 + 2 * 3 * NT * 64 * 64 * 4
     assert n % 256 == 0
@@ -76,9 +77,9 @@ def test_chunk_fwd_rejects_bad_arguments():
     assert _chunk(lib, Dk=96, ws_bytes=1 << 30) == 2
     assert _chunk(lib, Dv=32, ws_bytes=1 << 30) == 2
     assert _chunk(lib, dt=7, ws_bytes=1 << 30) == 2
-    assert _chunk(lib, ws=NULL) == 3
-    assert _chunk(lib, ws=FAKE + (7 << 32) + 4) == 3                 # misaligned
-    assert _chunk(lib, ws_bytes=1024) == 3                          # too small
+    assert _chunk(lib, ws=NULL, dt=0) == 3                           # fp32 path needs a workspace
+    assert _chunk(lib, ws=FAKE + (7 << 32) + 4, dt=0) == 3           # misaligned
+    assert _chunk(lib, ws_bytes=1024, dt=0) == 3                     # too small
     assert _chunk(lib, o=FAKE) == 1                                  # o overlaps q
     assert _chunk(lib, ht=FAKE + (5 << 32)) == 1                     # ht overlaps o
     assert _chunk(lib, h0=FAKE + (8 << 32), ht=FAKE + (8 << 32) + 256) == 1   # partial alias

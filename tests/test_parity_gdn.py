@@ -201,3 +201,24 @@ def test_long_context_full_size_sampled_heads():
         ro, rS = oracle.gdn_fwd(*sub, x["h0_f64"][:, h:h + 1], scale=x["scale"])
         assert rel_err(o[0, :, h], ro[0, :, 0]) <= TOL["bf16"]
         assert rel_err(S[0, h], rS[0, 0]) <= TOL["bf16"]
+
+
+def test_staged_entry_points_equal_fused_call():
+    """fp32: gdn_chunk_intra + gdn_chunk_walk enqueue exactly the work of gdn_chunk_fwd."""
+    x = gi.gdn_inputs(2, 200, 3, 128, 128, seed=66, dtype="fp32", h0=True)
+    q, k, v, g, beta, h0 = gdn_dev_args(x)
+    o1, S1 = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0)
+    G2, Tinv = gdn.gdn_chunk_intra(k, g, beta)
+    o2, S2 = gdn.gdn_chunk_walk(q, k, v, beta, G2, Tinv, h0)
+    assert (o1 == o2).all().item() and (S1 == S2).all().item()
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128)])
+def test_staged_bf16_path_parity(Dk, Dv):
+    """The two-stage path on bf16 inputs (gdn_chunk_fwd itself runs the single
+    kernel for bf16) also matches the oracle."""
+    x = gi.gdn_inputs(2, 200, 3, Dk, Dv, seed=67, dtype="bf16", h0=True)
+    q, k, v, g, beta, h0 = gdn_dev_args(x)
+    G2, Tinv = gdn.gdn_chunk_intra(k, g, beta)
+    o, S = gdn.gdn_chunk_walk(q, k, v, beta, G2, Tinv, h0)
+    _check(x, host(o), host(S))
