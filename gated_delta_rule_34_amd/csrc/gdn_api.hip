@@ -146,18 +146,68 @@ gdn_status gdn_chunk_walk(const void *q, const void *k, const void *v, const flo
                                      scale, (hipStream_t)stream));
 }
 
+// Workspace of the GDN-2 forward, per chunk of each head: Ehat, Qhat, Khat
+// [64, Dk] in the MFMA operand type (fp16 for bf16 inputs, else fp32),
+// Gamma_C [Dk], T - I and strict P [64, 64], diag P [64], all fp32; each
+// array 256-byte aligned.
+struct Gdn2Ws {
+    size_t e_off, q_off, k_off, gam_off, t_off, p_off, d_off, total;
+};
+
+Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
+    const size_t NT = (size_t)(T + kBT - 1) / kBT;
+    const size_t chunks = (size_t)B * H * NT;
+    const size_t mts = dt == GDN_BF16 ? 2 : 4;
+    Gdn2Ws w;
+    size_t off = 0;
+    w.e_off = off; off += align_up(chunks * kBT * Dk * mts);
+    w.q_off = off; off += align_up(chunks * kBT * Dk * mts);
+    w.k_off = off; off += align_up(chunks * kBT * Dk * mts);
+    w.gam_off = off; off += align_up(chunks * Dk * 4);
+    w.t_off = off; off += align_up(chunks * kBT * kBT * 4);
+    w.p_off = off; off += align_up(chunks * kBT * kBT * 4);
+    w.d_off = off; off += align_up(chunks * kBT * 4);
+    w.total = off;
+    return w;
+}
+
 size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
-    (void)B; (void)T; (void)H; (void)Dk; (void)Dv; (void)dtype;
-    return 0;
+    if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
+    return gdn2_ws(B, T, H, Dk, dtype).total;
 }
 
 gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
                           const void *w, const float *h0, float *o, float *ht, int B, int T, int H, int Dk,
                           int Dv, gdn_dtype dtype, float scale, void *ws, size_t ws_bytes, void *stream) {
-    (void)q; (void)k; (void)v; (void)log_alpha; (void)b; (void)w; (void)h0; (void)o; (void)ht;
-    (void)B; (void)T; (void)H; (void)Dk; (void)Dv; (void)dtype; (void)scale; (void)ws; (void)ws_bytes;
-    (void)stream;
-    return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
+    const Gdn2Ws lay = gdn2_ws(B, T, H, Dk, dtype);
+    const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es};
+    const Range rla{log_alpha, ntok * Dk * 4}, rb{b, ntok * Dk * es}, rw{w, ntok * Dv * es};
+    const Range rh0{h0, h0 ? nstate : 0}, ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0}, rws{ws, lay.total};
+    for (Range in : {rq, rk, rv, rla, rb, rw, rh0, rws})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    if (ht) {
+        if (overlap(rht, rh0) && ht != h0) return GDN_ERR_INVALID_ARG;
+        for (Range in : {rq, rk, rv, rla, rb, rw, ro, rws})
+            if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
+    }
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    for (Range in : {rq, rk, rv, rla, rb, rw, rh0})
+        if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char *base = (char *)ws;
+    void *E = base + lay.e_off, *Qh = base + lay.q_off, *Kh = base + lay.k_off;
+    float *Gam = (float *)(base + lay.gam_off), *Tinv = (float *)(base + lay.t_off);
+    float *P = (float *)(base + lay.p_off), *D = (float *)(base + lay.d_off);
+    const bool bf = dtype == GDN_BF16;
+    gdn_status s = from_hip(gdn::launch_gdn2_intra(q, k, log_alpha, b, E, Qh, Kh, Gam, Tinv, P, D, B, T, H, Dk, bf, st));
+    if (s != GDN_OK) return s;
+    return from_hip(gdn::launch_gdn2_walk(E, Qh, Kh, Gam, Tinv, P, D, v, w, h0, o, ht, B, T, H, Dk, Dv, bf, scale, st));
 }
 
 gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

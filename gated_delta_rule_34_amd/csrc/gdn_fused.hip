@@ -78,12 +78,18 @@ struct FusedCfg {
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
-    _Float16 K[2][BT * C::LDK], Q[2][BT * C::LDK];
-    _Float16 Kt[2][DK * C::LDKT];
-    _Float16 P[2][BT * C::LDP], Tm[2][BT * C::LDP];
-    uint16_t V[2][BT * C::LDV];
-    float gam[2][BT], beta[2][BT], diag[2][BT];
-    _Float16 A[BT * C::LDP];
+    alignas(16) _Float16 K[2][BT * C::LDK];
+    alignas(16) _Float16 Q[2][BT * C::LDK];
+    alignas(16) _Float16 Kt[2][DK * C::LDKT];
+    alignas(16) _Float16 P[2][BT * C::LDP];
+    alignas(16) _Float16 Tm[2][BT * C::LDP];
+    alignas(16) uint16_t V[2][BT * C::LDV];
+    alignas(16) float gam[2][BT];
+    alignas(16) float beta[2][BT];
+    alignas(16) float diag[2][BT];
+    alignas(16) _Float16 A[BT * C::LDP];
+    alignas(16) float g2T[BT], betaT[BT];  // gate tables private to the inverse producer
+    alignas(16) float g2P[BT];             // ... and to the P producer
 };
 
 // Raw inputs of one chunk held by a producer lane (lane = (g, r)):
@@ -107,13 +113,16 @@ template <int DK>
 __device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16_t *__restrict__ src,
                                           const HeadArgs &a, int chunk, int lane) {
     const int r = lane & 15, g = lane >> 4;
+    const bool full = (chunk + 1) * BT <= a.T;
+    const long rowstride = (long)a.H * DK;
+    const uint16_t *base = src + ((a.b * a.T + chunk * BT + r) * a.H + a.h) * (long)DK + 8 * g;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const int t = chunk * BT + 16 * I + r;
-        const long off = ((a.b * a.T + t) * a.H + a.h) * (long)DK + 8 * g;
+        const uint16_t *p = base + 16 * I * rowstride;
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s)
-            dst[I][s] = (t < a.T) ? *(const uint4 *)(src + off + 32 * s) : make_uint4(0, 0, 0, 0);
+            dst[I][s] = (full || t < a.T) ? *(const uint4 *)(p + 32 * s) : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -154,7 +163,17 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    const float G2 = chunk_g2(R.g, lane);
+    sm.g2T[lane] = chunk_g2(R.g, lane);
+    sm.betaT[lane] = R.beta;
+    // this lane's rows i = 16I + 4g + e and columns j = 16J + r of every tile
+    f32x4 rowG2[4], rowB[4];
+    float colG2[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        rowG2[I] = *(const f32x4 *)&sm.g2T[16 * I + 4 * g];
+        rowB[I] = *(const f32x4 *)&sm.betaT[16 * I + 4 * g];
+        colG2[I] = sm.g2T[16 * I + r];
+    }
     // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j)), bf16 MFMA on raw inputs
 #pragma unroll
     for (int tile = 0; tile < 10; ++tile) {
@@ -163,13 +182,11 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[I][s], R.k[J][s]);
         const int j = 16 * J + r;
-        const float G2j = __shfl(G2, j, 64);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
-            const float G2i = __shfl(G2, i, 64);
-            const float bi = __shfl(R.beta, i, 64);
-            sm.A[i * C::LDP + j] = (_Float16)((i > j) ? acc[e] * bi * exp2f(G2i - G2j) : 0.f);
+            const float val = acc[e] * rowB[I][e] * __builtin_amdgcn_exp2f(rowG2[I][e] - colG2[J]);
+            sm.A[i * C::LDP + j] = (_Float16)((i > j) ? val : 0.f);
         }
     }
     if (next >= 0) {
@@ -233,7 +250,16 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
     const float G2 = chunk_g2(R.g, lane);
-    const float G2L = __shfl(G2, BT - 1, 64);
+    sm.g2P[lane] = G2;
+    const float G2L = sm.g2P[BT - 1];
+    // this lane's rows i = 16I + r and columns j = 16J + 4g + e of every tile
+    f32x4 colG2[4];
+    float rowG2[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        colG2[I] = *(const f32x4 *)&sm.g2P[16 * I + 4 * g];
+        rowG2[I] = sm.g2P[16 * I + r];
+    }
     // P tiles: lane gets P[16I + r][16J + 4g + e] = (q_i . k_j) 2^(G2_i - G2_j)
     _Float16 *P = sm.P[buf];
 #pragma unroll
@@ -243,16 +269,15 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[J][s], R.q[I][s]);
         const int i = 16 * I + r;
-        const float G2i = __shfl(G2, i, 64);
+        f16x4 hv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 16 * J + 4 * g + e;
-            const float G2j = __shfl(G2, j, 64);
-            float val = 0.f;
-            if (i > j) val = acc[e] * exp2f(G2i - G2j);
-            if (i == j) sm.diag[buf][i] = acc[e];
-            P[i * C::LDP + j] = (_Float16)val;
+            const float val = acc[e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            hv[e] = (_Float16)((i > j) ? val : 0.f);
+            if (I == J && i == j) sm.diag[buf][i] = acc[e];
         }
+        *(f16x4 *)&P[i * C::LDP + 16 * J + 4 * g] = hv;
     }
     // fp16 copy of Q for the consumers; then Q's registers are free
 #pragma unroll
@@ -275,7 +300,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const int j = 16 * I + r;
-        const float dj = exp2f(G2L - __shfl(G2, j, 64));
+        const float dj = __builtin_amdgcn_exp2f(G2L - rowG2[I]);
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
             const uint4 w = R.k[I][s];
@@ -299,7 +324,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
         *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
     }
-    sm.gam[buf][lane] = exp2f(G2);
+    sm.gam[buf][lane] = __builtin_amdgcn_exp2f(G2);
     sm.beta[buf][lane] = R.beta;
     if (next >= 0) {
         load_rows<DK>(R.k, ha.k, ha, next, lane);
@@ -331,16 +356,19 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         }
     }
     // R = beta (V - gamma X)
-    f32x4 Rr[4];
+    f32x4 Rr[4], gam[4];
     const int cl = wave * 16 + r;
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I) {
+        gam[I] = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
+        const f32x4 bet = *(const f32x4 *)&sm.beta[buf][16 * I + 4 * g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
             const float vv = __uint_as_float(((uint32_t)sm.V[buf][i * C::LDV + cl]) << 16);
-            Rr[I][e] = sm.beta[buf][i] * (vv - sm.gam[buf][i] * X[I][e]);
+            Rr[I][e] = bet[e] * (vv - gam[I][e] * X[I][e]);
         }
+    }
     // Vnew = R + (T - I) R
     _Float16 rf[2][8];
     frag_from_acc(rf[0], Rr[0], Rr[1]);
@@ -362,14 +390,15 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     frag_from_acc(vf[1], Vn[2], Vn[3]);
     const int t0 = chunk * BT;
     const int col = ha.vcol0 + cl;
+    const bool full = t0 + BT <= ha.T;
+    float *obase = o + ((ha.b * ha.T + t0) * ha.H + ha.h) * (long)DV + col;
+    const long ostride = (long)ha.H * DV;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         f32x4 acc;
+        const f32x4 dg = *(const f32x4 *)&sm.diag[buf][16 * I + 4 * g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * g + e;
-            acc[e] = sm.gam[buf][i] * Y[I][e] + sm.diag[buf][i] * Vn[I][e];
-        }
+        for (int e = 0; e < 4; ++e) acc[e] = gam[I][e] * Y[I][e] + dg[e] * Vn[I][e];
 #pragma unroll
         for (int s = 0; s <= (I >> 1); ++s) {
             _Float16 a[8];
@@ -378,8 +407,8 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 16 * I + 4 * g + e;
-            if (t < ha.T) o[((ha.b * ha.T + t) * ha.H + ha.h) * (long)DV + col] = scale * acc[e];
+            const int ti = 16 * I + 4 * g + e;
+            if (full || t0 + ti < ha.T) obase[ti * ostride] = scale * acc[e];
         }
     }
     // S = gamma_C S + Kdecayed^T Vnew
@@ -431,42 +460,49 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
         (&sm.Tm[0][0])[idx] = (_Float16)0.f;
     }
 
-    f32x4 S[C::NKB];
-    ChunkRegs<C::NS> R;
     const long sbase = bh * (long)DK * DV;
+    // Each role runs its own loop with the same barrier count (one per
+    // iteration), so the registers of one role are never live in another.
+    // Iteration c: consumers walk chunk c (LDS half c & 1); producers prepare
+    // chunk c + 1 (LDS half (c + 1) & 1) and fetch chunk c + 2.
     if (wave < 2) {
+        f32x4 S[C::NKB];
         const int col = ha.vcol0 + wave * 16 + r;
 #pragma unroll
         for (int m = 0; m < C::NKB; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
-    } else {
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, scale, lane);
+            __syncthreads();
+        }
+        if (ht) {
+#pragma unroll
+            for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+        }
+    } else if (wave == 2) {
+        ChunkRegs<C::NS> R;
         load_rows<DK>(R.k, k, ha, 0, lane);
         load_gates(R.g, R.beta, ha, 0, lane);
-        if (wave == 3) {
-            load_rows<DK>(R.q, q, ha, 0, lane);
-            load_v<DV>(R.v, ha, 0, lane);
-        }
-    }
-    __syncthreads();
-    // Iteration c: consumers walk chunk c (LDS half c & 1); producers prepare
-    // chunk c + 1 (LDS half (c + 1) & 1) and fetch chunk c + 2.
-    for (int c = -1; c < NT; ++c) {
-        if (wave < 2) {
-            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, scale, lane);
-        } else if (c + 1 < NT) {
-            const int next = (c + 2 < NT) ? c + 2 : -1;
-            if (wave == 2) produce_T(sm, R, (c + 1) & 1, next, ha, lane);
-            else produce_P(sm, R, (c + 1) & 1, next, ha, lane);
-        }
         __syncthreads();
-    }
-    if (wave < 2 && ht) {
-        const int col = ha.vcol0 + wave * 16 + r;
-#pragma unroll
-        for (int m = 0; m < C::NKB; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+        for (int c = -1; c < NT; ++c) {
+            if (c + 1 < NT) produce_T(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, lane);
+            __syncthreads();
+        }
+    } else {
+        ChunkRegs<C::NS> R;
+        load_rows<DK>(R.k, k, ha, 0, lane);
+        load_rows<DK>(R.q, q, ha, 0, lane);
+        load_v<DV>(R.v, ha, 0, lane);
+        load_gates(R.g, R.beta, ha, 0, lane);
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c + 1 < NT) produce_P(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, lane);
+            __syncthreads();
+        }
     }
 }
 

@@ -18,6 +18,17 @@ hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const 
                              const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
                              float scale, hipStream_t st);
 
+// Gated DeltaNet-2, two stages: per-chunk prepared operands (decayed e, q
+// and k; Gamma_C; T - I; strict P; diag P), then the state walk.
+hipError_t launch_gdn2_intra(const void *q, const void *k, const float *la, const void *bg, void *Ehat, void *Qhat,
+                             void *Khat, float *GamC, float *Tinv, float *P, float *D, int B, int T, int H, int Dk,
+                             bool bf16, hipStream_t st);
+
+hipError_t launch_gdn2_walk(const void *Ehat, const void *Qhat, const void *Khat, const float *GamC,
+                            const float *Tinv, const float *P, const float *D, const void *v, const void *wg,
+                            const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv, bool bf16,
+                            float scale, hipStream_t st);
+
 hipError_t launch_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                        hipStream_t st);

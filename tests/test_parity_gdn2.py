@@ -1,0 +1,124 @@
+"""GPU parity of the chunked Gated DeltaNet-2 forward (gdn2_chunk_fwd through
+the C ABI) against the fp64 oracle, element by element on the same seeded
+inputs.  Tolerance (max|diff| / rms(oracle), o and final state): 1e-4 on the
+fp32-input path, 2e-2 on the bf16-input path."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_34_amd as gdn
+import gdn_inputs as gi
+import oracle
+from tests.gpu_util import TOL, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "log_alpha", "b", "w", "h0")
+
+
+def _run(x):
+    o, ht = gdn.gdn2_chunk_fwd(*[dev(x[n]) for n in NAMES], scale=x["scale"])
+    return host(o), host(ht)
+
+
+def _ref(x):
+    return oracle.gdn2_fwd(*[x[n + "_f64"] for n in NAMES], scale=x["scale"])
+
+
+def _check(x, o, S):
+    ro, rS = _ref(x)
+    eo, es = rel_err(o, ro), rel_err(S, rS)
+    tol = TOL[x["dtype"]]
+    assert eo <= tol and es <= tol, f"o err {eo:.3e}, S err {es:.3e}, tol {tol}"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_head_sizes_ragged(dtype, Dk, Dv):
+    x = gi.gdn2_inputs(2, 200, 2, Dk, Dv, seed=200 + Dk + Dv, dtype=dtype, h0=True)
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+@pytest.mark.parametrize("T", [1, 16, 63, 64, 65, 130])
+def test_sequence_lengths(T):
+    for dtype in ("fp32", "bf16"):
+        x = gi.gdn2_inputs(1, T, 2, 128, 128, seed=300 + T, dtype=dtype, h0=True)
+        o, S = _run(x)
+        _check(x, o, S)
+
+
+def test_weak_decay():
+    x = gi.gdn2_inputs(2, 512, 2, 128, 128, seed=301, dtype="bf16", h0=True)
+    x["log_alpha"] = (x["log_alpha"] * 0.01).astype(np.float32)
+    x["log_alpha_f64"] = x["log_alpha"].astype(np.float64)
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_tied_gates_equal_gdn():
+    """b = w = beta and log_alpha = g on every channel: GDN-2 is Gated DeltaNet
+    (Gated DeltaNet-2 article, 7minutos.es, section 'Regla-2 del Delta cerrado')."""
+    x = gi.gdn_inputs(2, 200, 2, 64, 64, seed=302, dtype="fp32", h0=True, a_range=(0.05, 1.0))
+    B, T, H, Dk = x["q"].shape
+    la = np.repeat(x["g"][..., None], Dk, -1)
+    bb = np.repeat(x["beta"][..., None], Dk, -1)
+    ww = np.repeat(x["beta"][..., None], x["Dv"], -1)
+    o2, S2 = gdn.gdn2_chunk_fwd(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(la), dev(bb), dev(ww), dev(x["h0"]))
+    o1, S1 = gdn.gdn_chunk_fwd(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["g"]), dev(x["beta"]), dev(x["h0"]))
+    assert rel_err(host(o2), host(o1)) < 1e-4 and rel_err(host(S2), host(S1)) < 1e-4
+    ro, rS = oracle.gdn_fwd(*[x[n + "_f64"] for n in ("q", "k", "v", "g", "beta", "h0")])
+    assert rel_err(host(o2), ro) <= TOL["fp32"] and rel_err(host(S2), rS) <= TOL["fp32"]
+
+
+def test_erase_gate_one_writes_gated_value():
+    """b = 1, |k| = 1 (fp32): k_T^T S_T = (w_T . v_T)^T for the last token."""
+    x = gi.gdn2_inputs(1, 100, 2, 64, 64, seed=303, dtype="fp32")
+    x["b"][:] = 1.0
+    x["b_f64"][:] = 1.0
+    o, S = _run(x)
+    kS = np.einsum("bhk,bhkv->bhv", x["k_f64"][:, -1], S)
+    assert np.abs(kS - (x["w_f64"] * x["v_f64"])[:, -1]).max() < 1e-4
+    _check(x, o, S)
+
+
+def test_one_hot_keys():
+    rng = np.random.default_rng(304)
+    x = gi.gdn2_inputs(1, 150, 2, 64, 64, seed=304, dtype="fp32", h0=True)
+    c = rng.integers(0, 64, size=(1, 150, 2))
+    k = np.zeros((1, 150, 2, 64))
+    np.put_along_axis(k, c[..., None], 1.0, axis=-1)
+    x["k"], x["k_f64"] = k.astype(np.float32), k
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_split_call_resumes():
+    import torch
+    x = gi.gdn2_inputs(2, 300, 2, 128, 128, seed=305, dtype="bf16", h0=True)
+    a = [dev(x[n]) for n in NAMES]
+    T1 = 100
+    oa, Sa = gdn.gdn2_chunk_fwd(*[t[:, :T1].contiguous() for t in a[:6]], a[6])
+    ob, Sb = gdn.gdn2_chunk_fwd(*[t[:, T1:].contiguous() for t in a[:6]], Sa)
+    ro, rS = _ref(x)
+    assert rel_err(host(torch.cat([oa, ob], 1)), ro) <= TOL["bf16"]
+    assert rel_err(host(Sb), rS) <= TOL["bf16"]
+
+
+def test_deterministic():
+    x = gi.gdn2_inputs(2, 260, 2, 128, 128, seed=306, dtype="bf16", h0=True)
+    a = [dev(x[n]) for n in NAMES]
+    o1, S1 = gdn.gdn2_chunk_fwd(*a)
+    o2, S2 = gdn.gdn2_chunk_fwd(*a)
+    assert (o1 == o2).all().item() and (S1 == S2).all().item()
+
+
+def test_gdn2_workload_full_size_sampled_heads():
+    """The GDN-2 workload at full size (B=4 H=8 T=4096 d=128, bf16); the oracle
+    checks 3 heads."""
+    x = gi.workload("gdn2_bf16")
+    o, S = _run(x)
+    for b, h in [(0, 0), (2, 5), (3, 7)]:
+        sub = [x[n + "_f64"][b:b + 1, :, h:h + 1] for n in NAMES[:6]]
+        ro, rS = oracle.gdn2_fwd(*sub, None, scale=x["scale"])
+        assert rel_err(o[b, :, h], ro[0, :, 0]) <= TOL["bf16"]
+        assert rel_err(S[b, h], rS[0, 0]) <= TOL["bf16"]
