@@ -2,10 +2,11 @@
 """Benchmark of the chunked gated delta rule forward on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-that is already resident in HBM: the intra-chunk stage (cumsum, A, (I+A)^-1)
-followed by the state walk (W/U applied, state carry, output) -- exactly the
-launches gdn_chunk_fwd makes, issued through the two stage entry points so
-each kernel can be timed with HIP events on the stream it runs on.
+that is already resident in HBM: one gdn_chunk_fwd call (for bf16 inputs a
+single kernel: gate cumsum, A, (I+A)^-1, the WY new values, state carry and
+output), timed with HIP events on the stream it runs on.  fp32 workloads run
+the two stage entry points and time each stage.  Other workloads: the decode
+step (--workload decode_bf16) and Gated DeltaNet-2 (--workload gdn2_bf16).
 
 Default workload: B=8, H=8, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates,
 fp32 output and state (the layer-shaped case).  Prints ONE JSON line on
@@ -226,6 +227,76 @@ def bench_gdn(args, wl):
     return res
 
 
+def bench_gdn2(args, wl):
+    import torch
+    import gated_delta_rule_34_amd as gdn
+    import gdn_inputs as gi
+    import oracle
+
+    dev = torch.device("cuda:0")
+    x = gi.workload(wl)
+    B, T, H, Dk, Dv = x["B"], x["T"], x["H"], x["Dk"], x["Dv"]
+    names = ("q", "k", "v", "log_alpha", "b", "w", "h0")
+    base = {n: to_dev(x[n], dev) for n in names}
+    sets = []
+    for i in range(args.sets):
+        s = {n: (t.clone() if t is not None else None) for n, t in base.items()}
+        s["o"] = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+        s["ht"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        sets.append(s)
+    code = gdn.GDN_BF16 if x["dtype"] == "bf16" else gdn.GDN_F32
+    ws = torch.empty(gdn.gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, code), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        gdn.gdn2_chunk_fwd(*[s[n] for n in names], scale=x["scale"], workspace=ws, out=s["o"],
+                           final_state=s["ht"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = e0.elapsed_time(e1) / args.steps
+    esz = 2 if x["dtype"] == "bf16" else 4
+    # q, k, b (Dk) and v, w (Dv) in the input dtype, log_alpha fp32, o fp32, final state
+    kbytes = float(B) * T * H * ((3 * Dk + 2 * Dv) * esz + 4 * Dk + 4 * Dv) + B * H * Dk * Dv * 4.0
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
+    res = {
+        "metric": "chunk gated delta rule-2 fwd tokens/s, T=4096 d=128",
+        "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16" if esz == 2 else "f32", "data": "synthetic",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
+                   "inputs": x["dtype"], "kernels": "gdn2 intra-chunk stage + state walk",
+                   "buffer_sets": args.sets, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gdn2_intra_kernel+gdn2_walk_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3, "traffic": None},
+        "mfma": {"algorithmic_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                 "flop_model": "full-tile 2*64*(3*Dk+2*Dv)+6*Dk*Dv per token-head"},
+    }
+    if not args.no_cpu_baseline:
+        args64 = [x[n + "_f64"] for n in names]
+        nb = 1
+        t0 = time.perf_counter()
+        oracle.gdn2_fwd(*[a[:nb] if a is not None else None for a in args64[:6]], None)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": nb * T / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle",
+                               "sample": f"{nb} of {B} sequences x {H} heads x {T} tokens, {dt:.2f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def bench_step(args, wl):
     import torch
     import gated_delta_rule_34_amd as gdn
@@ -292,9 +363,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16",
-                    choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16"])
+                    choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "gdn2_bf16"])
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run one plain device copy of MIB MiB (outside the timed region) "
+                         "so that hardware byte counters can be scaled against a known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -309,8 +383,18 @@ def main():
         sys.exit(1)
     if args.workload == "decode_bf16":
         res = bench_step(args, args.workload)
+    elif args.workload == "gdn2_bf16":
+        res = bench_gdn2(args, args.workload)
     else:
         res = bench_gdn(args, args.workload)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
     print(json.dumps(res), flush=True)
 
 
