@@ -33,9 +33,11 @@
 // producers in a phase are never the ones the consumers read in it.
 //
 // Precision: products of exact bf16 inputs (K K^T, Q K^T) run on bf16 MFMA;
-// products with intermediate operands (state, new values, decayed keys,
-// T - I, P) use fp16 operands; every accumulation, the state, the diagonal
-// terms beta_i v_i and (q_i.k_i) vnew_i, and the output are fp32.
+// the state reads K S and Q S run on bf16 MFMA with the fp32 state split
+// into bf16 hi + lo parts (two products, ~16 significant bits); the other
+// products with intermediate operands (new values, decayed keys, T - I, P)
+// use fp16 operands; every accumulation, the state, the diagonal terms
+// beta_i v_i and (q_i.k_i) vnew_i, and the output are fp32.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -66,11 +68,64 @@ struct FusedCfg {
     static constexpr int BV = 32;
     static constexpr int NS = DK / 32;   // 32-wide k slabs
     static constexpr int NKB = DK / 16;  // 16-row blocks of the state
-    static constexpr int LDK = DK + 4;   // fp16 row stride of sK, sQ
-    static constexpr int LDKT = BT + 4;  // fp16 row stride of sKt
+    // sK, sQ: fp16 rows of DK halves.  With DK = 128 a row is 64 dwords, so
+    // the 4-dword column groups are XOR-swizzled by (row & 15): the 8-byte
+    // fragment reads of 16 rows x 2 column groups then hit 64 distinct banks.
+    // With DK = 64 rows are padded by 8 halves instead (4-bank row shift).
+    static constexpr bool KQ_SWZ = DK == 128;
+    static constexpr int LDK = KQ_SWZ ? DK : DK + 8;
+    static constexpr int LDKT = BT;      // fp16 row stride of sKt (swizzled by (row >> 1) & 7)
     static constexpr int LDP = BT + 4;   // fp16 row stride of sP, sT, sA
     static constexpr int LDV = BV + 8;   // bf16 row stride of sV
 };
+
+// Element offset (in halves) of column `col` (multiple of 4) of row `row` in sK / sQ.
+template <int DK, int DV>
+__device__ __forceinline__ int kq_off(int row, int col) {
+    using C = FusedCfg<DK, DV>;
+    if (C::KQ_SWZ) return row * C::LDK + (col ^ ((row & 15) << 3));
+    return row * C::LDK + col;
+}
+
+// Element offset of column `col` (multiple of 4) of row `row` in sKt: rows
+// of 64 halves (32 dwords); 4-dword groups XOR-swizzled by (row >> 1) & 7 so
+// that the 16 rows x 2 column groups of a fragment read use 32 distinct
+// 2-bank pairs per half-wave, with row parity choosing the 32-bank half.
+__device__ __forceinline__ int kt_off(int row, int col) { return row * BT + (col ^ (((row >> 1) & 7) << 3)); }
+
+// Fragment of a 32-wide slab (k-slots 4g + e and 16 + 4g + e, as in
+// frag_rows) read from a swizzled raw-bf16 matrix.
+template <int DK, int DV>
+__device__ __forceinline__ uint4 frag_rows_kq(const uint16_t *M, int row0, int k0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const uint2 lo = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 4 * g)];
+    const uint2 hi = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 16 + 4 * g)];
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// The state as two bf16 B fragments whose sum carries ~16 significant bits:
+// hi = bf16(S), lo = bf16(S - hi); both from accumulator tiles (k-blocks 2s, 2s+1).
+__device__ __forceinline__ void state_frags_hilo(bf16x8 &hi, bf16x8 &lo, const f32x4 &t0, const f32x4 &t1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h0 = (__bf16)t0[e], h1 = (__bf16)t1[e];
+        hi[e] = h0;
+        hi[e + 4] = h1;
+        lo[e] = (__bf16)(t0[e] - (float)h0);
+        lo[e + 4] = (__bf16)(t1[e] - (float)h1);
+    }
+}
+
+__device__ __forceinline__ void frag_rows_kt(_Float16 (&f)[8], const _Float16 *M, int row0, int k0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const f16x4 lo = *(const f16x4 *)&M[kt_off(row0 + r, k0 + 4 * g)];
+    const f16x4 hi = *(const f16x4 *)&M[kt_off(row0 + r, k0 + 16 + 4 * g)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = lo[e];
+        f[e + 4] = hi[e];
+    }
+}
 
 // Everything the consumers read for one chunk is double-buffered (index =
 // chunk parity), so producers fill chunk c + 1 while consumers read chunk c
@@ -78,8 +133,8 @@ struct FusedCfg {
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
-    alignas(16) _Float16 K[2][BT * C::LDK];
-    alignas(16) _Float16 Q[2][BT * C::LDK];
+    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows (swizzled, see kq_off)
+    alignas(16) uint16_t Q[2][BT * C::LDK];
     alignas(16) _Float16 Kt[2][DK * C::LDKT];
     alignas(16) _Float16 P[2][BT * C::LDP];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
@@ -144,15 +199,26 @@ __device__ __forceinline__ void load_gates(float &gv, float &bv, const HeadArgs 
     bv = (t < a.T) ? a.beta[idx] : 0.f;
 }
 
-// log2(e) * chunk-local inclusive cumsum of g, one token per lane (fp64 scan).
+// Value of `x` moved by a DPP row operation; lanes without a source get 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xf,
+                                                                 false));
+}
+
+// log2(e) * chunk-local inclusive cumsum of g, one token per lane: an fp32
+// wave scan on DPP (shifts 1, 2, 4, 8 within each row of 16 lanes, then the
+// row totals broadcast by lane 15 and lane 31), no LDS round trip.
 __device__ __forceinline__ float chunk_g2(float gv, int lane) {
-    double x = gv;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return (float)(x * 1.4426950408889634);
+    (void)lane;
+    float x = gv * 1.4426950408889634f;
+    x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
 }
 
 // ------------------------------------------------------- producer: A and T
@@ -194,63 +260,94 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         load_gates(R.g, R.beta, ha, next, lane);
     }
     _Float16 *Tm = sm.Tm[buf];
-    // Diagonal blocks: lane (block bb, column cc) solves its column of T_bb.
+    // Diagonal blocks: lane (block bb, column cc) solves its column of T_bb,
+    // x_i = [i == cc] - sum_{j<i} A_ij x_j, with four partial sums per row.
     {
         const int bb = lane >> 4, cc = lane & 15;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float s = (i == cc) ? 1.f : 0.f;
             const _Float16 *arow = &sm.A[(16 * bb + i) * C::LDP + 16 * bb];
+            f16x4 av[4];
 #pragma unroll
-            for (int j = 0; j < i; ++j) s -= (float)arow[j] * x[j];
-            x[i] = s;
+            for (int q4 = 0; q4 < 4; ++q4)
+                if (4 * q4 < i) av[q4] = *(const f16x4 *)&arow[4 * q4];
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < i; ++j) part[j & 3] = fmaf((float)av[j >> 2][j & 3], x[j], part[j & 3]);
+            x[i] = ((i == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             Tm[(16 * bb + i) * C::LDP + 16 * bb + cc] = (_Float16)(x[i] - (i == cc ? 1.f : 0.f));
     }
-    // Off-diagonal blocks, one sub-diagonal at a time:
+    // Off-diagonal blocks, one sub-diagonal level d at a time; the blocks of a
+    // level are independent and are computed together:
     //   T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ.
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
-        // sub-diagonal d = 1: (1,0) (2,1) (3,2); d = 2: (2,0) (3,1); d = 3: (3,0)
-        const int d = n < 3 ? 1 : n < 5 ? 2 : 3;
-        const int J = n < 3 ? n : n < 5 ? n - 3 : 0;
-        const int I = J + d;
-        f32x4 M;
+    for (int d = 1; d < 4; ++d) {
+        constexpr int NB_MAX = 3;
+        f32x4 M[NB_MAX];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) M[e] = (float)sm.A[(16 * I + 4 * g + e) * C::LDP + 16 * J + r];
+        for (int J = 0; J < 4 - d; ++J) {
+            const int I = J + d;
 #pragma unroll
-        for (int K = J; K < I; ++K) {
-            f16x4 a, bq;
+            for (int e = 0; e < 4; ++e) M[J][e] = (float)sm.A[(16 * I + 4 * g + e) * C::LDP + 16 * J + r];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[e] = sm.A[(16 * I + r) * C::LDP + 16 * K + 4 * g + e];
-                bq[e] = Tm[(16 * K + 4 * g + e) * C::LDP + 16 * J + r];
+            for (int K = J; K < I; ++K) {
+                const f16x4 a = *(const f16x4 *)&sm.A[(16 * I + r) * C::LDP + 16 * K + 4 * g];
+                f16x4 bq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bq[e] = Tm[(16 * K + 4 * g + e) * C::LDP + 16 * J + r];
+                M[J] = mma_f16_block(M[J], a, bq);
             }
-            M = mma_f16_block(M, a, bq);
         }
-        f16x4 a, bq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = Tm[(16 * I + r) * C::LDP + 16 * I + 4 * g + e];
-            bq[e] = (_Float16)M[e];
+        for (int J = 0; J < 4 - d; ++J) {
+            const int I = J + d;
+            const f16x4 a = *(const f16x4 *)&Tm[(16 * I + r) * C::LDP + 16 * I + 4 * g];
+            f16x4 bq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bq[e] = (_Float16)M[J][e];
+            const f32x4 res = mma_f16_block(M[J], a, bq);  // T_II M = M + strict(T_II) M
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * g + e) * C::LDP + 16 * J + r] = (_Float16)(-res[e]);
         }
-        const f32x4 res = mma_f16_block(M, a, bq);  // T_II M = M + strict(T_II) M
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * g + e) * C::LDP + 16 * J + r] = (_Float16)(-res[e]);
     }
 }
 
 // ------------------------------------------- producer: P and consumer inputs
+// Selection matrix for the MFMA transpose: as the B operand of a 32-wide
+// slab (contiguous k-slots 8g + e), column n picks k = n + 16h.
+__device__ __forceinline__ uint4 sel_bf16(int h, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = (8 * g + 2 * p == r + 16 * h) ? 0x3f80u : 0u;      // bf16 1.0
+        const uint32_t hi = (8 * g + 2 * p + 1 == r + 16 * h) ? 0x3f80u : 0u;
+        w[p] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <int DK, int DV>
 __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
+    // V tile (raw bf16) first, so its registers can be refilled early
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
+        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
+    }
+    if (next >= 0) load_v<DV>(R.v, ha, next, lane);
     const float G2 = chunk_g2(R.g, lane);
     sm.g2P[lane] = G2;
+    sm.gam[buf][lane] = __builtin_amdgcn_exp2f(G2);
+    sm.beta[buf][lane] = R.beta;
+    if (next >= 0) load_gates(R.g, R.beta, ha, next, lane);
     const float G2L = sm.g2P[BT - 1];
     // this lane's rows i = 16I + r and columns j = 16J + 4g + e of every tile
     f32x4 colG2[4];
@@ -279,58 +376,42 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         }
         *(f16x4 *)&P[i * C::LDP + 16 * J + 4 * g] = hv;
     }
-    // fp16 copy of Q for the consumers; then Q's registers are free
+    // raw bf16 copy of Q for the consumers; then Q's registers are refilled
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-            const uint4 w = R.q[I][s];
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-            f16x8 hv;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                hv[2 * p] = (_Float16)bf_lo(u[p]);
-                hv[2 * p + 1] = (_Float16)bf_hi(u[p]);
-            }
-            *(f16x8 *)&sm.Q[buf][(16 * I + r) * C::LDK + 32 * s + 8 * g] = hv;
-        }
+        for (int s = 0; s < C::NS; ++s)
+            *(uint4 *)&sm.Q[buf][kq_off<DK, DV>(16 * I + r, 32 * s + 8 * g)] = R.q[I][s];
     if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
-    // fp16 K and the decayed, transposed keys Kt[kc][j] = k_j[kc] 2^(G2_last - G2_j)
+    // Decayed keys, transposed: Kt[kc][j] = k_j[kc] 2^(G2_last - G2_j).  An
+    // MFMA against a 0/1 selection matrix hands each lane 4 consecutive rows j
+    // of one column kc, written as one 8-byte store.
     _Float16 *Kt = sm.Kt[buf];
+    const uint4 sel0 = sel_bf16(0, lane), sel1 = sel_bf16(1, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        const int j = 16 * I + r;
-        const float dj = __builtin_amdgcn_exp2f(G2L - rowG2[I]);
+        const f32x4 gj = colG2[I];  // G2 of rows 16I + 4g + e
+        f32x4 dj;
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-            const uint4 w = R.k[I][s];
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-            f16x8 hv;
+        for (int e = 0; e < 4; ++e) dj[e] = __builtin_amdgcn_exp2f(G2L - gj[e]);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float lo = bf_lo(u[p]), hi = bf_hi(u[p]);
-                hv[2 * p] = (_Float16)lo;
-                hv[2 * p + 1] = (_Float16)hi;
-                const int kc = 32 * s + 8 * g + 2 * p;
-                Kt[kc * C::LDKT + j] = (_Float16)(lo * dj);
-                Kt[(kc + 1) * C::LDKT + j] = (_Float16)(hi * dj);
+        for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const f32x4 t = mma_bf16_raw(zero4(), R.k[I][s], hh ? sel1 : sel0);
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(t[e] * dj[e]);
+                *(f16x4 *)&Kt[kt_off(32 * s + 16 * hh + r, 16 * I + 4 * g)] = hv;
             }
-            *(f16x8 *)&sm.K[buf][j * C::LDK + 32 * s + 8 * g] = hv;
-        }
     }
-    // V tile (raw bf16), gamma, beta
+    // raw bf16 copy of K; then K's registers are refilled
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
-        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
-    }
-    sm.gam[buf][lane] = __builtin_amdgcn_exp2f(G2);
-    sm.beta[buf][lane] = R.beta;
-    if (next >= 0) {
-        load_rows<DK>(R.k, ha.k, ha, next, lane);
-        load_v<DV>(R.v, ha, next, lane);
-        load_gates(R.g, R.beta, ha, next, lane);
-    }
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s)
+            *(uint4 *)&sm.K[buf][kq_off<DK, DV>(16 * I + r, 32 * s + 8 * g)] = R.k[I][s];
+    if (next >= 0) load_rows<DK>(R.k, ha.k, ha, next, lane);
 }
 
 // ---------------------------------------------------------------- consumers
@@ -339,20 +420,24 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
                                         const HeadArgs &ha, int chunk, int wave, float scale, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
+    // X = K S and Y = Q S on bf16 MFMA: exact bf16 K, Q against the state
+    // split into bf16 hi + lo parts.
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-        _Float16 sb[8];
-        frag_from_acc(sb, S[2 * s], S[2 * s + 1]);
+        bf16x8 shi, slo;
+        state_frags_hilo(shi, slo, S[2 * s], S[2 * s + 1]);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            _Float16 a[8];
-            frag_rows(a, sm.K[buf], C::LDK, 16 * I, 32 * s, lane);
-            X[I] = mma_slab(X[I], a, sb);
-            frag_rows(a, sm.Q[buf], C::LDK, 16 * I, 32 * s, lane);
-            Y[I] = mma_slab(Y[I], a, sb);
+            const uint4 ka = frag_rows_kq<DK, DV>(sm.K[buf], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_kq<DK, DV>(sm.Q[buf], 16 * I, 32 * s, lane);
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, ka), qb = __builtin_bit_cast(bf16x8, qa);
+            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, shi, X[I], 0, 0, 0);
+            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, shi, Y[I], 0, 0, 0);
+            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, slo, X[I], 0, 0, 0);
+            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, slo, Y[I], 0, 0, 0);
         }
     }
     // R = beta (V - gamma X)
@@ -419,7 +504,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             _Float16 a[8];
-            frag_rows(a, sm.Kt[buf], C::LDKT, 16 * m, 32 * s, lane);
+            frag_rows_kt(a, sm.Kt[buf], 16 * m, 32 * s, lane);
             acc = mma_slab(acc, a, vf[s]);
         }
         S[m] = acc;
