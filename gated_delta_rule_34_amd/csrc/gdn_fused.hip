@@ -68,13 +68,14 @@ struct FusedCfg {
     static constexpr int BV = 32;
     static constexpr int NS = DK / 32;   // 32-wide k slabs
     static constexpr int NKB = DK / 16;  // 16-row blocks of the state
-    // sK, sQ: fp16 rows of DK halves.  With DK = 128 a row is 64 dwords, so
-    // the 4-dword column groups are XOR-swizzled by (row & 15): the 8-byte
-    // fragment reads of 16 rows x 2 column groups then hit 64 distinct banks.
-    // With DK = 64 rows are padded by 8 halves instead (4-bank row shift).
+    // sK, sQ: raw bf16 rows of DK halves.  With DK = 128 a row is 64 dwords
+    // (all rows bank-aligned), so column groups are XOR-swizzled per row:
+    // 16-half segments by (row & 7), 8-half groups by bit 3 of the row.  The
+    // 8-byte fragment reads (16 rows x 2 column groups per half-wave) and the
+    // transpose reads of the state update (8 rows x one 16-half segment) then
+    // each cover 64 distinct banks.  With DK = 64 rows are padded instead.
     static constexpr bool KQ_SWZ = DK == 128;
     static constexpr int LDK = KQ_SWZ ? DK : DK + 8;
-    static constexpr int LDKT = BT;      // fp16 row stride of sKt (swizzled by (row >> 1) & 7)
     static constexpr int LDP = BT + 4;   // fp16 row stride of sP, sT, sA
     static constexpr int LDV = BV + 8;   // bf16 row stride of sV
 };
@@ -83,15 +84,9 @@ struct FusedCfg {
 template <int DK, int DV>
 __device__ __forceinline__ int kq_off(int row, int col) {
     using C = FusedCfg<DK, DV>;
-    if (C::KQ_SWZ) return row * C::LDK + (col ^ ((row & 15) << 3));
+    if (C::KQ_SWZ) return row * C::LDK + (col ^ (((row & 7) << 4) ^ (((row >> 3) & 1) << 3)));
     return row * C::LDK + col;
 }
-
-// Element offset of column `col` (multiple of 4) of row `row` in sKt: rows
-// of 64 halves (32 dwords); 4-dword groups XOR-swizzled by (row >> 1) & 7 so
-// that the 16 rows x 2 column groups of a fragment read use 32 distinct
-// 2-bank pairs per half-wave, with row parity choosing the 32-bank half.
-__device__ __forceinline__ int kt_off(int row, int col) { return row * BT + (col ^ (((row >> 1) & 7) << 3)); }
 
 // Fragment of a 32-wide slab (k-slots 4g + e and 16 + 4g + e, as in
 // frag_rows) read from a swizzled raw-bf16 matrix.
@@ -101,6 +96,27 @@ __device__ __forceinline__ uint4 frag_rows_kq(const uint16_t *M, int row0, int k
     const uint2 lo = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 4 * g)];
     const uint2 hi = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 16 + 4 * g)];
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// A fragment of K^T for the state update, read from the row-major raw bf16
+// K tile with the gfx950 LDS transpose load: within each 16-lane group, lane
+// j receives element (j % 4) of the 8-byte chunks addressed by lanes j/4,
+// j/4 + 4, j/4 + 8, j/4 + 12.  Lane (g, r) therefore addresses row
+// j0 + 4g + r/4, columns kc0 + 4(r % 4), and receives K[j0 + 4g + e][kc0 + r],
+// e = 0..3: the A-operand slots of rows kc0 + r of K^T.  Two such loads
+// (j0 and j0 + 16) make the 32-wide slab.
+template <int DK, int DV>
+__device__ __forceinline__ uint4 frag_kT(const uint16_t *M, int j0, int kc0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint16_t *p0 = &M[kq_off<DK, DV>(j0 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
+    const uint16_t *p1 = &M[kq_off<DK, DV>(j0 + 16 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
 }
 
 // The state as two bf16 B fragments whose sum carries ~16 significant bits:
@@ -116,16 +132,6 @@ __device__ __forceinline__ void state_frags_hilo(bf16x8 &hi, bf16x8 &lo, const f
     }
 }
 
-__device__ __forceinline__ void frag_rows_kt(_Float16 (&f)[8], const _Float16 *M, int row0, int k0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    const f16x4 lo = *(const f16x4 *)&M[kt_off(row0 + r, k0 + 4 * g)];
-    const f16x4 hi = *(const f16x4 *)&M[kt_off(row0 + r, k0 + 16 + 4 * g)];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[e] = lo[e];
-        f[e + 4] = hi[e];
-    }
-}
 
 // Everything the consumers read for one chunk is double-buffered (index =
 // chunk parity), so producers fill chunk c + 1 while consumers read chunk c
@@ -135,13 +141,13 @@ struct FusedSmem {
     using C = FusedCfg<DK, DV>;
     alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows (swizzled, see kq_off)
     alignas(16) uint16_t Q[2][BT * C::LDK];
-    alignas(16) _Float16 Kt[2][DK * C::LDKT];
     alignas(16) _Float16 P[2][BT * C::LDP];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
     alignas(16) uint16_t V[2][BT * C::LDV];
     alignas(16) float gam[2][BT];
     alignas(16) float beta[2][BT];
     alignas(16) float diag[2][BT];
+    alignas(16) float dk[2][BT];              // 2^(G2_last - G2_j): decay of key j to the chunk end
     alignas(16) _Float16 A[BT * C::LDP];
     alignas(16) float g2T[BT], betaT[BT];  // gate tables private to the inverse producer
     alignas(16) float g2P[BT];             // ... and to the P producer
@@ -317,20 +323,6 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 }
 
 // ------------------------------------------- producer: P and consumer inputs
-// Selection matrix for the MFMA transpose: as the B operand of a 32-wide
-// slab (contiguous k-slots 8g + e), column n picks k = n + 16h.
-__device__ __forceinline__ uint4 sel_bf16(int h, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = (8 * g + 2 * p == r + 16 * h) ? 0x3f80u : 0u;      // bf16 1.0
-        const uint32_t hi = (8 * g + 2 * p + 1 == r + 16 * h) ? 0x3f80u : 0u;
-        w[p] = lo | (hi << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 template <int DK, int DV>
 __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
                                           const HeadArgs &ha, int lane) {
@@ -349,6 +341,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     sm.beta[buf][lane] = R.beta;
     if (next >= 0) load_gates(R.g, R.beta, ha, next, lane);
     const float G2L = sm.g2P[BT - 1];
+    sm.dk[buf][lane] = __builtin_amdgcn_exp2f(G2L - G2);
     // this lane's rows i = 16I + r and columns j = 16J + 4g + e of every tile
     f32x4 colG2[4];
     float rowG2[4];
@@ -383,28 +376,6 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         for (int s = 0; s < C::NS; ++s)
             *(uint4 *)&sm.Q[buf][kq_off<DK, DV>(16 * I + r, 32 * s + 8 * g)] = R.q[I][s];
     if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
-    // Decayed keys, transposed: Kt[kc][j] = k_j[kc] 2^(G2_last - G2_j).  An
-    // MFMA against a 0/1 selection matrix hands each lane 4 consecutive rows j
-    // of one column kc, written as one 8-byte store.
-    _Float16 *Kt = sm.Kt[buf];
-    const uint4 sel0 = sel_bf16(0, lane), sel1 = sel_bf16(1, lane);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const f32x4 gj = colG2[I];  // G2 of rows 16I + 4g + e
-        f32x4 dj;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dj[e] = __builtin_amdgcn_exp2f(G2L - gj[e]);
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const f32x4 t = mma_bf16_raw(zero4(), R.k[I][s], hh ? sel1 : sel0);
-                f16x4 hv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(t[e] * dj[e]);
-                *(f16x4 *)&Kt[kt_off(32 * s + 16 * hh + r, 16 * I + 4 * g)] = hv;
-            }
-    }
     // raw bf16 copy of K; then K's registers are refilled
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -496,16 +467,31 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             if (full || t0 + ti < ha.T) obase[ti * ostride] = scale * acc[e];
         }
     }
-    // S = gamma_C S + Kdecayed^T Vnew
+    // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =
+    // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
+    // straight from the raw K tile by transpose loads, and d . Vnew enters as
+    // bf16 hi + lo parts.
+    bf16x8 dvh[2], dvl[2];
+    {
+        f32x4 dv[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 dd = *(const f32x4 *)&sm.dk[buf][16 * I + 4 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[I][e] = dd[e] * Vn[I][e];
+        }
+        state_frags_hilo(dvh[0], dvl[0], dv[0], dv[1]);
+        state_frags_hilo(dvh[1], dvl[1], dv[2], dv[3]);
+    }
     const float gl = sm.gam[buf][BT - 1];
 #pragma unroll
     for (int m = 0; m < C::NKB; ++m) {
         f32x4 acc = S[m] * gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            _Float16 a[8];
-            frag_rows_kt(a, sm.Kt[buf], 16 * m, 32 * s, lane);
-            acc = mma_slab(acc, a, vf[s]);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, frag_kT<DK, DV>(sm.K[buf], 32 * s, 16 * m, lane));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dvh[s], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dvl[s], acc, 0, 0, 0);
         }
         S[m] = acc;
     }
