@@ -237,14 +237,15 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     const int r = lane & 15, g = lane >> 4;
     sm.g2T[lane] = chunk_g2(R.g, lane);
     sm.betaT[lane] = R.beta;
-    // this lane's rows i = 16I + 4g + e and columns j = 16J + r of every tile
-    f32x4 rowG2[4], rowB[4];
-    float colG2[4];
+    // K_J K_I^T: this lane gets row i = 16I + r and columns j = 16J + 4g + e
+    // of every tile, stored as 4 adjacent halves
+    float rowG2[4], rowB[4];
+    f32x4 colG2[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        rowG2[I] = *(const f32x4 *)&sm.g2T[16 * I + 4 * g];
-        rowB[I] = *(const f32x4 *)&sm.betaT[16 * I + 4 * g];
-        colG2[I] = sm.g2T[16 * I + r];
+        rowG2[I] = sm.g2T[16 * I + r];
+        rowB[I] = sm.betaT[16 * I + r];
+        colG2[I] = *(const f32x4 *)&sm.g2T[16 * I + 4 * g];
     }
     // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j)), bf16 MFMA on raw inputs
 #pragma unroll
@@ -252,14 +253,16 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         const int I = tileI(tile), J = tileJ(tile);
         f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[I][s], R.k[J][s]);
-        const int j = 16 * J + r;
+        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[J][s], R.k[I][s]);
+        const int i = 16 * I + r;
+        f16x4 hv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * g + e;
-            const float val = acc[e] * rowB[I][e] * __builtin_amdgcn_exp2f(rowG2[I][e] - colG2[J]);
-            sm.A[i * C::LDP + j] = (_Float16)((i > j) ? val : 0.f);
+            const int j = 16 * J + 4 * g + e;
+            const float val = acc[e] * rowB[I] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            hv[e] = (_Float16)((i > j) ? val : 0.f);
         }
+        *(f16x4 *)&sm.A[i * C::LDP + 16 * J + 4 * g] = hv;
     }
     if (next >= 0) {
         load_rows<DK>(R.k, ha.k, ha, next, lane);
