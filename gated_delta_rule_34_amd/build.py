@@ -24,11 +24,18 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-file extras.  The fused kernel keeps its MFMA accumulators in
+# architectural VGPRs (it fits in 256 without spilling); the default
+# accumulator-register form makes the compiler copy the state between the
+# two register files around every VALU step.
+FILE_FLAGS = {
+    "gdn_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str, resource_usage: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)

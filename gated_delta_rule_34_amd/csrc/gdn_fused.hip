@@ -121,15 +121,27 @@ __device__ __forceinline__ uint4 frag_kT(const uint16_t *M, int j0, int kc0, int
 
 // The state as two bf16 B fragments whose sum carries ~16 significant bits:
 // hi = bf16(S), lo = bf16(S - hi); both from accumulator tiles (k-blocks 2s, 2s+1).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// hi = bf16(x), lo = bf16(x - hi) for a pair of floats, on the packed
+// round-to-nearest conversion.
+__device__ __forceinline__ void split_pair(bf16x2 &h, bf16x2 &l, float a, float b) {
+    const f32x2 x = {a, b};
+    h = __builtin_convertvector(x, bf16x2);
+    l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), bf16x2);
+}
+
 __device__ __forceinline__ void state_frags_hilo(bf16x8 &hi, bf16x8 &lo, const f32x4 &t0, const f32x4 &t1) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h0 = (__bf16)t0[e], h1 = (__bf16)t1[e];
-        hi[e] = h0;
-        hi[e + 4] = h1;
-        lo[e] = (__bf16)(t0[e] - (float)h0);
-        lo[e + 4] = (__bf16)(t1[e] - (float)h1);
-    }
+    bf16x2 h[4], l[4];
+    split_pair(h[0], l[0], t0[0], t0[1]);
+    split_pair(h[1], l[1], t0[2], t0[3]);
+    split_pair(h[2], l[2], t1[0], t1[1]);
+    split_pair(h[3], l[3], t1[2], t1[3]);
+    hi = __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
+                                 __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    lo = __builtin_shufflevector(__builtin_shufflevector(l[0], l[1], 0, 1, 2, 3),
+                                 __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 
