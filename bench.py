@@ -39,7 +39,9 @@ def log(*a):
 
 def source_sha() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc", "*"))):
+    files = sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "gated_delta_rule_34_amd", "build.py"))  # compile flags shape the kernels too
+    for p in files:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
