@@ -24,12 +24,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-# Per-file extras.  The fused kernel keeps its MFMA accumulators in
-# architectural VGPRs (it fits in 256 without spilling); the default
+# Per-file extras.  The fused kernels keep their MFMA accumulators in
+# architectural VGPRs (they fit in 256 without spilling); the default
 # accumulator-register form makes the compiler copy the state between the
 # two register files around every VALU step.
 FILE_FLAGS = {
     "gdn_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gdn2_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

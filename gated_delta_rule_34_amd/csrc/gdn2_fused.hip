@@ -1,0 +1,525 @@
+// gdn2_fused.hip -- chunked Gated DeltaNet-2 forward for bf16 inputs on
+// gfx950, in two kernels.
+//
+// Recurrence (Gated DeltaNet-2 article, "Regla-2 del Delta cerrado"): per
+// token, S <- Diag(alpha) S, u = w . v - S^T (b . k), S <- S + k u^T, and the
+// readout o = scale S^T q.  Chunk form over 64 tokens, with the chunk-local
+// per-channel log-decay sums G_i = sum_{s<=i} log alpha_s and Gamma_i = e^{G_i}
+// (the chunked-training section of the same article: the channel decay is
+// absorbed into both factors of each product):
+//   A_ij = sum_c b_ic k_ic k_jc e^{G_ic - G_jc}        (j < i)
+//   P_ij = sum_c q_ic k_jc e^{G_ic - G_jc}             (j <= i)
+//   Vnew = (I + A)^-1 (w . V - Ehat S),   Ehat_i = Gamma_i . b_i . k_i
+//   O    = scale (Qhat S + P Vnew),       Qhat_i = Gamma_i . q_i
+//   S'   = Diag(Gamma_C) S + Khat^T Vnew, Khat_j = k_j . Gamma_C / Gamma_j
+//
+// prep kernel (one workgroup per (batch, head, chunk), all chunks in
+// parallel): the cumsum, Ehat, Qhat, Khat, Gamma_C, T - I = (I + A)^-1 - I and
+// the strict and diagonal parts of P, written as one block per chunk.
+//   Off-diagonal 16x16 blocks of A and P are fp16 MFMA products of factors
+//   anchored at the first row a of the block row: (x_i e^{G_i - G_a}) and
+//   (k_j e^{G_a - G_j}), both at most 1 in size since j < a <= i.  Diagonal
+//   blocks have no such anchor and are summed exactly on the VALU.
+// walk kernel (one workgroup per (batch, head, 32 value columns)): two
+//   consumer waves carry the state in registers through the chunks, two
+//   loader waves stage the next chunk's block and value slices into LDS.
+//
+// Precision: Ehat, Qhat, Khat, T - I and P are fp16; the state enters K S and
+// Q S as fp16 hi + lo parts and Vnew enters the state update the same way;
+// accumulation, the state and the output are fp32.  fp16 operands bound the
+// state entries below 65504.
+#include "gdn_launch.h"
+#include "gdn_tile.h"
+
+namespace gdn {
+
+// Per-chunk block of the workspace (all offsets in bytes, 256-aligned total).
+template <int DK>
+struct Gdn2Blk {
+    static constexpr int E = 0;                       // fp16 [64][DK]
+    static constexpr int Q = E + BT * DK * 2;         // fp16 [64][DK]
+    static constexpr int K = Q + BT * DK * 2;         // fp16 [64][DK]
+    static constexpr int TM = K + BT * DK * 2;        // fp16 [64][64], T - I (lower tiles)
+    static constexpr int PM = TM + BT * BT * 2;       // fp16 [64][64], strict lower P
+    static constexpr int DG = PM + BT * BT * 2;       // fp32 [64], P_ii = q_i . k_i
+    static constexpr int GAM = DG + BT * 4;           // fp32 [DK], Gamma_C
+    static constexpr int BYTES = (GAM + DK * 4 + 255) / 256 * 256;
+};
+
+size_t gdn2_fused_block_bytes(int Dk) { return Dk == 64 ? Gdn2Blk<64>::BYTES : Gdn2Blk<128>::BYTES; }
+
+
+// --------------------------------------------------------------- prep kernel
+template <int DK>
+struct Gdn2PrepSmem {
+    static constexpr int LDR = DK + 8;   // raw bf16 rows
+    static constexpr int LDG = DK + 4;   // fp32 rows of G2
+    static constexpr int LDP = BT + 8;   // fp16 rows of A, T - I, P
+    alignas(16) uint16_t k[BT * LDR];
+    alignas(16) uint16_t q[BT * LDR];
+    alignas(16) uint16_t b[BT * LDR];
+    alignas(16) float G2[BT * LDG];      // log2(e) * chunk-local cumsum of log alpha
+    alignas(16) float half[2][DK];       // cumsum of rows 0..31 (scan of two halves)
+    alignas(16) _Float16 A[BT * LDP];
+    alignas(16) _Float16 Tm[BT * LDP];
+    alignas(16) _Float16 P[BT * LDP];
+    alignas(16) float dg[BT];
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                         const float *__restrict__ la, const uint16_t *__restrict__ bg,
+                                                         char *__restrict__ ws, int T, int H, int NT) {
+    using SM = Gdn2PrepSmem<DK>;
+    using BL = Gdn2Blk<DK>;
+    constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP;
+    constexpr int C8 = DK / 8;  // uint4 per row of a raw tile
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const long cb = blockIdx.x;
+    const int c = (int)(cb % NT);
+    const long bh = cb / NT;
+    const int h = (int)(bh % H);
+    const long bb = bh / H;
+    const int t0 = c * BT;
+    const long row0 = (bb * T + t0) * H + h;  // token-head row of the chunk's first token
+    char *blk = ws + cb * (long)BL::BYTES;
+
+    // 1. raw rows (zero past T) and the per-channel cumsum of log alpha
+    for (int u = tid; u < BT * C8; u += 256) {
+        const int row = u / C8, c8 = u % C8;
+        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv, bv = kv;
+        if (t0 + row < T) {
+            const long off = (row0 + (long)row * H) * DK + 8 * c8;
+            kv = *(const uint4 *)(k + off);
+            qv = *(const uint4 *)(q + off);
+            bv = *(const uint4 *)(bg + off);
+        }
+        *(uint4 *)&sm.k[row * LDR + 8 * c8] = kv;
+        *(uint4 *)&sm.q[row * LDR + 8 * c8] = qv;
+        *(uint4 *)&sm.b[row * LDR + 8 * c8] = bv;
+    }
+    {
+        // thread (half hf, channel ch) scans rows 32 hf .. 32 hf + 31 of its channel
+        const int ch = tid % DK, hf = tid / DK;  // DK = 128: 2 halves; DK = 64: 4 quarters, two of them idle
+        if (hf < 2) {
+            float acc = 0.f;
+            for (int i = 0; i < 32; ++i) {
+                const int row = 32 * hf + i;
+                const float x = (t0 + row < T) ? la[(row0 + (long)row * H) * DK + ch] : 0.f;
+                acc += x * 1.4426950408889634f;
+                sm.G2[row * LDG + ch] = acc;
+            }
+            sm.half[hf][ch] = acc;
+        }
+    }
+    __syncthreads();
+    for (int u = tid; u < 32 * DK; u += 256) {
+        const int row = 32 + u / DK, ch = u % DK;
+        sm.G2[row * LDG + ch] += sm.half[0][ch];
+    }
+    __syncthreads();
+
+    // 2. decayed operands and Gamma_C
+    for (int u = tid; u < BT * C8; u += 256) {
+        const int row = u / C8, c0 = 8 * (u % C8);
+        const uint4 kv = *(const uint4 *)&sm.k[row * LDR + c0];
+        const uint4 qv = *(const uint4 *)&sm.q[row * LDR + c0];
+        const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
+        const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
+        f16x8 eo, qo, ko;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
+            const float gam = __builtin_amdgcn_exp2f(G);
+            const float kf = bf16_to_f32(kk[e]);
+            eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
+            qo[e] = (_Float16)(bf16_to_f32(qq[e]) * gam);
+            ko[e] = (_Float16)(kf * __builtin_amdgcn_exp2f(GL - G));
+        }
+        const long o = ((long)row * DK + c0) * 2;
+        *(f16x8 *)(blk + BL::E + o) = eo;
+        *(f16x8 *)(blk + BL::Q + o) = qo;
+        *(f16x8 *)(blk + BL::K + o) = ko;
+    }
+    for (int ch = tid; ch < DK; ch += 256)
+        ((float *)(blk + BL::GAM))[ch] = __builtin_amdgcn_exp2f(sm.G2[(BT - 1) * LDG + ch]);
+    // the upper tiles of T - I and P are never written below
+    for (int u = tid; u < BT * LDP; u += 256) {
+        sm.Tm[u] = (_Float16)0.f;
+        sm.P[u] = (_Float16)0.f;
+    }
+    __syncthreads();
+
+    // 3. off-diagonal blocks (I > J) of A and P on fp16 MFMA, anchored at
+    //    a = 16 I; lane gets [16I + 4g + e][16J + r]
+    for (int t = wave; t < 6; t += 4) {
+        const int I = t < 1 ? 1 : t < 3 ? 2 : 3;
+        const int J = t < 1 ? 0 : t < 3 ? t - 1 : t - 3;
+        const int a = 16 * I, i = 16 * I + r, j = 16 * J + r;
+        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            f16x8 fe, fq, fk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
+                const float Ga = sm.G2[a * LDG + cc];
+                const float ri = __builtin_amdgcn_exp2f(sm.G2[i * LDG + cc] - Ga);
+                const float kj = __builtin_amdgcn_exp2f(Ga - sm.G2[j * LDG + cc]);
+                const float ki = bf16_to_f32(sm.k[i * LDR + cc]);
+                fe[e] = (_Float16)(bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri);
+                fq[e] = (_Float16)(bf16_to_f32(sm.q[i * LDR + cc]) * ri);
+                fk[e] = (_Float16)(bf16_to_f32(sm.k[j * LDR + cc]) * kj);
+            }
+            accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(fe, fk, accA, 0, 0, 0);
+            accP = __builtin_amdgcn_mfma_f32_16x16x32_f16(fq, fk, accP, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = 16 * I + 4 * g + e, jj = 16 * J + r;
+            sm.A[ii * LDP + jj] = (_Float16)accA[e];
+            sm.P[ii * LDP + jj] = (_Float16)accP[e];
+        }
+    }
+    // 4. diagonal blocks exactly: thread (row i, quarter qq of the channels)
+    {
+        constexpr int CQ = DK / 4;
+        const int i = tid >> 2, qq = tid & 3;
+        const int j0 = i & ~15;
+        const int cbeg = qq * CQ;
+        float ei[CQ], qi[CQ], gi[CQ];
+#pragma unroll
+        for (int x = 0; x < CQ; ++x) {
+            const int cc = cbeg + x;
+            ei[x] = bf16_to_f32(sm.b[i * LDR + cc]) * bf16_to_f32(sm.k[i * LDR + cc]);
+            qi[x] = bf16_to_f32(sm.q[i * LDR + cc]);
+            gi[x] = sm.G2[i * LDG + cc];
+        }
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = j0 + jj;
+            float pa = 0.f, pp = 0.f;
+            if (j <= i) {
+#pragma unroll
+                for (int x = 0; x < CQ; ++x) {
+                    const int cc = cbeg + x;
+                    const float kd = bf16_to_f32(sm.k[j * LDR + cc]) * __builtin_amdgcn_exp2f(gi[x] - sm.G2[j * LDG + cc]);
+                    pa = fmaf(ei[x], kd, pa);
+                    pp = fmaf(qi[x], kd, pp);
+                }
+            }
+            pa += __shfl_xor(pa, 1);
+            pa += __shfl_xor(pa, 2);
+            pp += __shfl_xor(pp, 1);
+            pp += __shfl_xor(pp, 2);
+            if (qq == 0 && j <= i) {
+                if (j < i) {
+                    sm.A[i * LDP + j] = (_Float16)pa;
+                    sm.P[i * LDP + j] = (_Float16)pp;
+                } else {
+                    sm.dg[i] = pp;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // 5. T - I on one wave
+    if (wave == 0) unit_lower_inverse<LDP>(sm.A, sm.Tm, lane);
+    __syncthreads();
+    // 6. T - I, P and diag P out
+    for (int u = tid; u < BT * 8; u += 256) {
+        const int row = u >> 3, c0 = 8 * (u & 7);
+        *(uint4 *)(blk + BL::TM + (row * BT + c0) * 2) = *(const uint4 *)&sm.Tm[row * LDP + c0];
+        *(uint4 *)(blk + BL::PM + (row * BT + c0) * 2) = *(const uint4 *)&sm.P[row * LDP + c0];
+    }
+    if (tid < BT) ((float *)(blk + BL::DG))[tid] = sm.dg[tid];
+}
+
+// --------------------------------------------------------------- walk kernel
+template <int DK, int DV>
+struct Gdn2WalkCfg {
+    static constexpr int BV = 32;
+    static constexpr int NS = DK / 32;
+    static constexpr int NKB = DK / 16;
+    static constexpr int LDK = RowTile<DK>::LD;
+    static constexpr int LDP = BT + 8;    // fp16 rows of T - I and P (16-byte aligned)
+    static constexpr int LDV = BV + 8;   // bf16 rows of the v and w slices
+    static constexpr int UT = BT * DK / 8 / 128;  // uint4 per loader thread per DK tile
+};
+
+template <int DK, int DV>
+struct Gdn2WalkSmem {
+    using C = Gdn2WalkCfg<DK, DV>;
+    alignas(16) uint16_t E[2][BT * C::LDK];   // fp16 bits, swizzled rows (tile_off)
+    alignas(16) uint16_t Q[2][BT * C::LDK];
+    alignas(16) uint16_t K[2][BT * C::LDK];
+    alignas(16) _Float16 Tm[2][BT * C::LDP];
+    alignas(16) _Float16 P[2][BT * C::LDP];
+    alignas(16) uint16_t V[2][BT * C::LDV];   // raw bf16
+    alignas(16) uint16_t W[2][BT * C::LDV];
+    alignas(16) float dg[2][BT];
+    alignas(16) float gam[2][DK];
+};
+
+struct Gdn2Head {
+    const char *ws;      // this head's first chunk block
+    const uint16_t *v, *w;
+    long row0;           // token-head row of token 0 of this head
+    int T, H, vcol0;
+};
+
+// Everything a loader thread moves for one chunk.
+template <int DK>
+struct Gdn2Stage {
+    uint4 e[Gdn2WalkCfg<DK, DK>::UT], q[Gdn2WalkCfg<DK, DK>::UT], k[Gdn2WalkCfg<DK, DK>::UT];
+    uint4 tm[4], p[4], v[2], w[2], tab;
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void stage_load(Gdn2Stage<DK> &R, const Gdn2Head &hd, int chunk, int lt) {
+    using BL = Gdn2Blk<DK>;
+    using C = Gdn2WalkCfg<DK, DV>;
+    const char *blk = hd.ws + (long)chunk * BL::BYTES;
+#pragma unroll
+    for (int x = 0; x < C::UT; ++x) {
+        const int u = lt + 128 * x;
+        R.e[x] = *(const uint4 *)(blk + BL::E + u * 16);
+        R.q[x] = *(const uint4 *)(blk + BL::Q + u * 16);
+        R.k[x] = *(const uint4 *)(blk + BL::K + u * 16);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int u = lt + 128 * x;
+        R.tm[x] = *(const uint4 *)(blk + BL::TM + u * 16);
+        R.p[x] = *(const uint4 *)(blk + BL::PM + u * 16);
+    }
+    // dg (16 uint4) then Gamma_C (DK / 4 uint4), contiguous in the block
+    R.tab = (lt < 16 + DK / 4) ? *(const uint4 *)(blk + BL::DG + lt * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int u = lt + 128 * x, row = u >> 2, c4 = u & 3;
+        const int t = chunk * BT + row;
+        const long off = (hd.row0 + (long)t * hd.H) * DV + hd.vcol0 + 8 * c4;
+        const bool in = t < hd.T;
+        R.v[x] = in ? *(const uint4 *)(hd.v + off) : make_uint4(0, 0, 0, 0);
+        R.w[x] = in ? *(const uint4 *)(hd.w + off) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void stage_store(Gdn2WalkSmem<DK, DV> &sm, const Gdn2Stage<DK> &R, int buf, int lt) {
+    using C = Gdn2WalkCfg<DK, DV>;
+    constexpr int C8 = DK / 8;
+#pragma unroll
+    for (int x = 0; x < C::UT; ++x) {
+        const int u = lt + 128 * x, row = u / C8, c0 = 8 * (u % C8);
+        *(uint4 *)&sm.E[buf][tile_off<DK>(row, c0)] = R.e[x];
+        *(uint4 *)&sm.Q[buf][tile_off<DK>(row, c0)] = R.q[x];
+        *(uint4 *)&sm.K[buf][tile_off<DK>(row, c0)] = R.k[x];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int u = lt + 128 * x, row = u >> 3, c0 = 8 * (u & 7);
+        *(uint4 *)&sm.Tm[buf][row * C::LDP + c0] = R.tm[x];
+        *(uint4 *)&sm.P[buf][row * C::LDP + c0] = R.p[x];
+    }
+    if (lt < 16)
+        *(uint4 *)&sm.dg[buf][4 * lt] = R.tab;
+    else if (lt < 16 + DK / 4)
+        *(uint4 *)&sm.gam[buf][4 * (lt - 16)] = R.tab;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int u = lt + 128 * x, row = u >> 2, c0 = 8 * (u & 3);
+        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[x];
+        *(uint4 *)&sm.W[buf][row * C::LDV + c0] = R.w[x];
+    }
+}
+
+// One chunk on consumer wave `wave` (value columns 16 wave .. +15 of the
+// slice); S holds d_k x 16 of the state as accumulator tiles.
+template <int DK, int DV>
+__device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf,
+                                             float *__restrict__ o, const Gdn2Head &hd, int chunk, int wave,
+                                             float scale, int lane) {
+    using C = Gdn2WalkCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+    // X = Ehat S, Y = Qhat S with the state as fp16 hi + lo
+    f32x4 X[4], Y[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        uint4 shi, slo;
+        hilo_frags<f16x2>(shi, slo, S[2 * s], S[2 * s + 1]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const uint4 ea = frag_rows_sw<DK>(sm.E[buf], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_sw<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+            X[I] = mma_f16_raw(X[I], ea, shi);
+            Y[I] = mma_f16_raw(Y[I], qa, shi);
+            X[I] = mma_f16_raw(X[I], ea, slo);
+            Y[I] = mma_f16_raw(Y[I], qa, slo);
+        }
+    }
+    // R = w . v - X
+    f32x4 Rr[4];
+    const int cl = wave * 16 + r;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            Rr[I][e] = bf16_to_f32(sm.W[buf][i * C::LDV + cl]) * bf16_to_f32(sm.V[buf][i * C::LDV + cl]) - X[I][e];
+        }
+    // Vnew = R + (T - I) R
+    _Float16 rf[2][8];
+    frag_from_acc(rf[0], Rr[0], Rr[1]);
+    frag_from_acc(rf[1], Rr[2], Rr[3]);
+    f32x4 Vn[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        Vn[I] = Rr[I];
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) {
+            _Float16 a[8];
+            frag_rows(a, sm.Tm[buf], C::LDP, 16 * I, 32 * s, lane);
+            Vn[I] = mma_slab(Vn[I], a, rf[s]);
+        }
+    }
+    // O = scale (Y + diag(P) Vnew + strict(P) Vnew)
+    _Float16 vf[2][8];
+    frag_from_acc(vf[0], Vn[0], Vn[1]);
+    frag_from_acc(vf[1], Vn[2], Vn[3]);
+    const int t0 = chunk * BT;
+    const bool full = t0 + BT <= hd.T;
+    float *obase = o + (hd.row0 + (long)t0 * hd.H) * DV + hd.vcol0 + cl;
+    const long ostride = (long)hd.H * DV;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const f32x4 dgv = *(const f32x4 *)&sm.dg[buf][16 * I + 4 * g];
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = Y[I][e] + dgv[e] * Vn[I][e];
+#pragma unroll
+        for (int s = 0; s <= (I >> 1); ++s) {
+            _Float16 a[8];
+            frag_rows(a, sm.P[buf], C::LDP, 16 * I, 32 * s, lane);
+            acc = mma_slab(acc, a, vf[s]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ti = 16 * I + 4 * g + e;
+            if (full || t0 + ti < hd.T) obase[ti * ostride] = scale * acc[e];
+        }
+    }
+    // S = Diag(Gamma_C) S + Khat^T Vnew, Khat^T by transpose loads, Vnew as fp16 hi + lo
+    uint4 vh[2], vl[2];
+    hilo_frags<f16x2>(vh[0], vl[0], Vn[0], Vn[1]);
+    hilo_frags<f16x2>(vh[1], vl[1], Vn[2], Vn[3]);
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m) {
+        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * m + 4 * g];
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = S[m][e] * gm[e];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            acc = mma_f16_raw(acc, a, vh[s]);
+            acc = mma_f16_raw(acc, a, vl[s]);
+        }
+        S[m] = acc;
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__restrict__ ws,
+                                                                  const uint16_t *__restrict__ v,
+                                                                  const uint16_t *__restrict__ wg,
+                                                                  const float *__restrict__ h0, float *__restrict__ o,
+                                                                  float *__restrict__ ht, int T, int H, int NT,
+                                                                  float scale) {
+    using C = Gdn2WalkCfg<DK, DV>;
+    static_assert(sizeof(Gdn2WalkSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ Gdn2WalkSmem<DK, DV> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    constexpr int NTILE = DV / C::BV;
+    // the column slices of one head get consecutive ids on one XCD (shared L2)
+    const int n = blockIdx.x, nwg = gridDim.x;
+    const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
+    const int vt = L % NTILE;
+    const long bh = L / NTILE;
+    Gdn2Head hd;
+    hd.ws = ws + bh * NT * (long)Gdn2Blk<DK>::BYTES;
+    hd.v = v;
+    hd.w = wg;
+    hd.H = H;
+    hd.T = T;
+    hd.row0 = (bh / H) * (long)T * H + (bh % H);
+    hd.vcol0 = vt * C::BV;
+    const long sbase = bh * (long)DK * DV;
+
+    if (wave < 2) {
+        f32x4 S[C::NKB];
+        const int col = hd.vcol0 + wave * 16 + r;
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c >= 0) gdn2_consume(sm, S, c & 1, o, hd, c, wave, scale, lane);
+            __syncthreads();
+        }
+        if (ht) {
+#pragma unroll
+            for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+        }
+    } else {
+        // loaders: iteration c stores chunk c + 1 and fetches chunk c + 2
+        const int lt = tid - 128;
+        Gdn2Stage<DK> R;
+        stage_load<DK, DV>(R, hd, 0, lt);
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c + 1 < NT) {
+                stage_store(sm, R, (c + 1) & 1, lt);
+                if (c + 2 < NT) stage_load<DK, DV>(R, hd, c + 2, lt);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ----------------------------------------------------------------- launchers
+template <int DK, int DV>
+static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                      const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
+                                      int H, float scale, hipStream_t st) {
+    const int NT = (T + BT - 1) / BT;
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
+                       (const uint16_t *)q, (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, T, H, NT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long grid = (long)B * H * (DV / Gdn2WalkCfg<DK, DV>::BV);
+    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const char *)ws, (const uint16_t *)v, (const uint16_t *)wg, h0, o, ht, T, H, NT, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                  const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
+                                  int H, int Dk, int Dv, float scale, hipStream_t st) {
+    if (Dk == 64 && Dv == 64) return launch_gdn2_fused_t<64, 64>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
+    if (Dk == 64 && Dv == 128) return launch_gdn2_fused_t<64, 128>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
+    if (Dk == 128 && Dv == 64) return launch_gdn2_fused_t<128, 64>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
+    if (Dk == 128 && Dv == 128)
+        return launch_gdn2_fused_t<128, 128>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

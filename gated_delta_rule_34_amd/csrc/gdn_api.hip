@@ -160,6 +160,11 @@ Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
     const size_t mts = dt == GDN_BF16 ? 2 : 4;
     Gdn2Ws w;
     size_t off = 0;
+    if (dt == GDN_BF16) {  // one block of prepared operands per chunk (gdn2_fused.hip)
+        w = Gdn2Ws{};
+        w.total = align_up(chunks * gdn::gdn2_fused_block_bytes(Dk));
+        return w;
+    }
     w.e_off = off; off += align_up(chunks * kBT * Dk * mts);
     w.q_off = off; off += align_up(chunks * kBT * Dk * mts);
     w.k_off = off; off += align_up(chunks * kBT * Dk * mts);
@@ -200,6 +205,8 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const flo
     for (Range in : {rq, rk, rv, rla, rb, rw, rh0})
         if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
+    if (dtype == GDN_BF16)
+        return from_hip(gdn::launch_gdn2_fused_bf16(q, k, log_alpha, b, v, w, h0, o, ht, ws, B, T, H, Dk, Dv, scale, st));
     char *base = (char *)ws;
     void *E = base + lay.e_off, *Qh = base + lay.q_off, *Kh = base + lay.k_off;
     float *Gam = (float *)(base + lay.gam_off), *Tinv = (float *)(base + lay.t_off);

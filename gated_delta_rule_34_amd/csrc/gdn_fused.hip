@@ -38,112 +38,20 @@
 // products with intermediate operands (new values, decayed keys, T - I, P)
 // use fp16 operands; every accumulation, the state, the diagonal terms
 // beta_i v_i and (q_i.k_i) vnew_i, and the output are fp32.
-#include "gdn_device.h"
 #include "gdn_launch.h"
+#include "gdn_tile.h"
 
 namespace gdn {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-
-__device__ __forceinline__ f32x4 mma_bf16_raw(f32x4 acc, const uint4 &a, const uint4 &b) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   acc, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mma_f16_block(f32x4 acc, const f16x4 &a, const f16x4 &b) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
-}
-
-// bf16 pair packed in a u32 -> two floats
-__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
-// The 10 lower-triangular 16x16 tiles (I >= J) of a 64x64 chunk matrix;
-// compile-time so that register arrays are indexed statically.
-__device__ constexpr int tileI(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
-__device__ constexpr int tileJ(int t) { return t - tileI(t) * (tileI(t) + 1) / 2; }
 
 template <int DK, int DV>
 struct FusedCfg {
     static constexpr int BV = 32;
     static constexpr int NS = DK / 32;   // 32-wide k slabs
     static constexpr int NKB = DK / 16;  // 16-row blocks of the state
-    // sK, sQ: raw bf16 rows of DK halves.  With DK = 128 a row is 64 dwords
-    // (all rows bank-aligned), so column groups are XOR-swizzled per row:
-    // 16-half segments by (row & 7), 8-half groups by bit 3 of the row.  The
-    // 8-byte fragment reads (16 rows x 2 column groups per half-wave) and the
-    // transpose reads of the state update (8 rows x one 16-half segment) then
-    // each cover 64 distinct banks.  With DK = 64 rows are padded instead.
-    static constexpr bool KQ_SWZ = DK == 128;
-    static constexpr int LDK = KQ_SWZ ? DK : DK + 8;
+    static constexpr int LDK = RowTile<DK>::LD;  // row stride of the raw K and Q tiles
     static constexpr int LDP = BT + 4;   // fp16 row stride of sP, sT, sA
     static constexpr int LDV = BV + 8;   // bf16 row stride of sV
 };
-
-// Element offset (in halves) of column `col` (multiple of 4) of row `row` in sK / sQ.
-template <int DK, int DV>
-__device__ __forceinline__ int kq_off(int row, int col) {
-    using C = FusedCfg<DK, DV>;
-    if (C::KQ_SWZ) return row * C::LDK + (col ^ (((row & 7) << 4) ^ (((row >> 3) & 1) << 3)));
-    return row * C::LDK + col;
-}
-
-// Fragment of a 32-wide slab (k-slots 4g + e and 16 + 4g + e, as in
-// frag_rows) read from a swizzled raw-bf16 matrix.
-template <int DK, int DV>
-__device__ __forceinline__ uint4 frag_rows_kq(const uint16_t *M, int row0, int k0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    const uint2 lo = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 4 * g)];
-    const uint2 hi = *(const uint2 *)&M[kq_off<DK, DV>(row0 + r, k0 + 16 + 4 * g)];
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-
-// A fragment of K^T for the state update, read from the row-major raw bf16
-// K tile with the gfx950 LDS transpose load: within each 16-lane group, lane
-// j receives element (j % 4) of the 8-byte chunks addressed by lanes j/4,
-// j/4 + 4, j/4 + 8, j/4 + 12.  Lane (g, r) therefore addresses row
-// j0 + 4g + r/4, columns kc0 + 4(r % 4), and receives K[j0 + 4g + e][kc0 + r],
-// e = 0..3: the A-operand slots of rows kc0 + r of K^T.  Two such loads
-// (j0 and j0 + 16) make the 32-wide slab.
-template <int DK, int DV>
-__device__ __forceinline__ uint4 frag_kT(const uint16_t *M, int j0, int kc0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const uint16_t *p0 = &M[kq_off<DK, DV>(j0 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
-    const uint16_t *p1 = &M[kq_off<DK, DV>(j0 + 16 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
-}
-
-// The state as two bf16 B fragments whose sum carries ~16 significant bits:
-// hi = bf16(S), lo = bf16(S - hi); both from accumulator tiles (k-blocks 2s, 2s+1).
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
-// hi = bf16(x), lo = bf16(x - hi) for a pair of floats, on the packed
-// round-to-nearest conversion.
-__device__ __forceinline__ void split_pair(bf16x2 &h, bf16x2 &l, float a, float b) {
-    const f32x2 x = {a, b};
-    h = __builtin_convertvector(x, bf16x2);
-    l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), bf16x2);
-}
-
-__device__ __forceinline__ void state_frags_hilo(bf16x8 &hi, bf16x8 &lo, const f32x4 &t0, const f32x4 &t1) {
-    bf16x2 h[4], l[4];
-    split_pair(h[0], l[0], t0[0], t0[1]);
-    split_pair(h[1], l[1], t0[2], t0[3]);
-    split_pair(h[2], l[2], t1[0], t1[1]);
-    split_pair(h[3], l[3], t1[2], t1[3]);
-    hi = __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
-                                 __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    lo = __builtin_shufflevector(__builtin_shufflevector(l[0], l[1], 0, 1, 2, 3),
-                                 __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 
 // Everything the consumers read for one chunk is double-buffered (index =
 // chunk parity), so producers fill chunk c + 1 while consumers read chunk c
@@ -151,7 +59,7 @@ __device__ __forceinline__ void state_frags_hilo(bf16x8 &hi, bf16x8 &lo, const f
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
-    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows (swizzled, see kq_off)
+    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows (swizzled, see tile_off)
     alignas(16) uint16_t Q[2][BT * C::LDK];
     alignas(16) _Float16 P[2][BT * C::LDP];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
@@ -217,28 +125,6 @@ __device__ __forceinline__ void load_gates(float &gv, float &bv, const HeadArgs 
     bv = (t < a.T) ? a.beta[idx] : 0.f;
 }
 
-// Value of `x` moved by a DPP row operation; lanes without a source get 0.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xf,
-                                                                 false));
-}
-
-// log2(e) * chunk-local inclusive cumsum of g, one token per lane: an fp32
-// wave scan on DPP (shifts 1, 2, 4, 8 within each row of 16 lanes, then the
-// row totals broadcast by lane 15 and lane 31), no LDS round trip.
-__device__ __forceinline__ float chunk_g2(float gv, int lane) {
-    (void)lane;
-    float x = gv * 1.4426950408889634f;
-    x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
-    x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
-    x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
-    x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
-    x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-    x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
-
 // ------------------------------------------------------- producer: A and T
 // Chunk `chunk` from registers into T - I of LDS half `buf`; issues the
 // loads of chunk `next` (if any) once the registers are free.
@@ -247,7 +133,7 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    sm.g2T[lane] = chunk_g2(R.g, lane);
+    sm.g2T[lane] = chunk_g2(R.g);
     sm.betaT[lane] = R.beta;
     // K_J K_I^T: this lane gets row i = 16I + r and columns j = 16J + 4g + e
     // of every tile, stored as 4 adjacent halves
@@ -281,60 +167,7 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         load_gates(R.g, R.beta, ha, next, lane);
     }
     _Float16 *Tm = sm.Tm[buf];
-    // Diagonal blocks: lane (block bb, column cc) solves its column of T_bb,
-    // x_i = [i == cc] - sum_{j<i} A_ij x_j, with four partial sums per row.
-    {
-        const int bb = lane >> 4, cc = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const _Float16 *arow = &sm.A[(16 * bb + i) * C::LDP + 16 * bb];
-            f16x4 av[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                if (4 * q4 < i) av[q4] = *(const f16x4 *)&arow[4 * q4];
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < i; ++j) part[j & 3] = fmaf((float)av[j >> 2][j & 3], x[j], part[j & 3]);
-            x[i] = ((i == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            Tm[(16 * bb + i) * C::LDP + 16 * bb + cc] = (_Float16)(x[i] - (i == cc ? 1.f : 0.f));
-    }
-    // Off-diagonal blocks, one sub-diagonal level d at a time; the blocks of a
-    // level are independent and are computed together:
-    //   T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ.
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        constexpr int NB_MAX = 3;
-        f32x4 M[NB_MAX];
-#pragma unroll
-        for (int J = 0; J < 4 - d; ++J) {
-            const int I = J + d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) M[J][e] = (float)sm.A[(16 * I + 4 * g + e) * C::LDP + 16 * J + r];
-#pragma unroll
-            for (int K = J; K < I; ++K) {
-                const f16x4 a = *(const f16x4 *)&sm.A[(16 * I + r) * C::LDP + 16 * K + 4 * g];
-                f16x4 bq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bq[e] = Tm[(16 * K + 4 * g + e) * C::LDP + 16 * J + r];
-                M[J] = mma_f16_block(M[J], a, bq);
-            }
-        }
-#pragma unroll
-        for (int J = 0; J < 4 - d; ++J) {
-            const int I = J + d;
-            const f16x4 a = *(const f16x4 *)&Tm[(16 * I + r) * C::LDP + 16 * I + 4 * g];
-            f16x4 bq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bq[e] = (_Float16)M[J][e];
-            const f32x4 res = mma_f16_block(M[J], a, bq);  // T_II M = M + strict(T_II) M
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * g + e) * C::LDP + 16 * J + r] = (_Float16)(-res[e]);
-        }
-    }
+    unit_lower_inverse<C::LDP>(sm.A, Tm, lane);
 }
 
 // ------------------------------------------- producer: P and consumer inputs
@@ -350,7 +183,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
     }
     if (next >= 0) load_v<DV>(R.v, ha, next, lane);
-    const float G2 = chunk_g2(R.g, lane);
+    const float G2 = chunk_g2(R.g);
     sm.g2P[lane] = G2;
     sm.gam[buf][lane] = __builtin_amdgcn_exp2f(G2);
     sm.beta[buf][lane] = R.beta;
@@ -389,14 +222,14 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int s = 0; s < C::NS; ++s)
-            *(uint4 *)&sm.Q[buf][kq_off<DK, DV>(16 * I + r, 32 * s + 8 * g)] = R.q[I][s];
+            *(uint4 *)&sm.Q[buf][tile_off<DK>(16 * I + r, 32 * s + 8 * g)] = R.q[I][s];
     if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
     // raw bf16 copy of K; then K's registers are refilled
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int s = 0; s < C::NS; ++s)
-            *(uint4 *)&sm.K[buf][kq_off<DK, DV>(16 * I + r, 32 * s + 8 * g)] = R.k[I][s];
+            *(uint4 *)&sm.K[buf][tile_off<DK>(16 * I + r, 32 * s + 8 * g)] = R.k[I][s];
     if (next >= 0) load_rows<DK>(R.k, ha.k, ha, next, lane);
 }
 
@@ -413,12 +246,13 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-        bf16x8 shi, slo;
-        state_frags_hilo(shi, slo, S[2 * s], S[2 * s + 1]);
+        uint4 uhi, ulo;
+        hilo_frags<bf16x2>(uhi, ulo, S[2 * s], S[2 * s + 1]);
+        const bf16x8 shi = __builtin_bit_cast(bf16x8, uhi), slo = __builtin_bit_cast(bf16x8, ulo);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint4 ka = frag_rows_kq<DK, DV>(sm.K[buf], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_kq<DK, DV>(sm.Q[buf], 16 * I, 32 * s, lane);
+            const uint4 ka = frag_rows_sw<DK>(sm.K[buf], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_sw<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
             const bf16x8 kb = __builtin_bit_cast(bf16x8, ka), qb = __builtin_bit_cast(bf16x8, qa);
             X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, shi, X[I], 0, 0, 0);
             Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, shi, Y[I], 0, 0, 0);
@@ -486,7 +320,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
     // straight from the raw K tile by transpose loads, and d . Vnew enters as
     // bf16 hi + lo parts.
-    bf16x8 dvh[2], dvl[2];
+    uint4 dvh[2], dvl[2];
     {
         f32x4 dv[4];
 #pragma unroll
@@ -495,8 +329,8 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv[I][e] = dd[e] * Vn[I][e];
         }
-        state_frags_hilo(dvh[0], dvl[0], dv[0], dv[1]);
-        state_frags_hilo(dvh[1], dvl[1], dv[2], dv[3]);
+        hilo_frags<bf16x2>(dvh[0], dvl[0], dv[0], dv[1]);
+        hilo_frags<bf16x2>(dvh[1], dvl[1], dv[2], dv[3]);
     }
     const float gl = sm.gam[buf][BT - 1];
 #pragma unroll
@@ -504,9 +338,9 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         f32x4 acc = S[m] * gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, frag_kT<DK, DV>(sm.K[buf], 32 * s, 16 * m, lane));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dvh[s], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dvl[s], acc, 0, 0, 0);
+            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            acc = mma_bf16_raw(acc, a, dvh[s]);
+            acc = mma_bf16_raw(acc, a, dvl[s]);
         }
         S[m] = acc;
     }

@@ -29,6 +29,14 @@ hipError_t launch_gdn2_walk(const void *Ehat, const void *Qhat, const void *Khat
                             const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv, bool bf16,
                             float scale, hipStream_t st);
 
+// Gated DeltaNet-2 for bf16 inputs: a parallel prep kernel writes one block
+// of prepared operands per chunk into ws (gdn2_fused_block_bytes(Dk) each),
+// then the walk kernel carries the state through the chunks.
+size_t gdn2_fused_block_bytes(int Dk);
+hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                  const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
+                                  int H, int Dk, int Dv, float scale, hipStream_t st);
+
 hipError_t launch_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                        hipStream_t st);
