@@ -86,33 +86,49 @@ __global__ __launch_bounds__(256) void gdn2_prep_kernel(const uint16_t *__restri
     const long row0 = (bb * T + t0) * H + h;  // token-head row of the chunk's first token
     char *blk = ws + cb * (long)BL::BYTES;
 
-    // 1. raw rows (zero past T) and the per-channel cumsum of log alpha
-    for (int u = tid; u < BT * C8; u += 256) {
-        const int row = u / C8, c8 = u % C8;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv, bv = kv;
-        if (t0 + row < T) {
-            const long off = (row0 + (long)row * H) * DK + 8 * c8;
-            kv = *(const uint4 *)(k + off);
-            qv = *(const uint4 *)(q + off);
-            bv = *(const uint4 *)(bg + off);
-        }
-        *(uint4 *)&sm.k[row * LDR + 8 * c8] = kv;
-        *(uint4 *)&sm.q[row * LDR + 8 * c8] = qv;
-        *(uint4 *)&sm.b[row * LDR + 8 * c8] = bv;
+    // 1. raw rows (zero past T) and the per-channel cumsum of log alpha.  All
+    //    loads are issued before any is used; rows past T read the last token
+    //    (always in bounds) and are then zeroed.
+    constexpr int NU = BT * C8 / 256;  // uint4 per thread per raw tile
+    uint4 kr[NU], qr[NU], br[NU];
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+        const int u = tid + 256 * x, row = u / C8, c8 = u % C8;
+        const int tr = min(t0 + row, T - 1) - t0;
+        const long off = (row0 + (long)tr * H) * DK + 8 * c8;
+        kr[x] = *(const uint4 *)(k + off);
+        qr[x] = *(const uint4 *)(q + off);
+        br[x] = *(const uint4 *)(bg + off);
     }
-    {
-        // thread (half hf, channel ch) scans rows 32 hf .. 32 hf + 31 of its channel
-        const int ch = tid % DK, hf = tid / DK;  // DK = 128: 2 halves; DK = 64: 4 quarters, two of them idle
-        if (hf < 2) {
-            float acc = 0.f;
-            for (int i = 0; i < 32; ++i) {
-                const int row = 32 * hf + i;
-                const float x = (t0 + row < T) ? la[(row0 + (long)row * H) * DK + ch] : 0.f;
-                acc += x * 1.4426950408889634f;
-                sm.G2[row * LDG + ch] = acc;
-            }
-            sm.half[hf][ch] = acc;
+    // thread (half hf, channel ch) scans rows 32 hf .. 32 hf + 31 of its channel
+    // (DK = 128: two halves; DK = 64: four groups of 64 threads, two of them idle)
+    const int ch = tid % DK, hf = tid / DK;
+    float lv[32];
+    if (hf < 2) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int tr = min(t0 + 32 * hf + i, T - 1) - t0;
+            lv[i] = la[(row0 + (long)tr * H) * DK + ch];
         }
+    }
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+        const int u = tid + 256 * x, row = u / C8, c8 = u % C8;
+        const bool in = t0 + row < T;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        *(uint4 *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
+        *(uint4 *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
+        *(uint4 *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
+    }
+    if (hf < 2) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int row = 32 * hf + i;
+            acc += (t0 + row < T) ? lv[i] * 1.4426950408889634f : 0.f;
+            sm.G2[row * LDG + ch] = acc;
+        }
+        sm.half[hf][ch] = acc;
     }
     __syncthreads();
     for (int u = tid; u < 32 * DK; u += 256) {
