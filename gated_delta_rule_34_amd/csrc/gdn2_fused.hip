@@ -19,7 +19,8 @@
 //   Off-diagonal 16x16 blocks of A and P are fp16 MFMA products of factors
 //   anchored at the first row a of the block row: (x_i e^{G_i - G_a}) and
 //   (k_j e^{G_a - G_j}), both at most 1 in size since j < a <= i.  Diagonal
-//   blocks have no such anchor and are summed exactly on the VALU.
+//   blocks use the same anchor on fp32 MFMA while the block's decay keeps
+//   both factors inside 2^(+-100), and are summed directly otherwise.
 // walk kernel (one workgroup per (batch, head, 32 value columns)): two
 //   consumer waves carry the state in registers through the chunks, two
 //   loader waves stage the next chunk's block and value slices into LDS.
@@ -55,28 +56,144 @@ struct Gdn2PrepSmem {
     static constexpr int LDR = DK + 8;   // raw bf16 rows
     static constexpr int LDG = DK + 4;   // fp32 rows of G2
     static constexpr int LDP = BT + 8;   // fp16 rows of A, T - I, P
+    static constexpr int NG = 512 / DK;  // row groups of the cumsum
     alignas(16) uint16_t k[BT * LDR];
     alignas(16) uint16_t q[BT * LDR];
     alignas(16) uint16_t b[BT * LDR];
     alignas(16) float G2[BT * LDG];      // log2(e) * chunk-local cumsum of log alpha
-    alignas(16) float half[2][DK];       // cumsum of rows 0..31 (scan of two halves)
+    alignas(16) float part[NG][DK];      // per-group totals of the cumsum
     alignas(16) _Float16 A[BT * LDP];
     alignas(16) _Float16 Tm[BT * LDP];
     alignas(16) _Float16 P[BT * LDP];
     alignas(16) float dg[BT];
 };
 
+// Largest |G2[x][c] - G2[a][c]| over the 16 rows x of the block at row a and
+// all channels: the size of the anchored factors in log2 units.
+template <int DK, int LDG>
+__device__ __forceinline__ float block_span(const float *G2, int a, int lane) {
+    float m = 0.f;
+    for (int c = lane; c < DK; c += 64) {
+        const float ga = G2[a * LDG + c];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) m = fmaxf(m, fabsf(G2[(a + x) * LDG + c] - ga));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    return m;
+}
+
+// Diagonal block (rows and columns a .. a + 15) of A and P, one wave.  When
+// every channel's decay within the block stays inside 2^(+-100) of row a, the
+// block is a product of factors anchored at a, e_i 2^(G2_i - G2_a) and
+// k_j 2^(G2_a - G2_j), on fp32 MFMA (exact fp32 operands, no overflow or
+// underflow of either factor); otherwise each entry is summed directly.
 template <int DK>
-__global__ __launch_bounds__(256) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+__device__ __forceinline__ void diag_block(Gdn2PrepSmem<DK> &sm, int a, int lane) {
+    using SM = Gdn2PrepSmem<DK>;
+    constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP;
+    const int r = lane & 15, g = lane >> 4;
+    if (block_span<DK, LDG>(sm.G2, a, lane) < 100.f) {
+        f32x4 accA = zero4(), accP = zero4();
+        const int i = a + r;  // A-operand row and B-operand column of this lane
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            float fa[8], fq[8], fb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
+                const float Ga = sm.G2[a * LDG + cc], Gi = sm.G2[i * LDG + cc];
+                const float ri = __builtin_amdgcn_exp2f(Gi - Ga), ki = bf16_to_f32(sm.k[i * LDR + cc]);
+                fa[e] = bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri;
+                fq[e] = bf16_to_f32(sm.q[i * LDR + cc]) * ri;
+                fb[e] = ki * __builtin_amdgcn_exp2f(Ga - Gi);
+            }
+            accA = mma_slab(accA, fa, fb);
+            accP = mma_slab(accP, fq, fb);
+        }
+        // lane holds [a + 4g + e][a + r]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = 4 * g + e;
+            if (r < ii) {
+                sm.A[(a + ii) * LDP + a + r] = (_Float16)accA[e];
+                sm.P[(a + ii) * LDP + a + r] = (_Float16)accP[e];
+            } else if (r == ii) {
+                sm.dg[a + ii] = accP[e];
+            }
+        }
+    } else {
+        for (int pr = lane; pr < 256; pr += 64) {
+            const int il = pr >> 4, jl = pr & 15;
+            if (jl > il) continue;
+            const int i = a + il, j = a + jl;
+            float pa = 0.f, pp = 0.f;
+            for (int c = 0; c < DK; ++c) {
+                const float kd = bf16_to_f32(sm.k[j * LDR + c]) *
+                                 __builtin_amdgcn_exp2f(sm.G2[i * LDG + c] - sm.G2[j * LDG + c]);
+                pa = fmaf(bf16_to_f32(sm.b[i * LDR + c]) * bf16_to_f32(sm.k[i * LDR + c]), kd, pa);
+                pp = fmaf(bf16_to_f32(sm.q[i * LDR + c]), kd, pp);
+            }
+            if (jl < il) {
+                sm.A[i * LDP + j] = (_Float16)pa;
+                sm.P[i * LDP + j] = (_Float16)pp;
+            } else {
+                sm.dg[i] = pp;
+            }
+        }
+    }
+}
+
+// Off-diagonal tile (I > J) of A and P on fp16 MFMA, anchored at a = 16 I:
+// e_i 2^(G2_i - G2_a) and k_j 2^(G2_a - G2_j) are both at most 1 since
+// j < a <= i and the log-decays are not positive.
+template <int DK>
+__device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int lane) {
+    using SM = Gdn2PrepSmem<DK>;
+    constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP;
+    const int r = lane & 15, g = lane >> 4;
+    const int I = t < 1 ? 1 : t < 3 ? 2 : 3;
+    const int J = t < 1 ? 0 : t < 3 ? t - 1 : t - 3;
+    const int a = 16 * I, i = 16 * I + r, j = 16 * J + r;
+    f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        f16x8 fe, fq, fk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
+            const float Ga = sm.G2[a * LDG + cc];
+            const float ri = __builtin_amdgcn_exp2f(sm.G2[i * LDG + cc] - Ga);
+            const float kj = __builtin_amdgcn_exp2f(Ga - sm.G2[j * LDG + cc]);
+            const float ki = bf16_to_f32(sm.k[i * LDR + cc]);
+            fe[e] = (_Float16)(bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri);
+            fq[e] = (_Float16)(bf16_to_f32(sm.q[i * LDR + cc]) * ri);
+            fk[e] = (_Float16)(bf16_to_f32(sm.k[j * LDR + cc]) * kj);
+        }
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(fe, fk, accA, 0, 0, 0);
+        accP = __builtin_amdgcn_mfma_f32_16x16x32_f16(fq, fk, accP, 0, 0, 0);
+    }
+    // lane holds [16I + 4g + e][16J + r]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int ii = 16 * I + 4 * g + e, jj = 16 * J + r;
+        sm.A[ii * LDP + jj] = (_Float16)accA[e];
+        sm.P[ii * LDP + jj] = (_Float16)accP[e];
+    }
+}
+
+template <int DK>
+__global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                          const float *__restrict__ la, const uint16_t *__restrict__ bg,
                                                          char *__restrict__ ws, int T, int H, int NT) {
     using SM = Gdn2PrepSmem<DK>;
     using BL = Gdn2Blk<DK>;
-    constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP;
-    constexpr int C8 = DK / 8;  // uint4 per row of a raw tile
+    constexpr int NTH = 512;
+    constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP, NG = SM::NG;
+    constexpr int C8 = DK / 8;      // uint4 per row of a raw tile
+    constexpr int RG = BT / NG;     // rows per cumsum group
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
     const long cb = blockIdx.x;
     const int c = (int)(cb % NT);
     const long bh = cb / NT;
@@ -89,167 +206,104 @@ __global__ __launch_bounds__(256) void gdn2_prep_kernel(const uint16_t *__restri
     // 1. raw rows (zero past T) and the per-channel cumsum of log alpha.  All
     //    loads are issued before any is used; rows past T read the last token
     //    (always in bounds) and are then zeroed.
-    constexpr int NU = BT * C8 / 256;  // uint4 per thread per raw tile
+    constexpr int NU = BT * C8 / NTH;  // uint4 per thread per raw tile
     uint4 kr[NU], qr[NU], br[NU];
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
-        const int u = tid + 256 * x, row = u / C8, c8 = u % C8;
+        const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
         const int tr = min(t0 + row, T - 1) - t0;
         const long off = (row0 + (long)tr * H) * DK + 8 * c8;
         kr[x] = *(const uint4 *)(k + off);
         qr[x] = *(const uint4 *)(q + off);
         br[x] = *(const uint4 *)(bg + off);
     }
-    // thread (half hf, channel ch) scans rows 32 hf .. 32 hf + 31 of its channel
-    // (DK = 128: two halves; DK = 64: four groups of 64 threads, two of them idle)
-    const int ch = tid % DK, hf = tid / DK;
-    float lv[32];
-    if (hf < 2) {
+    // thread (group gr, channel ch) scans rows RG gr .. RG gr + RG - 1 of its channel
+    const int ch = tid % DK, gr = tid / DK;
+    float lv[RG];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int tr = min(t0 + 32 * hf + i, T - 1) - t0;
-            lv[i] = la[(row0 + (long)tr * H) * DK + ch];
-        }
+    for (int x = 0; x < RG; ++x) {
+        const int tr = min(t0 + RG * gr + x, T - 1) - t0;
+        lv[x] = la[(row0 + (long)tr * H) * DK + ch];
     }
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
-        const int u = tid + 256 * x, row = u / C8, c8 = u % C8;
+        const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
         const bool in = t0 + row < T;
         const uint4 z = make_uint4(0, 0, 0, 0);
         *(uint4 *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
         *(uint4 *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
         *(uint4 *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
     }
-    if (hf < 2) {
-        float acc = 0.f;
+    float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int row = 32 * hf + i;
-            acc += (t0 + row < T) ? lv[i] * 1.4426950408889634f : 0.f;
-            sm.G2[row * LDG + ch] = acc;
-        }
-        sm.half[hf][ch] = acc;
+    for (int x = 0; x < RG; ++x) {
+        acc += (t0 + RG * gr + x < T) ? lv[x] * 1.4426950408889634f : 0.f;
+        lv[x] = acc;
     }
-    __syncthreads();
-    for (int u = tid; u < 32 * DK; u += 256) {
-        const int row = 32 + u / DK, ch = u % DK;
-        sm.G2[row * LDG + ch] += sm.half[0][ch];
-    }
-    __syncthreads();
-
-    // 2. decayed operands and Gamma_C
-    for (int u = tid; u < BT * C8; u += 256) {
-        const int row = u / C8, c0 = 8 * (u % C8);
-        const uint4 kv = *(const uint4 *)&sm.k[row * LDR + c0];
-        const uint4 qv = *(const uint4 *)&sm.q[row * LDR + c0];
-        const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
-        const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
-        f16x8 eo, qo, ko;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
-            const float gam = __builtin_amdgcn_exp2f(G);
-            const float kf = bf16_to_f32(kk[e]);
-            eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
-            qo[e] = (_Float16)(bf16_to_f32(qq[e]) * gam);
-            ko[e] = (_Float16)(kf * __builtin_amdgcn_exp2f(GL - G));
-        }
-        const long o = ((long)row * DK + c0) * 2;
-        *(f16x8 *)(blk + BL::E + o) = eo;
-        *(f16x8 *)(blk + BL::Q + o) = qo;
-        *(f16x8 *)(blk + BL::K + o) = ko;
-    }
-    for (int ch = tid; ch < DK; ch += 256)
-        ((float *)(blk + BL::GAM))[ch] = __builtin_amdgcn_exp2f(sm.G2[(BT - 1) * LDG + ch]);
+    sm.part[gr][ch] = acc;
     // the upper tiles of T - I and P are never written below
-    for (int u = tid; u < BT * LDP; u += 256) {
+    for (int u = tid; u < BT * LDP; u += NTH) {
         sm.Tm[u] = (_Float16)0.f;
         sm.P[u] = (_Float16)0.f;
     }
     __syncthreads();
-
-    // 3. off-diagonal blocks (I > J) of A and P on fp16 MFMA, anchored at
-    //    a = 16 I; lane gets [16I + 4g + e][16J + r]
-    for (int t = wave; t < 6; t += 4) {
-        const int I = t < 1 ? 1 : t < 3 ? 2 : 3;
-        const int J = t < 1 ? 0 : t < 3 ? t - 1 : t - 3;
-        const int a = 16 * I, i = 16 * I + r, j = 16 * J + r;
-        f32x4 accA = zero4(), accP = zero4();
+    {
+        float off = 0.f;
+        for (int x = 0; x < gr; ++x) off += sm.part[x][ch];
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            f16x8 fe, fq, fk;
+        for (int x = 0; x < RG; ++x) sm.G2[(RG * gr + x) * LDG + ch] = lv[x] + off;
+    }
+    __syncthreads();
+
+    // 2. A and P: waves 0..3 the diagonal blocks, waves 4..7 the 6 off-diagonal tiles
+    if (wave < 4) {
+        diag_block<DK>(sm, 16 * wave, lane);
+    } else {
+        offdiag_tile<DK>(sm, wave - 4, lane);
+        if (wave < 6) offdiag_tile<DK>(sm, wave, lane);
+    }
+    __syncthreads();
+
+    // 3. wave 0: T - I; the other waves: decayed operands, Gamma_C, P, diag P
+    if (wave == 0) {
+        unit_lower_inverse<LDP>(sm.A, sm.Tm, lane);
+    } else {
+        const int ot = tid - 64;  // 0 .. 447
+        for (int u = ot; u < BT * C8; u += NTH - 64) {
+            const int row = u / C8, c0 = 8 * (u % C8);
+            const uint4 kv = *(const uint4 *)&sm.k[row * LDR + c0];
+            const uint4 qv = *(const uint4 *)&sm.q[row * LDR + c0];
+            const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
+            const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
+            f16x8 eo, qo, ko;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
-                const float Ga = sm.G2[a * LDG + cc];
-                const float ri = __builtin_amdgcn_exp2f(sm.G2[i * LDG + cc] - Ga);
-                const float kj = __builtin_amdgcn_exp2f(Ga - sm.G2[j * LDG + cc]);
-                const float ki = bf16_to_f32(sm.k[i * LDR + cc]);
-                fe[e] = (_Float16)(bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri);
-                fq[e] = (_Float16)(bf16_to_f32(sm.q[i * LDR + cc]) * ri);
-                fk[e] = (_Float16)(bf16_to_f32(sm.k[j * LDR + cc]) * kj);
+                const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
+                const float gam = __builtin_amdgcn_exp2f(G);
+                const float kf = bf16_to_f32(kk[e]);
+                eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
+                qo[e] = (_Float16)(bf16_to_f32(qq[e]) * gam);
+                ko[e] = (_Float16)(kf * __builtin_amdgcn_exp2f(GL - G));
             }
-            accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(fe, fk, accA, 0, 0, 0);
-            accP = __builtin_amdgcn_mfma_f32_16x16x32_f16(fq, fk, accP, 0, 0, 0);
+            const long o = ((long)row * DK + c0) * 2;
+            *(f16x8 *)(blk + BL::E + o) = eo;
+            *(f16x8 *)(blk + BL::Q + o) = qo;
+            *(f16x8 *)(blk + BL::K + o) = ko;
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ii = 16 * I + 4 * g + e, jj = 16 * J + r;
-            sm.A[ii * LDP + jj] = (_Float16)accA[e];
-            sm.P[ii * LDP + jj] = (_Float16)accP[e];
+        for (int u = ot; u < BT * 8; u += NTH - 64) {
+            const int row = u >> 3, c0 = 8 * (u & 7);
+            *(uint4 *)(blk + BL::PM + (row * BT + c0) * 2) = *(const uint4 *)&sm.P[row * LDP + c0];
         }
-    }
-    // 4. diagonal blocks exactly: thread (row i, quarter qq of the channels)
-    {
-        constexpr int CQ = DK / 4;
-        const int i = tid >> 2, qq = tid & 3;
-        const int j0 = i & ~15;
-        const int cbeg = qq * CQ;
-        float ei[CQ], qi[CQ], gi[CQ];
-#pragma unroll
-        for (int x = 0; x < CQ; ++x) {
-            const int cc = cbeg + x;
-            ei[x] = bf16_to_f32(sm.b[i * LDR + cc]) * bf16_to_f32(sm.k[i * LDR + cc]);
-            qi[x] = bf16_to_f32(sm.q[i * LDR + cc]);
-            gi[x] = sm.G2[i * LDG + cc];
-        }
-        for (int jj = 0; jj < 16; ++jj) {
-            const int j = j0 + jj;
-            float pa = 0.f, pp = 0.f;
-            if (j <= i) {
-#pragma unroll
-                for (int x = 0; x < CQ; ++x) {
-                    const int cc = cbeg + x;
-                    const float kd = bf16_to_f32(sm.k[j * LDR + cc]) * __builtin_amdgcn_exp2f(gi[x] - sm.G2[j * LDG + cc]);
-                    pa = fmaf(ei[x], kd, pa);
-                    pp = fmaf(qi[x], kd, pp);
-                }
-            }
-            pa += __shfl_xor(pa, 1);
-            pa += __shfl_xor(pa, 2);
-            pp += __shfl_xor(pp, 1);
-            pp += __shfl_xor(pp, 2);
-            if (qq == 0 && j <= i) {
-                if (j < i) {
-                    sm.A[i * LDP + j] = (_Float16)pa;
-                    sm.P[i * LDP + j] = (_Float16)pp;
-                } else {
-                    sm.dg[i] = pp;
-                }
-            }
-        }
+        if (ot < BT) ((float *)(blk + BL::DG))[ot] = sm.dg[ot];
+        if (ot >= BT && ot < BT + DK)
+            ((float *)(blk + BL::GAM))[ot - BT] = __builtin_amdgcn_exp2f(sm.G2[(BT - 1) * LDG + ot - BT]);
     }
     __syncthreads();
-    // 5. T - I on one wave
-    if (wave == 0) unit_lower_inverse<LDP>(sm.A, sm.Tm, lane);
-    __syncthreads();
-    // 6. T - I, P and diag P out
-    for (int u = tid; u < BT * 8; u += 256) {
+    // 4. T - I out
+    for (int u = tid; u < BT * 8; u += NTH) {
         const int row = u >> 3, c0 = 8 * (u & 7);
         *(uint4 *)(blk + BL::TM + (row * BT + c0) * 2) = *(const uint4 *)&sm.Tm[row * LDP + c0];
-        *(uint4 *)(blk + BL::PM + (row * BT + c0) * 2) = *(const uint4 *)&sm.P[row * LDP + c0];
     }
-    if (tid < BT) ((float *)(blk + BL::DG))[tid] = sm.dg[tid];
 }
 
 // --------------------------------------------------------------- walk kernel
@@ -517,7 +571,7 @@ static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float 
                                       const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
                                       int H, float scale, hipStream_t st) {
     const int NT = (T + BT - 1) / BT;
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)((long)B * H * NT)), dim3(512), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, T, H, NT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -122,3 +122,25 @@ def test_gdn2_workload_full_size_sampled_heads():
         ro, rS = oracle.gdn2_fwd(*sub, None, scale=x["scale"])
         assert rel_err(o[b, :, h], ro[0, :, 0]) <= TOL["bf16"]
         assert rel_err(S[b, h], rS[0, 0]) <= TOL["bf16"]
+
+
+def test_strong_decay_blocks_summed_directly():
+    """Per-token log-decays near -20: within a 16-token block the channel decay
+    spans far more than 2^100, so every diagonal block of the bf16 path takes
+    the direct per-entry sum instead of the anchored product."""
+    x = gi.gdn2_inputs(2, 200, 2, 128, 128, seed=307, dtype="bf16", h0=True)
+    x["log_alpha"] = (x["log_alpha"] * 30.0).astype(np.float32)
+    x["log_alpha_f64"] = x["log_alpha"].astype(np.float64)
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_one_channel_strong_decay_mixed_blocks():
+    """One channel decays by e^-40 per token inside one chunk only: the blocks
+    of that chunk are summed directly, all other blocks use the anchored
+    product, within the same call."""
+    x = gi.gdn2_inputs(1, 256, 2, 128, 128, seed=308, dtype="bf16", h0=True)
+    x["log_alpha"][0, 64:128, :, 5] = -40.0
+    x["log_alpha_f64"] = x["log_alpha"].astype(np.float64)
+    o, S = _run(x)
+    _check(x, o, S)
