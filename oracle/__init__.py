@@ -51,15 +51,20 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        i = ctypes.c_int
-        d = ctypes.c_double
-        lib.gdn_oracle_fwd.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
-        lib.gdn2_oracle_fwd.argtypes = [_dp] * 9 + [i] * 5 + [d, i]
-        lib.gdn_oracle_step.argtypes = [_dp] * 7 + [i] * 4 + [d, i]
-        lib.gdn_oracle_max_threads.restype = i
-        _lib = lib
+        _lib = configure(ctypes.CDLL(_LIB_PATH))
     return _lib
+
+
+def configure(lib):
+    """Argument types of the oracle's C functions on a loaded library."""
+    i = ctypes.c_int
+    d = ctypes.c_double
+    lib.gdn_oracle_fwd.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
+    lib.gdn2_oracle_fwd.argtypes = [_dp] * 9 + [i] * 5 + [d, i]
+    lib.gdn_oracle_step.argtypes = [_dp] * 7 + [i] * 4 + [d, i]
+    lib.gdn2_oracle_step.argtypes = [_dp] * 8 + [i] * 4 + [d, i]
+    lib.gdn_oracle_max_threads.restype = i
+    return lib
 
 
 def _c(x):
@@ -114,4 +119,19 @@ def gdn_step(q, k, v, g, beta, S, scale=None, nthreads=0):
     o = np.zeros((B, H, Dv))
     _load().gdn_oracle_step(*[p for _, p in keep], S_new.ctypes.data_as(_dp), o.ctypes.data_as(_dp),
                             B, H, Dk, Dv, float(scale), int(nthreads))
+    return o, S_new
+
+
+def gdn2_step(q, k, v, log_alpha, b, w, S, scale=None, nthreads=0):
+    """One GDN-2 decode step.  q, k, log_alpha, b [B,H,Dk]; v, w [B,H,Dv];
+    S [B,H,Dk,Dv].  Returns (o [B,H,Dv], S_new); the input S is not modified."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if scale is None:
+        scale = Dk ** -0.5
+    keep = [_c(x) for x in (q, k, v, log_alpha, b, w)]
+    S_new = np.array(S, dtype=np.float64, copy=True, order="C")
+    o = np.zeros((B, H, Dv))
+    _load().gdn2_oracle_step(*[p for _, p in keep], S_new.ctypes.data_as(_dp), o.ctypes.data_as(_dp),
+                             B, H, Dk, Dv, float(scale), int(nthreads))
     return o, S_new

@@ -27,8 +27,8 @@
  *       u <- w_t . v_t - S^T (b_t . k_t)
  *       S <- S + k_t u^T ;   o_t <- scale * S^T q_t
  *
- *   Decode step: the Gated DeltaNet body above once, with S given, S updated
- *   in place.
+ *   Decode steps: the Gated DeltaNet or Gated DeltaNet-2 body above once, with
+ *   S given and updated in place (gdn_oracle_step, gdn2_oracle_step).
  *
  * Layouts (row-major, contiguous): q,k [B,T,H,Dk]; v [B,T,H,Dv];
  * g, beta [B,T,H]; log_alpha, b [B,T,H,Dk]; w [B,T,H,Dv];
@@ -105,6 +105,33 @@ void gdn_oracle_fwd(const double *q, const double *k, const double *v,
     }
 }
 
+/* One Gated DeltaNet-2 token on a d_k x d_v state (row-major), in place;
+ * u [Dv] and e [Dk] are scratch.  o (Dv values) may be NULL. */
+static void gdn2_token(double *S, const double *qt, const double *kt, const double *vt,
+                       const double *la, const double *bt, const double *wt, double *u, double *e,
+                       double *ot, int Dk, int Dv, double scale) {
+    /* decay each key row by its own channel rate, before the edit */
+    for (int i = 0; i < Dk; ++i) {
+        const double a = exp(la[i]);
+        for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a;
+        e[i] = bt[i] * kt[i];
+    }
+    for (int j = 0; j < Dv; ++j) {
+        double pred = 0.0;
+        for (int i = 0; i < Dk; ++i) pred += S[i * Dv + j] * e[i];
+        u[j] = wt[j] * vt[j] - pred;
+    }
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * u[j];
+    if (ot) {
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < Dk; ++i) acc += S[i * Dv + j] * qt[i];
+            ot[j] = scale * acc;
+        }
+    }
+}
+
 void gdn2_oracle_fwd(const double *q, const double *k, const double *v,
                      const double *log_alpha, const double *bgate, const double *wgate,
                      const double *h0, double *o, double *S_out,
@@ -121,27 +148,8 @@ void gdn2_oracle_fwd(const double *q, const double *k, const double *v,
         else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
         for (long t = 0; t < T; ++t) {
             const long th = (b * T + t) * H + h;
-            const double *qt = q + th * Dk, *kt = k + th * Dk, *vt = v + th * Dv;
-            const double *la = log_alpha + th * Dk, *bt = bgate + th * Dk, *wt = wgate + th * Dv;
-            /* decay each key row by its own channel rate, before the edit */
-            for (int i = 0; i < Dk; ++i) {
-                const double a = exp(la[i]);
-                for (int j = 0; j < Dv; ++j) S[i * Dv + j] *= a;
-                e[i] = bt[i] * kt[i];
-            }
-            for (int j = 0; j < Dv; ++j) {
-                double pred = 0.0;
-                for (int i = 0; i < Dk; ++i) pred += S[i * Dv + j] * e[i];
-                u[j] = wt[j] * vt[j] - pred;
-            }
-            for (int i = 0; i < Dk; ++i)
-                for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * u[j];
-            double *ot = o + th * Dv;
-            for (int j = 0; j < Dv; ++j) {
-                double acc = 0.0;
-                for (int i = 0; i < Dk; ++i) acc += S[i * Dv + j] * qt[i];
-                ot[j] = scale * acc;
-            }
+            gdn2_token(S, q + th * Dk, k + th * Dk, v + th * Dv, log_alpha + th * Dk, bgate + th * Dk,
+                       wgate + th * Dv, u, e, o + th * Dv, Dk, Dv, scale);
         }
         if (S_out) memcpy(S_out + unit * (long)Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
         free(S);
@@ -162,5 +170,23 @@ void gdn_oracle_step(const double *q, const double *k, const double *v,
         gdn_token(S + unit * (long)Dk * Dv, q + unit * Dk, k + unit * Dk, v + unit * Dv,
                   g[unit], beta[unit], u, o + unit * Dv, Dk, Dv, scale);
         free(u);
+    }
+}
+
+/* Single-token Gated DeltaNet-2 decode step: q,k,log_alpha,b [B,H,Dk],
+ * v,w [B,H,Dv], S [B,H,Dk,Dv] in/out. */
+void gdn2_oracle_step(const double *q, const double *k, const double *v,
+                      const double *log_alpha, const double *bgate, const double *wgate,
+                      double *S, double *o, int B, int H, int Dk, int Dv, double scale, int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        double *u = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)Dk);
+        gdn2_token(S + unit * (long)Dk * Dv, q + unit * Dk, k + unit * Dk, v + unit * Dv, log_alpha + unit * Dk,
+                   bgate + unit * Dk, wgate + unit * Dv, u, e, o + unit * Dv, Dk, Dv, scale);
+        free(u);
+        free(e);
     }
 }

@@ -43,6 +43,7 @@ PIN_FUNCS = [
     pins.test_two_token_hand_expansion,
     pins.test_one_hot_keys_are_scalar_emas,
     pins.test_gdn2_one_hot_keys_are_channel_emas,
+    pins.test_hand_worked_gdn2_step,
 ]
 
 
@@ -60,11 +61,7 @@ def _build_mutant(tmp_path, name, old, new):
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_reject_mutant(tmp_path, monkeypatch, name, old, new):
     so = _build_mutant(tmp_path, name, old, new)
-    lib = ctypes.CDLL(so)
-    i, d, dp = ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double)
-    lib.gdn_oracle_fwd.argtypes = [dp] * 8 + [i] * 5 + [d, i]
-    lib.gdn2_oracle_fwd.argtypes = [dp] * 9 + [i] * 5 + [d, i]
-    lib.gdn_oracle_step.argtypes = [dp] * 7 + [i] * 4 + [d, i]
+    lib = oracle.configure(ctypes.CDLL(so))
     monkeypatch.setattr(oracle, "_lib", lib)
     caught = []
     for f in PIN_FUNCS:

@@ -349,3 +349,39 @@ def test_chunk_intermediates_solve_the_triangular_system():
     gam = np.exp(np.cumsum(g[0, :, 0]))
     rhs = beta[0, :, 0, None] * v[0, :, 0] - (beta[0, :, 0] * gam)[:, None] * (k[0, :, 0] @ S0[0, 0])
     np.testing.assert_allclose((np.eye(64) + A) @ it["Vnew"], rhs, atol=1e-12)
+
+
+# ------------------------------------------------------------- GDN-2 decode
+
+
+def test_hand_worked_gdn2_step():
+    """The hand-worked GDN-2 token (tests/golden) through the decode-step entry."""
+    ex = json.load(open(GOLDEN))["gdn2_T1_d2"]
+    a = lambda n: np.array(ex[n], dtype=np.float64)
+    o, S = oracle.gdn2_step(a("q")[:, 0], a("k")[:, 0], a("v")[:, 0], np.log(a("alpha"))[:, 0], a("b")[:, 0],
+                            a("w")[:, 0], a("h0"), scale=ex["scale"])
+    np.testing.assert_allclose(o, a("o")[:, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S, a("S"), rtol=0, atol=1e-14)
+
+
+def test_gdn2_step_tied_gates_is_gdn_step():
+    """b = w = beta on every channel and log_alpha = g: one GDN-2 step is one
+    Gated DeltaNet step (Gated DeltaNet-2 article, 'Regla-2 del Delta cerrado')."""
+    q, k, v, g, beta, S0 = _rand(3, 1, 4, 8, 6, 21)
+    Dk, Dv = q.shape[-1], v.shape[-1]
+    o1, S1 = oracle.gdn_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, scale=0.3)
+    o2, S2 = oracle.gdn2_step(q[:, 0], k[:, 0], v[:, 0], np.repeat(g[:, 0, :, None], Dk, -1),
+                              np.repeat(beta[:, 0, :, None], Dk, -1), np.repeat(beta[:, 0, :, None], Dv, -1), S0,
+                              scale=0.3)
+    np.testing.assert_allclose(o2, o1, atol=1e-14)
+    np.testing.assert_allclose(S2, S1, atol=1e-14)
+
+
+def test_gdn2_steps_chain_to_forward():
+    q, k, v, la, b, w, S0 = _rand2(2, 7, 3, 8, 6, 22, h0=True)
+    o_f, S_f = oracle.gdn2_fwd(q, k, v, la, b, w, S0, scale=0.4)
+    S = S0
+    for t in range(q.shape[1]):
+        o_t, S = oracle.gdn2_step(q[:, t], k[:, t], v[:, t], la[:, t], b[:, t], w[:, t], S, scale=0.4)
+        np.testing.assert_allclose(o_t, o_f[:, t], atol=1e-13)
+    np.testing.assert_allclose(S, S_f, atol=1e-13)
