@@ -6,7 +6,8 @@ that is already resident in HBM: one gdn_chunk_fwd call (for bf16 inputs a
 single kernel: gate cumsum, A, (I+A)^-1, the WY new values, state carry and
 output), timed with HIP events on the stream it runs on.  fp32 workloads run
 the two stage entry points and time each stage.  Other workloads: the decode
-step (--workload decode_bf16) and Gated DeltaNet-2 (--workload gdn2_bf16).
+step (--workload decode_bf16), Gated DeltaNet-2 (--workload gdn2_bf16) and its
+decode step (--workload decode2_bf16).
 
 Default workload: B=8, H=8, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates,
 fp32 output and state (the layer-shaped case).  Prints ONE JSON line on
@@ -37,10 +38,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha() -> str:
+# Sources each measured kernel is compiled from (besides build.py, whose flags
+# shape every kernel): a traffic record stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "fused_kernel": ("gdn_fused.hip", "gdn_tile.h", "gdn_device.h"),
+    "step_kernel": ("gdn_step.hip", "gdn_device.h"),
+    "step2_kernel": ("gdn_step.hip", "gdn_device.h"),
+    "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
+}
+
+
+def source_sha(kernel: str = None) -> str:
+    """Hash of the sources of `kernel` (all of csrc when None) and build.py."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "gated_delta_rule_34_amd", "build.py"))  # compile flags shape the kernels too
+    csrc = os.path.join(ROOT, "gated_delta_rule_34_amd", "csrc")
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[kernel]]
+    files.append(os.path.join(ROOT, "gated_delta_rule_34_amd", "build.py"))
     for p in files:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
@@ -57,7 +73,7 @@ def read_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha():
+    if kv.get("source_sha") != source_sha(kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -299,24 +315,37 @@ def bench_gdn2(args, wl):
     return res
 
 
+# The two decode steps: input names, entry point, oracle, kernel, extra bytes per head.
+STEPS = {
+    "decode_bf16": dict(names=("q", "k", "v", "g", "beta"), fn="gdn_recurrent_step", ref="gdn_step",
+                        kernel="step_kernel", label="gdn_recurrent_step", gate_bytes=lambda Dk, Dv, es: 8),
+    "decode2_bf16": dict(names=("q", "k", "v", "log_alpha", "b", "w"), fn="gdn2_recurrent_step", ref="gdn2_step",
+                         kernel="step2_kernel", label="gdn2_recurrent_step",
+                         gate_bytes=lambda Dk, Dv, es: 4 * Dk + es * (Dk + Dv)),
+}
+
+
 def bench_step(args, wl):
     import torch
     import gated_delta_rule_34_amd as gdn
     import gdn_inputs as gi
     import oracle
 
+    spec = STEPS[wl]
     dev = torch.device("cuda:0")
     x = gi.workload(wl)
     B, H, Dk, Dv = x["B"], x["H"], x["Dk"], x["Dv"]
-    base = {n: to_dev(x[n], dev) for n in ("q", "k", "v", "g", "beta", "S")}
+    names = spec["names"]
+    base = {n: to_dev(x[n], dev) for n in names + ("S",)}
     sets = []
     for i in range(args.sets):
         s = {n: t.clone() for n, t in base.items()}
         s["o"] = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
         sets.append(s)
+    fn = getattr(gdn, spec["fn"])
 
     def step(s):
-        gdn.gdn_recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], s["S"], scale=x["scale"], out=s["o"])
+        fn(*[s[n] for n in names], s["S"], scale=x["scale"], out=s["o"])
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -331,25 +360,27 @@ def bench_step(args, wl):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = e0.elapsed_time(e1) / args.steps
     esz = 2 if x["dtype"] == "bf16" else 4
-    kbytes = float(B) * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * esz + 8 + Dv * 4)
+    # state read and written once, q, k, v, the gates, and o
+    kbytes = float(B) * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * esz + spec["gate_bytes"](Dk, Dv, esz) + Dv * 4)
     achieved = kbytes / (kms * 1e-3) / 1e9
     res = {
-        "metric": "gdn_recurrent_step decode tokens/s (HBM roofline), B=256 H=16 d=128",
+        "metric": f"{spec['label']} decode tokens/s (HBM roofline), B={B} H={H} d={Dk}",
         "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl, "B": B, "H": H, "Dk": Dk, "Dv": Dv, "inputs": x["dtype"],
                    "state": "fp32 in place", "buffer_sets": args.sets, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "step_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": spec["kernel"], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": kbytes,
-                     "avg_launch_us": kms * 1e3, "traffic": read_traffic("step_kernel", wl)},
+                     "avg_launch_us": kms * 1e3, "traffic": read_traffic(spec["kernel"], wl)},
     }
     if not args.no_cpu_baseline:
-        args_f64 = [x[n + "_f64"] for n in ("q", "k", "v", "g", "beta", "S")]
+        args_f64 = [x[n + "_f64"] for n in names + ("S",)]
+        ref = getattr(oracle, spec["ref"])
         t0 = time.perf_counter()
         reps = 0
         while time.perf_counter() - t0 < 10.0:
-            oracle.gdn_step(*args_f64)
+            ref(*args_f64)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
         res["cpu_baseline"] = {"value": B / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
@@ -365,7 +396,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16",
-                    choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "gdn2_bf16"])
+                    choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "decode2_bf16", "gdn2_bf16"])
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -383,7 +414,7 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if args.workload == "decode_bf16":
+    if args.workload in STEPS:
         res = bench_step(args, args.workload)
     elif args.workload == "gdn2_bf16":
         res = bench_gdn2(args, args.workload)

@@ -14,6 +14,7 @@ import os
 __all__ = [
     "lib_path", "load", "status_string",
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
+    "gdn2_recurrent_step",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
     "GDN_F32", "GDN_BF16", "BT",
 ]
@@ -55,6 +56,8 @@ def load():
     lib.gdn2_chunk_fwd.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_recurrent_step.restype = _i
     lib.gdn_recurrent_step.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _vp]
+    lib.gdn2_recurrent_step.restype = _i
+    lib.gdn2_recurrent_step.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _vp]
     _lib = lib
     return lib
 
@@ -270,4 +273,28 @@ def gdn_recurrent_step(q, k, v, g, beta, S, scale=None, out=None):
     _need(o, "out", (B, H, Dv), torch.float32, dev)
     _check(load().gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
                                      B, H, Dk, Dv, dt, float(scale), _stream(dev)), "gdn_recurrent_step")
+    return o
+
+
+def gdn2_recurrent_step(q, k, v, log_alpha, b, w, S, scale=None, out=None):
+    """One GDN-2 decode token: q, k, b [B,H,Dk] and v, w [B,H,Dv] in the path dtype,
+    log_alpha [B,H,Dk] fp32, S [B,H,Dk,Dv] fp32 updated in place.  Returns o [B,H,Dv] fp32."""
+    torch = _torch()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, H, Dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (B, H, Dk), torch.float32, dev)
+    _need(b, "b", (B, H, Dk), q.dtype, dev)
+    _need(w, "w", (B, H, Dv), q.dtype, dev)
+    _need(S, "S", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, H, Dv), torch.float32, dev)
+    _check(load().gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S),
+                                      _ptr(o), B, H, Dk, Dv, dt, float(scale), _stream(dev)), "gdn2_recurrent_step")
     return o

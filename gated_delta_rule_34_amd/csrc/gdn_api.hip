@@ -236,4 +236,24 @@ gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const
                                      (hipStream_t)stream));
 }
 
+gdn_status gdn2_recurrent_step(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                               const void *w, float *S, float *o, int B, int H, int Dk, int Dv, gdn_dtype dtype,
+                               float scale, void *stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !S || !o) return GDN_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || (long long)B * H * (Dv / 64 > 0 ? Dv / 64 : 1) >= (1LL << 31))
+        return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t nh = (size_t)B * H;
+    const Range rS{S, nh * Dk * Dv * 4}, ro{o, nh * Dv * 4};
+    const Range rq{q, nh * Dk * es}, rk{k, nh * Dk * es}, rv{v, nh * Dv * es};
+    const Range rla{log_alpha, nh * Dk * 4}, rb{b, nh * Dk * es}, rw{w, nh * Dv * es};
+    for (Range in : {rq, rk, rv, rla, rb, rw, ro})
+        if (overlap(rS, in)) return GDN_ERR_INVALID_ARG;
+    for (Range in : {rq, rk, rv, rla, rb, rw})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_step2(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dtype == GDN_BF16, scale,
+                                      (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -41,4 +41,8 @@ hipError_t launch_step(const void *q, const void *k, const void *v, const float 
                        float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                        hipStream_t st);
 
+hipError_t launch_step2(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                        const void *wg, float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
+                        hipStream_t st);
+
 }  // namespace gdn

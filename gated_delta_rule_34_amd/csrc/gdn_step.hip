@@ -54,6 +54,52 @@ __global__ __launch_bounds__(64) void step_kernel(const typename Pol::in_t *__re
     o[unit * DV + col] = scale * acc;
 }
 
+// One Gated DeltaNet-2 decode token (Gated DeltaNet-2 article, "Regla-2 del
+// Delta cerrado", one step of the recurrence): rows of S decay by their own
+// channel rate, S <- Diag(alpha) S; u = w . v - S^T (b . k); S <- S + k u^T;
+// o = scale S^T q.  Same layout as step_kernel: one thread per value column,
+// the column's Dk state values in registers.
+template <class Pol, int DK, int DV>
+__global__ __launch_bounds__(64) void step2_kernel(const typename Pol::in_t *__restrict__ q,
+                                                   const typename Pol::in_t *__restrict__ k,
+                                                   const typename Pol::in_t *__restrict__ v,
+                                                   const float *__restrict__ la,
+                                                   const typename Pol::in_t *__restrict__ bg,
+                                                   const typename Pol::in_t *__restrict__ wg, float *__restrict__ S,
+                                                   float *__restrict__ o, float scale) {
+    constexpr int NCB = DV / 64;  // 64-column blocks per head
+    __shared__ float sq[DK], sk[DK], se[DK], sa[DK];
+    const long unit = blockIdx.x / NCB;  // (b, h)
+    const int col = (blockIdx.x % NCB) * 64 + threadIdx.x;
+    for (int i = threadIdx.x; i < DK; i += 64) {
+        const float kk = load_elem(k + unit * DK + i);
+        sq[i] = load_elem(q + unit * DK + i);
+        sk[i] = kk;
+        se[i] = load_elem(bg + unit * DK + i) * kk;
+        sa[i] = expf(la[unit * DK + i]);
+    }
+    __syncthreads();
+    float *Sc = S + unit * (long)DK * DV + col;
+    float s[DK];
+#pragma unroll
+    for (int i = 0; i < DK; ++i) s[i] = Sc[(long)i * DV];
+    float pred = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+        s[i] *= sa[i];
+        pred = fmaf(s[i], se[i], pred);
+    }
+    const float uu = load_elem(wg + unit * DV + col) * load_elem(v + unit * DV + col) - pred;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+        s[i] = fmaf(sk[i], uu, s[i]);
+        acc = fmaf(s[i], sq[i], acc);
+        Sc[(long)i * DV] = s[i];
+    }
+    o[unit * DV + col] = scale * acc;
+}
+
 template <class Pol, int DK, int DV>
 static hipError_t launch_step_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
                                 float *S, float *o, int B, int H, float scale, hipStream_t st) {
@@ -81,6 +127,36 @@ hipError_t launch_step(const void *q, const void *k, const void *v, const float 
         GDN_STEP(PolF32, 128, 128);
     }
 #undef GDN_STEP
+    return hipErrorInvalidValue;
+}
+
+template <class Pol, int DK, int DV>
+static hipError_t launch_step2_t(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                                 const void *wg, float *S, float *o, int B, int H, float scale, hipStream_t st) {
+    using in_t = typename Pol::in_t;
+    const long grid = (long)B * H * (DV / 64);
+    hipLaunchKernelGGL((step2_kernel<Pol, DK, DV>), dim3((unsigned)grid), dim3(64), 0, st, (const in_t *)q,
+                       (const in_t *)k, (const in_t *)v, la, (const in_t *)bg, (const in_t *)wg, S, o, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_step2(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                        const void *wg, float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
+                        hipStream_t st) {
+#define GDN_STEP2(P, DKv, DVv) \
+    if (Dk == DKv && Dv == DVv) return launch_step2_t<P, DKv, DVv>(q, k, v, la, bg, wg, S, o, B, H, scale, st)
+    if (bf16) {
+        GDN_STEP2(PolBF16, 64, 64);
+        GDN_STEP2(PolBF16, 64, 128);
+        GDN_STEP2(PolBF16, 128, 64);
+        GDN_STEP2(PolBF16, 128, 128);
+    } else {
+        GDN_STEP2(PolF32, 64, 64);
+        GDN_STEP2(PolF32, 64, 128);
+        GDN_STEP2(PolF32, 128, 64);
+        GDN_STEP2(PolF32, 128, 128);
+    }
+#undef GDN_STEP2
     return hipErrorInvalidValue;
 }
 

@@ -32,6 +32,7 @@ __all__ = [
     "gdn2_inputs",
     "step_inputs",
     "WORKLOADS",
+    "step2_inputs",
 ]
 
 # Named workloads: shapes and dtypes of the measured and parity cases.
@@ -41,6 +42,7 @@ WORKLOADS = {
     "long_bf16": dict(kind="gdn", B=1, H=16, T=65536, Dk=128, Dv=128, dtype="bf16", h0=True, seed=1002),
     "decode_bf16": dict(kind="step", B=256, H=16, Dk=128, Dv=128, dtype="bf16", seed=1003),
     "gdn2_bf16": dict(kind="gdn2", B=4, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1004),
+    "decode2_bf16": dict(kind="step2", B=256, H=16, Dk=128, Dv=128, dtype="bf16", seed=1005),
 }
 
 
@@ -162,6 +164,29 @@ def step_inputs(B, H, Dk, Dv, seed, dtype="bf16", a_range=(1.0, 16.0)):
     return out
 
 
+def step2_inputs(B, H, Dk, Dv, seed, dtype="bf16"):
+    """Inputs of one GDN-2 decode step: [B, H, D] token tensors and gates
+    (per-channel log-decay, erase and write gates drawn as in gdn2_inputs),
+    fp32 state S ~ N(0, 0.02) of shape [B, H, Dk, Dv]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(rng.standard_normal((B, H, Dk)))
+    k = _l2n(rng.standard_normal((B, H, Dk)))
+    v = rng.standard_normal((B, H, Dv))
+    log_alpha = -_softplus(rng.standard_normal((B, H, Dk)))
+    b = _sigmoid(rng.standard_normal((B, H, Dk)))
+    w = _sigmoid(rng.standard_normal((B, H, Dv)))
+    S = 0.02 * rng.standard_normal((B, H, Dk, Dv))
+    out = {"B": B, "H": H, "Dk": Dk, "Dv": Dv, "dtype": dtype, "scale": 1.0 / np.sqrt(Dk)}
+    _pack(out, "q", q, dtype)
+    _pack(out, "k", k, dtype)
+    _pack(out, "v", v, dtype)
+    out["log_alpha"], out["log_alpha_f64"] = _f32(log_alpha)
+    _pack(out, "b", b, dtype)
+    _pack(out, "w", w, dtype)
+    out["S"], out["S_f64"] = _f32(S)
+    return out
+
+
 def workload(name: str, **overrides):
     """Build the inputs of a named workload (see WORKLOADS); keyword overrides
     replace shape or seed fields (used for reduced-size parity cases)."""
@@ -176,4 +201,6 @@ def workload(name: str, **overrides):
                            dtype=cfg["dtype"], h0=cfg["h0"])
     if kind == "step":
         return step_inputs(cfg["B"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"], dtype=cfg["dtype"])
+    if kind == "step2":
+        return step2_inputs(cfg["B"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"], dtype=cfg["dtype"])
     raise ValueError(kind)

@@ -146,6 +146,26 @@ gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v,
                               int B, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
                               void *stream);
 
+/*
+ * gdn2_recurrent_step -- one decode token of Gated DeltaNet-2, state updated
+ * in place (one step of the recurrence in the Gated DeltaNet-2 article,
+ * section "Regla-2 del Delta cerrado"):
+ *   S <- Diag(exp(log_alpha)) S;  u = w . v - S^T (b . k);  S <- S + k u^T;
+ *   o = scale S^T q
+ *   q, k [B, H, Dk] dtype;  v [B, H, Dv] dtype
+ *   log_alpha [B, H, Dk] fp32 (<= 0);  b [B, H, Dk] dtype;  w [B, H, Dv] dtype
+ *   S    [B, H, Dk, Dv] fp32, read and written in place
+ *   o    [B, H, Dv] fp32
+ * Errors: GDN_ERR_INVALID_ARG for null pointers, non-positive sizes or
+ * overlapping S / o with any other buffer; GDN_ERR_UNSUPPORTED for head sizes
+ * other than 64 and 128 or an unknown dtype; GDN_ERR_HIP if the launch fails.
+ * Asynchronous on `stream`; the caller owns every buffer.
+ */
+gdn_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const void *b, const void *w,
+                               float *S, float *o, int B, int H, int Dk, int Dv,
+                               gdn_dtype dtype, float scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

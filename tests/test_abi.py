@@ -26,7 +26,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_intra",
+    for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn2_recurrent_step", "gdn_chunk_intra",
               "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string"):
         assert n in names
 
@@ -95,6 +95,18 @@ def test_step_and_intra_reject_bad_arguments():
     assert f(*base[:5], base[0], base[6], 4, 2, 128, 128, 1) == 1   # S overlaps q
     assert lib.gdn_chunk_intra(None, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 1, 64, 1, 128, 1, None) == 1
     assert lib.gdn_chunk_intra(_p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 1, 64, 1, 48, 1, None) == 2
+
+
+def test_gdn2_step_rejects_bad_arguments():
+    lib = gdn.load()
+    f = lambda *a: lib.gdn2_recurrent_step(*[_p(x) for x in a[:8]], *a[8:], 0.1, None)
+    base = [FAKE + (i << 32) for i in range(8)]
+    assert f(*base[:7], None, 4, 2, 128, 128, 1) == 1                  # no output
+    assert f(*base, 0, 2, 128, 128, 1) == 1                            # B = 0
+    assert f(*base, 4, 2, 96, 128, 1) == 2                             # unsupported head size
+    assert f(*base, 4, 2, 128, 128, 5) == 2                            # unknown dtype
+    assert f(*base[:6], base[3], base[7], 4, 2, 128, 128, 1) == 1      # S overlaps log_alpha
+    assert f(*base[:7], base[1], 4, 2, 128, 128, 1) == 1               # o overlaps k
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
