@@ -63,6 +63,7 @@ def configure(lib):
     lib.gdn2_oracle_fwd.argtypes = [_dp] * 9 + [i] * 5 + [d, i]
     lib.gdn_oracle_step.argtypes = [_dp] * 7 + [i] * 4 + [d, i]
     lib.gdn2_oracle_step.argtypes = [_dp] * 8 + [i] * 4 + [d, i]
+    lib.gdn_oracle_bwd.argtypes = [_dp] * 14 + [i] * 5 + [d, i]
     lib.gdn_oracle_max_threads.restype = i
     return lib
 
@@ -135,3 +136,22 @@ def gdn2_step(q, k, v, log_alpha, b, w, S, scale=None, nthreads=0):
     _load().gdn2_oracle_step(*[p for _, p in keep], S_new.ctypes.data_as(_dp), o.ctypes.data_as(_dp),
                              B, H, Dk, Dv, float(scale), int(nthreads))
     return o, S_new
+
+
+def gdn_bwd(q, k, v, g, beta, h0, dO, dST=None, scale=None, nthreads=0):
+    """Gradients of L = sum(dO * o) + sum(dST * S_T) for the per-token GDN
+    recurrence: returns dq, dk, dv, dg, dbeta, dh0 (dh0 is None when h0 is None)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if scale is None:
+        scale = Dk ** -0.5
+    keep = [_c(x) for x in (q, k, v, g, beta, h0, dO, dST)]
+    dq = np.zeros((B, T, H, Dk))
+    dk = np.zeros((B, T, H, Dk))
+    dv = np.zeros((B, T, H, Dv))
+    dg = np.zeros((B, T, H))
+    db = np.zeros((B, T, H))
+    dh0 = np.zeros((B, H, Dk, Dv)) if h0 is not None else None
+    outs = [a.ctypes.data_as(_dp) for a in (dq, dk, dv, dg, db)] + [dh0.ctypes.data_as(_dp) if dh0 is not None else None]
+    _load().gdn_oracle_bwd(*[p for _, p in keep], *outs, B, T, H, Dk, Dv, float(scale), int(nthreads))
+    return dq, dk, dv, dg, db, dh0

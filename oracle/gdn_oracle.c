@@ -190,3 +190,116 @@ void gdn2_oracle_step(const double *q, const double *k, const double *v,
         free(e);
     }
 }
+
+/*
+ * Backward of the Gated DeltaNet forward: reverse-mode differentiation of the
+ * per-token recurrence above for the loss L = sum(dO . o) + sum(dST . S_T).
+ * Per token, with S' = exp(g) S_{t-1}, p = S'^T k, u = beta (v - p),
+ * S_t = S' + k u^T, o = scale S_t^T q, and D the gradient of L w.r.t. S_t:
+ *   D   += scale q do^T          dq    = scale S_t do
+ *   dk   = D u                   du    = D^T k
+ *   dbeta = du . (v - p)         dv    = beta du
+ *   D'   = D - beta k du^T       dk   -= beta S' du
+ *   dg    = <D', S'>             D     = exp(g) D'      (gradient w.r.t. S_{t-1})
+ * and dh0 = D after the first token.  States are recomputed forward one
+ * 64-token segment at a time from stored segment-start states.
+ * dO [B,T,H,Dv]; dST [B,H,Dk,Dv] or NULL; outputs dq, dk [B,T,H,Dk],
+ * dv [B,T,H,Dv], dg, dbeta [B,T,H], dh0 [B,H,Dk,Dv] or NULL.
+ */
+void gdn_oracle_bwd(const double *q, const double *k, const double *v, const double *g, const double *beta,
+                    const double *h0, const double *dO, const double *dST, double *dq, double *dk, double *dv,
+                    double *dg, double *dbeta, double *dh0, int B, int T, int H, int Dk, int Dv, double scale,
+                    int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+    const int SEG = 64;
+    const int nseg = (T + SEG - 1) / SEG;
+    const size_t SS = (size_t)Dk * Dv;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        const long b = unit / H, h = unit % H;
+        double *starts = (double *)malloc(sizeof(double) * SS * (size_t)nseg);
+        double *Sp = (double *)malloc(sizeof(double) * SS * (size_t)SEG);  /* S' of each token of a segment */
+        double *us = (double *)malloc(sizeof(double) * (size_t)Dv * SEG);   /* u of each token */
+        double *ps = (double *)malloc(sizeof(double) * (size_t)Dv * SEG);   /* p of each token */
+        double *S = (double *)malloc(sizeof(double) * SS);
+        double *St = (double *)malloc(sizeof(double) * SS);
+        double *D = (double *)malloc(sizeof(double) * SS);
+        double *du = (double *)malloc(sizeof(double) * (size_t)Dv);
+        /* forward: segment-start states */
+        if (h0) memcpy(S, h0 + unit * (long)SS, sizeof(double) * SS);
+        else memset(S, 0, sizeof(double) * SS);
+        for (long t = 0; t < T; ++t) {
+            if (t % SEG == 0) memcpy(starts + (size_t)(t / SEG) * SS, S, sizeof(double) * SS);
+            const long th = (b * T + t) * H + h;
+            gdn_token(S, q + th * Dk, k + th * Dk, v + th * Dv, g[th], beta[th], du, NULL, Dk, Dv, scale);
+        }
+        if (dST) memcpy(D, dST + unit * (long)SS, sizeof(double) * SS);
+        else memset(D, 0, sizeof(double) * SS);
+        for (int sg = nseg - 1; sg >= 0; --sg) {
+            const long t0 = (long)sg * SEG, t1 = (t0 + SEG < T) ? t0 + SEG : T;
+            /* recompute S', p, u of the segment */
+            memcpy(S, starts + (size_t)sg * SS, sizeof(double) * SS);
+            for (long t = t0; t < t1; ++t) {
+                const long th = (b * T + t) * H + h, x = t - t0;
+                const double *kt = k + th * Dk, *vt = v + th * Dv;
+                const double decay = exp(g[th]);
+                double *spx = Sp + (size_t)x * SS;
+                for (size_t i = 0; i < SS; ++i) spx[i] = S[i] * decay;
+                for (int j = 0; j < Dv; ++j) {
+                    double p = 0.0;
+                    for (int i = 0; i < Dk; ++i) p += spx[i * Dv + j] * kt[i];
+                    ps[(size_t)x * Dv + j] = p;
+                    us[(size_t)x * Dv + j] = beta[th] * (vt[j] - p);
+                }
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) S[i * Dv + j] = spx[i * Dv + j] + kt[i] * us[(size_t)x * Dv + j];
+            }
+            /* reverse through the segment */
+            for (long t = t1 - 1; t >= t0; --t) {
+                const long th = (b * T + t) * H + h, x = t - t0;
+                const double *qt = q + th * Dk, *kt = k + th * Dk, *vt = v + th * Dv, *dot = dO + th * Dv;
+                const double *spx = Sp + (size_t)x * SS, *ux = us + (size_t)x * Dv, *px = ps + (size_t)x * Dv;
+                const double bt = beta[th];
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) St[i * Dv + j] = spx[i * Dv + j] + kt[i] * ux[j];
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) D[i * Dv + j] += scale * qt[i] * dot[j];
+                double *dqt = dq + th * Dk, *dkt = dk + th * Dk, *dvt = dv + th * Dv;
+                for (int i = 0; i < Dk; ++i) {
+                    double a = 0.0, c = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        a += St[i * Dv + j] * dot[j];
+                        c += D[i * Dv + j] * ux[j];
+                    }
+                    dqt[i] = scale * a;
+                    dkt[i] = c;
+                }
+                double db = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    double a = 0.0;
+                    for (int i = 0; i < Dk; ++i) a += D[i * Dv + j] * kt[i];
+                    du[j] = a;
+                    db += a * (vt[j] - px[j]);
+                    dvt[j] = bt * a;
+                }
+                dbeta[th] = db;
+                for (int i = 0; i < Dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        D[i * Dv + j] -= bt * kt[i] * du[j];
+                        a += spx[i * Dv + j] * du[j];
+                    }
+                    dkt[i] -= bt * a;
+                }
+                double dgt = 0.0;
+                for (size_t i = 0; i < SS; ++i) dgt += D[i] * spx[i];
+                dg[th] = dgt;
+                const double decay = exp(g[th]);
+                for (size_t i = 0; i < SS; ++i) D[i] *= decay;
+            }
+        }
+        if (dh0) memcpy(dh0 + unit * (long)SS, D, sizeof(double) * SS);
+        free(starts); free(Sp); free(us); free(ps); free(S); free(St); free(D); free(du);
+    }
+}

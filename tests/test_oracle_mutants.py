@@ -9,6 +9,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_bwd as bwd_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
@@ -29,6 +30,13 @@ MUTANTS = [
     ("gdn2_write_gate_on_error", "u[j] = wt[j] * vt[j] - pred;", "u[j] = wt[j] * (vt[j] - pred);"),
     ("gdn2_decay_uniform", "const double a = exp(la[i]);", "const double a = exp(la[0]);"),
     ("gdn2_readout_scale", "ot[j] = scale * acc;", "ot[j] = acc;"),
+    ("bwd_dq_pre_edit_state", "a += St[i * Dv + j] * dot[j];", "a += spx[i * Dv + j] * dot[j];"),
+    ("bwd_dk_erase_term_dropped", "dkt[i] -= bt * a;", "dkt[i] -= 0.0 * a;"),
+    ("bwd_dbeta_raw_value", "db += a * (vt[j] - px[j]);", "db += a * vt[j];"),
+    ("bwd_no_state_decay", "for (size_t i = 0; i < SS; ++i) D[i] *= decay;", "for (size_t i = 0; i < SS; ++i) D[i] *= 1.0;"),
+    ("bwd_dg_post_edit_state", "for (size_t i = 0; i < SS; ++i) dgt += D[i] * spx[i];",
+     "for (size_t i = 0; i < SS; ++i) dgt += D[i] * St[i];"),
+    ("bwd_output_grad_unscaled", "D[i * Dv + j] += scale * qt[i] * dot[j];", "D[i * Dv + j] += qt[i] * dot[j];"),
 ]
 
 PIN_FUNCS = [
@@ -44,6 +52,7 @@ PIN_FUNCS = [
     pins.test_one_hot_keys_are_scalar_emas,
     pins.test_gdn2_one_hot_keys_are_channel_emas,
     pins.test_hand_worked_gdn2_step,
+    bwd_pins.pin_backward_fd,
 ]
 
 
