@@ -134,3 +134,108 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, h0=None, scale=None, C=64):
                 q[bb, :, h], k[bb, :, h], v[bb, :, h], log_alpha[bb, :, h], b[bb, :, h],
                 w[bb, :, h], S0, scale, C)
     return o, S
+
+
+def gdn_chunk_bwd_head(q, k, v, g, beta, S0, dO, dST, scale, C=64):
+    """Backward of gdn_chunk_head for one head (the chunk equations above,
+    differentiated in reverse chunk order).  dO [T,Dv], dST [Dk,Dv] or None.
+    Returns dq, dk [T,Dk], dv [T,Dv], dg, dbeta [T], dS0 [Dk,Dv].
+
+    Per chunk with entry state S (from a forward pass), D_ij = exp(G_i - G_j)
+    for j <= i, Kd_j = k_j exp(G_C - G_j), R = diag(beta) (V - diag(gamma) K S),
+    Vnew = T R, O = scale (diag(gamma) Q S + P Vnew), S' = gamma_C S + Kd^T Vnew,
+    and dS' the gradient of the state leaving the chunk:
+        dVnew = scale P^T dO + Kd dS'        dR = T^T dVnew
+        dA    = -strict_lower(dR Vnew^T)     dP = scale lower(dO Vnew^T)
+        dS    = gamma_C dS' + scale (diag(gamma) Q)^T dO - (diag(beta gamma) K)^T dR
+    then the chain rule through A_ij = beta_i (k_i.k_j) D_ij, P_ij = (q_i.k_j) D_ij,
+    R, the state term of O, and Kd gives dq, dk, dv, dbeta and dG; dg is the
+    reverse cumulative sum of dG within the chunk."""
+    T = q.shape[0]
+    Dk, Dv = q.shape[1], v.shape[1]
+    # forward: entry states of the chunks
+    starts = []
+    S = np.array(S0, dtype=np.float64, copy=True)
+    for s in range(0, T, C):
+        starts.append(S)
+        _, S, _ = gdn_chunk_head(q[s:s + C], k[s:s + C], v[s:s + C], g[s:s + C], beta[s:s + C], S, scale, C)
+    dq = np.zeros((T, Dk))
+    dk = np.zeros((T, Dk))
+    dv = np.zeros((T, Dv))
+    dg = np.zeros(T)
+    db = np.zeros(T)
+    dS = np.zeros((Dk, Dv)) if dST is None else np.array(dST, dtype=np.float64, copy=True)
+    for ci in range(len(starts) - 1, -1, -1):
+        s = ci * C
+        e = min(s + C, T)
+        S = starts[ci]
+        Q, K, V, gc, bc, dOc = q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e], dO[s:e]
+        n = e - s
+        G = np.cumsum(gc)
+        gamma = np.exp(G)
+        lower_incl = np.tril(np.ones((n, n), dtype=bool))
+        D = np.exp(np.where(lower_incl, G[:, None] - G[None, :], -np.inf))
+        KK = K @ K.T
+        A = np.tril(bc[:, None] * KK * D, -1)
+        Tm = _tri_inverse(A)
+        KS = K @ S
+        R = bc[:, None] * (V - gamma[:, None] * KS)
+        Vn = Tm @ R
+        P = (Q @ K.T) * D
+        dec = np.exp(G[-1] - G)
+        Kd = K * dec[:, None]
+        dSp = dS                                          # gradient of the state leaving the chunk
+        dVn = scale * P.T @ dOc + Kd @ dSp
+        dR = Tm.T @ dVn
+        dA = -np.tril(dR @ Vn.T, -1)
+        dP = scale * np.tril(dOc @ Vn.T)
+        dS = gamma[-1] * dSp + scale * (gamma[:, None] * Q).T @ dOc - ((bc * gamma)[:, None] * K).T @ dR
+        dG = np.zeros(n)
+        # R = diag(beta) (V - diag(gamma) K S)
+        dv[s:e] = bc[:, None] * dR
+        db[s:e] += np.sum(dR * (V - gamma[:, None] * KS), axis=1)
+        dk[s:e] += -(bc * gamma)[:, None] * (dR @ S.T)
+        dG += -bc * gamma * np.sum(dR * KS, axis=1)
+        # A_ij = beta_i (k_i.k_j) D_ij, strictly lower
+        dAs = dA * D
+        db[s:e] += np.sum(dAs * KK, axis=1)
+        dk[s:e] += bc[:, None] * (dAs @ K) + dAs.T @ (bc[:, None] * K)
+        dAA = dA * A
+        dG += np.sum(dAA, axis=1) - np.sum(dAA, axis=0)
+        # P_ij = (q_i.k_j) D_ij, lower incl. diagonal
+        dPs = dP * D
+        dq[s:e] += dPs @ K
+        dk[s:e] += dPs.T @ Q
+        dPP = dP * P
+        dG += np.sum(dPP, axis=1) - np.sum(dPP, axis=0)
+        # state term of O: scale diag(gamma) Q S
+        QS = Q @ S
+        dq[s:e] += scale * gamma[:, None] * (dOc @ S.T)
+        dG += scale * gamma * np.sum(dOc * QS, axis=1)
+        # S' = gamma_C S + Kd^T Vn
+        dG[-1] += gamma[-1] * np.sum(dSp * S)
+        dKd = Vn @ dSp.T
+        dk[s:e] += dec[:, None] * dKd
+        t = np.sum(dKd * Kd, axis=1)
+        dG[-1] += np.sum(t)
+        dG -= t
+        # G_i = sum_{s<=i} g_s within the chunk
+        dg[s:e] = np.cumsum(dG[::-1])[::-1]
+    return dq, dk, dv, dg, db, dS
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, h0, dO, dST=None, scale=None, C=64):
+    """All heads, [B,T,H,D] layout.  Returns dq, dk, dv, dg, dbeta, dh0."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if scale is None:
+        scale = Dk ** -0.5
+    dq = np.zeros((B, T, H, Dk)); dk = np.zeros((B, T, H, Dk)); dv = np.zeros((B, T, H, Dv))
+    dg = np.zeros((B, T, H)); db = np.zeros((B, T, H)); dh0 = np.zeros((B, H, Dk, Dv))
+    for b in range(B):
+        for h in range(H):
+            S0 = np.zeros((Dk, Dv)) if h0 is None else h0[b, h]
+            r = gdn_chunk_bwd_head(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h], beta[b, :, h], S0, dO[b, :, h],
+                                   None if dST is None else dST[b, h], scale, C)
+            dq[b, :, h], dk[b, :, h], dv[b, :, h], dg[b, :, h], db[b, :, h], dh0[b, h] = r
+    return dq, dk, dv, dg, db, dh0

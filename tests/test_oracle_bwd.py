@@ -73,3 +73,15 @@ def test_no_final_state_gradient_and_no_h0():
 def pin_backward_fd():
     """Entry for the mutant check (not collected): the T = 150 finite-difference pin."""
     test_gradients_match_finite_differences(150)
+
+
+@pytest.mark.parametrize("T,C", [(150, 64), (200, 16), (64, 64), (1, 64)])
+def test_chunked_backward_equals_recurrence_backward(T, C):
+    """The chunked (WY-form) backward in oracle/chunked.py, which the GPU
+    backward follows, equals the pinned per-token backward."""
+    from oracle import chunked
+    x, dO, dST = _case(2, T, 2, 6, 5, seed=500 + T)
+    ref = oracle.gdn_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], dO, dST, scale=0.7)
+    got = chunked.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], dO, dST, scale=0.7, C=C)
+    for a, b in zip(ref, got):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12 * max(1.0, np.abs(a).max()))
