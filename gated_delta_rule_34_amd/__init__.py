@@ -14,7 +14,7 @@ import os
 __all__ = [
     "lib_path", "load", "status_string",
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
-    "gdn2_recurrent_step",
+    "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
     "GDN_F32", "GDN_BF16", "BT",
 ]
@@ -56,6 +56,10 @@ def load():
     lib.gdn2_chunk_fwd.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_recurrent_step.restype = _i
     lib.gdn_recurrent_step.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _vp]
+    lib.gdn_chunk_bwd_workspace.restype = _sz
+    lib.gdn_chunk_bwd_workspace.argtypes = [_i] * 6
+    lib.gdn_chunk_bwd.restype = _i
+    lib.gdn_chunk_bwd.argtypes = [_vp] * 14 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn2_recurrent_step.restype = _i
     lib.gdn2_recurrent_step.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _vp]
     _lib = lib
@@ -159,6 +163,49 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=None, output_final_state=True
                              B, T, H, Dk, Dv, dt, float(scale), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(dev)), "gdn_chunk_fwd")
     return o, ht
+
+
+def gdn_chunk_bwd_workspace(B, T, H, Dk, Dv, dtype_code):
+    return int(load().gdn_chunk_bwd_workspace(B, T, H, Dk, Dv, dtype_code))
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, h0, do, dht=None, scale=None, workspace=None):
+    """Backward of gdn_chunk_fwd: gradients of sum(do * o) + sum(dht * ht).
+    Inputs as gdn_chunk_fwd (h0 may be None), do [B,T,H,Dv] fp32, dht [B,H,Dk,Dv]
+    fp32 or None.  Returns (dq, dk, dv, dg, dbeta, dh0) fp32; dh0 is None when h0 is."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(do, "do", (B, T, H, Dv), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if dht is not None:
+        _need(dht, "dht", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    dg = torch.empty((B, T, H), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dh0 = torch.empty((B, H, Dk, Dv), **f32) if h0 is not None else None
+    lib = load()
+    need = lib.gdn_chunk_bwd_workspace(B, T, H, Dk, Dv, dt)
+    if need == 0:
+        _check(2, "gdn_chunk_bwd_workspace")
+    ws = workspace if workspace is not None else _workspace(need, dev)[1]
+    _check(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, dt,
+                             float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)), "gdn_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def gdn_chunk_intra(k, g, beta, G2_out=None, Tinv_out=None):

@@ -118,7 +118,7 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     float *Tinv = (float *)((char *)ws + lay.t_off);
     gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, dtype == GDN_BF16, st));
     if (s != GDN_OK) return s;
-    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, Dk, Dv, dtype == GDN_BF16,
+    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, nullptr, B, T, H, Dk, Dv, dtype == GDN_BF16,
                                      scale, st));
 }
 
@@ -142,7 +142,7 @@ gdn_status gdn_chunk_walk(const void *q, const void *k, const void *v, const flo
         for (Range in : {rq, rk, rv, rb, rg2, rt, ro})
             if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
     }
-    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, Dk, Dv, dtype == GDN_BF16,
+    return from_hip(gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, o, ht, nullptr, B, T, H, Dk, Dv, dtype == GDN_BF16,
                                      scale, (hipStream_t)stream));
 }
 
@@ -254,6 +254,66 @@ gdn_status gdn2_recurrent_step(const void *q, const void *k, const void *v, cons
         if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
     return from_hip(gdn::launch_step2(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dtype == GDN_BF16, scale,
                                       (hipStream_t)stream));
+}
+
+// Workspace of the backward: the forward's intra stage (G2, T - I), then the
+// entry state and the leaving-state gradient of every chunk, fp32
+// [B, H, NT, Dk, Dv] each.
+struct BwdWs {
+    size_t ck_off, dck_off, total;
+};
+
+BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv) {
+    const size_t NT = (size_t)(T + kBT - 1) / kBT;
+    const size_t st = align_up((size_t)B * H * NT * Dk * Dv * sizeof(float));
+    BwdWs w;
+    w.ck_off = chunk_ws(B, T, H).total;
+    w.dck_off = w.ck_off + st;
+    w.total = w.dck_off + st;
+    return w;
+}
+
+size_t gdn_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
+    if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
+    return bwd_ws(B, T, H, Dk, Dv).total;
+}
+
+gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *h0, const float *dO, const float *dht, float *dq, float *dk, float *dv,
+                         float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv, gdn_dtype dtype,
+                         float scale, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta) return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const BwdWs lay = bwd_ws(B, T, H, Dk, Dv);
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
+    const Range ins[] = {{q, ntok * Dk * es}, {k, ntok * Dk * es}, {v, ntok * Dv * es}, {g, ntok * 4},
+                         {beta, ntok * 4}, {h0, h0 ? nstate : 0}, {dO, ntok * Dv * 4}, {dht, dht ? nstate : 0}};
+    const Range outs[] = {{dq, ntok * Dk * 4}, {dk, ntok * Dk * 4}, {dv, ntok * Dv * 4}, {dg, ntok * 4},
+                          {dbeta, ntok * 4}, {dh0, dh0 ? nstate : 0}, {ws, lay.total}};
+    const int nouts = sizeof(outs) / sizeof(outs[0]);
+    for (int a = 0; a < nouts; ++a) {
+        for (Range in : ins)
+            if (overlap(outs[a], in)) return GDN_ERR_INVALID_ARG;
+        for (int c = a + 1; c < nouts; ++c)
+            if (overlap(outs[a], outs[c])) return GDN_ERR_INVALID_ARG;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const ChunkWs cw = chunk_ws(B, T, H);
+    char *base = (char *)ws;
+    float *G2 = (float *)(base + cw.g2_off), *Tinv = (float *)(base + cw.t_off);
+    float *Sck = (float *)(base + lay.ck_off), *dSck = (float *)(base + lay.dck_off);
+    const bool bf = dtype == GDN_BF16;
+    gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, bf, st, true));
+    if (s != GDN_OK) return s;
+    s = from_hip(
+        gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, nullptr, nullptr, Sck, B, T, H, Dk, Dv, bf, scale, st, true));
+    if (s != GDN_OK) return s;
+    return from_hip(gdn::launch_bwd(q, k, v, beta, dO, dht, G2, Tinv, Sck, dSck, dq, dk, dv, dg, dbeta, dh0, B, T, H,
+                                    Dk, Dv, bf, scale, st));
 }
 
 }  // extern "C"

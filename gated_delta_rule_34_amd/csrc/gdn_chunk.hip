@@ -167,8 +167,8 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
                                                       const float *__restrict__ G2ws,
                                                       const float *__restrict__ Tws,
                                                       const float *__restrict__ h0, float *__restrict__ o,
-                                                      float *__restrict__ ht, int T, int H, int NT,
-                                                      float scale) {
+                                                      float *__restrict__ ht, float *__restrict__ ck, int T,
+                                                      int H, int NT, float scale) {
     using mt = typename Pol::mt;
     using in_t = typename Pol::in_t;
     constexpr int NW = BV / 16;
@@ -203,6 +203,12 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
     for (int c = 0; c < NT; ++c) {
         const int t0 = c * BT;
         const long cbase = bh * NT + c;
+        if (ck) {  // entry state of chunk c, [B, H, NT, DK, DV]
+#pragma unroll
+            for (int m = 0; m < NKB; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ck[cbase * DK * DV + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+        }
         if (tid < BT) {
             const float G2 = G2ws[cbase * BT + tid];
             const float G2L = G2ws[cbase * BT + BT - 1];
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = t0 + 16 * I + 4 * g + e;
-                if (t < T) o[((b * T + t) * H + h) * (long)DV + col] = scale * acc[e];
+                if (o && t < T) o[((b * T + t) * H + h) * (long)DV + col] = scale * acc[e];
             }
         }
         // State carry: S = gamma_C S + Kdecayed^T Vnew.
@@ -369,7 +375,11 @@ static hipError_t launch_intra_t(const void *k, const float *g, const float *bet
 }
 
 hipError_t launch_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
-                        int T, int H, int Dk, bool bf16, hipStream_t st) {
+                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact) {
+    if (bf16 && exact) {
+        if (Dk == 64) return launch_intra_t<PolBF16F32, 64>(k, g, beta, G2, Tinv, B, T, H, st);
+        return launch_intra_t<PolBF16F32, 128>(k, g, beta, G2, Tinv, B, T, H, st);
+    }
     if (bf16) {
         if (Dk == 64) return launch_intra_t<PolBF16, 64>(k, g, beta, G2, Tinv, B, T, H, st);
         return launch_intra_t<PolBF16, 128>(k, g, beta, G2, Tinv, B, T, H, st);
@@ -381,23 +391,28 @@ hipError_t launch_intra(const void *k, const float *g, const float *beta, float 
 template <class Pol, int DK, int DV>
 static hipError_t launch_walk_t(const void *q, const void *k, const void *v, const float *beta,
                                 const float *G2, const float *Tinv, const float *h0, float *o, float *ht,
-                                int B, int T, int H, float scale, hipStream_t st) {
+                                float *ck, int B, int T, int H, float scale, hipStream_t st) {
     constexpr int BV = 32;
     const int NT = (T + BT - 1) / BT;
     const long grid = (long)B * H * (DV / BV);
     using in_t = typename Pol::in_t;
     hipLaunchKernelGGL((walk_kernel<Pol, DK, DV, BV>), dim3((unsigned)grid), dim3(BV * 4), 0, st,
-                       (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, G2, Tinv, h0, o, ht, T, H,
+                       (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, G2, Tinv, h0, o, ht, ck, T, H,
                        NT, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_walk(const void *q, const void *k, const void *v, const float *beta, const float *G2,
-                       const float *Tinv, const float *h0, float *o, float *ht, int B, int T, int H,
-                       int Dk, int Dv, bool bf16, float scale, hipStream_t st) {
+                       const float *Tinv, const float *h0, float *o, float *ht, float *ck, int B, int T, int H,
+                       int Dk, int Dv, bool bf16, float scale, hipStream_t st, bool exact) {
 #define GDN_WALK(P, DKv, DVv) \
-    if (Dk == DKv && Dv == DVv) return launch_walk_t<P, DKv, DVv>(q, k, v, beta, G2, Tinv, h0, o, ht, B, T, H, scale, st)
-    if (bf16) {
+    if (Dk == DKv && Dv == DVv) return launch_walk_t<P, DKv, DVv>(q, k, v, beta, G2, Tinv, h0, o, ht, ck, B, T, H, scale, st)
+    if (bf16 && exact) {
+        GDN_WALK(PolBF16F32, 64, 64);
+        GDN_WALK(PolBF16F32, 64, 128);
+        GDN_WALK(PolBF16F32, 128, 64);
+        GDN_WALK(PolBF16F32, 128, 128);
+    } else if (bf16) {
         GDN_WALK(PolBF16, 64, 64);
         GDN_WALK(PolBF16, 64, 128);
         GDN_WALK(PolBF16, 128, 64);

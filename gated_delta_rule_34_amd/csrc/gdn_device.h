@@ -45,6 +45,12 @@ struct PolBF16 {
     using in_t = uint16_t;  // bf16 bits
     using mt = _Float16;    // 11-bit significand; bf16 inputs in [2^-14, 65504] convert exactly
 };
+// bf16 inputs with fp32 operands everywhere (the backward's recompute of the
+// forward, whose entry states must carry fp32 accuracy)
+struct PolBF16F32 {
+    using in_t = uint16_t;
+    using mt = float;
+};
 
 template <class T> __device__ __forceinline__ T to_mt(float x);
 template <> __device__ __forceinline__ float to_mt<float>(float x) { return x; }

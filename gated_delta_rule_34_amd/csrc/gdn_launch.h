@@ -6,12 +6,15 @@
 
 namespace gdn {
 
+// exact: fp32 operands also for bf16 inputs (used by the backward's recompute).
 hipError_t launch_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
-                        int T, int H, int Dk, bool bf16, hipStream_t st);
+                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact = false);
 
+// ck (nullable): entry state of every chunk, [B, H, NT, Dk, Dv] fp32; o may
+// then be null to skip the output.
 hipError_t launch_walk(const void *q, const void *k, const void *v, const float *beta, const float *G2,
-                       const float *Tinv, const float *h0, float *o, float *ht, int B, int T, int H,
-                       int Dk, int Dv, bool bf16, float scale, hipStream_t st);
+                       const float *Tinv, const float *h0, float *o, float *ht, float *ck, int B, int T, int H,
+                       int Dk, int Dv, bool bf16, float scale, hipStream_t st, bool exact = false);
 
 // Single-kernel chunked forward for bf16 inputs (no workspace).
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -44,5 +47,13 @@ hipError_t launch_step(const void *q, const void *k, const void *v, const float 
 hipError_t launch_step2(const void *q, const void *k, const void *v, const float *la, const void *bg,
                         const void *wg, float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                         hipStream_t st);
+
+// Backward of the chunked GDN forward (gdn_bwd.hip): the reverse state walk
+// (dS' of every chunk into dSck, dh0) and the per-chunk gradients, given the
+// intra stage (G2, T - I) and the entry state of every chunk (Sck).
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *beta, const float *dO,
+                      const float *dht, const float *G2, const float *Tinv, const float *Sck, float *dSck, float *dq,
+                      float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv,
+                      bool bf16, float scale, hipStream_t st);
 
 }  // namespace gdn

@@ -27,6 +27,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn2_recurrent_step", "gdn_chunk_intra",
+              "gdn_chunk_bwd", "gdn_chunk_bwd_workspace",
               "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string"):
         assert n in names
 
@@ -107,6 +108,32 @@ def test_gdn2_step_rejects_bad_arguments():
     assert f(*base, 4, 2, 128, 128, 5) == 2                            # unknown dtype
     assert f(*base[:6], base[3], base[7], 4, 2, 128, 128, 1) == 1      # S overlaps log_alpha
     assert f(*base[:7], base[1], 4, 2, 128, 128, 1) == 1               # o overlaps k
+
+
+def test_bwd_workspace_and_validation():
+    lib = gdn.load()
+    B, T, H, Dk, Dv = 2, 100, 3, 128, 128
+    n = lib.gdn_chunk_bwd_workspace(B, T, H, Dk, Dv, 1)
+    NT = 2
+    assert n >= 2 * B * H * NT * Dk * Dv * 4 + B * H * NT * 64 * 64 * 4
+    assert n % 256 == 0
+    assert lib.gdn_chunk_bwd_workspace(B, T, H, 96, Dv, 1) == 0
+    ptrs = [FAKE + (i << 32) for i in range(14)]   # q k v g beta h0 dO dht dq dk dv dg dbeta dh0
+    ws = FAKE + (20 << 32)
+
+    def f(p=ptrs, Dk=Dk, dt=1, w=ws, nbytes=n):
+        return lib.gdn_chunk_bwd(*[_p(x) for x in p], B, T, H, Dk, Dv, dt, 0.1, _p(w), nbytes, None)
+
+    assert f(p=ptrs[:6] + [None] + ptrs[7:]) == 1                   # no dO
+    assert f(p=ptrs[:8] + [None] + ptrs[9:]) == 1                   # no dq
+    assert f(Dk=96) == 2
+    assert f(dt=4) == 2
+    assert f(w=None) == 3
+    assert f(nbytes=n - 256) == 3
+    assert f(w=ws + 8) == 3                                          # misaligned
+    assert f(p=ptrs[:8] + [ptrs[0]] + ptrs[9:]) == 1                # dq overlaps q
+    assert f(p=ptrs[:9] + [ptrs[8]] + ptrs[10:]) == 1               # dk overlaps dq
+    assert f(p=ptrs[:13] + [ws]) == 1                               # dh0 overlaps the workspace
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
