@@ -34,14 +34,19 @@ namespace gdn {
 // acc (the 16x16 tile at rows i0, columns j0 of C) += A B over k in [0, K):
 // A(i, k) = A[i * sar + k * sac], B(k, j) = B[k * sbr + j * sbc] (LDS, fp32),
 // optionally B(k, j) * ks[k].  Lane (g, r) ends with C[i0 + 4g + e][j0 + r].
+// K is a compile-time constant so the loop unrolls and the LDS reads of
+// successive steps are issued ahead of their MFMAs.
+template <int K>
 __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float *A, int sar, int sac, const float *B, int sbr,
-                                          int sbc, const float *ks, int i0, int j0, int K, int lane) {
+                                          int sbc, const float *ks, int i0, int j0, int lane) {
     const int r = lane & 15, g = lane >> 4;
+    const float *pa = A + (i0 + r) * sar + g * sac;
+    const float *pb = B + g * sbr + (j0 + r) * sbc;
+#pragma unroll
     for (int k0 = 0; k0 < K; k0 += 4) {
-        const int kk = k0 + g;
-        const float a = A[(i0 + r) * sar + kk * sac];
-        float b = B[kk * sbr + (j0 + r) * sbc];
-        if (ks) b *= ks[kk];
+        const float a = pa[k0 * sac];
+        float b = pb[k0 * sbr];
+        if (ks) b *= ks[k0 + g];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
     return acc;
@@ -56,26 +61,57 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Eight consecutive inputs as fp32 (bf16 bits or fp32), from 16-byte aligned memory.
+__device__ __forceinline__ void load8(float (&x)[8], const uint16_t *p) {
+    const uint4 u = *(const uint4 *)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(float (&x)[8], const float *p) {
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Rows t0 .. t0 + 63 of a [B, T, H, D] tensor (this head) into LDS as fp32,
+// row stride LD; rows past T are zero.  Every load is issued before any is
+// stored: rows past T read the last token (in bounds) and are then zeroed.
+// ROWS x D must be a multiple of 8 * NTHR.
+template <int D, int LD, int NTHR, class In>
+__device__ __forceinline__ void stage_rows(float *dst, const In *src, long b, int h, int t0, int T, int H, int c0,
+                                           int DFULL, int tid) {
+    constexpr int U = BT * D / 8 / NTHR;
+    static_assert(U * 8 * NTHR == BT * D, "staging layout");
+    float x[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
+        const int t = min(t0 + row, T - 1);
+        load8(x[u], src + ((b * T + t) * H + h) * (long)DFULL + c0 + c8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
+        const bool in = t0 + row < T;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[row * LD + c8 + e] = in ? x[u][e] : 0.f;
+    }
+}
+
 // Chunk inputs common to both backward kernels: Q, K rows (zero past T) and
 // the gate tables of chunk c.
-template <class Pol, int DK, int LDQ>
+template <class Pol, int DK, int LDQ, int NTHR>
 __device__ __forceinline__ void load_chunk_qk(float *sQ, float *sK, float *sG2, float *sGam, float *sDec, float *sBeta,
                                               const typename Pol::in_t *q, const typename Pol::in_t *k,
                                               const float *beta, const float *G2ws, long b, int h, int c, long cb,
-                                              int T, int H, int tid, int nthr) {
+                                              int T, int H, int tid) {
     const int t0 = c * BT;
-    for (int idx = tid; idx < BT * DK; idx += nthr) {
-        const int row = idx / DK, col = idx % DK;
-        const int t = t0 + row;
-        float xq = 0.f, xk = 0.f;
-        if (t < T) {
-            const long off = ((b * T + t) * H + h) * (long)DK + col;
-            xq = load_elem(q + off);
-            xk = load_elem(k + off);
-        }
-        sQ[row * LDQ + col] = xq;
-        sK[row * LDQ + col] = xk;
-    }
+    stage_rows<DK, LDQ, NTHR>(sQ, q, b, h, t0, T, H, 0, DK, tid);
+    stage_rows<DK, LDQ, NTHR>(sK, k, b, h, t0, T, H, 0, DK, tid);
     if (tid < BT) {
         const int t = t0 + tid;
         const float G2 = G2ws[cb * BT + tid], G2L = G2ws[cb * BT + BT - 1];
@@ -83,6 +119,23 @@ __device__ __forceinline__ void load_chunk_qk(float *sQ, float *sK, float *sG2, 
         sGam[tid] = exp2f(G2);
         sDec[tid] = exp2f(G2L - G2);
         sBeta[tid] = (t < T) ? beta[(b * T + t) * H + h] : 0.f;
+    }
+}
+
+// A 64 x 64 fp32 matrix (T - I of a chunk) into LDS with row stride LD.
+template <int LD, int NTHR>
+__device__ __forceinline__ void stage_tm(float *dst, const float *src, int tid) {
+    constexpr int U = BT * BT / 4 / NTHR;
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = *(const float4 *)(src + 4 * (tid + NTHR * u));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = 4 * (tid + NTHR * u), row = idx / BT, col = idx % BT;
+        dst[row * LD + col] = x[u].x;
+        dst[row * LD + col + 1] = x[u].y;
+        dst[row * LD + col + 2] = x[u].z;
+        dst[row * LD + col + 3] = x[u].w;
     }
 }
 
@@ -119,17 +172,15 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         const long cb = bh * NT + c;
         const int t0 = c * BT;
         // gradient of the state leaving chunk c, for the per-chunk stage
-        for (int idx = tid; idx < DK * BV; idx += NTHR) {
-            const int row = idx / BV, col = idx % BV;
-            dSck[cb * DK * DV + (long)row * DV + vcol0 + col] = sdS[row * LDB + col];
+#pragma unroll
+        for (int u = 0; u < DK * BV / 4 / NTHR; ++u) {
+            const int idx = 4 * (tid + NTHR * u), row = idx / BV, col = idx % BV;
+            const float *p = &sdS[row * LDB + col];
+            *(float4 *)(dSck + cb * DK * DV + (long)row * DV + vcol0 + col) = make_float4(p[0], p[1], p[2], p[3]);
         }
-        load_chunk_qk<Pol, DK, LDQ>(sQ, sK, sG2, sGam, sDec, sBeta, q, k, beta, G2ws, b, h, c, cb, T, H, tid, NTHR);
-        for (int idx = tid; idx < BT * BT; idx += NTHR) sTm[(idx / BT) * LDC + idx % BT] = Tws[cb * BT * BT + idx];
-        for (int idx = tid; idx < BT * BV; idx += NTHR) {
-            const int row = idx / BV, col = idx % BV;
-            const int t = t0 + row;
-            sdO[row * LDB + col] = (t < T) ? dO[((b * T + t) * H + h) * (long)DV + vcol0 + col] : 0.f;
-        }
+        load_chunk_qk<Pol, DK, LDQ, NTHR>(sQ, sK, sG2, sGam, sDec, sBeta, q, k, beta, G2ws, b, h, c, cb, T, H, tid);
+        stage_tm<LDC, NTHR>(sTm, Tws + cb * BT * BT, tid);
+        stage_rows<BV, LDB, NTHR>(sdO, dO, b, h, t0, T, H, vcol0, DV, tid);
         __syncthreads();
         if (tid < BT) {
             sGdO[tid] = sGam[tid];               // B-row scale of (gamma Q)^T dO
@@ -139,7 +190,7 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         for (int tile = wave; tile < 10; tile += 4) {
             const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J = tile - I * (I + 1) / 2;
-            f32x4 acc = tile_mma(zero4(), sQ, LDQ, 1, sK, 1, LDQ, nullptr, 16 * I, 16 * J, DK, lane);
+            f32x4 acc = tile_mma<DK>(zero4(), sQ, LDQ, 1, sK, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e, j = 16 * J + r;
@@ -150,8 +201,8 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         // dVn = scale P^T dO + Kd dS' (8 tiles of 64 x 32)
         for (int tile = wave; tile < 8; tile += 4) {
             const int I = tile >> 1, J = tile & 1;
-            const f32x4 a1 = tile_mma(zero4(), sP, 1, LDC, sdO, LDB, 1, nullptr, 16 * I, 16 * J, BT, lane);
-            const f32x4 a2 = tile_mma(zero4(), sK, LDQ, 1, sdS, LDB, 1, nullptr, 16 * I, 16 * J, DK, lane);
+            const f32x4 a1 = tile_mma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, nullptr, 16 * I, 16 * J, lane);
+            const f32x4 a2 = tile_mma<DK>(zero4(), sK, LDQ, 1, sdS, LDB, 1, nullptr, 16 * I, 16 * J, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
@@ -162,7 +213,7 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         // dR = dVn + (T - I)^T dVn
         for (int tile = wave; tile < 8; tile += 4) {
             const int I = tile >> 1, J = tile & 1;
-            const f32x4 a = tile_mma(zero4(), sTm, 1, LDC, sdVn, LDB, 1, nullptr, 16 * I, 16 * J, BT, lane);
+            const f32x4 a = tile_mma<BT>(zero4(), sTm, 1, LDC, sdVn, LDB, 1, nullptr, 16 * I, 16 * J, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
@@ -174,8 +225,8 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         const float gC = sGam[BT - 1];
         for (int tile = wave; tile < (DK / 16) * 2; tile += 4) {
             const int M = tile >> 1, J = tile & 1;
-            const f32x4 a1 = tile_mma(zero4(), sQ, 1, LDQ, sdO, LDB, 1, sGdO, 16 * M, 16 * J, BT, lane);
-            const f32x4 a2 = tile_mma(zero4(), sK, 1, LDQ, sdR, LDB, 1, sBG, 16 * M, 16 * J, BT, lane);
+            const f32x4 a1 = tile_mma<BT>(zero4(), sQ, 1, LDQ, sdO, LDB, 1, sGdO, 16 * M, 16 * J, lane);
+            const f32x4 a2 = tile_mma<BT>(zero4(), sK, 1, LDQ, sdR, LDB, 1, sBG, 16 * M, 16 * J, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float *d = &sdS[(16 * M + 4 * g + e) * LDB + 16 * J + r];
@@ -225,9 +276,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const int t0 = c * BT;
     const int I = wave;  // this wave's 16-row block of every chunk-row product
 
-    load_chunk_qk<Pol, DK, LDQ>(sm.Q, sm.K, sm.G2, sm.Gam, sm.Dec, sm.Beta, q, k, beta, G2ws, b, h, c, cb, T, H,
-                                tid, NTHR);
-    for (int idx = tid; idx < BT * BT; idx += NTHR) sm.Tm[(idx / BT) * LDC + idx % BT] = Tws[cb * BT * BT + idx];
+    load_chunk_qk<Pol, DK, LDQ, NTHR>(sm.Q, sm.K, sm.G2, sm.Gam, sm.Dec, sm.Beta, q, k, beta, G2ws, b, h, c, cb, T,
+                                      H, tid);
+    stage_tm<LDC, NTHR>(sm.Tm, Tws + cb * BT * BT, tid);
     if (tid < BT) {
         sm.dB[tid] = 0.f;
         sm.dG[tid] = 0.f;
@@ -236,7 +287,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     // P = (Q K^T) . D, lower with the diagonal (all 16 tiles, upper ones zero)
     for (int tile = wave; tile < 16; tile += 4) {
         const int TI = tile >> 2, TJ = tile & 3;
-        const f32x4 acc = tile_mma(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * TI, 16 * TJ, DK, lane);
+        const f32x4 acc = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * TI, 16 * TJ, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
@@ -253,30 +304,32 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 
     for (int c0 = 0; c0 < DV; c0 += CW) {
         __syncthreads();  // previous slice fully consumed
-        for (int idx = tid; idx < DK * CW; idx += NTHR) {
-            const int row = idx / CW, col = idx % CW;
-            const long off = cb * DK * DV + (long)row * DV + c0 + col;
-            const float sv = Sck[off], dsv = dSck[off];
-            sm.S[row * LDW + col] = sv;
-            sm.dS[row * LDW + col] = dsv;
-            dGC = fmaf(sv, dsv, dGC);
-        }
-        for (int idx = tid; idx < BT * CW; idx += NTHR) {
-            const int row = idx / CW, col = idx % CW;
-            const int t = t0 + row;
-            float vv = 0.f, dd = 0.f;
-            if (t < T) {
-                const long off = ((b * T + t) * H + h) * (long)DV + c0 + col;
-                vv = load_elem(v + off);
-                dd = dO[off];
+        {
+            // S and dS' slices: DK x CW fp32, 4 columns per thread and pass
+            constexpr int US = DK * CW / 4 / NTHR;
+            float4 xs[US], xd[US];
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
+                const long off = cb * DK * DV + (long)row * DV + c0 + col;
+                xs[u] = *(const float4 *)(Sck + off);
+                xd[u] = *(const float4 *)(dSck + off);
             }
-            sm.V[row * LDW + col] = vv;
-            sm.dO[row * LDW + col] = dd;
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
+                float *ps = &sm.S[row * LDW + col], *pd = &sm.dS[row * LDW + col];
+                ps[0] = xs[u].x; ps[1] = xs[u].y; ps[2] = xs[u].z; ps[3] = xs[u].w;
+                pd[0] = xd[u].x; pd[1] = xd[u].y; pd[2] = xd[u].z; pd[3] = xd[u].w;
+                dGC += xs[u].x * xd[u].x + xs[u].y * xd[u].y + xs[u].z * xd[u].z + xs[u].w * xd[u].w;
+            }
         }
+        if (tid < BT * CW / 8) stage_rows<CW, LDW, BT * CW / 8>(sm.V, v, b, h, t0, T, H, c0, DV, tid);
+        else if (tid < BT * CW / 4) stage_rows<CW, LDW, BT * CW / 8>(sm.dO, dO, b, h, t0, T, H, c0, DV, tid - BT * CW / 8);
         __syncthreads();
         // KS, QS, R for rows of block I
-        const f32x4 KS = tile_mma(zero4(), sm.K, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, DK, lane);
-        const f32x4 QS = tile_mma(zero4(), sm.Q, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, DK, lane);
+        const f32x4 KS = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
+        const f32x4 QS = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
         f32x4 Rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -287,9 +340,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         __syncthreads();
         // Vn = R + (T - I) R;  dVn = scale P^T dO + Kd dS'
         {
-            const f32x4 a = tile_mma(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, nullptr, 16 * I, 0, BT, lane);
-            const f32x4 b1 = tile_mma(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, nullptr, 16 * I, 0, BT, lane);
-            const f32x4 b2 = tile_mma(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, nullptr, 16 * I, 0, DK, lane);
+            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, nullptr, 16 * I, 0, lane);
+            const f32x4 b1 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, nullptr, 16 * I, 0, lane);
+            const f32x4 b2 = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, nullptr, 16 * I, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
@@ -301,7 +354,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         // dR = dVn + (T - I)^T dVn; dv; the row sums of dbeta and dG
         f32x4 dRr;
         {
-            const f32x4 a = tile_mma(zero4(), sm.Tm, 1, LDC, sm.dVn, LDW, 1, nullptr, 16 * I, 0, BT, lane);
+            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sm.dVn, LDW, 1, nullptr, 16 * I, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
@@ -326,17 +379,17 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             // B(k, j) = Vn[j][k]
-            const f32x4 x = tile_mma(zero4(), sm.R, LDW, 1, sm.Vn, 1, LDW, nullptr, 16 * I, 16 * J, CW, lane);
-            const f32x4 y = tile_mma(zero4(), sm.dO, LDW, 1, sm.Vn, 1, LDW, nullptr, 16 * I, 16 * J, CW, lane);
+            const f32x4 x = tile_mma<CW>(zero4(), sm.R, LDW, 1, sm.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
+            const f32x4 y = tile_mma<CW>(zero4(), sm.dO, LDW, 1, sm.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
             dA[J] -= x;
             dP[J] += y * scale;
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             // B(k, m) = S[m][k] and dS'[m][k]
-            dqs[m] = tile_mma(dqs[m], sm.dO, LDW, 1, sm.S, 1, LDW, nullptr, 16 * I, 16 * m, CW, lane);
-            dkR[m] = tile_mma(dkR[m], sm.R, LDW, 1, sm.S, 1, LDW, nullptr, 16 * I, 16 * m, CW, lane);
-            dKd[m] = tile_mma(dKd[m], sm.Vn, LDW, 1, sm.dS, 1, LDW, nullptr, 16 * I, 16 * m, CW, lane);
+            dqs[m] = tile_mma<CW>(dqs[m], sm.dO, LDW, 1, sm.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+            dkR[m] = tile_mma<CW>(dkR[m], sm.R, LDW, 1, sm.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+            dKd[m] = tile_mma<CW>(dKd[m], sm.Vn, LDW, 1, sm.dS, 1, LDW, nullptr, 16 * I, 16 * m, lane);
         }
     }
     __syncthreads();  // every wave is done with Tm and P
@@ -345,8 +398,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     float colp[4][4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        const f32x4 KK = tile_mma(zero4(), sm.K, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, DK, lane);
-        const f32x4 QK = tile_mma(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, DK, lane);
+        const f32x4 KK = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
+        const f32x4 QK = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
         const int j = 16 * J + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -382,10 +435,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     float tdec[4] = {0.f, 0.f, 0.f, 0.f};  // sum_m dKd_im K_im for the 4 rows of this lane
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const f32x4 t1 = tile_mma(zero4(), sm.Tm, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, BT, lane);
-        const f32x4 t2 = tile_mma(zero4(), sm.Tm, 1, LDC, sm.K, LDQ, 1, sm.Beta, 16 * I, 16 * m, BT, lane);
-        const f32x4 t3 = tile_mma(zero4(), sm.P, 1, LDC, sm.Q, LDQ, 1, nullptr, 16 * I, 16 * m, BT, lane);
-        const f32x4 t4 = tile_mma(zero4(), sm.P, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, BT, lane);
+        const f32x4 t1 = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+        const f32x4 t2 = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sm.K, LDQ, 1, sm.Beta, 16 * I, 16 * m, lane);
+        const f32x4 t3 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sm.Q, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+        const f32x4 t4 = tile_mma<BT>(zero4(), sm.P, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e, col = 16 * m + r;
