@@ -61,47 +61,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Eight consecutive inputs as fp32 (bf16 bits or fp32), from 16-byte aligned memory.
-__device__ __forceinline__ void load8(float (&x)[8], const uint16_t *p) {
-    const uint4 u = *(const uint4 *)p;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(w[e] << 16);
-        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void load8(float (&x)[8], const float *p) {
-    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
-// Rows t0 .. t0 + 63 of a [B, T, H, D] tensor (this head) into LDS as fp32,
-// row stride LD; rows past T are zero.  Every load is issued before any is
-// stored: rows past T read the last token (in bounds) and are then zeroed.
-// ROWS x D must be a multiple of 8 * NTHR.
-template <int D, int LD, int NTHR, class In>
-__device__ __forceinline__ void stage_rows(float *dst, const In *src, long b, int h, int t0, int T, int H, int c0,
-                                           int DFULL, int tid) {
-    constexpr int U = BT * D / 8 / NTHR;
-    static_assert(U * 8 * NTHR == BT * D, "staging layout");
-    float x[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int idx = tid + NTHR * u, row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
-        const int t = min(t0 + row, T - 1);
-        load8(x[u], src + ((b * T + t) * H + h) * (long)DFULL + c0 + c8);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int idx = tid + NTHR * u, row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
-        const bool in = t0 + row < T;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[row * LD + c8 + e] = in ? x[u][e] : 0.f;
-    }
-}
-
 // Chunk inputs common to both backward kernels: Q, K rows (zero past T) and
 // the gate tables of chunk c.
 template <class Pol, int DK, int LDQ, int NTHR>

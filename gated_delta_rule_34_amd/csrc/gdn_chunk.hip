@@ -177,7 +177,9 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
     constexpr int LDQ = DK + 8;
     constexpr int LDKT = BT + 8;
     constexpr int LDP = BT + 8;
-    __shared__ mt sQ[BT * LDQ], sK[BT * LDQ], sKt[DK * LDKT], sP[BT * LDP];
+    constexpr int LDV = BV + 1;
+    __shared__ mt sQ[BT * LDQ], sK[BT * LDQ], sKt[DK * LDKT], sP[BT * LDP], sT[BT * LDP];
+    __shared__ float sV[BT * LDV];
     __shared__ float sG2[BT], sBeta[BT], sGam[BT], sDecK[BT], sDiag[BT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -218,22 +220,28 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
             sDecK[tid] = exp2f(G2L - G2);
             sBeta[tid] = (t < T) ? betain[(b * T + t) * H + h] : 0.f;
         }
-        for (int idx = tid; idx < BT * DK / 4; idx += NTHR) {
-            const int row = idx / (DK / 4), cc = (idx % (DK / 4)) * 4;
-            const int t = t0 + row;
-            float xq[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
-            if (t < T) {
-                const long off = ((b * T + t) * H + h) * (long)DK + cc;
+        // Q, K rows, the value slice and T - I of the chunk into LDS (vector
+        // loads, issued ahead of their stores)
+        stage_rows<DK, LDQ, NTHR>(sQ, q, b, h, t0, T, H, 0, DK, tid);
+        stage_rows<DK, LDQ, NTHR>(sK, k, b, h, t0, T, H, 0, DK, tid);
+        stage_rows<BV, LDV, NTHR>(sV, v, b, h, t0, T, H, vt * BV, DV, tid);
+        {
+            const float *Tc = Tws + cbase * (BT * BT);
+            constexpr int UT = BT * BT / 4 / NTHR;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xq[e] = load_elem(q + off + e);
-                    xk[e] = load_elem(k + off + e);
+            for (int u0 = 0; u0 < UT; u0 += 4) {
+                float4 x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = *(const float4 *)(Tc + 4 * (tid + NTHR * (u0 + u)));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int idx = 4 * (tid + NTHR * (u0 + u)), row = idx / BT, cc = idx % BT;
+                    mt *d = &sT[row * LDP + cc];
+                    d[0] = to_mt<mt>(x[u].x);
+                    d[1] = to_mt<mt>(x[u].y);
+                    d[2] = to_mt<mt>(x[u].z);
+                    d[3] = to_mt<mt>(x[u].w);
                 }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sQ[row * LDQ + cc + e] = to_mt<mt>(xq[e]);
-                sK[row * LDQ + cc + e] = to_mt<mt>(xk[e]);
             }
         }
         __syncthreads();
@@ -290,15 +298,12 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
-                const int t = t0 + i;
-                const float vv = (t < T) ? load_elem(v + ((b * T + t) * H + h) * (long)DV + col) : 0.f;
-                R[I][e] = sBeta[i] * (vv - sGam[i] * X[I][e]);
+                R[I][e] = sBeta[i] * (sV[i * LDV + wave * 16 + r] - sGam[i] * X[I][e]);
             }
         // Vnew = R + (T - I) R; block row I only needs column blocks J <= I.
         mt rf[2][8];
         frag_from_acc(rf[0], R[0], R[1]);
         frag_from_acc(rf[1], R[2], R[3]);
-        const float *Tc = Tws + cbase * (BT * BT);
         f32x4 Vn[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -306,12 +311,7 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
 #pragma unroll
             for (int s = 0; s <= (I >> 1); ++s) {
                 mt a[8];
-                const float *p = Tc + (16 * I + r) * BT + 32 * s + 4 * g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = to_mt<mt>(p[e]);
-                    a[e + 4] = to_mt<mt>(p[16 + e]);
-                }
+                frag_rows(a, sT, LDP, 16 * I, 32 * s, lane);
                 Vn[I] = mma_slab(Vn[I], a, rf[s]);
             }
         }

@@ -34,6 +34,52 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_floa
 __device__ __forceinline__ float load_elem(const float *p) { return *p; }
 __device__ __forceinline__ float load_elem(const uint16_t *p) { return bf16_to_f32(*p); }
 
+// Eight consecutive inputs as fp32 (bf16 bits or fp32), from 16-byte aligned memory.
+__device__ __forceinline__ void load8(float (&x)[8], const uint16_t *p) {
+    const uint4 u = *(const uint4 *)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(float (&x)[8], const float *p) {
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Columns c0 .. c0 + D - 1 of rows t0 .. t0 + 63 of a [B, T, H, DFULL] tensor
+// (head h of batch b) into LDS as type M with row stride LD; rows past T are
+// zero.  Loads go out in groups of four per thread before their stores; rows
+// past T read the last token (in bounds) and are then zeroed.  64 x D must be
+// a multiple of 8 * NTHR.
+template <int D, int LD, int NTHR, class M, class In>
+__device__ __forceinline__ void stage_rows(M *dst, const In *src, long b, int h, int t0, int T, int H, int c0,
+                                           int DFULL, int tid) {
+    constexpr int U = BT * D / 8 / NTHR;
+    static_assert(U * 8 * NTHR == BT * D, "staging layout");
+    constexpr int GRP = U < 4 ? U : 4;
+#pragma unroll
+    for (int u0 = 0; u0 < U; u0 += GRP) {
+        float x[GRP][8];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+            const int idx = tid + NTHR * (u0 + u), row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
+            const int t = min(t0 + row, T - 1);
+            load8(x[u], src + ((b * T + t) * H + h) * (long)DFULL + c0 + c8);
+        }
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+            const int idx = tid + NTHR * (u0 + u), row = idx / (D / 8), c8 = 8 * (idx % (D / 8));
+            const bool in = t0 + row < T;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[row * LD + c8 + e] = (M)(in ? x[u][e] : 0.f);
+        }
+    }
+}
+
 // Numeric policies.  `in_t` is the storage type of q, k, v (and GDN-2 b, w);
 // `mt` is the MFMA operand type used for products whose operands are not
 // exact inputs (state, new values, decayed keys, the attention-like matrix).
