@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "step_kernel": ("gdn_step.hip", "gdn_device.h"),
     "step2_kernel": ("gdn_step.hip", "gdn_device.h"),
     "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
+    "gdn_bwd": ("gdn_bwd.hip", "gdn_chunk.hip", "gdn_device.h"),
 }
 
 
