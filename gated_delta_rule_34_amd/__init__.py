@@ -14,7 +14,7 @@ import os
 __all__ = [
     "lib_path", "load", "status_string",
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
-    "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace",
+    "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
     "GDN_F32", "GDN_BF16", "BT",
 ]
@@ -56,6 +56,8 @@ def load():
     lib.gdn2_chunk_fwd.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_recurrent_step.restype = _i
     lib.gdn_recurrent_step.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _vp]
+    lib.gdn_chunk_fwd_varlen.restype = _i
+    lib.gdn_chunk_fwd_varlen.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
     lib.gdn_chunk_bwd_workspace.restype = _sz
     lib.gdn_chunk_bwd_workspace.argtypes = [_i] * 6
     lib.gdn_chunk_bwd.restype = _i
@@ -162,6 +164,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=None, output_final_state=True
     _check(lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
                              B, T, H, Dk, Dv, dt, float(scale), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(dev)), "gdn_chunk_fwd")
+    return o, ht
+
+
+def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, output_final_state=True):
+    """Chunked forward over packed variable-length sequences.  q, k [total_T,H,Dk] and
+    v [total_T,H,Dv] bf16 (a leading batch dim of 1 is accepted), g, beta [total_T,H]
+    fp32, cu_seqlens int32 [N+1] on the device, h0 [N,H,Dk,Dv] fp32 or None.
+    Returns (o [total_T,H,Dv] fp32, ht [N,H,Dk,Dv] or None)."""
+    torch = _torch()
+    if q.dim() == 4:
+        q, k, v, g, beta = q[0], k[0], v[0], g[0], beta[0]
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    dt = _dtype_code(q)
+    _need(q, "q", (total_T, H, Dk), q.dtype, dev)
+    _need(k, "k", (total_T, H, Dk), q.dtype, dev)
+    _need(v, "v", (total_T, H, Dv), q.dtype, dev)
+    _need(g, "g", (total_T, H), torch.float32, dev)
+    _need(beta, "beta", (total_T, H), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (N, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = torch.empty((total_T, H, Dv), dtype=torch.float32, device=dev)
+    ht = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    _check(load().gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0),
+                                       _ptr(o), _ptr(ht), N, total_T, H, Dk, Dv, dt, float(scale), _stream(dev)),
+           "gdn_chunk_fwd_varlen")
     return o, ht
 
 

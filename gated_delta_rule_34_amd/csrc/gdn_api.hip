@@ -109,7 +109,7 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     }
     hipStream_t st = (hipStream_t)stream;
     if (fused)
-        return from_hip(gdn::launch_fused_bf16(q, k, v, g, beta, h0, o, ht, B, T, H, Dk, Dv, scale, st));
+        return from_hip(gdn::launch_fused_bf16(q, k, v, g, beta, h0, o, ht, nullptr, B, T, H, Dk, Dv, scale, st));
     if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
     for (Range in : {rq, rk, rv, rg, rb, rh0})
         if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
@@ -254,6 +254,31 @@ gdn_status gdn2_recurrent_step(const void *q, const void *k, const void *v, cons
         if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
     return from_hip(gdn::launch_step2(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dtype == GDN_BF16, scale,
                                       (hipStream_t)stream));
+}
+
+gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                const int *cu_seqlens, const float *h0, float *o, float *ht, int N, int total_T,
+                                int H, int Dk, int Dv, gdn_dtype dtype, float scale, void *stream) {
+    if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+    if (N < 1 || total_T < 1 || H < 1 || (long long)N * H * (Dv / 32 > 0 ? Dv / 32 : 1) >= (1LL << 31))
+        return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)total_T * H;
+    const size_t nstate = (size_t)N * H * Dk * Dv * sizeof(float);
+    const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es}, rg{g, ntok * 4},
+        rb{beta, ntok * 4}, rcu{cu_seqlens, (size_t)(N + 1) * sizeof(int)}, rh0{h0, h0 ? nstate : 0},
+        ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0};
+    for (Range in : {rq, rk, rv, rg, rb, rcu, rh0})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    if (ht) {
+        if (overlap(rht, rh0) && ht != h0) return GDN_ERR_INVALID_ARG;
+        for (Range in : {rq, rk, rv, rg, rb, rcu, ro})
+            if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
+    }
+    return from_hip(gdn::launch_fused_bf16(q, k, v, g, beta, h0, o, ht, cu_seqlens, N, total_T, H, Dk, Dv, scale,
+                                           (hipStream_t)stream));
 }
 
 // Workspace of the backward: the forward's intra stage (G2, T - I), then the

@@ -83,10 +83,13 @@ struct ChunkRegs {
     float g, beta;
 };
 
+// One workgroup's sequence: token t of it is token-head row (tok0 + t) * H + h
+// of the [., H, D] tensors (tok0 = b T for a dense batch, the sequence start
+// for packed variable-length input).
 struct HeadArgs {
     const uint16_t *q, *k, *v;
     const float *g, *beta;
-    long b;
+    long tok0;
     int h, T, H, vcol0;
 };
 
@@ -96,7 +99,7 @@ __device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16
     const int r = lane & 15, g = lane >> 4;
     const bool full = (chunk + 1) * BT <= a.T;
     const long rowstride = (long)a.H * DK;
-    const uint16_t *base = src + ((a.b * a.T + chunk * BT + r) * a.H + a.h) * (long)DK + 8 * g;
+    const uint16_t *base = src + ((a.tok0 + chunk * BT + r) * a.H + a.h) * (long)DK + 8 * g;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const int t = chunk * BT + 16 * I + r;
@@ -112,7 +115,7 @@ __device__ __forceinline__ void load_v(uint4 (&dst)[4], const HeadArgs &a, int c
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int t = chunk * BT + 16 * p + (lane >> 2);
-        dst[p] = (t < a.T) ? *(const uint4 *)(a.v + ((a.b * a.T + t) * a.H + a.h) * (long)DV + a.vcol0 +
+        dst[p] = (t < a.T) ? *(const uint4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 +
                                               (lane & 3) * 8)
                            : make_uint4(0, 0, 0, 0);
     }
@@ -120,7 +123,7 @@ __device__ __forceinline__ void load_v(uint4 (&dst)[4], const HeadArgs &a, int c
 
 __device__ __forceinline__ void load_gates(float &gv, float &bv, const HeadArgs &a, int chunk, int lane) {
     const int t = chunk * BT + lane;
-    const long idx = (a.b * a.T + t) * a.H + a.h;
+    const long idx = (a.tok0 + t) * a.H + a.h;
     gv = (t < a.T) ? a.g[idx] : 0.f;
     bv = (t < a.T) ? a.beta[idx] : 0.f;
 }
@@ -296,7 +299,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     const int t0 = chunk * BT;
     const int col = ha.vcol0 + cl;
     const bool full = t0 + BT <= ha.T;
-    float *obase = o + ((ha.b * ha.T + t0) * ha.H + ha.h) * (long)DV + col;
+    float *obase = o + ((ha.tok0 + t0) * ha.H + ha.h) * (long)DV + col;
     const long ostride = (long)ha.H * DV;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -353,7 +356,8 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
                                                        const float *__restrict__ gin,
                                                        const float *__restrict__ betain,
                                                        const float *__restrict__ h0, float *__restrict__ o,
-                                                       float *__restrict__ ht, int T, int H, int NT, float scale) {
+                                                       float *__restrict__ ht, const int *__restrict__ cu_seqlens,
+                                                       int T, int H, float scale) {
     using C = FusedCfg<DK, DV>;
     static_assert(sizeof(FusedSmem<DK, DV>) <= 160 * 1024, "LDS budget");
     __shared__ FusedSmem<DK, DV> sm;
@@ -369,9 +373,21 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
     HeadArgs ha;
     ha.q = q; ha.k = k; ha.v = v; ha.g = gin; ha.beta = betain;
     ha.h = (int)(bh % H);
-    ha.b = bh / H;
-    ha.T = T; ha.H = H;
+    ha.H = H;
     ha.vcol0 = vt * C::BV;
+    if (cu_seqlens) {
+        // packed sequences: T is the total token count; the bounds are clamped
+        // into [0, T] so that malformed offsets can never address out of range
+        const long n_seq = bh / H;
+        const int s0 = min(max(cu_seqlens[n_seq], 0), T);
+        const int s1 = min(max(cu_seqlens[n_seq + 1], s0), T);
+        ha.tok0 = s0;
+        ha.T = s1 - s0;
+    } else {
+        ha.tok0 = (bh / H) * (long)T;
+        ha.T = T;
+    }
+    const int NT = (ha.T + BT - 1) / BT;  // this workgroup's chunks
 
     // The upper tiles (0,1) and (2,3) of P and T - I are read by the 32-wide
     // slabs of the consumers but never written: zero them once.
@@ -428,22 +444,25 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
 
 template <int DK, int DV>
 static hipError_t launch_fused_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                                 const float *h0, float *o, float *ht, int B, int T, int H, float scale,
-                                 hipStream_t st) {
-    const int NT = (T + BT - 1) / BT;
+                                 const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H,
+                                 float scale, hipStream_t st) {
     const long grid = (long)B * H * (DV / FusedCfg<DK, DV>::BV);
     hipLaunchKernelGGL((fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t *)q,
-                       (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, o, ht, T, H, NT, scale);
+                       (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, o, ht, cu_seqlens, T, H, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                             const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
-                             float scale, hipStream_t st) {
-    if (Dk == 64 && Dv == 64) return launch_fused_t<64, 64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
-    if (Dk == 64 && Dv == 128) return launch_fused_t<64, 128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
-    if (Dk == 128 && Dv == 64) return launch_fused_t<128, 64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
-    if (Dk == 128 && Dv == 128) return launch_fused_t<128, 128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, st);
+                             const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H, int Dk,
+                             int Dv, float scale, hipStream_t st) {
+#define GDN_FUSED(DKv, DVv)                                                                                     \
+    if (Dk == DKv && Dv == DVv)                                                                                 \
+    return launch_fused_t<DKv, DVv>(q, k, v, g, beta, h0, o, ht, cu_seqlens, B, T, H, scale, st)
+    GDN_FUSED(64, 64);
+    GDN_FUSED(64, 128);
+    GDN_FUSED(128, 64);
+    GDN_FUSED(128, 128);
+#undef GDN_FUSED
     return hipErrorInvalidValue;
 }
 

@@ -16,10 +16,12 @@ hipError_t launch_walk(const void *q, const void *k, const void *v, const float 
                        const float *Tinv, const float *h0, float *o, float *ht, float *ck, int B, int T, int H,
                        int Dk, int Dv, bool bf16, float scale, hipStream_t st, bool exact = false);
 
-// Single-kernel chunked forward for bf16 inputs (no workspace).
+// Single-kernel chunked forward for bf16 inputs (no workspace).  With
+// cu_seqlens (device, B + 1 int32 offsets) the tensors hold B packed
+// sequences of T tokens in total; otherwise a dense [B, T, H, D] batch.
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                             const float *h0, float *o, float *ht, int B, int T, int H, int Dk, int Dv,
-                             float scale, hipStream_t st);
+                             const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H, int Dk,
+                             int Dv, float scale, hipStream_t st);
 
 // Gated DeltaNet-2, two stages: per-chunk prepared operands (decayed e, q
 // and k; Gamma_C; T - I; strict P; diag P), then the state walk.

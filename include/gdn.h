@@ -167,6 +167,25 @@ gdn_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
                                gdn_dtype dtype, float scale, void *stream);
 
 /*
+ * gdn_chunk_fwd_varlen -- gdn_chunk_fwd on N packed sequences of different
+ * lengths (the production input form; each sequence is chunked and carried
+ * on its own, exactly as a batch entry of gdn_chunk_fwd).
+ *   q, k [total_T, H, Dk] and v [total_T, H, Dv] bf16; g, beta [total_T, H] fp32
+ *   cu_seqlens  device int32 [N + 1]: sequence n is tokens cu_seqlens[n] ..
+ *               cu_seqlens[n + 1] - 1; non-decreasing from 0 to total_T (the
+ *               kernel clamps the offsets into [0, total_T], so malformed
+ *               offsets give wrong sequences but never an out-of-range access;
+ *               an empty sequence passes its initial state through)
+ *   h0, ht [N, H, Dk, Dv] fp32 (nullable; ht may alias h0);  o [total_T, H, Dv] fp32
+ * bf16 only (GDN_ERR_UNSUPPORTED for fp32); no workspace.  Errors as
+ * gdn_chunk_fwd, plus GDN_ERR_INVALID_ARG for a null cu_seqlens.
+ */
+gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const int *cu_seqlens, const float *h0,
+                                float *o, float *ht, int N, int total_T, int H, int Dk, int Dv,
+                                gdn_dtype dtype, float scale, void *stream);
+
+/*
  * Backward of gdn_chunk_fwd (training): gradients of
  * L = sum(dO . o) + sum(dht . ht) with respect to every input, by reverse-mode
  * differentiation of the chunk equations of the forward (WY form over 64-token

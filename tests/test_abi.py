@@ -27,7 +27,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn2_recurrent_step", "gdn_chunk_intra",
-              "gdn_chunk_bwd", "gdn_chunk_bwd_workspace",
+              "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
               "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string"):
         assert n in names
 
@@ -134,6 +134,22 @@ def test_bwd_workspace_and_validation():
     assert f(p=ptrs[:8] + [ptrs[0]] + ptrs[9:]) == 1                # dq overlaps q
     assert f(p=ptrs[:9] + [ptrs[8]] + ptrs[10:]) == 1               # dk overlaps dq
     assert f(p=ptrs[:13] + [ws]) == 1                               # dh0 overlaps the workspace
+
+
+def test_varlen_rejects_bad_arguments():
+    lib = gdn.load()
+    p = [FAKE + (i << 32) for i in range(9)]   # q k v g beta cu h0 o ht
+
+    def f(ptrs=p, N=3, total=300, Dk=128, dt=1):
+        return lib.gdn_chunk_fwd_varlen(*[_p(x) for x in ptrs], N, total, 2, Dk, 128, dt, 0.1, None)
+
+    assert f(ptrs=p[:5] + [None] + p[6:]) == 1      # no cu_seqlens
+    assert f(N=0) == 1
+    assert f(total=0) == 1
+    assert f(dt=0) == 2                             # fp32: not supported on this path
+    assert f(Dk=96) == 2
+    assert f(ptrs=p[:7] + [p[0]] + p[8:]) == 1      # o overlaps q
+    assert f(ptrs=p[:7] + [p[5]] + p[8:]) == 1      # o overlaps cu_seqlens
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
