@@ -8,7 +8,9 @@ output), timed with HIP events on the stream it runs on.  fp32 workloads run
 the two stage entry points and time each stage.  Other workloads: the decode
 step (--workload decode_bf16), Gated DeltaNet-2 (--workload gdn2_bf16) and its
 decode step (--workload decode2_bf16), and the backward of the chunked forward
-on the layer-shaped inputs (--workload layer_bwd_bf16).
+on the layer-shaped inputs (--workload layer_bwd_bf16), and the whole layer
+around the rule: prologue, chunked forward and gated RMSNorm
+(--workload layer_full_bf16).
 
 Default workload: B=8, H=8, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates,
 fp32 output and state (the layer-shaped case).  Prints ONE JSON line on
@@ -47,6 +49,7 @@ KERNEL_SOURCES = {
     "step2_kernel": ("gdn_step.hip", "gdn_device.h"),
     "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
     "gdn_bwd": ("gdn_bwd.hip", "gdn_chunk.hip", "gdn_device.h"),
+    "prologue_kernel": ("gdn_prologue.hip", "gdn_device.h"),
 }
 
 
@@ -464,6 +467,95 @@ def bench_bwd(args, wl):
     return res
 
 
+def bench_layer(args, wl):
+    """The layer around the rule: prologue (short convolution, SiLU, L2 norm, gates)
+    -> chunked forward -> gated RMSNorm, each kernel timed with HIP events."""
+    import torch
+    import gated_delta_rule_34_amd as gdn
+    import gdn_inputs as gi
+
+    dev = torch.device("cuda:0")
+    x = gi.workload(wl)
+    B, T, H, Dk, Dv = x["B"], x["T"], x["H"], x["Dk"], x["Dv"]
+    names = ("xq", "xk", "xv", "a", "b", "wq", "wk", "wv", "A_log", "dt_bias", "z", "norm_w")
+    base = {n: to_dev(x[n], dev) for n in names}
+    sets = []
+    for i in range(args.sets):
+        s = {n: t.clone() for n, t in base.items()}
+        s["o"] = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+        s["ht"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        s["y"] = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace(B, T, H, Dk, Dv, gdn.GDN_BF16), dtype=torch.uint8, device=dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        q, k, v, g, beta, _ = gdn.gdn_prologue(*[s[n] for n in names[:10]])
+        if ev is not None:
+            ev[1].record()
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, None, scale=x["scale"], workspace=ws, out=s["o"], final_state=s["ht"])
+        if ev is not None:
+            ev[2].record()
+        gdn.gdn_gated_rmsnorm(s["o"], s["z"], s["norm_w"], eps=1e-5, out=s["y"])
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    seg = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    th = float(B) * T * H
+    stage_bytes = [th * (2 * (2 * Dk + Dv) * 2 + 16),                       # projections in, q k v out, gates
+                   walk_algorithmic_bytes(B, T, H, Dk, Dv, 2, False) + 4.0 * th,
+                   th * Dv * 8.0]                                            # o fp32, z in; y out
+    knames = ["prologue_kernel", "fused_kernel", "gated_rmsnorm_kernel"]
+    stages = {kn: {"avg_launch_us": t * 1e3, "algorithmic_bytes_per_launch": by,
+                   "achieved_gbs": by / (t * 1e-3) / 1e9, "frac": by / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+              for kn, t, by in zip(knames, seg, stage_bytes)}
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step wall; " +
+        ", ".join(f"{k} {v['avg_launch_us']:.1f} us ({v['frac']:.3f} of HBM peak)" for k, v in stages.items()))
+    dom = max(range(3), key=lambda j: seg[j])
+    res = {
+        "metric": f"gated delta rule layer (prologue + chunked fwd + gated RMSNorm) tokens/s, T={T} d={Dk}",
+        "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
+                   "inputs": "bf16 projections", "kernels": "prologue, fused chunked forward, gated RMSNorm",
+                   "buffer_sets": args.sets, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": knames[dom], "achieved": stages[knames[dom]]["achieved_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": stages[knames[dom]]["frac"],
+                     "algorithmic_bytes_per_launch": stage_bytes[dom], "avg_launch_us": seg[dom] * 1e3,
+                     "traffic": None},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's prologue and epilogue on one sequence of the workload
+        import oracle
+        import oracle.prologue as op
+        sub = {n: x[n + "_f64"][:1] for n in ("xq", "xk", "xv", "a", "b", "z")}
+        t0 = time.perf_counter()
+        q, k, v, g, beta, _ = op.prologue(sub["xq"], sub["xk"], sub["xv"], sub["a"], sub["b"],
+                                          *[x[n + "_f64"] for n in ("wq", "wk", "wv", "A_log", "dt_bias")])
+        o, _ = oracle.gdn_fwd(q, k, v, g, beta, None, scale=x["scale"])
+        op.gated_rmsnorm(o, sub["z"], x["norm_w_f64"])
+        dt_cpu = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": T / dt_cpu, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle",
+                               "sample": f"1 of {B} sequences x {H} heads x {T} tokens through the oracle's "
+                                         f"prologue, recurrence and epilogue, {dt_cpu:.2f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,7 +563,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16",
                     choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "decode2_bf16", "gdn2_bf16",
-                             "layer_bwd_bf16"])
+                             "layer_bwd_bf16", "layer_full_bf16"])
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -495,6 +587,8 @@ def main():
         res = bench_bwd(args, args.workload)
     elif args.workload == "gdn2_bf16":
         res = bench_gdn2(args, args.workload)
+    elif args.workload == "layer_full_bf16":
+        res = bench_layer(args, args.workload)
     else:
         res = bench_gdn(args, args.workload)
     if args.copy_calibration > 0:

@@ -15,7 +15,7 @@ __all__ = [
     "lib_path", "load", "status_string",
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
     "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
-    "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace",
+    "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_prologue", "gdn_gated_rmsnorm",
     "GDN_F32", "GDN_BF16", "BT",
 ]
 
@@ -64,6 +64,10 @@ def load():
     lib.gdn_chunk_bwd.argtypes = [_vp] * 14 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn2_recurrent_step.restype = _i
     lib.gdn2_recurrent_step.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _vp]
+    lib.gdn_prologue.restype = _i
+    lib.gdn_prologue.argtypes = [_vp] * 17 + [_i] * 5 + [_vp]
+    lib.gdn_gated_rmsnorm.restype = _i
+    lib.gdn_gated_rmsnorm.argtypes = [_vp] * 4 + [ctypes.c_longlong, _i, _f, _vp]
     _lib = lib
     return lib
 
@@ -378,3 +382,60 @@ def gdn2_recurrent_step(q, k, v, log_alpha, b, w, S, scale=None, out=None):
     _check(load().gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S),
                                       _ptr(o), B, H, Dk, Dv, dt, float(scale), _stream(dev)), "gdn2_recurrent_step")
     return o
+
+
+def gdn_prologue(xq, xk, xv, a, b, wq, wk, wv, A_log, dt_bias, conv_state=None, update_conv_state=False):
+    """Short convolution, SiLU, q/k L2 norm and gates in one pass.  xq, xk [B,T,H,Dk] and
+    xv [B,T,H,Dv] bf16; a, b [B,T,H] fp32; wq, wk [H*Dk,4], wv [H*Dv,4], A_log, dt_bias [H]
+    fp32; conv_state [B,3,H*(2Dk+Dv)] fp32 or None.  Returns (q, k, v bf16, g, beta fp32,
+    new conv state or None); with update_conv_state the new state overwrites conv_state."""
+    torch = _torch()
+    B, T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    dev = xq.device
+    bf, f32 = torch.bfloat16, torch.float32
+    _need(xq, "xq", (B, T, H, Dk), bf, dev)
+    _need(xk, "xk", (B, T, H, Dk), bf, dev)
+    _need(xv, "xv", (B, T, H, Dv), bf, dev)
+    _need(a, "a", (B, T, H), f32, dev)
+    _need(b, "b", (B, T, H), f32, dev)
+    _need(wq, "wq", (H * Dk, 4), f32, dev)
+    _need(wk, "wk", (H * Dk, 4), f32, dev)
+    _need(wv, "wv", (H * Dv, 4), f32, dev)
+    _need(A_log, "A_log", (H,), f32, dev)
+    _need(dt_bias, "dt_bias", (H,), f32, dev)
+    C = H * (2 * Dk + Dv)
+    if conv_state is not None:
+        _need(conv_state, "conv_state", (B, 3, C), f32, dev)
+    if update_conv_state:
+        if conv_state is None:
+            raise ValueError("update_conv_state needs conv_state")
+        new_state = conv_state
+    else:
+        new_state = torch.empty((B, 3, C), dtype=f32, device=dev)
+    q = torch.empty((B, T, H, Dk), dtype=bf, device=dev)
+    k = torch.empty((B, T, H, Dk), dtype=bf, device=dev)
+    v = torch.empty((B, T, H, Dv), dtype=bf, device=dev)
+    g = torch.empty((B, T, H), dtype=f32, device=dev)
+    beta = torch.empty((B, T, H), dtype=f32, device=dev)
+    _check(load().gdn_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(a), _ptr(b), _ptr(wq), _ptr(wk), _ptr(wv),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(conv_state), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(new_state), B, T, H, Dk, Dv, _stream(dev)), "gdn_prologue")
+    return q, k, v, g, beta, new_state
+
+
+def gdn_gated_rmsnorm(o, z, weight, eps=1e-5, out=None):
+    """y = o / sqrt(mean(o^2) + eps) * weight * SiLU(z) over the last axis.  o [..., Dv]
+    fp32, z [..., Dv] bf16, weight [Dv] fp32.  Returns y [..., Dv] bf16."""
+    torch = _torch()
+    Dv = o.shape[-1]
+    dev = o.device
+    _need(o, "o", tuple(o.shape), torch.float32, dev)
+    _need(z, "z", tuple(o.shape), torch.bfloat16, dev)
+    _need(weight, "weight", (Dv,), torch.float32, dev)
+    y = out if out is not None else torch.empty(o.shape, dtype=torch.bfloat16, device=dev)
+    _need(y, "out", tuple(o.shape), torch.bfloat16, dev)
+    rows = o.numel() // Dv
+    _check(load().gdn_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(weight), _ptr(y), rows, Dv, float(eps), _stream(dev)),
+           "gdn_gated_rmsnorm")
+    return y

@@ -50,6 +50,8 @@ bool sizes_ok(int B, int T, int H) {
     return (long long)B * H * NT < (1LL << 31);
 }
 
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 }  // namespace
@@ -339,6 +341,54 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     if (s != GDN_OK) return s;
     return from_hip(gdn::launch_bwd(q, k, v, beta, dO, dht, G2, Tinv, Sck, dSck, dq, dk, dv, dg, dbeta, dh0, B, T, H,
                                     Dk, Dv, bf, scale, st));
+}
+
+gdn_status gdn_prologue(const void *xq, const void *xk, const void *xv, const float *a, const float *b,
+                        const float *wq, const float *wk, const float *wv, const float *A_log, const float *dt_bias,
+                        const float *conv_in, void *q, void *k, void *v, float *g, float *beta, float *conv_out,
+                        int B, int T, int H, int Dk, int Dv, void *stream) {
+    if (!xq || !xk || !xv || !a || !b || !wq || !wk || !wv || !A_log || !dt_bias || !q || !k || !v || !g || !beta)
+        return GDN_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || H < 1 || (long long)B * T * H >= (1LL << 33)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv)) return GDN_ERR_UNSUPPORTED;
+    for (const void *p : {xq, xk, xv, (const void *)q, (const void *)k, (const void *)v, (const void *)wq,
+                          (const void *)wk, (const void *)wv, (const void *)conv_in})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(conv_out, 4)) return GDN_ERR_INVALID_ARG;
+    const size_t ntok = (size_t)B * T * H, C = (size_t)H * (2 * Dk + Dv);
+    const size_t nstate = (size_t)B * 3 * C * sizeof(float);
+    const Range rxq{xq, ntok * Dk * 2}, rxk{xk, ntok * Dk * 2}, rxv{xv, ntok * Dv * 2}, ra{a, ntok * 4},
+        rb{b, ntok * 4}, rwq{wq, (size_t)H * Dk * 16}, rwk{wk, (size_t)H * Dk * 16}, rwv{wv, (size_t)H * Dv * 16},
+        rA{A_log, (size_t)H * 4}, rdt{dt_bias, (size_t)H * 4}, rci{conv_in, conv_in ? nstate : 0},
+        rq{q, ntok * Dk * 2}, rk{k, ntok * Dk * 2}, rv{v, ntok * Dv * 2}, rg{g, ntok * 4}, rbe{beta, ntok * 4},
+        rco{conv_out, conv_out ? nstate : 0};
+    const Range ins[] = {rxq, rxk, rxv, ra, rb, rwq, rwk, rwv, rA, rdt, rci};
+    const Range outs[] = {rq, rk, rv, rg, rbe};
+    for (int i = 0; i < 5; ++i) {
+        for (Range in : ins)
+            if (overlap(outs[i], in)) return GDN_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_INVALID_ARG;
+        if (overlap(outs[i], rco)) return GDN_ERR_INVALID_ARG;
+    }
+    if (conv_out) {
+        if (overlap(rco, rci) && conv_out != conv_in) return GDN_ERR_INVALID_ARG;
+        for (int i = 0; i < 10; ++i)
+            if (overlap(rco, ins[i])) return GDN_ERR_INVALID_ARG;
+    }
+    return from_hip(gdn::launch_prologue(xq, xk, xv, a, b, wq, wk, wv, A_log, dt_bias, conv_in, q, k, v, g, beta,
+                                         conv_out, B, T, H, Dk, Dv, (hipStream_t)stream));
+}
+
+gdn_status gdn_gated_rmsnorm(const float *o, const void *z, const float *weight, void *y, long long rows, int Dv,
+                             float eps, void *stream) {
+    if (!o || !z || !weight || !y || rows < 1 || rows >= (1LL << 33) || !(eps > 0.f)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dv)) return GDN_ERR_UNSUPPORTED;
+    if (!aligned(o, 16) || !aligned(z, 16) || !aligned(weight, 16) || !aligned(y, 16)) return GDN_ERR_INVALID_ARG;
+    const Range ry{y, (size_t)rows * Dv * 2};
+    for (Range in : {Range{o, (size_t)rows * Dv * 4}, Range{z, (size_t)rows * Dv * 2}, Range{weight, (size_t)Dv * 4}})
+        if (overlap(ry, in)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_gated_rmsnorm(o, z, weight, y, (long)rows, Dv, eps, (hipStream_t)stream));
 }
 
 }  // extern "C"

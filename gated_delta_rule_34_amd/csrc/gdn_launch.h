@@ -58,4 +58,12 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *
                       float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv,
                       bool bf16, float scale, hipStream_t st);
 
+// Prologue and epilogue around the rule (gdn_prologue.hip).
+hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, const float *a, const float *b,
+                           const float *wq, const float *wk, const float *wv, const float *A_log,
+                           const float *dt_bias, const float *state_in, void *q, void *k, void *v, float *g,
+                           float *beta, float *state_out, int B, int T, int H, int Dk, int Dv, hipStream_t st);
+hipError_t launch_gated_rmsnorm(const float *o, const void *z, const float *w, void *y, long rows, int Dv, float eps,
+                                hipStream_t st);
+
 }  // namespace gdn

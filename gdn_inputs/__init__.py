@@ -33,6 +33,7 @@ __all__ = [
     "step_inputs",
     "WORKLOADS",
     "step2_inputs",
+    "layer_inputs",
 ]
 
 # Named workloads: shapes and dtypes of the measured and parity cases.
@@ -44,6 +45,8 @@ WORKLOADS = {
     "gdn2_bf16": dict(kind="gdn2", B=4, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1004),
     "decode2_bf16": dict(kind="step2", B=256, H=16, Dk=128, Dv=128, dtype="bf16", seed=1005),
     "layer_bwd_bf16": dict(kind="gdn", B=8, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1001),
+    "layer_full_bf16": dict(kind="layer", B=8, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", conv_state=False,
+                            seed=1006),
 }
 
 
@@ -188,6 +191,37 @@ def step2_inputs(B, H, Dk, Dv, seed, dtype="bf16"):
     return out
 
 
+def layer_inputs(B, T, H, Dk, Dv, seed, conv_state=False):
+    """Inputs of the layer around the rule: the projections entering the short
+    convolution (bf16), the gate pre-activations a, b (fp32), the convolution
+    taps, A_log and dt_bias (fp32), the output gate z (bf16) and the RMSNorm
+    weight (fp32); conv_state [B, 3, H*(2Dk+Dv)] fp32 when asked.
+    Recipe: projections, a, b, z ~ N(0, 1); taps ~ U(-0.5, 0.5) (a depthwise
+    convolution's default bound 1/sqrt(4)); A = exp(A_log) ~ U(1, 16);
+    dt_bias = softplus^-1(dt) with log dt ~ U(log 1e-3, log 0.1); RMSNorm
+    weight 1 + 0.1 N(0, 1); conv_state ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "dtype": "bf16", "scale": 1.0 / np.sqrt(Dk)}
+    _pack(out, "xq", rng.standard_normal((B, T, H, Dk)), "bf16")
+    _pack(out, "xk", rng.standard_normal((B, T, H, Dk)), "bf16")
+    _pack(out, "xv", rng.standard_normal((B, T, H, Dv)), "bf16")
+    out["a"], out["a_f64"] = _f32(rng.standard_normal((B, T, H)))
+    out["b"], out["b_f64"] = _f32(rng.standard_normal((B, T, H)))
+    out["wq"], out["wq_f64"] = _f32(rng.uniform(-0.5, 0.5, size=(H * Dk, 4)))
+    out["wk"], out["wk_f64"] = _f32(rng.uniform(-0.5, 0.5, size=(H * Dk, 4)))
+    out["wv"], out["wv_f64"] = _f32(rng.uniform(-0.5, 0.5, size=(H * Dv, 4)))
+    out["A_log"], out["A_log_f64"] = _f32(np.log(rng.uniform(1.0, 16.0, size=(H,))))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), size=(H,)))
+    out["dt_bias"], out["dt_bias_f64"] = _f32(dt + np.log(-np.expm1(-dt)))
+    _pack(out, "z", rng.standard_normal((B, T, H, Dv)), "bf16")
+    out["norm_w"], out["norm_w_f64"] = _f32(1.0 + 0.1 * rng.standard_normal((Dv,)))
+    if conv_state:
+        out["conv"], out["conv_f64"] = _f32(rng.standard_normal((B, 3, H * (2 * Dk + Dv))))
+    else:
+        out["conv"], out["conv_f64"] = None, None
+    return out
+
+
 def workload(name: str, **overrides):
     """Build the inputs of a named workload (see WORKLOADS); keyword overrides
     replace shape or seed fields (used for reduced-size parity cases)."""
@@ -204,4 +238,7 @@ def workload(name: str, **overrides):
         return step_inputs(cfg["B"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"], dtype=cfg["dtype"])
     if kind == "step2":
         return step2_inputs(cfg["B"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"], dtype=cfg["dtype"])
+    if kind == "layer":
+        return layer_inputs(cfg["B"], cfg["T"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"],
+                            conv_state=cfg["conv_state"])
     raise ValueError(kind)

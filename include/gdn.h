@@ -212,6 +212,53 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
                          gdn_dtype dtype, float scale, void *ws, size_t ws_bytes,
                          void *stream);
 
+/*
+ * gdn_prologue -- the per-token work between the input projections and the
+ * rule, in one pass ("GatedDeltaNet walkthrough", the data-flow overview and
+ * the sections on the short convolution and the gates):
+ *   q = l2norm(SiLU(conv(xq))), k = l2norm(SiLU(conv(xk))), v = SiLU(conv(xv))
+ *   g = -exp(A_log[h]) * softplus(a + dt_bias[h]),  beta = sigmoid(b)
+ * conv is a causal depthwise convolution over the last 4 tokens of each
+ * channel, without bias, whose last tap multiplies the current token:
+ *   conv(x)_t[c] = sum_{j=0..3} w[c][j] x_{t-3+j}[c]
+ * Before t = 0 it reads the carried convolution state (zeros when NULL).
+ * l2norm divides by sqrt(sum of squares over the head's channels + 1e-6).
+ *   xq, xk  [B, T, H, Dk] bf16,  xv [B, T, H, Dv] bf16  projections
+ *   a, b    [B, T, H] fp32      gate pre-activations
+ *   wq, wk  [H*Dk, 4] fp32, wv [H*Dv, 4] fp32  taps per channel
+ *   A_log, dt_bias [H] fp32
+ *   conv_in  [B, 3, H*(2 Dk + Dv)] fp32, nullable: the 3 inputs before t = 0,
+ *            oldest first; channels are the q channels, then k, then v
+ *   q, k [B, T, H, Dk] bf16, v [B, T, H, Dv] bf16, g, beta [B, T, H] fp32: outputs,
+ *            ready as inputs of gdn_chunk_fwd / gdn_recurrent_step
+ *   conv_out same layout as conv_in, nullable: the 3 inputs ending at token
+ *            T - 1 (the decode cache); may be conv_in itself (updated in place)
+ * Every pointer except a, b, A_log, dt_bias, g, beta and conv_out must be
+ * 16-byte aligned (conv_out 4-byte).
+ * Errors: GDN_ERR_INVALID_ARG for null required pointers, bad sizes,
+ * misalignment or overlapping outputs; GDN_ERR_UNSUPPORTED for head sizes
+ * other than 64 and 128; GDN_ERR_HIP if a launch fails.  Asynchronous.
+ */
+gdn_status gdn_prologue(const void *xq, const void *xk, const void *xv, const float *a,
+                        const float *b, const float *wq, const float *wk, const float *wv,
+                        const float *A_log, const float *dt_bias, const float *conv_in, void *q,
+                        void *k, void *v, float *g, float *beta, float *conv_out, int B, int T,
+                        int H, int Dk, int Dv, void *stream);
+
+/*
+ * gdn_gated_rmsnorm -- the output stage after the rule (same walkthrough,
+ * data-flow overview: RMS normalisation with a SiLU output gate):
+ *   y = o / sqrt(mean(o^2) + eps) * weight * SiLU(z), per row of Dv channels
+ *   o [rows, Dv] fp32, z [rows, Dv] bf16, weight [Dv] fp32 (one weight per
+ *   channel, shared by every head), y [rows, Dv] bf16; all 16-byte aligned;
+ *   rows = B * T * H for the layout of gdn_chunk_fwd's o.  eps > 0.
+ * Errors: GDN_ERR_INVALID_ARG (null, rows < 1, eps <= 0, misalignment, y
+ * overlapping an input), GDN_ERR_UNSUPPORTED (Dv not 64 or 128),
+ * GDN_ERR_HIP.  Asynchronous.
+ */
+gdn_status gdn_gated_rmsnorm(const float *o, const void *z, const float *weight, void *y,
+                             long long rows, int Dv, float eps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn2_recurrent_step", "gdn_chunk_intra",
               "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
-              "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string"):
+              "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string",
+              "gdn_prologue", "gdn_gated_rmsnorm"):
         assert n in names
 
 
@@ -150,6 +151,45 @@ def test_varlen_rejects_bad_arguments():
     assert f(Dk=96) == 2
     assert f(ptrs=p[:7] + [p[0]] + p[8:]) == 1      # o overlaps q
     assert f(ptrs=p[:7] + [p[5]] + p[8:]) == 1      # o overlaps cu_seqlens
+
+
+def test_prologue_rejects_bad_arguments():
+    lib = gdn.load()
+    # xq xk xv a b wq wk wv A_log dt_bias conv_in | q k v g beta conv_out
+    p = [FAKE + (i << 32) for i in range(17)]
+
+    def f(ptrs=p, B=2, T=100, H=3, Dk=128, Dv=128):
+        return lib.gdn_prologue(*[_p(x) for x in ptrs], B, T, H, Dk, Dv, None)
+
+    assert f(ptrs=[None] + p[1:]) == 1               # no xq
+    assert f(ptrs=p[:14] + [None] + p[15:]) == 1     # no g
+    assert f(B=0) == 1
+    assert f(T=0) == 1
+    assert f(Dk=96) == 2
+    assert f(Dv=32) == 2
+    assert f(ptrs=p[:11] + [p[0]] + p[12:]) == 1     # q overlaps xq
+    assert f(ptrs=p[:12] + [p[11]] + p[13:]) == 1    # k overlaps q
+    assert f(ptrs=p[:16] + [p[12]]) == 1             # conv_out overlaps k
+    assert f(ptrs=p[:16] + [p[0]]) == 1              # conv_out overlaps xq
+    assert f(ptrs=p[:16] + [p[10] + 4]) == 1         # conv_out partly overlaps conv_in
+    assert f(ptrs=p[:5] + [p[5] + 4] + p[6:]) == 1   # taps not 16-byte aligned
+    assert f(ptrs=[p[0] + 8] + p[1:]) == 1           # projection not 16-byte aligned
+
+
+def test_gated_rmsnorm_rejects_bad_arguments():
+    lib = gdn.load()
+    p = [FAKE + (i << 32) for i in range(4)]         # o z weight y
+
+    def f(ptrs=p, rows=1000, Dv=128, eps=1e-5):
+        return lib.gdn_gated_rmsnorm(*[_p(x) for x in ptrs], rows, Dv, eps, None)
+
+    assert f(ptrs=[None] + p[1:]) == 1
+    assert f(rows=0) == 1
+    assert f(eps=0.0) == 1
+    assert f(Dv=96) == 2
+    assert f(ptrs=p[:3] + [p[0]]) == 1               # y overlaps o
+    assert f(ptrs=p[:3] + [p[1] + 64]) == 1          # y overlaps z
+    assert f(ptrs=[p[0] + 8] + p[1:]) == 1           # o not 16-byte aligned
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
