@@ -48,7 +48,7 @@ struct FusedCfg {
     static constexpr int BV = 32;
     static constexpr int NS = DK / 32;   // 32-wide k slabs
     static constexpr int NKB = DK / 16;  // 16-row blocks of the state
-    static constexpr int LDK = RowTile<DK>::LD;  // row stride of the raw K and Q tiles
+    static constexpr int LDK = DK;       // row stride of the raw K and Q tiles (paired-group layout)
     static constexpr int LDP = BT + 4;   // fp16 row stride of sP, sT, sA
     static constexpr int LDV = BV + 8;   // bf16 row stride of sV
 };
@@ -59,14 +59,15 @@ struct FusedCfg {
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
-    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows (swizzled, see tile_off)
+    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows, paired-group layout (tile_off_pg)
     alignas(16) uint16_t Q[2][BT * C::LDK];
     alignas(16) _Float16 P[2][BT * C::LDP];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
     alignas(16) uint16_t V[2][BT * C::LDV];
     alignas(16) float gam[2][BT];
+    alignas(16) float gs[2][BT];               // scale * gam
     alignas(16) float beta[2][BT];
-    alignas(16) float diag[2][BT];
+    alignas(16) float diag[2][BT];             // scale * (q_i . k_i)
     alignas(16) float dk[2][BT];              // 2^(G2_last - G2_j): decay of key j to the chunk end
     alignas(16) _Float16 A[BT * C::LDP];
     alignas(16) float g2T[BT], betaT[BT];  // gate tables private to the inverse producer
@@ -176,7 +177,7 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 // ------------------------------------------- producer: P and consumer inputs
 template <int DK, int DV>
 __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
-                                          const HeadArgs &ha, int lane) {
+                                          const HeadArgs &ha, float scale, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
     // V tile (raw bf16) first, so its registers can be refilled early
@@ -188,7 +189,9 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     if (next >= 0) load_v<DV>(R.v, ha, next, lane);
     const float G2 = chunk_g2(R.g);
     sm.g2P[lane] = G2;
-    sm.gam[buf][lane] = __builtin_amdgcn_exp2f(G2);
+    const float gmv = __builtin_amdgcn_exp2f(G2);
+    sm.gam[buf][lane] = gmv;
+    sm.gs[buf][lane] = scale * gmv;
     sm.beta[buf][lane] = R.beta;
     if (next >= 0) load_gates(R.g, R.beta, ha, next, lane);
     const float G2L = sm.g2P[BT - 1];
@@ -201,7 +204,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         colG2[I] = *(const f32x4 *)&sm.g2P[16 * I + 4 * g];
         rowG2[I] = sm.g2P[16 * I + r];
     }
-    // P tiles: lane gets P[16I + r][16J + 4g + e] = (q_i . k_j) 2^(G2_i - G2_j)
+    // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
     _Float16 *P = sm.P[buf];
 #pragma unroll
     for (int tile = 0; tile < 10; ++tile) {
@@ -214,32 +217,40 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 16 * J + 4 * g + e;
-            const float val = acc[e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            const float val = scale * acc[e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
             hv[e] = (_Float16)((i > j) ? val : 0.f);
-            if (I == J && i == j) sm.diag[buf][i] = acc[e];
+            if (I == J && i == j) sm.diag[buf][i] = scale * acc[e];
         }
         *(f16x4 *)&P[i * C::LDP + 16 * J + 4 * g] = hv;
     }
-    // raw bf16 copy of Q for the consumers; then Q's registers are refilled
+    // raw bf16 copy of Q for the consumers in the paired-group layout (the two
+    // 4-column halves of a register go to their stored groups); then Q's
+    // registers are refilled
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-            *(uint4 *)&sm.Q[buf][tile_off<DK>(16 * I + r, 32 * s + 8 * g)] = R.q[I][s];
+        for (int s = 0; s < C::NS; ++s) {
+            const int row = 16 * I + r, c0 = 32 * s + 8 * g;
+            *(uint2 *)&sm.Q[buf][tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(R.q[I][s].x, R.q[I][s].y);
+            *(uint2 *)&sm.Q[buf][tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(R.q[I][s].z, R.q[I][s].w);
+        }
     if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
     // raw bf16 copy of K; then K's registers are refilled
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-            *(uint4 *)&sm.K[buf][tile_off<DK>(16 * I + r, 32 * s + 8 * g)] = R.k[I][s];
+        for (int s = 0; s < C::NS; ++s) {
+            const int row = 16 * I + r, c0 = 32 * s + 8 * g;
+            *(uint2 *)&sm.K[buf][tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(R.k[I][s].x, R.k[I][s].y);
+            *(uint2 *)&sm.K[buf][tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(R.k[I][s].z, R.k[I][s].w);
+        }
     if (next >= 0) load_rows<DK>(R.k, ha.k, ha, next, lane);
 }
 
 // ---------------------------------------------------------------- consumers
 template <int DK, int DV>
 __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, float *__restrict__ o,
-                                        const HeadArgs &ha, int chunk, int wave, float scale, int lane) {
+                                        const HeadArgs &ha, int chunk, int wave, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
     // X = K S and Y = Q S on bf16 MFMA: exact bf16 K, Q against the state
@@ -254,8 +265,8 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         const bf16x8 shi = __builtin_bit_cast(bf16x8, uhi), slo = __builtin_bit_cast(bf16x8, ulo);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint4 ka = frag_rows_sw<DK>(sm.K[buf], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_sw<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+            const uint4 ka = frag_rows_pg<DK>(sm.K[buf], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
             const bf16x8 kb = __builtin_bit_cast(bf16x8, ka), qb = __builtin_bit_cast(bf16x8, qa);
             X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, shi, X[I], 0, 0, 0);
             Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, shi, Y[I], 0, 0, 0);
@@ -263,18 +274,21 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, slo, Y[I], 0, 0, 0);
         }
     }
-    // R = beta (V - gamma X)
-    f32x4 Rr[4], gam[4];
+    // R = beta (V - gamma X); V[16I + 4g + e][this wave's column r] by
+    // transpose loads of the row-major V tile
+    f32x4 Rr[4];
     const int cl = wave * 16 + r;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        gam[I] = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
+        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
         const f32x4 bet = *(const f32x4 *)&sm.beta[buf][16 * I + 4 * g];
+        const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)&sm.V[buf][(16 * I + 4 * g + (r >> 2)) * C::LDV + wave * 16 + 4 * (r & 3)]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * g + e;
-            const float vv = __uint_as_float(((uint32_t)sm.V[buf][i * C::LDV + cl]) << 16);
-            Rr[I][e] = bet[e] * (vv - gam[I][e] * X[I][e]);
+            const float vv = __uint_as_float(((uint32_t)(uint16_t)vt[e]) << 16);
+            Rr[I][e] = bet[e] * (vv - gm[e] * X[I][e]);
         }
     }
     // Vnew = R + (T - I) R
@@ -292,7 +306,8 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             Vn[I] = mma_slab(Vn[I], a, rf[s]);
         }
     }
-    // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew)
+    // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew), with scale folded
+    // into the gs, diag and P tables
     _Float16 vf[2][8];
     frag_from_acc(vf[0], Vn[0], Vn[1]);
     frag_from_acc(vf[1], Vn[2], Vn[3]);
@@ -301,23 +316,34 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     const bool full = t0 + BT <= ha.T;
     float *obase = o + ((ha.tok0 + t0) * ha.H + ha.h) * (long)DV + col;
     const long ostride = (long)ha.H * DV;
+    f32x4 O[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        f32x4 acc;
+        const f32x4 gs = *(const f32x4 *)&sm.gs[buf][16 * I + 4 * g];
         const f32x4 dg = *(const f32x4 *)&sm.diag[buf][16 * I + 4 * g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = gam[I][e] * Y[I][e] + dg[e] * Vn[I][e];
+        for (int e = 0; e < 4; ++e) O[I][e] = gs[e] * Y[I][e] + dg[e] * Vn[I][e];
 #pragma unroll
         for (int s = 0; s <= (I >> 1); ++s) {
             _Float16 a[8];
             frag_rows(a, sm.P[buf], C::LDP, 16 * I, 32 * s, lane);
-            acc = mma_slab(acc, a, vf[s]);
+            O[I] = mma_slab(O[I], a, vf[s]);
         }
+    }
+    // row 16I + 4g + e of the chunk: the lane's base row 4g, plus a
+    // wave-uniform offset
+    float *ob = obase + (4 * g) * ostride;
+    if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ti = 16 * I + 4 * g + e;
-            if (full || t0 + ti < ha.T) obase[ti * ostride] = scale * acc[e];
-        }
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[(16 * I + e) * ostride] = O[I][e];
+    } else {
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t0 + 16 * I + 4 * g + e < ha.T) ob[(16 * I + e) * ostride] = O[I][e];
     }
     // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =
     // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
@@ -341,7 +367,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         f32x4 acc = S[m] * gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            const uint4 a = frag_T_pg<DK>(sm.K[buf], 32 * s, 16 * m, lane);
             acc = mma_bf16_raw(acc, a, dvh[s]);
             acc = mma_bf16_raw(acc, a, dvl[s]);
         }
@@ -410,7 +436,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, scale, lane);
+            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, lane);
             __syncthreads();
         }
         if (ht) {
@@ -436,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
         load_gates(R.g, R.beta, ha, 0, lane);
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) produce_P(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, lane);
+            if (c + 1 < NT) produce_P(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, scale, lane);
             __syncthreads();
         }
     }

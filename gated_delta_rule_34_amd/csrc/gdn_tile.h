@@ -66,6 +66,37 @@ __device__ __forceinline__ uint4 frag_rows_sw(const uint16_t *M, int row0, int k
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
+// Paired-group column layout: within each 32-column slab the 4-column groups
+// a and a + 4 (a = 0..3) sit side by side, so the 8 values that MFMA lane
+// group g supplies for a 32-deep slab (columns 4g.. and 16 + 4g..) are 16
+// contiguous bytes.  pair_col maps a logical column to its stored column
+// before the row swizzle of tile_off_pg.
+__device__ __forceinline__ int pair_col(int c) {
+    const int a = (c >> 2) & 7;
+    const int pa = (a < 4) ? 2 * a : 2 * a - 7;
+    return (c & ~31) | (pa << 2) | (c & 3);
+}
+
+// Offset (in halves) of stored column `col` of row `row` in a paired-group
+// tile (unpadded rows of D halves).  The 8-column units are XOR-swizzled by
+// row so that both the 16-byte fragment reads (16 rows, one 8-column unit
+// each) and the 8-byte transpose reads (4 rows x 4 alternate 4-column
+// groups) touch 64 distinct banks (64 banks of 4 bytes).
+template <int D>
+__device__ __forceinline__ int tile_off_pg(int row, int col) {
+    static_assert(D == 64 || D == 128, "head size");
+    if (D == 128) return row * D + (col ^ (((row & 3) << 5) | (((row >> 2) & 3) << 3)));
+    return row * D + (col ^ ((((row >> 1) & 1) << 5) | (((row >> 2) & 3) << 3)));
+}
+
+// Fragment of the 32-wide slab at column k0 of rows row0 .. row0 + 15 of a
+// paired-group tile: one 16-byte read per lane.
+template <int D>
+__device__ __forceinline__ uint4 frag_rows_pg(const uint16_t *M, int row0, int k0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    return *(const uint4 *)&M[tile_off_pg<D>(row0 + r, k0 + 8 * g)];
+}
+
 // A fragment of the transpose (rows kc0 .. kc0 + 15 of M^T, slab of M rows
 // j0 .. j0 + 31) read from the row-major tile with the gfx950 LDS transpose
 // load: within each 16-lane group, lane j receives element (j % 4) of the
@@ -79,6 +110,21 @@ __device__ __forceinline__ uint4 frag_T_sw(const uint16_t *M, int j0, int kc0, i
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const uint16_t *p0 = &M[tile_off<D>(j0 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
     const uint16_t *p1 = &M[tile_off<D>(j0 + 16 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
+}
+
+// frag_T_sw for a paired-group tile (logical columns kc0 + 4(r % 4) .. + 3
+// are one stored 4-column group).
+template <int D>
+__device__ __forceinline__ uint4 frag_T_pg(const uint16_t *M, int j0, int kc0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int pc = pair_col(kc0 + 4 * (r & 3));
+    const uint16_t *p0 = &M[tile_off_pg<D>(j0 + 4 * g + (r >> 2), pc)];
+    const uint16_t *p1 = &M[tile_off_pg<D>(j0 + 16 + 4 * g + (r >> 2), pc)];
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
     const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
