@@ -53,14 +53,17 @@ struct FusedCfg {
     static constexpr int LDV = BV + 8;   // bf16 row stride of sV
 };
 
-// Everything the consumers read for one chunk is double-buffered (index =
-// chunk parity), so producers fill chunk c + 1 while consumers read chunk c
-// and one barrier per chunk suffices.  A is private to the inverse producer.
+// The raw K and Q rows of chunk c sit in buffer c % 3: they are written two
+// iterations ahead (chunk c + 2 in iteration c), read by both producers one
+// iteration ahead and by the consumers in iteration c.  Everything else the
+// consumers read for a chunk is double-buffered (index = chunk parity).  One
+// barrier per iteration separates every write from its reads.  A is private
+// to the inverse producer.
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
-    alignas(16) uint16_t K[2][BT * C::LDK];   // raw bf16 rows, paired-group layout (tile_off_pg)
-    alignas(16) uint16_t Q[2][BT * C::LDK];
+    alignas(16) uint16_t K[3][BT * C::LDK];   // raw bf16 rows, paired-group layout (tile_off_pg)
+    alignas(16) uint16_t Q[3][BT * C::LDK];
     alignas(16) _Float16 P[2][BT * C::LDP];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
     alignas(16) uint16_t V[2][BT * C::LDV];
@@ -94,20 +97,21 @@ struct HeadArgs {
     int h, T, H, vcol0;
 };
 
+// The loaders are branch-free, so the compiler can count the loads in
+// flight and wait only for the ones it needs.  Rows past the end of the
+// sequence read its last row (a.T >= 1 is the caller's guarantee): with
+// beta = g = 0 there (load_gates zeroes them) such rows add nothing to A,
+// T - I, the new values or the state, and their outputs are not stored.
 template <int DK>
 __device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16_t *__restrict__ src,
                                           const HeadArgs &a, int chunk, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    const bool full = (chunk + 1) * BT <= a.T;
-    const long rowstride = (long)a.H * DK;
-    const uint16_t *base = src + ((a.tok0 + chunk * BT + r) * a.H + a.h) * (long)DK + 8 * g;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        const int t = chunk * BT + 16 * I + r;
-        const uint16_t *p = base + 16 * I * rowstride;
+        const int t = min(chunk * BT + 16 * I + r, a.T - 1);
+        const uint16_t *p = src + ((a.tok0 + t) * a.H + a.h) * (long)DK + 8 * g;
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s)
-            dst[I][s] = (full || t < a.T) ? *(const uint4 *)(p + 32 * s) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < DK / 32; ++s) dst[I][s] = *(const uint4 *)(p + 32 * s);
     }
 }
 
@@ -115,32 +119,84 @@ template <int DV>
 __device__ __forceinline__ void load_v(uint4 (&dst)[4], const HeadArgs &a, int chunk, int lane) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int t = chunk * BT + 16 * p + (lane >> 2);
-        dst[p] = (t < a.T) ? *(const uint4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 +
-                                              (lane & 3) * 8)
-                           : make_uint4(0, 0, 0, 0);
+        const int t = min(chunk * BT + 16 * p + (lane >> 2), a.T - 1);
+        dst[p] = *(const uint4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 + (lane & 3) * 8);
     }
 }
 
+// Raw gates of the chunk's token `lane`; finish_gates zeroes them past the
+// end of the sequence once they have arrived.
 __device__ __forceinline__ void load_gates(float &gv, float &bv, const HeadArgs &a, int chunk, int lane) {
-    const int t = chunk * BT + lane;
-    const long idx = (a.tok0 + t) * a.H + a.h;
-    gv = (t < a.T) ? a.g[idx] : 0.f;
-    bv = (t < a.T) ? a.beta[idx] : 0.f;
+    const long idx = (a.tok0 + min(chunk * BT + lane, a.T - 1)) * a.H + a.h;
+    gv = a.g[idx];
+    bv = a.beta[idx];
+}
+
+__device__ __forceinline__ void finish_gates(float &gv, float &bv, const HeadArgs &a, int chunk, int lane) {
+    const bool in = chunk * BT + lane < a.T;
+    gv = in ? gv : 0.f;
+    bv = in ? bv : 0.f;
+}
+
+// Raw K and Q rows held in registers into kq-buffer `kb` in the paired-group
+// layout (the two 4-column halves of a register go to their stored groups).
+template <int DK, int DV>
+__device__ __forceinline__ void write_kq(FusedSmem<DK, DV> &sm, const ChunkRegs<DK / 32> &R, int kb, int lane) {
+    using C = FusedCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const int row = 16 * I + r, c0 = 32 * s + 8 * g;
+            uint16_t *q0 = &sm.Q[kb][tile_off_pg<DK>(row, pair_col(c0))];
+            uint16_t *q1 = &sm.Q[kb][tile_off_pg<DK>(row, pair_col(c0 + 4))];
+            uint16_t *k0 = &sm.K[kb][tile_off_pg<DK>(row, pair_col(c0))];
+            uint16_t *k1 = &sm.K[kb][tile_off_pg<DK>(row, pair_col(c0 + 4))];
+            *(uint2 *)q0 = make_uint2(R.q[I][s].x, R.q[I][s].y);
+            *(uint2 *)q1 = make_uint2(R.q[I][s].z, R.q[I][s].w);
+            *(uint2 *)k0 = make_uint2(R.k[I][s].x, R.k[I][s].y);
+            *(uint2 *)k1 = make_uint2(R.k[I][s].z, R.k[I][s].w);
+        }
+}
+
+// The 10 lower 16x16 tiles of X_J Y_I^T (tile t: I = tileI(t), J = tileJ(t))
+// from two paired-group tiles in LDS: this lane gets row 16J + 4g + e and
+// column 16I + r of tile t in acc[t][e].
+template <int DK>
+__device__ __forceinline__ void lower_tiles(f32x4 (&acc)[10], const uint16_t *X, const uint16_t *Y, int lane) {
+#pragma unroll
+    for (int t = 0; t < 10; ++t) acc[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        uint4 xf[4], yf[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            xf[I] = frag_rows_pg<DK>(X, 16 * I, 32 * s, lane);
+            yf[I] = (X == Y) ? xf[I] : frag_rows_pg<DK>(Y, 16 * I, 32 * s, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < 10; ++t) acc[t] = mma_bf16_raw(acc[t], xf[tileJ(t)], yf[tileI(t)]);
+    }
 }
 
 // ------------------------------------------------------- producer: A and T
-// Chunk `chunk` from registers into T - I of LDS half `buf`; issues the
-// loads of chunk `next` (if any) once the registers are free.
+// Chunk c1 (its K rows in kq-buffer c1 % 3) into T - I of LDS half c1 & 1;
+// R holds the gates of chunk c1 and receives those of c1 + 1.
 template <int DK, int DV>
-__device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
+__device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int NT,
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
+    finish_gates(R.g, R.beta, ha, c1, lane);
     sm.g2T[lane] = chunk_g2(R.g);
     sm.betaT[lane] = R.beta;
+    load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
     // K_J K_I^T: this lane gets row i = 16I + r and columns j = 16J + 4g + e
     // of every tile, stored as 4 adjacent halves
+    f32x4 acc[10];
+    const uint16_t *Kt = sm.K[c1 % 3];
+    lower_tiles<DK>(acc, Kt, Kt, lane);
     float rowG2[4], rowB[4];
     f32x4 colG2[4];
 #pragma unroll
@@ -149,54 +205,60 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         rowB[I] = sm.betaT[16 * I + r];
         colG2[I] = *(const f32x4 *)&sm.g2T[16 * I + 4 * g];
     }
-    // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j)), bf16 MFMA on raw inputs
+    // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j))
 #pragma unroll
     for (int tile = 0; tile < 10; ++tile) {
         const int I = tileI(tile), J = tileJ(tile);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[J][s], R.k[I][s]);
         const int i = 16 * I + r;
         f16x4 hv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 16 * J + 4 * g + e;
-            const float val = acc[e] * rowB[I] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            const float val = acc[tile][e] * rowB[I] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
             hv[e] = (_Float16)((i > j) ? val : 0.f);
         }
         *(f16x4 *)&sm.A[i * C::LDP + 16 * J + 4 * g] = hv;
     }
-    if (next >= 0) {
-        load_rows<DK>(R.k, ha.k, ha, next, lane);
-        load_gates(R.g, R.beta, ha, next, lane);
-    }
-    _Float16 *Tm = sm.Tm[buf];
-    unit_lower_inverse<C::LDP>(sm.A, Tm, lane);
+    unit_lower_inverse<C::LDP>(sm.A, sm.Tm[c1 & 1], lane);
 }
 
 // ------------------------------------------- producer: P and consumer inputs
+// Chunk c1: V, gate tables and P into LDS half c1 & 1 (P from the K and Q
+// rows in kq-buffer c1 % 3).  R holds V and the gates of chunk c1 and the raw
+// K, Q rows of chunk c1 + 1; those rows go to kq-buffer (c1 + 1) % 3 and R
+// receives the rows of chunk c1 + 2, a full iteration before they are stored.
 template <int DK, int DV>
-__device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int buf, int next,
+__device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int NT,
                                           const HeadArgs &ha, float scale, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    // V tile (raw bf16) first, so its registers can be refilled early
+    const int buf = c1 & 1;
+    // first store everything that arrived during the previous iteration: the
+    // V tile, the gates and the raw rows of chunk c1 + 1 (when it is past the
+    // end, its buffer is written but never read)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
         *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
     }
-    if (next >= 0) load_v<DV>(R.v, ha, next, lane);
+    finish_gates(R.g, R.beta, ha, c1, lane);
     const float G2 = chunk_g2(R.g);
     sm.g2P[lane] = G2;
     const float gmv = __builtin_amdgcn_exp2f(G2);
     sm.gam[buf][lane] = gmv;
     sm.gs[buf][lane] = scale * gmv;
     sm.beta[buf][lane] = R.beta;
-    if (next >= 0) load_gates(R.g, R.beta, ha, next, lane);
+    write_kq(sm, R, (c1 + 1) % 3, lane);
+    // then fetch the next ones together (indices clamped to the last chunk)
+    load_v<DV>(R.v, ha, min(c1 + 1, NT - 1), lane);
+    load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
+    load_rows<DK>(R.q, ha.q, ha, min(c1 + 2, NT - 1), lane);
+    load_rows<DK>(R.k, ha.k, ha, min(c1 + 2, NT - 1), lane);
     const float G2L = sm.g2P[BT - 1];
     sm.dk[buf][lane] = __builtin_amdgcn_exp2f(G2L - G2);
-    // this lane's rows i = 16I + r and columns j = 16J + 4g + e of every tile
+    // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
+    f32x4 acc[10];
+    lower_tiles<DK>(acc, sm.K[c1 % 3], sm.Q[c1 % 3], lane);
     f32x4 colG2[4];
     float rowG2[4];
 #pragma unroll
@@ -204,52 +266,27 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         colG2[I] = *(const f32x4 *)&sm.g2P[16 * I + 4 * g];
         rowG2[I] = sm.g2P[16 * I + r];
     }
-    // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
     _Float16 *P = sm.P[buf];
 #pragma unroll
     for (int tile = 0; tile < 10; ++tile) {
         const int I = tileI(tile), J = tileJ(tile);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) acc = mma_bf16_raw(acc, R.k[J][s], R.q[I][s]);
         const int i = 16 * I + r;
         f16x4 hv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 16 * J + 4 * g + e;
-            const float val = scale * acc[e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            const float val = scale * acc[tile][e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
             hv[e] = (_Float16)((i > j) ? val : 0.f);
-            if (I == J && i == j) sm.diag[buf][i] = scale * acc[e];
+            if (I == J && i == j) sm.diag[buf][i] = scale * acc[tile][e];
         }
         *(f16x4 *)&P[i * C::LDP + 16 * J + 4 * g] = hv;
     }
-    // raw bf16 copy of Q for the consumers in the paired-group layout (the two
-    // 4-column halves of a register go to their stored groups); then Q's
-    // registers are refilled
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-            const int row = 16 * I + r, c0 = 32 * s + 8 * g;
-            *(uint2 *)&sm.Q[buf][tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(R.q[I][s].x, R.q[I][s].y);
-            *(uint2 *)&sm.Q[buf][tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(R.q[I][s].z, R.q[I][s].w);
-        }
-    if (next >= 0) load_rows<DK>(R.q, ha.q, ha, next, lane);
-    // raw bf16 copy of K; then K's registers are refilled
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-            const int row = 16 * I + r, c0 = 32 * s + 8 * g;
-            *(uint2 *)&sm.K[buf][tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(R.k[I][s].x, R.k[I][s].y);
-            *(uint2 *)&sm.K[buf][tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(R.k[I][s].z, R.k[I][s].w);
-        }
-    if (next >= 0) load_rows<DK>(R.k, ha.k, ha, next, lane);
 }
 
 // ---------------------------------------------------------------- consumers
 template <int DK, int DV>
-__device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, float *__restrict__ o,
+__device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, int kb,
+                                        float *__restrict__ o,
                                         const HeadArgs &ha, int chunk, int wave, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
@@ -265,8 +302,8 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         const bf16x8 shi = __builtin_bit_cast(bf16x8, uhi), slo = __builtin_bit_cast(bf16x8, ulo);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint4 ka = frag_rows_pg<DK>(sm.K[buf], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+            const uint4 ka = frag_rows_pg<DK>(sm.K[kb], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_pg<DK>(sm.Q[kb], 16 * I, 32 * s, lane);
             const bf16x8 kb = __builtin_bit_cast(bf16x8, ka), qb = __builtin_bit_cast(bf16x8, qa);
             X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, shi, X[I], 0, 0, 0);
             Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, shi, Y[I], 0, 0, 0);
@@ -367,7 +404,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         f32x4 acc = S[m] * gl;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_pg<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            const uint4 a = frag_T_pg<DK>(sm.K[kb], 32 * s, 16 * m, lane);
             acc = mma_bf16_raw(acc, a, dvh[s]);
             acc = mma_bf16_raw(acc, a, dvl[s]);
         }
@@ -425,8 +462,9 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
     const long sbase = bh * (long)DK * DV;
     // Each role runs its own loop with the same barrier count (one per
     // iteration), so the registers of one role are never live in another.
-    // Iteration c: consumers walk chunk c (LDS half c & 1); producers prepare
-    // chunk c + 1 (LDS half (c + 1) & 1) and fetch chunk c + 2.
+    // Iteration c: consumers walk chunk c (LDS half c & 1, kq-buffer c % 3);
+    // producers prepare chunk c + 1, the P producer also stores the raw rows
+    // of chunk c + 2 and fetches chunk c + 3.
     if (wave < 2) {
         f32x4 S[C::NKB];
         const int col = ha.vcol0 + wave * 16 + r;
@@ -436,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c >= 0) consume(sm, S, c & 1, o, ha, c, wave, lane);
+            if (c >= 0) consume(sm, S, c & 1, c % 3, o, ha, c, wave, lane);
             __syncthreads();
         }
         if (ht) {
@@ -447,22 +485,28 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
         }
     } else if (wave == 2) {
         ChunkRegs<C::NS> R;
-        load_rows<DK>(R.k, k, ha, 0, lane);
-        load_gates(R.g, R.beta, ha, 0, lane);
+        if (NT > 0) load_gates(R.g, R.beta, ha, 0, lane);
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) produce_T(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, lane);
+            if (c + 1 < NT) produce_T(sm, R, c + 1, NT, ha, lane);
             __syncthreads();
         }
     } else {
         ChunkRegs<C::NS> R;
-        load_rows<DK>(R.k, k, ha, 0, lane);
-        load_rows<DK>(R.q, q, ha, 0, lane);
-        load_v<DV>(R.v, ha, 0, lane);
-        load_gates(R.g, R.beta, ha, 0, lane);
+        // chunk 0's raw rows go to kq-buffer 0 before the first barrier;
+        // chunk 1's wait in registers (an empty sequence loads nothing)
+        if (NT > 0) {
+            load_rows<DK>(R.k, k, ha, 0, lane);
+            load_rows<DK>(R.q, q, ha, 0, lane);
+            load_v<DV>(R.v, ha, 0, lane);
+            load_gates(R.g, R.beta, ha, 0, lane);
+            write_kq(sm, R, 0, lane);
+            load_rows<DK>(R.k, k, ha, min(1, NT - 1), lane);
+            load_rows<DK>(R.q, q, ha, min(1, NT - 1), lane);
+        }
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) produce_P(sm, R, (c + 1) & 1, (c + 2 < NT) ? c + 2 : -1, ha, scale, lane);
+            if (c + 1 < NT) produce_P(sm, R, c + 1, NT, ha, scale, lane);
             __syncthreads();
         }
     }
