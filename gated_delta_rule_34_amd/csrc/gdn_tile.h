@@ -176,6 +176,19 @@ __device__ __forceinline__ float chunk_g2(float gv) {
     return x;
 }
 
+// Four rows of one column of a 16x16 fp16 block by the gfx950 LDS transpose
+// load: lane (g, r) receives M[row0 + 4g + e][col0 + r], e = 0..3 (row
+// stride LDP halves, a multiple of 4; col0 a multiple of 4).
+template <int LDP>
+__device__ __forceinline__ f16x4 col4_tr(const _Float16 *M, int row0, int col0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)&M[(row0 + 4 * g + (r >> 2)) * LDP + col0 + 4 * (r & 3)]);
+    return __builtin_bit_cast(f16x4, v);
+}
+
 // T - I for T = (I + A)^-1 of one chunk, A strictly lower (fp16, row stride
 // LDP, the strict-lower part of every 16x16 block filled, other entries of
 // the lower tiles zero); one wave.  Tm receives the lower tiles of T - I.
@@ -183,7 +196,9 @@ __device__ __forceinline__ float chunk_g2(float gv) {
 //    x_i = [i == cc] - sum_{j<i} A_ij x_j, with four partial sums per row.
 //  Off-diagonal blocks, one sub-diagonal level d at a time (the blocks of a
 //    level are independent and are computed together):
-//    T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ.
+//    T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ,
+//    with column pieces read by transpose loads and T_IJ formed as
+//    (M^T T_II^T)^T so each lane stores 4 adjacent entries of a row.
 template <int LDP>
 __device__ __forceinline__ void unit_lower_inverse(const _Float16 *A, _Float16 *Tm, int lane) {
     const int r = lane & 15, g = lane >> 4;
@@ -211,27 +226,37 @@ __device__ __forceinline__ void unit_lower_inverse(const _Float16 *A, _Float16 *
 #pragma unroll
         for (int J = 0; J < 4 - d; ++J) {
             const int I = J + d;
+            // M starts as A_IJ: lane (g, r) holds A[16I + 4g + e][16J + r]
+            const f16x4 aij = col4_tr<LDP>(A, 16 * I, 16 * J, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) M[J][e] = (float)A[(16 * I + 4 * g + e) * LDP + 16 * J + r];
+            for (int e = 0; e < 4; ++e) M[J][e] = (float)aij[e];
 #pragma unroll
             for (int K = J; K < I; ++K) {
                 const f16x4 a = *(const f16x4 *)&A[(16 * I + r) * LDP + 16 * K + 4 * g];
-                f16x4 bq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bq[e] = Tm[(16 * K + 4 * g + e) * LDP + 16 * J + r];
-                M[J] = mma_f16_block(M[J], a, bq);
+                M[J] = mma_f16_block(M[J], a, col4_tr<LDP>(Tm, 16 * K, 16 * J, lane));
             }
         }
+        // T_IJ = -T_II M, formed transposed as M^T T_II^T so that this lane
+        // holds row 16I + r, columns 16J + 4g .. + 3 and stores them at once
 #pragma unroll
         for (int J = 0; J < 4 - d; ++J) {
             const int I = J + d;
-            const f16x4 a = *(const f16x4 *)&Tm[(16 * I + r) * LDP + 16 * I + 4 * g];
-            f16x4 bq;
+            f16x4 tb = *(const f16x4 *)&Tm[(16 * I + r) * LDP + 16 * I + 4 * g];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bq[e] = (_Float16)M[J][e];
-            const f32x4 res = mma_f16_block(M[J], a, bq);  // T_II M = M + strict(T_II) M
+            for (int e = 0; e < 4; ++e)
+                if (4 * g + e == r) tb[e] = (_Float16)1.f;  // T_II = I + strict(T_II)
+            // M enters as fp16 hi + lo parts, so T_II M keeps ~22 bits of M
+            f16x4 mh, ml;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * g + e) * LDP + 16 * J + r] = (_Float16)(-res[e]);
+            for (int e = 0; e < 4; ++e) {
+                mh[e] = (_Float16)M[J][e];
+                ml[e] = (_Float16)(M[J][e] - (float)mh[e]);
+            }
+            const f32x4 res = mma_f16_block(mma_f16_block(zero4(), mh, tb), ml, tb);
+            f16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (_Float16)(-res[e]);
+            *(f16x4 *)&Tm[(16 * I + r) * LDP + 16 * J + 4 * g] = out;
         }
     }
 }
