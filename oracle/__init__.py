@@ -64,6 +64,7 @@ def configure(lib):
     lib.gdn_oracle_step.argtypes = [_dp] * 7 + [i] * 4 + [d, i]
     lib.gdn2_oracle_step.argtypes = [_dp] * 8 + [i] * 4 + [d, i]
     lib.gdn_oracle_bwd.argtypes = [_dp] * 14 + [i] * 5 + [d, i]
+    lib.gdn2_oracle_bwd.argtypes = [_dp] * 16 + [i] * 5 + [d, i]
     lib.gdn_oracle_max_threads.restype = i
     return lib
 
@@ -155,3 +156,25 @@ def gdn_bwd(q, k, v, g, beta, h0, dO, dST=None, scale=None, nthreads=0):
     outs = [a.ctypes.data_as(_dp) for a in (dq, dk, dv, dg, db)] + [dh0.ctypes.data_as(_dp) if dh0 is not None else None]
     _load().gdn_oracle_bwd(*[p for _, p in keep], *outs, B, T, H, Dk, Dv, float(scale), int(nthreads))
     return dq, dk, dv, dg, db, dh0
+
+
+def gdn2_bwd(q, k, v, log_alpha, b, w, h0, dO, dST=None, scale=None, nthreads=0):
+    """Gradients of L = sum(dO * o) + sum(dST * S_T) for the per-token GDN-2
+    recurrence: returns dq, dk, dv, dlog_alpha, db, dw, dh0 (dh0 is None when
+    h0 is None)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if scale is None:
+        scale = Dk ** -0.5
+    keep = [_c(x) for x in (q, k, v, log_alpha, b, w, h0, dO, dST)]
+    dq = np.zeros((B, T, H, Dk))
+    dk = np.zeros((B, T, H, Dk))
+    dv = np.zeros((B, T, H, Dv))
+    dla = np.zeros((B, T, H, Dk))
+    db = np.zeros((B, T, H, Dk))
+    dw = np.zeros((B, T, H, Dv))
+    dh0 = np.zeros((B, H, Dk, Dv)) if h0 is not None else None
+    outs = [a.ctypes.data_as(_dp) for a in (dq, dk, dv, dla, db, dw)] + \
+        [dh0.ctypes.data_as(_dp) if dh0 is not None else None]
+    _load().gdn2_oracle_bwd(*[p for _, p in keep], *outs, B, T, H, Dk, Dv, float(scale), int(nthreads))
+    return dq, dk, dv, dla, db, dw, dh0

@@ -303,3 +303,123 @@ void gdn_oracle_bwd(const double *q, const double *k, const double *v, const dou
         free(starts); free(Sp); free(us); free(ps); free(S); free(St); free(D); free(du);
     }
 }
+
+/*
+ * Backward of the Gated DeltaNet-2 forward (same loss as gdn_oracle_bwd).
+ * Per token, with P = Diag(exp(log_alpha)) S_{t-1}, e = b . k,
+ * p = P^T e, u = w . v - p, S_t = P + k u^T, o = scale S_t^T q, and D the
+ * gradient of L w.r.t. S_t:
+ *   D   += scale q do^T          dq   = scale S_t do
+ *   dk   = D u                   du   = D^T k
+ *   dw   = du . v                dv   = du . w
+ *   de   = -P du                 D'   = D - e du^T   (gradient w.r.t. P)
+ *   db   = de . k                dk  += de . b
+ *   dlog_alpha_i = sum_j D'_ij P_ij                   D = Diag(exp(log_alpha)) D'
+ * and dh0 = D after the first token.  States are recomputed forward one
+ * 64-token segment at a time from stored segment-start states.
+ * Outputs dq, dk, dla, db [B,T,H,Dk], dv, dw [B,T,H,Dv], dh0 [B,H,Dk,Dv] or NULL.
+ */
+void gdn2_oracle_bwd(const double *q, const double *k, const double *v, const double *log_alpha,
+                     const double *bgate, const double *wgate, const double *h0, const double *dO,
+                     const double *dST, double *dq, double *dk, double *dv, double *dla, double *db,
+                     double *dw, double *dh0, int B, int T, int H, int Dk, int Dv, double scale, int nthreads) {
+    set_threads(nthreads);
+    const long units = (long)B * H;
+    const int SEG = 64;
+    const int nseg = (T + SEG - 1) / SEG;
+    const size_t SS = (size_t)Dk * Dv;
+#pragma omp parallel for schedule(static)
+    for (long unit = 0; unit < units; ++unit) {
+        const long b = unit / H, h = unit % H;
+        double *starts = (double *)malloc(sizeof(double) * SS * (size_t)nseg);
+        double *Ps = (double *)malloc(sizeof(double) * SS * (size_t)SEG);  /* P of each token of a segment */
+        double *us = (double *)malloc(sizeof(double) * (size_t)Dv * SEG);  /* u of each token */
+        double *S = (double *)malloc(sizeof(double) * SS);
+        double *St = (double *)malloc(sizeof(double) * SS);
+        double *D = (double *)malloc(sizeof(double) * SS);
+        double *du = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *de = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (h0) memcpy(S, h0 + unit * (long)SS, sizeof(double) * SS);
+        else memset(S, 0, sizeof(double) * SS);
+        for (long t = 0; t < T; ++t) {
+            if (t % SEG == 0) memcpy(starts + (size_t)(t / SEG) * SS, S, sizeof(double) * SS);
+            const long th = (b * T + t) * H + h;
+            gdn2_token(S, q + th * Dk, k + th * Dk, v + th * Dv, log_alpha + th * Dk, bgate + th * Dk,
+                       wgate + th * Dv, du, e, NULL, Dk, Dv, scale);
+        }
+        if (dST) memcpy(D, dST + unit * (long)SS, sizeof(double) * SS);
+        else memset(D, 0, sizeof(double) * SS);
+        for (int sg = nseg - 1; sg >= 0; --sg) {
+            const long t0 = (long)sg * SEG, t1 = (t0 + SEG < T) ? t0 + SEG : T;
+            /* recompute P and u of the segment */
+            memcpy(S, starts + (size_t)sg * SS, sizeof(double) * SS);
+            for (long t = t0; t < t1; ++t) {
+                const long th = (b * T + t) * H + h, x = t - t0;
+                const double *kt = k + th * Dk, *vt = v + th * Dv, *la = log_alpha + th * Dk;
+                const double *bt = bgate + th * Dk, *wt = wgate + th * Dv;
+                double *px = Ps + (size_t)x * SS;
+                for (int i = 0; i < Dk; ++i) {
+                    const double a = exp(la[i]);
+                    for (int j = 0; j < Dv; ++j) px[i * Dv + j] = S[i * Dv + j] * a;
+                }
+                for (int j = 0; j < Dv; ++j) {
+                    double p = 0.0;
+                    for (int i = 0; i < Dk; ++i) p += px[i * Dv + j] * bt[i] * kt[i];
+                    us[(size_t)x * Dv + j] = wt[j] * vt[j] - p;
+                }
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) S[i * Dv + j] = px[i * Dv + j] + kt[i] * us[(size_t)x * Dv + j];
+            }
+            /* reverse through the segment */
+            for (long t = t1 - 1; t >= t0; --t) {
+                const long th = (b * T + t) * H + h, x = t - t0;
+                const double *qt = q + th * Dk, *kt = k + th * Dk, *vt = v + th * Dv, *dot = dO + th * Dv;
+                const double *la = log_alpha + th * Dk, *bt = bgate + th * Dk, *wt = wgate + th * Dv;
+                const double *px = Ps + (size_t)x * SS, *ux = us + (size_t)x * Dv;
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) St[i * Dv + j] = px[i * Dv + j] + kt[i] * ux[j];
+                for (int i = 0; i < Dk; ++i)
+                    for (int j = 0; j < Dv; ++j) D[i * Dv + j] += scale * qt[i] * dot[j];
+                double *dqt = dq + th * Dk, *dkt = dk + th * Dk, *dvt = dv + th * Dv;
+                double *dlat = dla + th * Dk, *dbt = db + th * Dk, *dwt = dw + th * Dv;
+                for (int i = 0; i < Dk; ++i) {
+                    double a = 0.0, c = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        a += St[i * Dv + j] * dot[j];
+                        c += D[i * Dv + j] * ux[j];
+                    }
+                    dqt[i] = scale * a;
+                    dkt[i] = c;
+                }
+                for (int j = 0; j < Dv; ++j) {
+                    double a = 0.0;
+                    for (int i = 0; i < Dk; ++i) a += D[i * Dv + j] * kt[i];
+                    du[j] = a;
+                    dwt[j] = a * vt[j];
+                    dvt[j] = a * wt[j];
+                }
+                for (int i = 0; i < Dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < Dv; ++j) a += px[i * Dv + j] * du[j];
+                    de[i] = -a;
+                    dbt[i] = de[i] * kt[i];
+                    dkt[i] += de[i] * bt[i];
+                }
+                for (int i = 0; i < Dk; ++i) {
+                    const double ei = bt[i] * kt[i];
+                    double a = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        D[i * Dv + j] -= ei * du[j];
+                        a += D[i * Dv + j] * px[i * Dv + j];
+                    }
+                    dlat[i] = a;
+                    const double al = exp(la[i]);
+                    for (int j = 0; j < Dv; ++j) D[i * Dv + j] *= al;
+                }
+            }
+        }
+        if (dh0) memcpy(dh0 + unit * (long)SS, D, sizeof(double) * SS);
+        free(starts); free(Ps); free(us); free(S); free(St); free(D); free(du); free(e); free(de);
+    }
+}

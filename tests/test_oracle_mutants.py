@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_bwd as bwd_pins
+from tests import test_oracle_bwd2 as bwd2_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
@@ -37,6 +38,11 @@ MUTANTS = [
     ("bwd_dg_post_edit_state", "for (size_t i = 0; i < SS; ++i) dgt += D[i] * spx[i];",
      "for (size_t i = 0; i < SS; ++i) dgt += D[i] * St[i];"),
     ("bwd_output_grad_unscaled", "D[i * Dv + j] += scale * qt[i] * dot[j];", "D[i * Dv + j] += qt[i] * dot[j];"),
+    ("bwd2_dw_wrong_operand", "dwt[j] = a * vt[j];", "dwt[j] = a * wt[j];"),
+    ("bwd2_de_sign", "de[i] = -a;", "de[i] = a;"),
+    ("bwd2_dk_erase_term_dropped", "dkt[i] += de[i] * bt[i];", "dkt[i] += 0.0 * bt[i];"),
+    ("bwd2_dla_post_edit_state", "a += D[i * Dv + j] * px[i * Dv + j];", "a += D[i * Dv + j] * St[i * Dv + j];"),
+    ("bwd2_erase_with_raw_key", "D[i * Dv + j] -= ei * du[j];", "D[i * Dv + j] -= kt[i] * du[j];"),
 ]
 
 PIN_FUNCS = [
@@ -53,6 +59,7 @@ PIN_FUNCS = [
     pins.test_gdn2_one_hot_keys_are_channel_emas,
     pins.test_hand_worked_gdn2_step,
     bwd_pins.pin_backward_fd,
+    bwd2_pins.pin_backward2_fd,
 ]
 
 
