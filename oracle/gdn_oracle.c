@@ -360,8 +360,8 @@ void gdn2_oracle_bwd(const double *q, const double *k, const double *v, const do
                 const double *bt = bgate + th * Dk, *wt = wgate + th * Dv;
                 double *px = Ps + (size_t)x * SS;
                 for (int i = 0; i < Dk; ++i) {
-                    const double a = exp(la[i]);
-                    for (int j = 0; j < Dv; ++j) px[i * Dv + j] = S[i * Dv + j] * a;
+                    const double dec = exp(la[i]);
+                    for (int j = 0; j < Dv; ++j) px[i * Dv + j] = S[i * Dv + j] * dec;
                 }
                 for (int j = 0; j < Dv; ++j) {
                     double p = 0.0;
@@ -380,13 +380,13 @@ void gdn2_oracle_bwd(const double *q, const double *k, const double *v, const do
                 for (int i = 0; i < Dk; ++i)
                     for (int j = 0; j < Dv; ++j) St[i * Dv + j] = px[i * Dv + j] + kt[i] * ux[j];
                 for (int i = 0; i < Dk; ++i)
-                    for (int j = 0; j < Dv; ++j) D[i * Dv + j] += scale * qt[i] * dot[j];
+                    for (int j = 0; j < Dv; ++j) D[i * Dv + j] += scale * dot[j] * qt[i];
                 double *dqt = dq + th * Dk, *dkt = dk + th * Dk, *dvt = dv + th * Dv;
                 double *dlat = dla + th * Dk, *dbt = db + th * Dk, *dwt = dw + th * Dv;
                 for (int i = 0; i < Dk; ++i) {
                     double a = 0.0, c = 0.0;
                     for (int j = 0; j < Dv; ++j) {
-                        a += St[i * Dv + j] * dot[j];
+                        a += dot[j] * St[i * Dv + j];
                         c += D[i * Dv + j] * ux[j];
                     }
                     dqt[i] = scale * a;
