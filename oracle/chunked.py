@@ -239,3 +239,120 @@ def gdn_chunk_bwd(q, k, v, g, beta, h0, dO, dST=None, scale=None, C=64):
                                    None if dST is None else dST[b, h], scale, C)
             dq[b, :, h], dk[b, :, h], dv[b, :, h], dg[b, :, h], db[b, :, h], dh0[b, h] = r
     return dq, dk, dv, dg, db, dh0
+
+
+def gdn2_chunk_bwd_head(q, k, v, log_alpha, bgate, wgate, S0, dO, dST, scale, C=64):
+    """Backward of gdn2_chunk_head for one head (the GDN-2 chunk equations,
+    differentiated in reverse chunk order).  Returns dq, dk, dv, dlog_alpha,
+    db, dw and dS0.
+
+    Per chunk with entry state S, per-channel cumulative log-decay G_i (n x Dk),
+    Gam = exp(G), D_ijc = exp(G_ic - G_jc) for j <= i, E = b . k, Z = w . v:
+        A_ij = sum_c E_ic K_jc D_ijc (i > j),  T = (I + A)^-1
+        Ehat = Gam . E,  R = Z - Ehat S,  Dl = T R
+        P_ij = sum_c Q_ic K_jc D_ijc (j <= i),  Qhat = Gam . Q
+        O = scale (Qhat S + P Dl)
+        Khat_j = K_j . exp(G_last - G_j),  S' = Gam_last . S + Khat^T Dl
+    With dS' the gradient of the state leaving the chunk:
+        dDl = scale P^T dO + Khat dS'        dR = T^T dDl     dZ = dR
+        dEhat = -dR S^T                      dA = -strict_lower(dR Dl^T)
+        dP = scale lower(dO Dl^T)            dQhat = scale dO S^T
+        dKhat = Dl dS'^T
+        dS = Gam_last . dS' + scale Qhat^T dO - Ehat^T dR
+    then the chain rule through Ehat, Qhat, A, P, Khat and the Gam_last . S
+    term gives dq, dk, dE and dG; db = dE . k, dk += dE . b, dw = dZ . v,
+    dv = dZ . w, and dlog_alpha is the reverse cumulative sum of dG within
+    the chunk."""
+    T = q.shape[0]
+    Dk, Dv = q.shape[1], v.shape[1]
+    starts = []
+    S = np.array(S0, dtype=np.float64, copy=True)
+    for s in range(0, T, C):
+        starts.append(S)
+        _, S, _ = gdn2_chunk_head(q[s:s + C], k[s:s + C], v[s:s + C], log_alpha[s:s + C], bgate[s:s + C],
+                                  wgate[s:s + C], S, scale, C)
+    dq = np.zeros((T, Dk)); dk = np.zeros((T, Dk)); dla = np.zeros((T, Dk)); db = np.zeros((T, Dk))
+    dv = np.zeros((T, Dv)); dw = np.zeros((T, Dv))
+    dS = np.zeros((Dk, Dv)) if dST is None else np.array(dST, dtype=np.float64, copy=True)
+    for ci in range(len(starts) - 1, -1, -1):
+        s = ci * C
+        e = min(s + C, T)
+        S = starts[ci]
+        Q, K, V, Bg, Wg, dOc = q[s:e], k[s:e], v[s:e], bgate[s:e], wgate[s:e], dO[s:e]
+        n = e - s
+        G = np.cumsum(log_alpha[s:e], axis=0)
+        Gam = np.exp(G)
+        E = Bg * K
+        Z = Wg * V
+        lower_incl = np.tril(np.ones((n, n), dtype=bool))
+        D3 = np.exp(np.where(lower_incl[:, :, None], G[:, None, :] - G[None, :, :], -np.inf))
+        A = np.tril(np.einsum("ic,jc,ijc->ij", E, K, D3), -1)
+        Tm = _tri_inverse(A)
+        Eh = Gam * E
+        R = Z - Eh @ S
+        Dl = Tm @ R
+        P = np.einsum("ic,jc,ijc->ij", Q, K, D3)
+        Qh = Gam * Q
+        dec = np.exp(G[-1][None, :] - G)
+        Kh = K * dec
+        dSp = dS
+        dDl = scale * P.T @ dOc + Kh @ dSp
+        dR = Tm.T @ dDl
+        dEh = -dR @ S.T
+        dA = -np.tril(dR @ Dl.T, -1)
+        dP = scale * np.tril(dOc @ Dl.T)
+        dQh = scale * dOc @ S.T
+        dKh = Dl @ dSp.T
+        dS = Gam[-1][:, None] * dSp + scale * Qh.T @ dOc - Eh.T @ dR
+        dG = np.zeros((n, Dk))
+        dE = np.zeros((n, Dk))
+        dKc = np.zeros((n, Dk))
+        dQc = np.zeros((n, Dk))
+        # Z = w . v
+        dw[s:e] = dR * V
+        dv[s:e] = dR * Wg
+        # Ehat = Gam . E and Qhat = Gam . Q
+        dE += Gam * dEh
+        dG += Gam * E * dEh
+        dQc += Gam * dQh
+        dG += Gam * Q * dQh
+        # A_ij = sum_c E_ic K_jc D_ijc, strictly lower
+        dE += np.einsum("ij,jc,ijc->ic", dA, K, D3)
+        dKc += np.einsum("ij,ic,ijc->jc", dA, E, D3)
+        tA = dA[:, :, None] * E[:, None, :] * K[None, :, :] * D3
+        dG += tA.sum(axis=1) - tA.sum(axis=0)
+        # P_ij = sum_c Q_ic K_jc D_ijc, lower incl. diagonal
+        dQc += np.einsum("ij,jc,ijc->ic", dP, K, D3)
+        dKc += np.einsum("ij,ic,ijc->jc", dP, Q, D3)
+        tP = dP[:, :, None] * Q[:, None, :] * K[None, :, :] * D3
+        dG += tP.sum(axis=1) - tP.sum(axis=0)
+        # Khat_j = K_j exp(G_last - G_j) and the Gam_last . S term of S'
+        dKc += dec * dKh
+        t = dKh * Kh
+        dG -= t
+        dG[-1] += t.sum(axis=0) + Gam[-1] * np.sum(dSp * S, axis=1)
+        # E = b . k
+        db[s:e] = dE * K
+        dKc += dE * Bg
+        dq[s:e] = dQc
+        dk[s:e] = dKc
+        dla[s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dq, dk, dv, dla, db, dw, dS
+
+
+def gdn2_chunk_bwd(q, k, v, log_alpha, b, w, h0, dO, dST=None, scale=None, C=64):
+    """All heads, [B,T,H,D] layout.  Returns dq, dk, dv, dlog_alpha, db, dw, dh0."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if scale is None:
+        scale = Dk ** -0.5
+    out = [np.zeros((B, T, H, d)) for d in (Dk, Dk, Dv, Dk, Dk, Dv)] + [np.zeros((B, H, Dk, Dv))]
+    for bb in range(B):
+        for h in range(H):
+            S0 = np.zeros((Dk, Dv)) if h0 is None else h0[bb, h]
+            r = gdn2_chunk_bwd_head(q[bb, :, h], k[bb, :, h], v[bb, :, h], log_alpha[bb, :, h], b[bb, :, h],
+                                    w[bb, :, h], S0, dO[bb, :, h], None if dST is None else dST[bb, h], scale, C)
+            for i in range(6):
+                out[i][bb, :, h] = r[i]
+            out[6][bb, h] = r[6]
+    return tuple(out)

@@ -92,3 +92,15 @@ def test_gdn2_backward_collapses_to_gdn_backward():
 def pin_backward2_fd():
     """Entry for the mutant check (not collected): the T = 150 finite-difference pin."""
     test_gdn2_gradients_match_finite_differences(150)
+
+
+@pytest.mark.parametrize("T,C", [(150, 64), (100, 16), (64, 64), (1, 64), (9, 1)])
+def test_gdn2_chunked_backward_equals_recurrence_backward(T, C):
+    """The chunked GDN-2 backward in oracle/chunked.py (the chunk equations the
+    GPU backward follows) equals the per-token backward to rounding."""
+    from oracle import chunked
+    x, dO, dST = _case(2, T, 2, 6, 5, seed=530 + T)
+    ref = oracle.gdn2_bwd(*[x[nm] for nm in NAMES], dO, dST, scale=0.8)
+    got = chunked.gdn2_chunk_bwd(*[x[nm] for nm in NAMES], dO, dST, scale=0.8, C=C)
+    for name, a, r in zip(("dq", "dk", "dv", "dla", "db", "dw", "dh0"), got, ref):
+        np.testing.assert_allclose(a, r, atol=1e-10, rtol=1e-10, err_msg=name)
