@@ -16,6 +16,7 @@ __all__ = [
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
     "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_prologue", "gdn_gated_rmsnorm",
+    "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace",
     "GDN_F32", "GDN_BF16", "BT",
 ]
 
@@ -64,6 +65,10 @@ def load():
     lib.gdn_chunk_bwd.argtypes = [_vp] * 14 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn2_recurrent_step.restype = _i
     lib.gdn2_recurrent_step.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _vp]
+    lib.gdn2_chunk_bwd_workspace.restype = _sz
+    lib.gdn2_chunk_bwd_workspace.argtypes = [_i] * 6
+    lib.gdn2_chunk_bwd.restype = _i
+    lib.gdn2_chunk_bwd.argtypes = [_vp] * 16 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_prologue.restype = _i
     lib.gdn_prologue.argtypes = [_vp] * 17 + [_i] * 5 + [_vp]
     lib.gdn_gated_rmsnorm.restype = _i
@@ -243,6 +248,52 @@ def gdn_chunk_bwd(q, k, v, g, beta, h0, do, dht=None, scale=None, workspace=None
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, dt,
                              float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)), "gdn_chunk_bwd")
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn2_chunk_bwd_workspace(B, T, H, Dk, Dv, dtype_code):
+    return int(load().gdn2_chunk_bwd_workspace(B, T, H, Dk, Dv, dtype_code))
+
+
+def gdn2_chunk_bwd(q, k, v, log_alpha, b, w, h0, do, dht=None, scale=None, workspace=None):
+    """Backward of gdn2_chunk_fwd.  Inputs as gdn2_chunk_fwd (h0 may be None), do
+    [B,T,H,Dv] fp32, dht [B,H,Dk,Dv] fp32 or None.  Returns (dq, dk, dv, dlog_alpha,
+    db, dw, dh0) in fp32 (dh0 None when h0 is None)."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (B, T, H, Dk), torch.float32, dev)
+    _need(b, "b", (B, T, H, Dk), q.dtype, dev)
+    _need(w, "w", (B, T, H, Dv), q.dtype, dev)
+    _need(do, "do", (B, T, H, Dv), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if dht is not None:
+        _need(dht, "dht", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    f32 = torch.float32
+    dq = torch.empty((B, T, H, Dk), dtype=f32, device=dev)
+    dk = torch.empty((B, T, H, Dk), dtype=f32, device=dev)
+    dla = torch.empty((B, T, H, Dk), dtype=f32, device=dev)
+    db = torch.empty((B, T, H, Dk), dtype=f32, device=dev)
+    dv = torch.empty((B, T, H, Dv), dtype=f32, device=dev)
+    dw = torch.empty((B, T, H, Dv), dtype=f32, device=dev)
+    dh0 = torch.empty((B, H, Dk, Dv), dtype=f32, device=dev) if h0 is not None else None
+    nbytes = gdn2_chunk_bwd_workspace(B, T, H, Dk, Dv, dt)
+    if workspace is None:
+        _hold, ws = _workspace(nbytes, dev)
+    else:
+        ws = workspace
+    _check(load().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(h0), _ptr(do),
+                                 _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(db), _ptr(dw), _ptr(dh0),
+                                 B, T, H, Dk, Dv, dt, float(scale), _ptr(ws), ws.numel(), _stream(dev)),
+           "gdn2_chunk_bwd")
+    return dq, dk, dv, dla, db, dw, dh0
 
 
 def gdn_chunk_intra(k, g, beta, G2_out=None, Tinv_out=None):

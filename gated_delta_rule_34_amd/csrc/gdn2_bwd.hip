@@ -1,0 +1,514 @@
+// gdn2_bwd.hip -- backward of the chunked Gated DeltaNet-2 forward on gfx950
+// (fp32 arithmetic throughout; bf16 inputs are exact in fp32).
+//
+// Chunk equations (the chunked form of the Gated DeltaNet-2 update of the
+// 7minutos.es article, section "Regla-2 del Delta cerrado", with the channel
+// decay inside both factors of every product): in a chunk with entry state
+// S, per-channel cumulative log-decay G_i, Gam_i = exp(G_i), e = b . k,
+// z = w . v, D_ijc = exp(G_ic - G_jc) (j <= i):
+//   A_ij = sum_c e_ic k_jc D_ijc (i > j),  T = (I + A)^-1
+//   Ehat = Gam . e,  R = Z - Ehat S,  Dl = T R
+//   P_ij = sum_c q_ic k_jc D_ijc (j <= i),  Qhat = Gam . q,  O = scale (Qhat S + P Dl)
+//   Khat_j = k_j . exp(G_last - G_j),  S' = Gam_last . S + Khat^T Dl
+// Reverse mode, with dS' the gradient of the state leaving the chunk:
+//   dDl = scale P^T dO + Khat dS'        dR = T^T dDl      (dZ = dR)
+//   dS  = Gam_last . dS' + scale Qhat^T dO - Ehat^T dR
+//   dA = -strict(dR Dl^T)   dP = scale lower(dO Dl^T)
+//   dEhat = -dR S^T   dQhat = scale dO S^T   dKhat = Dl dS'^T
+// and the chain rule through Ehat, Qhat, A, P, Khat and Gam_last . S gives
+// dq, dk, de (db = de . k, dk += de . b), dw = dZ . v, dv = dZ . w and dG;
+// dlog_alpha is the reverse cumulative sum of dG within the chunk.
+//
+// Stages (all chunks of all heads), after the forward's fp32 intra stage
+// (Ehat, Qhat, Khat, Gam_C, T - I, P) and its walk writing every chunk's
+// entry state:
+//   gdn2_bwd_walk_kernel: dS' chunk by chunk from the last one back, one
+//     workgroup per 32 state columns; dh0 is the gradient entering chunk 0
+//   gdn2_bwd_value_kernel: one workgroup per chunk, value columns 16 at a
+//     time: dv, dw, and dA, dP, dEhat, dQhat, dKhat and sum_v dS' . S per
+//     key channel, written over the intra-stage operands of the chunk
+//   gdn2_bwd_key_kernel: one workgroup per (chunk, 64 key channels): the
+//     decay-weighted contractions with exact per-channel exponentials, then
+//     dq, dk, db and dlog_alpha.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+// acc (the 16x16 tile at rows i0, columns j0 of C) += A B over k in [0, K):
+// A(i, k) = A[i * sar + k * sac], B(k, j) = B[k * sbr + j * sbc] (LDS, fp32).
+// Lane (g, r) ends with C[i0 + 4g + e][j0 + r].
+template <int K>
+__device__ __forceinline__ f32x4 tmma(f32x4 acc, const float *A, int sar, int sac, const float *B, int sbr, int sbc,
+                                      int i0, int j0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float *pa = A + (i0 + r) * sar + g * sac;
+    const float *pb = B + g * sbr + (j0 + r) * sbc;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0 * sac], pb[k0 * sbr], acc, 0, 0, 0);
+    return acc;
+}
+
+// A [64, D] fp32 block (contiguous rows) into LDS with row stride LD.
+template <int D, int LD, int NTHR>
+__device__ __forceinline__ void stage_block(float *dst, const float *src, int tid) {
+    constexpr int U = BT * D / 4 / NTHR;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = 4 * (tid + NTHR * u), row = idx / D, col = idx % D;
+        const float4 x = *(const float4 *)(src + idx);
+        float *p = dst + row * LD + col;
+        p[0] = x.x; p[1] = x.y; p[2] = x.z; p[3] = x.w;
+    }
+}
+
+// Columns c0 .. c0 + 15 of rows t0 .. t0 + 63 of a [B, T, H, DF] tensor into
+// LDS (row stride LD), zero past T; 256 threads, four values each.
+template <int LD, class In>
+__device__ __forceinline__ void stage_cols16(float *dst, const In *src, long b, int h, int t0, int T, int H, int c0,
+                                             int DF, int tid) {
+    const int row = tid >> 2, c4 = 4 * (tid & 3);
+    const int t = t0 + row;
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < T) {
+        const In *p = src + ((b * T + t) * H + h) * (long)DF + c0 + c4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = load_elem(p + e);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[row * LD + c4 + e] = x[e];
+}
+
+// Tile index t (0..9) of the lower 4 x 4 block triangle: I = row block, J = column block.
+__device__ constexpr int lI(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__device__ constexpr int lJ(int t) { return t - lI(t) * (lI(t) + 1) / 2; }
+
+}  // namespace
+
+// ------------------------------------------------------- reverse state walk
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn2_bwd_walk_kernel(
+    const float *__restrict__ Eh, const float *__restrict__ Qh, const float *__restrict__ Kh,
+    const float *__restrict__ GamC, const float *__restrict__ Tws, const float *__restrict__ Pws,
+    const float *__restrict__ Dws, const float *__restrict__ dO, const float *__restrict__ dht,
+    float *__restrict__ dSck, float *__restrict__ dh0, int T, int H, int NT, float scale) {
+    constexpr int BV = 32, NTHR = 256, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
+    __shared__ float sA[BT * LDQ], sQ[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
+    __shared__ float sdO[BT * LDB], sdDl[BT * LDB], sdR[BT * LDB], sdS[DK * LDB], sGam[DK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    constexpr int NTILE = DV / BV;
+    const int vt = blockIdx.x % NTILE;
+    const long bh = blockIdx.x / NTILE;
+    const int h = (int)(bh % H);
+    const long b = bh / H;
+    const int vcol0 = vt * BV;
+    const long sbase = bh * (long)DK * DV;
+
+    for (int idx = tid; idx < DK * BV; idx += NTHR) {
+        const int row = idx / BV, col = idx % BV;
+        sdS[row * LDB + col] = dht ? dht[sbase + (long)row * DV + vcol0 + col] : 0.f;
+    }
+    __syncthreads();
+    for (int c = NT - 1; c >= 0; --c) {
+        const long cb = bh * NT + c;
+        const long ob = cb * (long)BT * DK;
+        // gradient of the state leaving chunk c, for the per-chunk stages
+        for (int idx = tid; idx < DK * BV / 4; idx += NTHR) {
+            const int row = (4 * idx) / BV, col = (4 * idx) % BV;
+            const float *p = &sdS[row * LDB + col];
+            *(float4 *)(dSck + cb * DK * DV + (long)row * DV + vcol0 + col) = make_float4(p[0], p[1], p[2], p[3]);
+        }
+        stage_block<DK, LDQ, NTHR>(sA, Kh + ob, tid);
+        stage_block<DK, LDQ, NTHR>(sQ, Qh + ob, tid);
+        for (int idx = tid; idx < BT * BT; idx += NTHR) {
+            const int i = idx >> 6, j = idx & 63;
+            sTm[i * LDC + j] = Tws[cb * BT * BT + idx];
+            sP[i * LDC + j] = (j < i) ? Pws[cb * BT * BT + idx] : (j == i ? Dws[cb * BT + i] : 0.f);
+        }
+        for (int idx = tid; idx < BT * BV; idx += NTHR) {
+            const int row = idx / BV, col = idx % BV;
+            const int t = c * BT + row;
+            sdO[row * LDB + col] = (t < T) ? dO[((b * T + t) * H + h) * (long)DV + vcol0 + col] : 0.f;
+        }
+        for (int idx = tid; idx < DK; idx += NTHR) sGam[idx] = GamC[cb * DK + idx];
+        __syncthreads();
+        // dDl = scale P^T dO + Khat dS' (8 tiles of 64 x 32)
+        for (int tile = wave; tile < 8; tile += 4) {
+            const int I = tile >> 1, J = tile & 1;
+            const f32x4 a1 = tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 16 * J, lane);
+            const f32x4 a2 = tmma<DK>(zero4(), sA, LDQ, 1, sdS, LDB, 1, 16 * I, 16 * J, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sdDl[(16 * I + 4 * g + e) * LDB + 16 * J + r] = scale * a1[e] + a2[e];
+        }
+        __syncthreads();
+        // dR = dDl + (T - I)^T dDl; Ehat replaces Khat in LDS meanwhile
+        for (int tile = wave; tile < 8; tile += 4) {
+            const int I = tile >> 1, J = tile & 1;
+            const f32x4 a = tmma<BT>(zero4(), sTm, 1, LDC, sdDl, LDB, 1, 16 * I, 16 * J, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                sdR[i * LDB + 16 * J + r] = sdDl[i * LDB + 16 * J + r] + a[e];
+            }
+        }
+        stage_block<DK, LDQ, NTHR>(sA, Eh + ob, tid);
+        __syncthreads();
+        // dS = Gam_C . dS' + scale Qhat^T dO - Ehat^T dR  (DK/16 x 2 tiles)
+        for (int tile = wave; tile < (DK / 16) * 2; tile += 4) {
+            const int M = tile >> 1, J = tile & 1;
+            const f32x4 a1 = tmma<BT>(zero4(), sQ, 1, LDQ, sdO, LDB, 1, 16 * M, 16 * J, lane);
+            const f32x4 a2 = tmma<BT>(zero4(), sA, 1, LDQ, sdR, LDB, 1, 16 * M, 16 * J, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 16 * M + 4 * g + e;
+                float *d = &sdS[m * LDB + 16 * J + r];
+                *d = sGam[m] * *d + scale * a1[e] - a2[e];
+            }
+        }
+        __syncthreads();
+    }
+    if (dh0) {
+        for (int idx = tid; idx < DK * BV; idx += NTHR) {
+            const int row = idx / BV, col = idx % BV;
+            dh0[sbase + (long)row * DV + vcol0 + col] = sdS[row * LDB + col];
+        }
+    }
+}
+
+// ------------------------------------------------- per-chunk, value side
+template <int DK>
+struct Gdn2BwdValueSmem {
+    static constexpr int LDQ = DK + 4, LDC = BT + 1, CW = 16, LDW = CW + 1;
+    float E[BT * LDQ], K[BT * LDQ];   // Ehat, Khat of the chunk
+    float Tm[BT * LDC], P[BT * LDC];  // T - I and P (lower with the diagonal)
+    float S[DK * LDW], dS[DK * LDW];  // column slice of the entry state and of dS'
+    float dO[BT * LDW], R[BT * LDW], Dl[BT * LDW], dDl[BT * LDW], dR[BT * LDW];
+    float W[BT * LDW], V[BT * LDW];
+};
+
+template <class Pol, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
+    const typename Pol::in_t *__restrict__ v, const typename Pol::in_t *__restrict__ wg,
+    const float *__restrict__ dO, const float *__restrict__ Sck, const float *__restrict__ dSck,
+    float *__restrict__ Eh, float *__restrict__ Qh, float *__restrict__ Kh, float *__restrict__ GamC,
+    float *__restrict__ Tws, float *__restrict__ Pws, const float *__restrict__ Dws, float *__restrict__ dv,
+    float *__restrict__ dw, int T, int H, int NT, float scale) {
+    using SM = Gdn2BwdValueSmem<DK>;
+    constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 256, NM = DK / 16;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const long cb = blockIdx.x;
+    const int c = (int)(cb % NT);
+    const long bh = cb / NT;
+    const int h = (int)(bh % H);
+    const long b = bh / H;
+    const int t0 = c * BT;
+    const long ob = cb * (long)BT * DK;
+    const int I = wave;  // this wave's 16-row block of every 64-row product
+
+    stage_block<DK, LDQ, NTHR>(sm.E, Eh + ob, tid);
+    stage_block<DK, LDQ, NTHR>(sm.K, Kh + ob, tid);
+    for (int idx = tid; idx < BT * BT; idx += NTHR) {
+        const int i = idx >> 6, j = idx & 63;
+        sm.Tm[i * LDC + j] = Tws[cb * BT * BT + idx];
+        sm.P[i * LDC + j] = (j < i) ? Pws[cb * BT * BT + idx] : (j == i ? Dws[cb * BT + i] : 0.f);
+    }
+    // accumulators over the value columns: the lower tiles of dA and dP owned
+    // by this wave (tiles t = wave, wave + 4, wave + 8), and row block I of
+    // dEhat, dQhat, dKhat (NM tiles each); sum_v dS' . S per key channel
+    f32x4 aA[3], aP[3], aE[NM], aQ[NM], aK[NM];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) aA[u] = aP[u] = zero4();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) aE[m] = aQ[m] = aK[m] = zero4();
+    float srow = 0.f;
+
+    for (int v0 = 0; v0 < DV; v0 += CW) {
+        __syncthreads();  // the previous slice's readers are done
+        for (int idx = tid; idx < DK * CW; idx += NTHR) {
+            const int row = idx / CW, col = idx % CW;
+            const long off = cb * (long)DK * DV + (long)row * DV + v0 + col;
+            sm.S[row * LDW + col] = Sck[off];
+            sm.dS[row * LDW + col] = dSck[off];
+        }
+        stage_cols16<LDW>(sm.V, v, b, h, t0, T, H, v0, DV, tid);
+        stage_cols16<LDW>(sm.W, wg, b, h, t0, T, H, v0, DV, tid);
+        stage_cols16<LDW>(sm.dO, dO, b, h, t0, T, H, v0, DV, tid);
+        __syncthreads();
+        if (tid < DK) {
+#pragma unroll
+            for (int j = 0; j < CW; ++j) srow += sm.dS[tid * LDW + j] * sm.S[tid * LDW + j];
+        }
+        // R = Z - Ehat S (row block I)
+        {
+            const f32x4 a = tmma<DK>(zero4(), sm.E, LDQ, 1, sm.S, LDW, 1, 16 * I, 0, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                sm.R[i * LDW + r] = sm.W[i * LDW + r] * sm.V[i * LDW + r] - a[e];
+            }
+        }
+        __syncthreads();
+        // Dl = R + (T - I) R; dDl = scale P^T dO + Khat dS'
+        {
+            const f32x4 a = tmma<BT>(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, 16 * I, 0, lane);
+            const f32x4 a1 = tmma<BT>(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, 16 * I, 0, lane);
+            const f32x4 a2 = tmma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, 16 * I, 0, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                sm.Dl[i * LDW + r] = sm.R[i * LDW + r] + a[e];
+                sm.dDl[i * LDW + r] = scale * a1[e] + a2[e];
+            }
+        }
+        __syncthreads();
+        // dR = dDl + (T - I)^T dDl; dv = dR . w, dw = dR . v
+        {
+            const f32x4 a = tmma<BT>(zero4(), sm.Tm, 1, LDC, sm.dDl, LDW, 1, 16 * I, 0, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                const float x = sm.dDl[i * LDW + r] + a[e];
+                sm.dR[i * LDW + r] = x;
+                const int t = t0 + i;
+                if (t < T) {
+                    const long off = ((b * T + t) * H + h) * (long)DV + v0 + r;
+                    dv[off] = x * sm.W[i * LDW + r];
+                    dw[off] = x * sm.V[i * LDW + r];
+                }
+            }
+        }
+        __syncthreads();
+        // dA += -dR Dl^T, dP += scale dO Dl^T on this wave's lower tiles
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int t = wave + 4 * u;
+            if (t < 10) {
+                const int TI = lI(t), TJ = lJ(t);
+                aA[u] = tmma<CW>(aA[u], sm.dR, LDW, 1, sm.Dl, 1, LDW, 16 * TI, 16 * TJ, lane);
+                aP[u] = tmma<CW>(aP[u], sm.dO, LDW, 1, sm.Dl, 1, LDW, 16 * TI, 16 * TJ, lane);
+            }
+        }
+        // dEhat += -dR S^T, dQhat += scale dO S^T, dKhat += Dl dS'^T (row block I)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            aE[m] = tmma<CW>(aE[m], sm.dR, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
+            aQ[m] = tmma<CW>(aQ[m], sm.dO, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
+            aK[m] = tmma<CW>(aK[m], sm.Dl, LDW, 1, sm.dS, 1, LDW, 16 * I, 16 * m, lane);
+        }
+    }
+    __syncthreads();  // every read of this chunk's operands is done: overwrite them
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int t = wave + 4 * u;
+        if (t < 10) {
+            const int TI = lI(t), TJ = lJ(t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
+                Tws[cb * BT * BT + i * BT + j] = (j < i) ? -aA[u][e] : 0.f;
+                Pws[cb * BT * BT + i * BT + j] = (j <= i) ? scale * aP[u][e] : 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long idx = ob + (long)(16 * I + 4 * g + e) * DK + 16 * m + r;
+            Eh[idx] = -aE[m][e];
+            Qh[idx] = scale * aQ[m][e];
+            Kh[idx] = aK[m][e];
+        }
+    if (tid < DK) GamC[cb * DK + tid] = srow;
+}
+
+// --------------------------------------------------- per-chunk, key side
+template <int CH>
+struct Gdn2BwdKeySmem {
+    static constexpr int LDA = BT + 1;
+    float K[BT * CH], E[BT * CH], Q[BT * CH], G[BT * CH], dG[BT * CH];
+    float dA[BT * LDA], dP[BT * LDA];
+    float rA[BT * CH], rP[BT * CH];   // row-side sums (the de and dq parts from A and P)
+    float tpart[4][CH];
+};
+
+template <class Pol, int DK>
+__global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
+    const typename Pol::in_t *__restrict__ q, const typename Pol::in_t *__restrict__ k,
+    const float *__restrict__ la, const typename Pol::in_t *__restrict__ bg, const float *__restrict__ dEh,
+    const float *__restrict__ dQh, const float *__restrict__ dKh, const float *__restrict__ srow,
+    const float *__restrict__ dAws, const float *__restrict__ dPws, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dla, float *__restrict__ db, int T, int H, int NT) {
+    constexpr int CH = 64;  // key channels per workgroup (one per lane)
+    using SM = Gdn2BwdKeySmem<CH>;
+    constexpr int LDA = SM::LDA;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NCH = DK / CH;
+    const int ch0 = (blockIdx.x % NCH) * CH;
+    const long cb = blockIdx.x / NCH;
+    const int c = (int)(cb % NT);
+    const long bh = cb / NT;
+    const int h = (int)(bh % H);
+    const long b = bh / H;
+    const int t0 = c * BT;
+    const long ob = cb * (long)BT * DK;
+    const int col = ch0 + lane;  // this lane's key channel
+
+    // inputs of the chunk (zero past T), one (row, channel) per thread and step
+    for (int i = wave; i < BT; i += 4) {
+        const int t = t0 + i;
+        float kv = 0.f, qv = 0.f, bv = 0.f, lv = 0.f;
+        if (t < T) {
+            const long off = ((b * T + t) * H + h) * (long)DK + col;
+            kv = load_elem(k + off);
+            qv = load_elem(q + off);
+            bv = load_elem(bg + off);
+            lv = la[off];
+        }
+        sm.K[i * CH + lane] = kv;
+        sm.Q[i * CH + lane] = qv;
+        sm.E[i * CH + lane] = bv * kv;
+        sm.G[i * CH + lane] = lv;
+        sm.dG[i * CH + lane] = 0.f;
+    }
+    for (int idx = tid; idx < BT * BT; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        sm.dA[i * LDA + j] = dAws[cb * BT * BT + idx];
+        sm.dP[i * LDA + j] = dPws[cb * BT * BT + idx];
+    }
+    __syncthreads();
+    if (wave == 0) {  // G = chunk-local cumsum of log_alpha per channel
+        float s = 0.f;
+        for (int i = 0; i < BT; ++i) {
+            s += sm.G[i * CH + lane];
+            sm.G[i * CH + lane] = s;
+        }
+    }
+    __syncthreads();
+    // row side (rows i = wave mod 4): rA_ic = sum_{j<i} dA_ij k_jc D_ijc,
+    // rP_ic = sum_{j<=i} dP_ij k_jc D_ijc
+    for (int i = wave; i < BT; i += 4) {
+        const float Gi = sm.G[i * CH + lane];
+        float ra = 0.f, rp = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const float kd = sm.K[j * CH + lane] * expf(Gi - sm.G[j * CH + lane]);
+            ra += sm.dA[i * LDA + j] * kd;
+            rp += sm.dP[i * LDA + j] * kd;
+        }
+        sm.rA[i * CH + lane] = ra;
+        sm.rP[i * CH + lane] = rp;
+        sm.dG[i * CH + lane] += sm.E[i * CH + lane] * ra + sm.Q[i * CH + lane] * rp;
+    }
+    __syncthreads();
+    // column side (columns j = wave mod 4): cA_jc = sum_{i>j} dA_ij e_ic D_ijc,
+    // cP_jc = sum_{i>=j} dP_ij q_ic D_ijc; then every per-element term
+    const float GL = sm.G[(BT - 1) * CH + lane];
+    float tsum = 0.f;
+    for (int j = wave; j < BT; j += 4) {
+        const float Gj = sm.G[j * CH + lane];
+        float ca = 0.f, cp = 0.f;
+        for (int i = j; i < BT; ++i) {
+            const float d = expf(sm.G[i * CH + lane] - Gj);
+            ca += sm.dA[i * LDA + j] * sm.E[i * CH + lane] * d;
+            cp += sm.dP[i * LDA + j] * sm.Q[i * CH + lane] * d;
+        }
+        const float kj = sm.K[j * CH + lane], ej = sm.E[j * CH + lane], qj = sm.Q[j * CH + lane];
+        const float gam = expf(Gj), dec = expf(GL - Gj);
+        const long gi = ob + (long)j * DK + col;
+        const float dEhv = dEh[gi], dQhv = dQh[gi], dKhv = dKh[gi];
+        const float de = sm.rA[j * CH + lane] + gam * dEhv;
+        const float dqv = sm.rP[j * CH + lane] + gam * dQhv;
+        const float tk = dKhv * kj * dec;
+        float dgv = -kj * (ca + cp) + gam * ej * dEhv + gam * qj * dQhv - tk;
+        tsum += tk;
+        sm.dG[j * CH + lane] += dgv;
+        sm.rA[j * CH + lane] = de;                    // de of row j, for db and dk below
+        sm.rP[j * CH + lane] = ca + cp + dec * dKhv;  // dk of row j without the erase term
+        const int t = t0 + j;
+        if (t < T) dq[((b * T + t) * H + h) * (long)DK + col] = dqv;
+    }
+    // the last row's G also enters Khat (sum_j dKhat . Khat) and the
+    // Gam_last . S term of S' (sum_v dS' . S): per-wave partial sums
+    sm.tpart[wave][lane] = tsum;
+    __syncthreads();
+    if (wave == 0)
+        sm.dG[(BT - 1) * CH + lane] += sm.tpart[0][lane] + sm.tpart[1][lane] + sm.tpart[2][lane] +
+                                       sm.tpart[3][lane] + expf(GL) * srow[cb * DK + col];
+    __syncthreads();
+    // db = de . k, dk = (the rest) + de . b, dlog_alpha = reverse cumsum of dG
+    for (int j = wave; j < BT; j += 4) {
+        const int t = t0 + j;
+        if (t < T) {
+            const long off = ((b * T + t) * H + h) * (long)DK + col;
+            const float de = sm.rA[j * CH + lane];
+            db[off] = de * sm.K[j * CH + lane];
+            dk[off] = sm.rP[j * CH + lane] + de * load_elem(bg + off);
+        }
+    }
+    if (wave == 0) {
+        float s = 0.f;
+        for (int i = BT - 1; i >= 0; --i) {
+            s += sm.dG[i * CH + lane];
+            const int t = t0 + i;
+            if (t < T) dla[((b * T + t) * H + h) * (long)DK + col] = s;
+        }
+    }
+}
+
+// ----------------------------------------------------------------- launcher
+template <class Pol, int DK, int DV>
+static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                                    const void *wg, const float *dO, const float *dht, float *Eh, float *Qh,
+                                    float *Kh, float *GamC, float *Tws, float *Pws, const float *Dws,
+                                    const float *Sck, float *dSck, float *dq, float *dk, float *dv, float *dla,
+                                    float *db, float *dw, float *dh0, int B, int T, int H, float scale,
+                                    hipStream_t st) {
+    using in_t = typename Pol::in_t;
+    const int NT = (T + BT - 1) / BT;
+    const long heads = (long)B * H;
+    hipLaunchKernelGGL((gdn2_bwd_walk_kernel<DK, DV>), dim3((unsigned)(heads * (DV / 32))), dim3(256), 0, st, Eh,
+                       Qh, Kh, GamC, Tws, Pws, Dws, dO, dht, dSck, dh0, T, H, NT, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn2_bwd_value_kernel<Pol, DK, DV>), dim3((unsigned)(heads * NT)), dim3(256), 0, st,
+                       (const in_t *)v, (const in_t *)wg, dO, Sck, dSck, Eh, Qh, Kh, GamC, Tws, Pws, Dws, dv, dw, T,
+                       H, NT, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn2_bwd_key_kernel<Pol, DK>), dim3((unsigned)(heads * NT * (DK / 64))), dim3(256), 0, st,
+                       (const in_t *)q, (const in_t *)k, la, (const in_t *)bg, Eh, Qh, Kh, GamC, Tws, Pws, dq, dk, dla,
+                       db, T, H, NT);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn2_bwd(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                           const void *wg, const float *dO, const float *dht, float *Eh, float *Qh, float *Kh,
+                           float *GamC, float *Tws, float *Pws, const float *Dws, const float *Sck, float *dSck,
+                           float *dq, float *dk, float *dv, float *dla, float *db, float *dw, float *dh0, int B, int T,
+                           int H, int Dk, int Dv, bool bf16, float scale, hipStream_t st) {
+#define GDN2_BWD(P_, DKv, DVv)                                                                                   \
+    if (Dk == DKv && Dv == DVv)                                                                                 \
+    return launch_gdn2_bwd_t<P_, DKv, DVv>(q, k, v, la, bg, wg, dO, dht, Eh, Qh, Kh, GamC, Tws, Pws, Dws, Sck, dSck, \
+                                           dq, dk, dv, dla, db, dw, dh0, B, T, H, scale, st)
+    if (bf16) {
+        GDN2_BWD(PolBF16F32, 64, 64);
+        GDN2_BWD(PolBF16F32, 64, 128);
+        GDN2_BWD(PolBF16F32, 128, 64);
+        GDN2_BWD(PolBF16F32, 128, 128);
+    } else {
+        GDN2_BWD(PolF32, 64, 64);
+        GDN2_BWD(PolF32, 64, 128);
+        GDN2_BWD(PolF32, 128, 64);
+        GDN2_BWD(PolF32, 128, 128);
+    }
+#undef GDN2_BWD
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
     const typename Pol::mt *__restrict__ Khat, const float *__restrict__ GamC, const float *__restrict__ Tws,
     const float *__restrict__ Pws, const float *__restrict__ Dws, const typename Pol::in_t *__restrict__ v,
     const typename Pol::in_t *__restrict__ wg, const float *__restrict__ h0, float *__restrict__ o,
-    float *__restrict__ ht, int T, int H, int NT, float scale) {
+    float *__restrict__ ht, float *__restrict__ ck, int T, int H, int NT, float scale) {
     using mt = typename Pol::mt;
     constexpr int NW = BV / 16;
     constexpr int NTHR = NW * 64;
@@ -255,6 +255,12 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
         const int t0 = c * BT;
         const long cb = bh * NT + c;
         const long ob = cb * (long)BT * DK;
+        if (ck) {  // entry state of chunk c (for the backward)
+#pragma unroll
+            for (int m = 0; m < NKB; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ck[cb * DK * DV + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+        }
         for (int idx = tid; idx < BT * DK; idx += NTHR) {
             const int row = idx / DK, kc = idx % DK;
             sE[row * LDQ + kc] = Ehat[ob + idx];
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = t0 + 16 * I + 4 * g + e;
-                if (t < T) o[((b * T + t) * H + h) * (long)DV + col] = scale * acc[e];
+                if (o && t < T) o[((b * T + t) * H + h) * (long)DV + col] = scale * acc[e];
             }
         }
         // S = Diag(Gamma_C) S + Khat^T Vnew (the decay scales key rows)
@@ -400,7 +406,7 @@ static hipError_t launch_gdn2_walk_t(const void *Ehat, const void *Qhat, const v
     const int NT = (T + BT - 1) / BT;
     hipLaunchKernelGGL((gdn2_walk_kernel<Pol, DK, DV, BV>), dim3((unsigned)((long)B * H * (DV / BV))),
                        dim3(BV * 4), 0, st, (const mt *)Ehat, (const mt *)Qhat, (const mt *)Khat, GamC, Tinv, P, D,
-                       (const in_t *)v, (const in_t *)wg, h0, o, ht, T, H, NT, scale);
+                       (const in_t *)v, (const in_t *)wg, h0, o, ht, (float *)nullptr, T, H, NT, scale);
     return hipGetLastError();
 }
 
@@ -424,6 +430,47 @@ hipError_t launch_gdn2_walk(const void *Ehat, const void *Qhat, const void *Khat
         GDN2_WALK(PolF32, 128, 128);
     }
 #undef GDN2_WALK
+    return hipErrorInvalidValue;
+}
+
+// The forward recompute of the backward: the intra stage and the walk in fp32
+// operands (bf16 inputs are exact in fp32), the walk writing every chunk's
+// entry state into ck [B, H, NT, Dk, Dv] and no output.
+template <class Pol, int DK, int DV>
+static hipError_t launch_gdn2_recompute_t(const void *q, const void *k, const float *la, const void *bg,
+                                          const void *v, const void *wg, const float *h0, float *Eh, float *Qh,
+                                          float *Kh, float *GamC, float *Tinv, float *P, float *D, float *ck, int B,
+                                          int T, int H, hipStream_t st) {
+    constexpr int BV = 32;
+    using in_t = typename Pol::in_t;
+    hipError_t e = launch_gdn2_intra_t<Pol, DK>(q, k, la, bg, Eh, Qh, Kh, GamC, Tinv, P, D, B, T, H, st);
+    if (e != hipSuccess) return e;
+    const int NT = (T + BT - 1) / BT;
+    hipLaunchKernelGGL((gdn2_walk_kernel<Pol, DK, DV, BV>), dim3((unsigned)((long)B * H * (DV / BV))), dim3(BV * 4),
+                       0, st, (const float *)Eh, (const float *)Qh, (const float *)Kh, GamC, Tinv, P, D,
+                       (const in_t *)v, (const in_t *)wg, h0, (float *)nullptr, (float *)nullptr, ck, T, H, NT, 1.f);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn2_recompute(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                 const void *wg, const float *h0, float *Eh, float *Qh, float *Kh, float *GamC,
+                                 float *Tinv, float *P, float *D, float *ck, int B, int T, int H, int Dk, int Dv,
+                                 bool bf16, hipStream_t st) {
+#define GDN2_RC(P_, DKv, DVv)                                                                                  \
+    if (Dk == DKv && Dv == DVv)                                                                               \
+    return launch_gdn2_recompute_t<P_, DKv, DVv>(q, k, la, bg, v, wg, h0, Eh, Qh, Kh, GamC, Tinv, P, D, ck, B, T, H, st)
+    if (bf16) {
+        GDN2_RC(PolBF16F32, 64, 64);
+        GDN2_RC(PolBF16F32, 64, 128);
+        GDN2_RC(PolBF16F32, 128, 64);
+        GDN2_RC(PolBF16F32, 128, 128);
+    } else {
+        GDN2_RC(PolF32, 64, 64);
+        GDN2_RC(PolF32, 64, 128);
+        GDN2_RC(PolF32, 128, 64);
+        GDN2_RC(PolF32, 128, 128);
+    }
+#undef GDN2_RC
     return hipErrorInvalidValue;
 }
 

@@ -156,7 +156,7 @@ struct Gdn2Ws {
     size_t e_off, q_off, k_off, gam_off, t_off, p_off, d_off, total;
 };
 
-Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
+static Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
     const size_t NT = (size_t)(T + kBT - 1) / kBT;
     const size_t chunks = (size_t)B * H * NT;
     const size_t mts = dt == GDN_BF16 ? 2 : 4;
@@ -290,7 +290,7 @@ struct BwdWs {
     size_t ck_off, dck_off, total;
 };
 
-BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv) {
+static BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv) {
     const size_t NT = (size_t)(T + kBT - 1) / kBT;
     const size_t st = align_up((size_t)B * H * NT * Dk * Dv * sizeof(float));
     BwdWs w;
@@ -341,6 +341,74 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     if (s != GDN_OK) return s;
     return from_hip(gdn::launch_bwd(q, k, v, beta, dO, dht, G2, Tinv, Sck, dSck, dq, dk, dv, dg, dbeta, dh0, B, T, H,
                                     Dk, Dv, bf, scale, st));
+}
+
+// Workspace of the GDN-2 backward, fp32 sections each 256-byte aligned:
+// Ehat, Qhat, Khat [B,H,NT,64,Dk]; Gamma_C [B,H,NT,Dk]; T - I, P
+// [B,H,NT,64,64]; diag(P) [B,H,NT,64]; chunk entry states and leaving-state
+// gradients [B,H,NT,Dk,Dv].
+struct Bwd2Ws {
+    size_t e_off, q_off, k_off, gam_off, t_off, p_off, d_off, ck_off, dck_off, total;
+};
+
+static Bwd2Ws bwd2_ws(int B, int T, int H, int Dk, int Dv) {
+    const size_t chunks = (size_t)B * H * ((T + kBT - 1) / kBT);
+    Bwd2Ws w;
+    size_t off = 0;
+    w.e_off = off; off += align_up(chunks * kBT * Dk * 4);
+    w.q_off = off; off += align_up(chunks * kBT * Dk * 4);
+    w.k_off = off; off += align_up(chunks * kBT * Dk * 4);
+    w.gam_off = off; off += align_up(chunks * Dk * 4);
+    w.t_off = off; off += align_up(chunks * kBT * kBT * 4);
+    w.p_off = off; off += align_up(chunks * kBT * kBT * 4);
+    w.d_off = off; off += align_up(chunks * kBT * 4);
+    w.ck_off = off; off += align_up(chunks * (size_t)Dk * Dv * 4);
+    w.dck_off = off; off += align_up(chunks * (size_t)Dk * Dv * 4);
+    w.total = off;
+    return w;
+}
+
+size_t gdn2_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
+    if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
+    return bwd2_ws(B, T, H, Dk, Dv).total;
+}
+
+gdn_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                          const void *w, const float *h0, const float *dO, const float *dht, float *dq, float *dk,
+                          float *dv, float *dlog_alpha, float *db, float *dw, float *dh0, int B, int T, int H, int Dk,
+                          int Dv, gdn_dtype dtype, float scale, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv || !dlog_alpha || !db || !dw)
+        return GDN_ERR_INVALID_ARG;
+    if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    const Bwd2Ws lay = bwd2_ws(B, T, H, Dk, Dv);
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
+    const Range ins[] = {{q, ntok * Dk * es}, {k, ntok * Dk * es}, {v, ntok * Dv * es}, {log_alpha, ntok * Dk * 4},
+                         {b, ntok * Dk * es}, {w, ntok * Dv * es}, {h0, h0 ? nstate : 0}, {dO, ntok * Dv * 4},
+                         {dht, dht ? nstate : 0}};
+    const Range outs[] = {{dq, ntok * Dk * 4}, {dk, ntok * Dk * 4}, {dv, ntok * Dv * 4}, {dlog_alpha, ntok * Dk * 4},
+                          {db, ntok * Dk * 4}, {dw, ntok * Dv * 4}, {dh0, dh0 ? nstate : 0}, {ws, lay.total}};
+    const int nouts = sizeof(outs) / sizeof(outs[0]);
+    for (int a = 0; a < nouts; ++a) {
+        for (Range in : ins)
+            if (overlap(outs[a], in)) return GDN_ERR_INVALID_ARG;
+        for (int c = a + 1; c < nouts; ++c)
+            if (overlap(outs[a], outs[c])) return GDN_ERR_INVALID_ARG;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    char *base = (char *)ws;
+    float *Eh = (float *)(base + lay.e_off), *Qh = (float *)(base + lay.q_off), *Kh = (float *)(base + lay.k_off);
+    float *Gam = (float *)(base + lay.gam_off), *Tm = (float *)(base + lay.t_off), *P = (float *)(base + lay.p_off);
+    float *D = (float *)(base + lay.d_off), *Sck = (float *)(base + lay.ck_off), *dSck = (float *)(base + lay.dck_off);
+    const bool bf = dtype == GDN_BF16;
+    gdn_status s = from_hip(gdn::launch_gdn2_recompute(q, k, log_alpha, b, v, w, h0, Eh, Qh, Kh, Gam, Tm, P, D, Sck,
+                                                       B, T, H, Dk, Dv, bf, st));
+    if (s != GDN_OK) return s;
+    return from_hip(gdn::launch_gdn2_bwd(q, k, v, log_alpha, b, w, dO, dht, Eh, Qh, Kh, Gam, Tm, P, D, Sck, dSck, dq,
+                                         dk, dv, dlog_alpha, db, dw, dh0, B, T, H, Dk, Dv, bf, scale, st));
 }
 
 gdn_status gdn_prologue(const void *xq, const void *xk, const void *xv, const float *a, const float *b,

@@ -58,6 +58,20 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *
                       float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv,
                       bool bf16, float scale, hipStream_t st);
 
+// Backward of the chunked GDN-2 forward: the fp32 forward recompute
+// (gdn2_chunk.hip; intra operands into Eh .. D, chunk entry states into ck),
+// then the reverse walk and the per-chunk gradients (gdn2_bwd.hip), which
+// overwrite Eh, Qh, Kh, GamC, Tinv and P with their gradients.
+hipError_t launch_gdn2_recompute(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                 const void *wg, const float *h0, float *Eh, float *Qh, float *Kh, float *GamC,
+                                 float *Tinv, float *P, float *D, float *ck, int B, int T, int H, int Dk, int Dv,
+                                 bool bf16, hipStream_t st);
+hipError_t launch_gdn2_bwd(const void *q, const void *k, const void *v, const float *la, const void *bg,
+                           const void *wg, const float *dO, const float *dht, float *Eh, float *Qh, float *Kh,
+                           float *GamC, float *Tws, float *Pws, const float *Dws, const float *Sck, float *dSck,
+                           float *dq, float *dk, float *dv, float *dla, float *db, float *dw, float *dh0, int B, int T,
+                           int H, int Dk, int Dv, bool bf16, float scale, hipStream_t st);
+
 // Prologue and epilogue around the rule (gdn_prologue.hip).
 hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, const float *a, const float *b,
                            const float *wq, const float *wk, const float *wv, const float *A_log,

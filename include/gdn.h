@@ -213,6 +213,31 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
                          void *stream);
 
 /*
+ * Backward of gdn2_chunk_fwd (training): gradients of
+ * L = sum(dO . o) + sum(dht . ht) with respect to every input, by reverse-mode
+ * differentiation of the GDN-2 chunk equations (the WY form with the channel
+ * decay inside both factors of every product, "NVIDIA AI lanza Gated
+ * DeltaNet-2", sections "Regla-2 del Delta cerrado" and on chunked training):
+ * an fp32 forward recompute stores every chunk's entry state, a reverse walk
+ * carries the state gradient, then every chunk is differentiated in parallel
+ * (the decay-weighted contractions with exact per-channel exponentials).
+ * fp32 arithmetic throughout.
+ *   inputs  as gdn2_chunk_fwd (h0 nullable), dO [B, T, H, Dv] fp32,
+ *           dht [B, H, Dk, Dv] fp32 or NULL (no gradient on the final state)
+ *   outputs dq, dk, dlog_alpha, db [B, T, H, Dk], dv, dw [B, T, H, Dv],
+ *           dh0 [B, H, Dk, Dv] or NULL, all fp32
+ *   ws      gdn2_chunk_bwd_workspace() bytes, 256-byte aligned, caller-owned
+ * Errors as gdn_chunk_bwd.  Asynchronous on `stream`.
+ */
+size_t gdn2_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
+
+gdn_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const void *b, const void *w, const float *h0, const float *dO,
+                          const float *dht, float *dq, float *dk, float *dv, float *dlog_alpha,
+                          float *db, float *dw, float *dh0, int B, int T, int H, int Dk, int Dv,
+                          gdn_dtype dtype, float scale, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * gdn_prologue -- the per-token work between the input projections and the
  * rule, in one pass ("GatedDeltaNet walkthrough", the data-flow overview and
  * the sections on the short convolution and the gates):

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     for n in ("gdn_chunk_fwd", "gdn2_chunk_fwd", "gdn_recurrent_step", "gdn2_recurrent_step", "gdn_chunk_intra",
               "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
               "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_status_string",
-              "gdn_prologue", "gdn_gated_rmsnorm"):
+              "gdn_prologue", "gdn_gated_rmsnorm", "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace"):
         assert n in names
 
 
@@ -151,6 +151,32 @@ def test_varlen_rejects_bad_arguments():
     assert f(Dk=96) == 2
     assert f(ptrs=p[:7] + [p[0]] + p[8:]) == 1      # o overlaps q
     assert f(ptrs=p[:7] + [p[5]] + p[8:]) == 1      # o overlaps cu_seqlens
+
+
+def test_gdn2_bwd_workspace_and_validation():
+    lib = gdn.load()
+    assert lib.gdn2_chunk_bwd_workspace(2, 100, 3, 128, 128, 1) > 0
+    assert lib.gdn2_chunk_bwd_workspace(2, 100, 3, 96, 128, 1) == 0
+    assert lib.gdn2_chunk_bwd_workspace(0, 100, 3, 128, 128, 1) == 0
+    # q k v la b w h0 dO dht | dq dk dv dla db dw dh0
+    p = [FAKE + (i << 32) for i in range(16)]
+    ws = FAKE + (20 << 32)
+    need = lib.gdn2_chunk_bwd_workspace(2, 100, 3, 128, 128, 1)
+
+    def f(ptrs=p, B=2, Dk=128, dt=1, w=ws, nbytes=need):
+        return lib.gdn2_chunk_bwd(*[_p(x) for x in ptrs], B, 100, 3, Dk, 128, dt, 0.1, _p(w), nbytes, None)
+
+    assert f(ptrs=[None] + p[1:]) == 1                # no q
+    assert f(ptrs=p[:9] + [None] + p[10:]) == 1       # no dq
+    assert f(B=0) == 1
+    assert f(Dk=96) == 2
+    assert f(dt=7) == 2
+    assert f(w=None) == 3
+    assert f(w=ws + 8) == 3                           # misaligned
+    assert f(nbytes=need - 1) == 3
+    assert f(ptrs=p[:9] + [p[0]] + p[10:]) == 1       # dq overlaps q
+    assert f(ptrs=p[:10] + [p[9]] + p[11:]) == 1      # dk overlaps dq
+    assert f(w=p[3]) == 1                             # workspace overlaps log_alpha
 
 
 def test_prologue_rejects_bad_arguments():
