@@ -8,7 +8,8 @@ output), timed with HIP events on the stream it runs on.  fp32 workloads run
 the two stage entry points and time each stage.  Other workloads: the decode
 step (--workload decode_bf16), Gated DeltaNet-2 (--workload gdn2_bf16) and its
 decode step (--workload decode2_bf16), and the backward of the chunked forward
-on the layer-shaped inputs (--workload layer_bwd_bf16), and the whole layer
+on the layer-shaped inputs (--workload layer_bwd_bf16), the Gated DeltaNet-2
+backward (--workload gdn2_bwd_bf16), and the whole layer
 around the rule: prologue, chunked forward and gated RMSNorm
 (--workload layer_full_bf16).
 
@@ -50,6 +51,7 @@ KERNEL_SOURCES = {
     "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
     "gdn_bwd": ("gdn_bwd.hip", "gdn_chunk.hip", "gdn_device.h"),
     "prologue_kernel": ("gdn_prologue.hip", "gdn_device.h"),
+    "gdn2_bwd": ("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn_device.h"),
 }
 
 
@@ -395,31 +397,45 @@ def bench_step(args, wl):
     return res
 
 
+# The two backwards: input names, entry point, oracle, extra gate bytes per token-head.
+BWDS = {
+    "layer_bwd_bf16": dict(names=("q", "k", "v", "g", "beta"), fn="gdn_chunk_bwd", ws="gdn_chunk_bwd_workspace",
+                           ref="gdn_bwd", kernel="gdn_bwd", label="chunk_gated_delta_rule bwd",
+                           extra=lambda Dk, Dv, es: 8 + 8),             # g, beta in; dg, dbeta out
+    "gdn2_bwd_bf16": dict(names=("q", "k", "v", "log_alpha", "b", "w"), fn="gdn2_chunk_bwd",
+                          ws="gdn2_chunk_bwd_workspace", ref="gdn2_bwd", kernel="gdn2_bwd",
+                          label="chunk gated delta rule-2 bwd",
+                          # b, w and log_alpha in; dlog_alpha, db, dw out
+                          extra=lambda Dk, Dv, es: (Dk + Dv) * es + 4 * Dk + (2 * Dk + Dv) * 4),
+}
+
+
 def bench_bwd(args, wl):
-    """Backward of the chunked forward (gdn_chunk_bwd) on the layer-shaped inputs:
-    one step = the four backward stages over the whole batch."""
+    """Backward of a chunked forward on its workload's inputs: one step = every
+    backward stage over the whole batch."""
     import numpy as np
     import torch
     import gated_delta_rule_34_amd as gdn
     import gdn_inputs as gi
-    import oracle
 
+    spec = BWDS[wl]
     dev = torch.device("cuda:0")
     x = gi.workload(wl)
     B, T, H, Dk, Dv = x["B"], x["T"], x["H"], x["Dk"], x["Dv"]
     rng = np.random.default_rng(x.get("seed", 0) + 7)
     do = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
     dht = rng.standard_normal((B, H, Dk, Dv)).astype(np.float32)
-    base = {n: to_dev(x[n], dev) for n in ("q", "k", "v", "g", "beta")}
+    names = spec["names"]
+    base = {n: to_dev(x[n], dev) for n in names}
     base["do"] = to_dev(do, dev)
     base["dht"] = to_dev(dht, dev)
     sets = [{n: t.clone() for n, t in base.items()} for _ in range(args.sets)]
     dt = gdn.GDN_BF16 if x["dtype"] == "bf16" else gdn.GDN_F32
-    ws = torch.empty(gdn.gdn_chunk_bwd_workspace(B, T, H, Dk, Dv, dt), dtype=torch.uint8, device=dev)
+    ws = torch.empty(getattr(gdn, spec["ws"])(B, T, H, Dk, Dv, dt), dtype=torch.uint8, device=dev)
+    fn = getattr(gdn, spec["fn"])
 
     def step(s):
-        gdn.gdn_chunk_bwd(s["q"], s["k"], s["v"], s["g"], s["beta"], None, s["do"], s["dht"], scale=x["scale"],
-                          workspace=ws)
+        fn(*[s[n] for n in names], None, s["do"], s["dht"], scale=x["scale"], workspace=ws)
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -434,30 +450,31 @@ def bench_bwd(args, wl):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = e0.elapsed_time(e1) / args.steps
     esz = 2 if x["dtype"] == "bf16" else 4
-    # inputs q, k, v, g, beta, dO, dht read once; dq, dk, dv, dg, dbeta written once
-    per_tok = (2 * Dk + Dv) * esz + 8 + Dv * 4 + (2 * Dk + Dv) * 4 + 8
+    # inputs q, k, v (and the gates), dO, dht read once; every gradient written once (fp32)
+    per_tok = (2 * Dk + Dv) * esz + Dv * 4 + (2 * Dk + Dv) * 4 + spec["extra"](Dk, Dv, esz)
     kbytes = float(B) * T * H * per_tok + float(B) * H * Dk * Dv * 4
     achieved = kbytes / (kms * 1e-3) / 1e9
     log(f"[bench] {args.steps} steps: {ms:.4f} ms/step wall; per call (HIP events) {kms * 1e3:.1f} us")
     res = {
-        "metric": f"chunk_gated_delta_rule bwd tokens/s, T={T} d={Dk}",
+        "metric": f"{spec['label']} tokens/s, T={T} d={Dk}",
         "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "inputs": x["dtype"],
-                   "gradients": "fp32", "stages": "intra, forward walk with chunk-entry states, reverse state "
+                   "gradients": "fp32", "stages": "fp32 forward recompute with chunk entry states, reverse state "
                                                  "walk, per-chunk gradients", "buffer_sets": args.sets,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gdn_chunk_bwd (4 kernels)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": f"{spec['fn']} (all stages)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3, "traffic": None},
     }
     if not args.no_cpu_baseline:
-        # oracle backward on one head (all of it)
-        sub = {n: x[n + "_f64"][:1, :, :1] for n in ("q", "k", "v", "g", "beta")}
+        import oracle
+        # the oracle backward on one head (all of it)
+        sub = [x[n + "_f64"][:1, :, :1] for n in names]
         t0 = time.perf_counter()
-        oracle.gdn_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], None,
-                       do[:1, :, :1].astype(np.float64), dht[:1, :1].astype(np.float64), scale=x["scale"])
+        getattr(oracle, spec["ref"])(*sub, None, do[:1, :, :1].astype(np.float64), dht[:1, :1].astype(np.float64),
+                                     scale=x["scale"])
         dt_cpu = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": T / dt_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                "sample": f"one head of the workload ({T} tokens); the oracle runs one head per "
@@ -563,7 +580,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16",
                     choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "decode2_bf16", "gdn2_bf16",
-                             "layer_bwd_bf16", "layer_full_bf16"])
+                             "layer_bwd_bf16", "gdn2_bwd_bf16", "layer_full_bf16"])
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -583,7 +600,7 @@ def main():
         sys.exit(1)
     if args.workload in STEPS:
         res = bench_step(args, args.workload)
-    elif args.workload == "layer_bwd_bf16":
+    elif args.workload in BWDS:
         res = bench_bwd(args, args.workload)
     elif args.workload == "gdn2_bf16":
         res = bench_gdn2(args, args.workload)

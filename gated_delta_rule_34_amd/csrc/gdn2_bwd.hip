@@ -55,12 +55,14 @@ __device__ __forceinline__ f32x4 tmma(f32x4 acc, const float *A, int sar, int sa
 template <int D, int LD, int NTHR>
 __device__ __forceinline__ void stage_block(float *dst, const float *src, int tid) {
     constexpr int U = BT * D / 4 / NTHR;
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = *(const float4 *)(src + 4 * (tid + NTHR * u));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int idx = 4 * (tid + NTHR * u), row = idx / D, col = idx % D;
-        const float4 x = *(const float4 *)(src + idx);
         float *p = dst + row * LD + col;
-        p[0] = x.x; p[1] = x.y; p[2] = x.z; p[3] = x.w;
+        p[0] = x[u].x; p[1] = x[u].y; p[2] = x[u].z; p[3] = x[u].w;
     }
 }
 
@@ -79,6 +81,37 @@ __device__ __forceinline__ void stage_cols16(float *dst, const In *src, long b, 
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[row * LD + c4 + e] = x[e];
+}
+
+// T - I and P (strict part plus diagonal) of a chunk into LDS (row stride
+// LD), float4 loads issued before their stores; 256 threads.
+template <int LD>
+__device__ __forceinline__ void stage_tp(float *sT, float *sP, const float *Tc, const float *Pc, const float *Dc,
+                                         int tid) {
+    constexpr int U = BT * BT / 4 / 256;
+    float4 xt[U], xp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        xt[u] = *(const float4 *)(Tc + 4 * (tid + 256 * u));
+        xp[u] = *(const float4 *)(Pc + 4 * (tid + 256 * u));
+    }
+    float dg[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = 4 * (tid + 256 * u), i = idx >> 6;
+        dg[u] = Dc[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = 4 * (tid + 256 * u), i = idx >> 6, j = idx & 63;
+        const float tv[4] = {xt[u].x, xt[u].y, xt[u].z, xt[u].w};
+        const float pv[4] = {xp[u].x, xp[u].y, xp[u].z, xp[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sT[i * LD + j + e] = tv[e];
+            sP[i * LD + j + e] = (j + e < i) ? pv[e] : (j + e == i ? dg[u] : 0.f);
+        }
+    }
 }
 
 // Tile index t (0..9) of the lower 4 x 4 block triangle: I = row block, J = column block.
@@ -123,15 +156,24 @@ __global__ __launch_bounds__(256) void gdn2_bwd_walk_kernel(
         }
         stage_block<DK, LDQ, NTHR>(sA, Kh + ob, tid);
         stage_block<DK, LDQ, NTHR>(sQ, Qh + ob, tid);
-        for (int idx = tid; idx < BT * BT; idx += NTHR) {
-            const int i = idx >> 6, j = idx & 63;
-            sTm[i * LDC + j] = Tws[cb * BT * BT + idx];
-            sP[i * LDC + j] = (j < i) ? Pws[cb * BT * BT + idx] : (j == i ? Dws[cb * BT + i] : 0.f);
-        }
-        for (int idx = tid; idx < BT * BV; idx += NTHR) {
-            const int row = idx / BV, col = idx % BV;
-            const int t = c * BT + row;
-            sdO[row * LDB + col] = (t < T) ? dO[((b * T + t) * H + h) * (long)DV + vcol0 + col] : 0.f;
+        stage_tp<LDC>(sTm, sP, Tws + cb * BT * BT, Pws + cb * BT * BT, Dws + cb * BT, tid);
+        {
+            constexpr int UO = BT * BV / 4 / NTHR;
+            float4 xo[UO];
+#pragma unroll
+            for (int u = 0; u < UO; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / BV, col = idx % BV;
+                const int t = min(c * BT + row, T - 1);
+                xo[u] = *(const float4 *)(dO + ((b * T + t) * H + h) * (long)DV + vcol0 + col);
+            }
+#pragma unroll
+            for (int u = 0; u < UO; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / BV, col = idx % BV;
+                const bool in = c * BT + row < T;
+                float *p = &sdO[row * LDB + col];
+                p[0] = in ? xo[u].x : 0.f; p[1] = in ? xo[u].y : 0.f;
+                p[2] = in ? xo[u].z : 0.f; p[3] = in ? xo[u].w : 0.f;
+            }
         }
         for (int idx = tid; idx < DK; idx += NTHR) sGam[idx] = GamC[cb * DK + idx];
         __syncthreads();
@@ -212,11 +254,7 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
 
     stage_block<DK, LDQ, NTHR>(sm.E, Eh + ob, tid);
     stage_block<DK, LDQ, NTHR>(sm.K, Kh + ob, tid);
-    for (int idx = tid; idx < BT * BT; idx += NTHR) {
-        const int i = idx >> 6, j = idx & 63;
-        sm.Tm[i * LDC + j] = Tws[cb * BT * BT + idx];
-        sm.P[i * LDC + j] = (j < i) ? Pws[cb * BT * BT + idx] : (j == i ? Dws[cb * BT + i] : 0.f);
-    }
+    stage_tp<LDC>(sm.Tm, sm.P, Tws + cb * BT * BT, Pws + cb * BT * BT, Dws + cb * BT, tid);
     // accumulators over the value columns: the lower tiles of dA and dP owned
     // by this wave (tiles t = wave, wave + 4, wave + 8), and row block I of
     // dEhat, dQhat, dKhat (NM tiles each); sum_v dS' . S per key channel
@@ -229,11 +267,23 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
 
     for (int v0 = 0; v0 < DV; v0 += CW) {
         __syncthreads();  // the previous slice's readers are done
-        for (int idx = tid; idx < DK * CW; idx += NTHR) {
-            const int row = idx / CW, col = idx % CW;
-            const long off = cb * (long)DK * DV + (long)row * DV + v0 + col;
-            sm.S[row * LDW + col] = Sck[off];
-            sm.dS[row * LDW + col] = dSck[off];
+        {
+            constexpr int US = DK * CW / 4 / NTHR;
+            float4 xs[US], xd[US];
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
+                const long off = cb * (long)DK * DV + (long)row * DV + v0 + col;
+                xs[u] = *(const float4 *)(Sck + off);
+                xd[u] = *(const float4 *)(dSck + off);
+            }
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
+                float *ps = &sm.S[row * LDW + col], *pd = &sm.dS[row * LDW + col];
+                ps[0] = xs[u].x; ps[1] = xs[u].y; ps[2] = xs[u].z; ps[3] = xs[u].w;
+                pd[0] = xd[u].x; pd[1] = xd[u].y; pd[2] = xd[u].z; pd[3] = xd[u].w;
+            }
         }
         stage_cols16<LDW>(sm.V, v, b, h, t0, T, H, v0, DV, tid);
         stage_cols16<LDW>(sm.W, wg, b, h, t0, T, H, v0, DV, tid);
@@ -383,21 +433,23 @@ __global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
         sm.dP[i * LDA + j] = dPws[cb * BT * BT + idx];
     }
     __syncthreads();
-    if (wave == 0) {  // G = chunk-local cumsum of log_alpha per channel
+    if (wave == 0) {  // G = log2(e) * chunk-local cumsum of log_alpha per channel (exp2 below)
         float s = 0.f;
         for (int i = 0; i < BT; ++i) {
-            s += sm.G[i * CH + lane];
+            s += sm.G[i * CH + lane] * LOG2E;
             sm.G[i * CH + lane] = s;
         }
     }
     __syncthreads();
+    // (G holds log2(e) G, so D_ijc = 2^(G_ic - G_jc) on the hardware exp2)
     // row side (rows i = wave mod 4): rA_ic = sum_{j<i} dA_ij k_jc D_ijc,
     // rP_ic = sum_{j<=i} dP_ij k_jc D_ijc
     for (int i = wave; i < BT; i += 4) {
         const float Gi = sm.G[i * CH + lane];
         float ra = 0.f, rp = 0.f;
+#pragma unroll 4
         for (int j = 0; j <= i; ++j) {
-            const float kd = sm.K[j * CH + lane] * expf(Gi - sm.G[j * CH + lane]);
+            const float kd = sm.K[j * CH + lane] * __builtin_amdgcn_exp2f(Gi - sm.G[j * CH + lane]);
             ra += sm.dA[i * LDA + j] * kd;
             rp += sm.dP[i * LDA + j] * kd;
         }
@@ -413,13 +465,14 @@ __global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
     for (int j = wave; j < BT; j += 4) {
         const float Gj = sm.G[j * CH + lane];
         float ca = 0.f, cp = 0.f;
+#pragma unroll 4
         for (int i = j; i < BT; ++i) {
-            const float d = expf(sm.G[i * CH + lane] - Gj);
+            const float d = __builtin_amdgcn_exp2f(sm.G[i * CH + lane] - Gj);
             ca += sm.dA[i * LDA + j] * sm.E[i * CH + lane] * d;
             cp += sm.dP[i * LDA + j] * sm.Q[i * CH + lane] * d;
         }
         const float kj = sm.K[j * CH + lane], ej = sm.E[j * CH + lane], qj = sm.Q[j * CH + lane];
-        const float gam = expf(Gj), dec = expf(GL - Gj);
+        const float gam = __builtin_amdgcn_exp2f(Gj), dec = __builtin_amdgcn_exp2f(GL - Gj);
         const long gi = ob + (long)j * DK + col;
         const float dEhv = dEh[gi], dQhv = dQh[gi], dKhv = dKh[gi];
         const float de = sm.rA[j * CH + lane] + gam * dEhv;
@@ -439,7 +492,7 @@ __global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
     __syncthreads();
     if (wave == 0)
         sm.dG[(BT - 1) * CH + lane] += sm.tpart[0][lane] + sm.tpart[1][lane] + sm.tpart[2][lane] +
-                                       sm.tpart[3][lane] + expf(GL) * srow[cb * DK + col];
+                                       sm.tpart[3][lane] + __builtin_amdgcn_exp2f(GL) * srow[cb * DK + col];
     __syncthreads();
     // db = de . k, dk = (the rest) + de . b, dlog_alpha = reverse cumsum of dG
     for (int j = wave; j < BT; j += 4) {

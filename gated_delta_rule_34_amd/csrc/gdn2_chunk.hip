@@ -27,6 +27,8 @@
 //  gdn2_walk_kernel (one workgroup per (b, h, 32 value columns)) walks the
 //    chunks with the state slice in MFMA accumulators, like the Gated
 //    DeltaNet walk, on the prepared operands.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -217,7 +219,9 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
     }
 }
 
-template <class Pol, int DK, int DV, int BV>
+// OUT = false: the backward's recompute, which needs only the chunk entry
+// states (no Qhat S, no P Vnew, no output).
+template <class Pol, int DK, int DV, int BV, bool OUT = true>
 __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
     const typename Pol::mt *__restrict__ Ehat, const typename Pol::mt *__restrict__ Qhat,
     const typename Pol::mt *__restrict__ Khat, const float *__restrict__ GamC, const float *__restrict__ Tws,
@@ -231,7 +235,8 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
     constexpr int LDQ = DK + 8;
     constexpr int LDKT = BT + 8;
     constexpr int LDP = BT + 8;
-    __shared__ mt sE[BT * LDQ], sQ[BT * LDQ], sKt[DK * LDKT], sP[BT * LDP];
+    constexpr int QN = OUT ? BT * LDQ : 1, PN = OUT ? BT * LDP : 1;
+    __shared__ mt sE[BT * LDQ], sQ[QN], sKt[DK * LDKT], sP[PN], sT[BT * LDP];
     __shared__ float sDiag[BT], sGam[DK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
     const long b = bh / H;
     const int col = vt * BV + wave * 16 + r;
 
-    for (int idx = tid; idx < BT * LDP; idx += NTHR) sP[idx] = to_mt<mt>(0.f);
+    for (int idx = tid; idx < PN; idx += NTHR) sP[idx] = to_mt<mt>(0.f);
     f32x4 S[NKB];
     const long sbase = bh * (long)DK * DV;
 #pragma unroll
@@ -261,17 +266,49 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ck[cb * DK * DV + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
         }
-        for (int idx = tid; idx < BT * DK; idx += NTHR) {
-            const int row = idx / DK, kc = idx % DK;
-            sE[row * LDQ + kc] = Ehat[ob + idx];
-            sQ[row * LDQ + kc] = Qhat[ob + idx];
-            sKt[kc * LDKT + row] = Khat[ob + idx];
+        if (OUT) {
+            for (int idx = tid; idx < BT * DK; idx += NTHR) {
+                const int row = idx / DK, kc = idx % DK;
+                sE[row * LDQ + kc] = Ehat[ob + idx];
+                sQ[row * LDQ + kc] = Qhat[ob + idx];
+                sKt[kc * LDKT + row] = Khat[ob + idx];
+            }
+            for (int idx = tid; idx < BT * BT; idx += NTHR) {
+                const int i = idx >> 6, j = idx & 63;
+                sT[i * LDP + j] = to_mt<mt>(Tws[cb * (BT * BT) + idx]);
+                if (j < i) sP[i * LDP + j] = to_mt<mt>(Pws[cb * (BT * BT) + idx]);
+            }
+        } else {
+            // fp32 operands only (the recompute): float4 loads, all issued
+            // before their LDS stores
+            constexpr int UE = BT * DK / 4 / NTHR, UT = BT * BT / 4 / NTHR;
+            float4 xe[UE], xk[UE], xt[UT];
+#pragma unroll
+            for (int u = 0; u < UE; ++u) {
+                xe[u] = *(const float4 *)((const float *)Ehat + ob + 4 * (tid + NTHR * u));
+                xk[u] = *(const float4 *)((const float *)Khat + ob + 4 * (tid + NTHR * u));
+            }
+#pragma unroll
+            for (int u = 0; u < UT; ++u) xt[u] = *(const float4 *)(Tws + cb * (BT * BT) + 4 * (tid + NTHR * u));
+#pragma unroll
+            for (int u = 0; u < UE; ++u) {
+                const int idx = 4 * (tid + NTHR * u), row = idx / DK, kc = idx % DK;
+                float *pe = (float *)&sE[row * LDQ + kc];
+                pe[0] = xe[u].x; pe[1] = xe[u].y; pe[2] = xe[u].z; pe[3] = xe[u].w;
+                float *pk = (float *)sKt;
+                pk[(kc + 0) * LDKT + row] = xk[u].x;
+                pk[(kc + 1) * LDKT + row] = xk[u].y;
+                pk[(kc + 2) * LDKT + row] = xk[u].z;
+                pk[(kc + 3) * LDKT + row] = xk[u].w;
+            }
+#pragma unroll
+            for (int u = 0; u < UT; ++u) {
+                const int idx = 4 * (tid + NTHR * u), i = idx >> 6, j = idx & 63;
+                float *pt = (float *)&sT[i * LDP + j];
+                pt[0] = xt[u].x; pt[1] = xt[u].y; pt[2] = xt[u].z; pt[3] = xt[u].w;
+            }
         }
-        for (int idx = tid; idx < BT * BT; idx += NTHR) {
-            const int i = idx >> 6, j = idx & 63;
-            if (j < i) sP[i * LDP + j] = to_mt<mt>(Pws[cb * (BT * BT) + idx]);
-        }
-        if (tid < BT) sDiag[tid] = Dws[cb * BT + tid];
+        if (OUT && tid < BT) sDiag[tid] = Dws[cb * BT + tid];
         for (int idx = tid; idx < DK; idx += NTHR) sGam[idx] = GamC[cb * DK + idx];
         __syncthreads();
 
@@ -287,8 +324,10 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
                 mt a[8];
                 frag_rows(a, sE, LDQ, 16 * I, 32 * s, lane);
                 X[I] = mma_slab(X[I], a, sb);
-                frag_rows(a, sQ, LDQ, 16 * I, 32 * s, lane);
-                Y[I] = mma_slab(Y[I], a, sb);
+                if (OUT) {
+                    frag_rows(a, sQ, LDQ, 16 * I, 32 * s, lane);
+                    Y[I] = mma_slab(Y[I], a, sb);
+                }
             }
         }
         // R = w . v - Ehat S
@@ -308,7 +347,6 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
         mt rf[2][8];
         frag_from_acc(rf[0], R[0], R[1]);
         frag_from_acc(rf[1], R[2], R[3]);
-        const float *Tc = Tws + cb * (BT * BT);
         f32x4 Vn[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -316,12 +354,7 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
 #pragma unroll
             for (int s = 0; s <= (I >> 1); ++s) {
                 mt a[8];
-                const float *p = Tc + (16 * I + r) * BT + 32 * s + 4 * g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = to_mt<mt>(p[e]);
-                    a[e + 4] = to_mt<mt>(p[16 + e]);
-                }
+                frag_rows(a, sT, LDP, 16 * I, 32 * s, lane);
                 Vn[I] = mma_slab(Vn[I], a, rf[s]);
             }
         }
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(BV * 4) void gdn2_walk_kernel(
         frag_from_acc(vf[0], Vn[0], Vn[1]);
         frag_from_acc(vf[1], Vn[2], Vn[3]);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < (OUT ? 4 : 0); ++I) {
             f32x4 acc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = Y[I][e] + sDiag[16 * I + 4 * g + e] * Vn[I][e];
@@ -442,11 +475,12 @@ static hipError_t launch_gdn2_recompute_t(const void *q, const void *k, const fl
                                           float *Kh, float *GamC, float *Tinv, float *P, float *D, float *ck, int B,
                                           int T, int H, hipStream_t st) {
     constexpr int BV = 32;
+    static_assert(std::is_same<typename Pol::mt, float>::value, "the recompute runs on fp32 operands");
     using in_t = typename Pol::in_t;
     hipError_t e = launch_gdn2_intra_t<Pol, DK>(q, k, la, bg, Eh, Qh, Kh, GamC, Tinv, P, D, B, T, H, st);
     if (e != hipSuccess) return e;
     const int NT = (T + BT - 1) / BT;
-    hipLaunchKernelGGL((gdn2_walk_kernel<Pol, DK, DV, BV>), dim3((unsigned)((long)B * H * (DV / BV))), dim3(BV * 4),
+    hipLaunchKernelGGL((gdn2_walk_kernel<Pol, DK, DV, BV, false>), dim3((unsigned)((long)B * H * (DV / BV))), dim3(BV * 4),
                        0, st, (const float *)Eh, (const float *)Qh, (const float *)Kh, GamC, Tinv, P, D,
                        (const in_t *)v, (const in_t *)wg, h0, (float *)nullptr, (float *)nullptr, ck, T, H, NT, 1.f);
     return hipGetLastError();

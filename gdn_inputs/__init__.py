@@ -45,6 +45,7 @@ WORKLOADS = {
     "gdn2_bf16": dict(kind="gdn2", B=4, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1004),
     "decode2_bf16": dict(kind="step2", B=256, H=16, Dk=128, Dv=128, dtype="bf16", seed=1005),
     "layer_bwd_bf16": dict(kind="gdn", B=8, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1001),
+    "gdn2_bwd_bf16": dict(kind="gdn2", B=4, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", h0=False, seed=1004),
     "layer_full_bf16": dict(kind="layer", B=8, H=8, T=4096, Dk=128, Dv=128, dtype="bf16", conv_state=False,
                             seed=1006),
 }
