@@ -207,15 +207,16 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
     //    loads are issued before any is used; rows past T read the last token
     //    (always in bounds) and are then zeroed.
     constexpr int NU = BT * C8 / NTH;  // uint4 per thread per raw tile
-    uint4 kr[NU], qr[NU], br[NU];
+    typedef __attribute__((ext_vector_type(4))) unsigned int v4u;  // native vectors stay in registers
+    v4u kr[NU], qr[NU], br[NU];
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
         const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
         const int tr = min(t0 + row, T - 1) - t0;
         const long off = (row0 + (long)tr * H) * DK + 8 * c8;
-        kr[x] = *(const uint4 *)(k + off);
-        qr[x] = *(const uint4 *)(q + off);
-        br[x] = *(const uint4 *)(bg + off);
+        kr[x] = *(const v4u *)(k + off);
+        qr[x] = *(const v4u *)(q + off);
+        br[x] = *(const v4u *)(bg + off);
     }
     // thread (group gr, channel ch) scans rows RG gr .. RG gr + RG - 1 of its channel
     const int ch = tid % DK, gr = tid / DK;
@@ -229,10 +230,10 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
     for (int x = 0; x < NU; ++x) {
         const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
         const bool in = t0 + row < T;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        *(uint4 *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
-        *(uint4 *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
-        *(uint4 *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
+        const v4u z = {0u, 0u, 0u, 0u};
+        *(v4u *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
+        *(v4u *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
+        *(v4u *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
     }
     float acc = 0.f;
 #pragma unroll
@@ -339,11 +340,14 @@ struct Gdn2Head {
     int T, H, vcol0;
 };
 
-// Everything a loader thread moves for one chunk.
+// Everything a loader thread moves for one chunk, as native 16-byte vectors
+// (HIP's uint4 is a struct the compiler keeps in scratch memory here).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
 template <int DK>
 struct Gdn2Stage {
-    uint4 e[Gdn2WalkCfg<DK, DK>::UT], q[Gdn2WalkCfg<DK, DK>::UT], k[Gdn2WalkCfg<DK, DK>::UT];
-    uint4 tm[4], p[4], v[2], w[2], tab;
+    u32x4 e[Gdn2WalkCfg<DK, DK>::UT], q[Gdn2WalkCfg<DK, DK>::UT], k[Gdn2WalkCfg<DK, DK>::UT];
+    u32x4 tm[4], p[4], v[2], w[2], tab;
 };
 
 template <int DK, int DV>
@@ -354,26 +358,26 @@ __device__ __forceinline__ void stage_load(Gdn2Stage<DK> &R, const Gdn2Head &hd,
 #pragma unroll
     for (int x = 0; x < C::UT; ++x) {
         const int u = lt + 128 * x;
-        R.e[x] = *(const uint4 *)(blk + BL::E + u * 16);
-        R.q[x] = *(const uint4 *)(blk + BL::Q + u * 16);
-        R.k[x] = *(const uint4 *)(blk + BL::K + u * 16);
+        R.e[x] = *(const u32x4 *)(blk + BL::E + u * 16);
+        R.q[x] = *(const u32x4 *)(blk + BL::Q + u * 16);
+        R.k[x] = *(const u32x4 *)(blk + BL::K + u * 16);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int u = lt + 128 * x;
-        R.tm[x] = *(const uint4 *)(blk + BL::TM + u * 16);
-        R.p[x] = *(const uint4 *)(blk + BL::PM + u * 16);
+        R.tm[x] = *(const u32x4 *)(blk + BL::TM + u * 16);
+        R.p[x] = *(const u32x4 *)(blk + BL::PM + u * 16);
     }
     // dg (16 uint4) then Gamma_C (DK / 4 uint4), contiguous in the block
-    R.tab = (lt < 16 + DK / 4) ? *(const uint4 *)(blk + BL::DG + lt * 16) : make_uint4(0, 0, 0, 0);
+    R.tab = (lt < 16 + DK / 4) ? *(const u32x4 *)(blk + BL::DG + lt * 16) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int u = lt + 128 * x, row = u >> 2, c4 = u & 3;
         const int t = chunk * BT + row;
         const long off = (hd.row0 + (long)t * hd.H) * DV + hd.vcol0 + 8 * c4;
         const bool in = t < hd.T;
-        R.v[x] = in ? *(const uint4 *)(hd.v + off) : make_uint4(0, 0, 0, 0);
-        R.w[x] = in ? *(const uint4 *)(hd.w + off) : make_uint4(0, 0, 0, 0);
+        R.v[x] = in ? *(const u32x4 *)(hd.v + off) : (u32x4){0u, 0u, 0u, 0u};
+        R.w[x] = in ? *(const u32x4 *)(hd.w + off) : (u32x4){0u, 0u, 0u, 0u};
     }
 }
 
@@ -384,25 +388,25 @@ __device__ __forceinline__ void stage_store(Gdn2WalkSmem<DK, DV> &sm, const Gdn2
 #pragma unroll
     for (int x = 0; x < C::UT; ++x) {
         const int u = lt + 128 * x, row = u / C8, c0 = 8 * (u % C8);
-        *(uint4 *)&sm.E[buf][tile_off<DK>(row, c0)] = R.e[x];
-        *(uint4 *)&sm.Q[buf][tile_off<DK>(row, c0)] = R.q[x];
-        *(uint4 *)&sm.K[buf][tile_off<DK>(row, c0)] = R.k[x];
+        *(u32x4 *)&sm.E[buf][tile_off<DK>(row, c0)] = R.e[x];
+        *(u32x4 *)&sm.Q[buf][tile_off<DK>(row, c0)] = R.q[x];
+        *(u32x4 *)&sm.K[buf][tile_off<DK>(row, c0)] = R.k[x];
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int u = lt + 128 * x, row = u >> 3, c0 = 8 * (u & 7);
-        *(uint4 *)&sm.Tm[buf][row * C::LDP + c0] = R.tm[x];
-        *(uint4 *)&sm.P[buf][row * C::LDP + c0] = R.p[x];
+        *(u32x4 *)&sm.Tm[buf][row * C::LDP + c0] = R.tm[x];
+        *(u32x4 *)&sm.P[buf][row * C::LDP + c0] = R.p[x];
     }
     if (lt < 16)
-        *(uint4 *)&sm.dg[buf][4 * lt] = R.tab;
+        *(u32x4 *)&sm.dg[buf][4 * lt] = R.tab;
     else if (lt < 16 + DK / 4)
-        *(uint4 *)&sm.gam[buf][4 * (lt - 16)] = R.tab;
+        *(u32x4 *)&sm.gam[buf][4 * (lt - 16)] = R.tab;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int u = lt + 128 * x, row = u >> 2, c0 = 8 * (u & 3);
-        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[x];
-        *(uint4 *)&sm.W[buf][row * C::LDV + c0] = R.w[x];
+        *(u32x4 *)&sm.V[buf][row * C::LDV + c0] = R.v[x];
+        *(u32x4 *)&sm.W[buf][row * C::LDV + c0] = R.w[x];
     }
 }
 
