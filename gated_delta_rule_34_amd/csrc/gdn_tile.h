@@ -189,74 +189,182 @@ __device__ __forceinline__ f16x4 col4_tr(const _Float16 *M, int row0, int col0, 
     return __builtin_bit_cast(f16x4, v);
 }
 
+// Four entries of one row of a 16x16 fp16 block: lane (g, r) receives
+// M[row0 + r][col0 + 4g + e], e = 0..3 (an A operand, or the B operand of a
+// product formed transposed).
+template <int LDP>
+__device__ __forceinline__ f16x4 row4(const _Float16 *M, int row0, int col0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    return *(const f16x4 *)&M[(row0 + r) * LDP + col0 + 4 * g];
+}
+
+// A fragment of T - I (zero diagonal) turned into T: entry e of lane (g, r)
+// sits on the diagonal when 4g + e == r, for a column read and a row read.
+__device__ __forceinline__ f16x4 plus_eye(f16x4 v, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (4 * g + e == r) v[e] = (_Float16)1.f;
+    return v;
+}
+
+__device__ __forceinline__ void split_hl(f16x4 &h, f16x4 &l, const f32x4 &x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (_Float16)x[e];
+        l[e] = (_Float16)(x[e] - (float)h[e]);
+    }
+}
+
+__device__ __forceinline__ f16x8 cat8(const f16x4 &a, const f16x4 &b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // T - I for T = (I + A)^-1 of one chunk, A strictly lower (fp16, row stride
 // LDP, the strict-lower part of every 16x16 block filled, other entries of
-// the lower tiles zero); one wave.  Tm receives the lower tiles of T - I.
-//  Diagonal blocks: lane (block bb, column cc) solves its column of T_bb,
-//    x_i = [i == cc] - sum_{j<i} A_ij x_j, with four partial sums per row.
-//  Off-diagonal blocks, one sub-diagonal level d at a time (the blocks of a
-//    level are independent and are computed together):
-//    T_IJ = -T_II M,  M = A_IJ + sum_{K=J}^{I-1} A_IK (T - I)_KJ,
-//    with column pieces read by transpose loads and T_IJ formed as
-//    (M^T T_II^T)^T so each lane stores 4 adjacent entries of a row.
+// the lower tiles zero); one wave.  Tm receives the lower tiles of T - I;
+// its upper 16x16 tiles and the upper-right 8x8 quadrant of each diagonal
+// block must be zero on entry (they are read as zero and never written).
+// For a block-lower matrix L = [L11 0; L21 L22], L^-1 has the diagonal
+// blocks L11^-1, L22^-1 and the off-diagonal block -L22^-1 L21 L11^-1, so
+// the inverse doubles its block size level by level:
+//  8 x 8:   lane (block b, column c) solves its column by forward
+//           substitution, x_i = [i == c] - sum_{j<i} A_ij x_j;
+//  16 x 16: the lower-left 8x8 quadrant of each diagonal block,
+//           -T22 A21 T11, four blocks side by side on MFMA;
+//  32 x 32: blocks (1,0) and (3,2), -T_II A_IJ T_JJ;
+//  64 x 64: blocks (2..3, 0..1): Z = A_[23][01] T_[01][01] on 32-deep MFMA,
+//           then -T_[23][23] Z.
+// Each product W = A T is exact (fp16 operands from LDS, fp32 sums); the
+// outer product -T W takes W as fp16 hi + lo parts (~22 bits) and is
+// formed transposed, (W^T T^T)^T, so that a lane holds 4 adjacent entries
+// of a row of the result and stores them at once.  Quadrants of Tm left by
+// an earlier chunk are masked where an operand would read them.
 template <int LDP>
 __device__ __forceinline__ void unit_lower_inverse(const _Float16 *A, _Float16 *Tm, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    {
-        const int bb = lane >> 4, cc = lane & 15;
-        float x[16];
+    const bool ll_col = g >= 2 && r < 8, ll_row = r >= 8 && g < 2;
+    const f16x4 z4 = {};
+    // Every read of A is issued first: the levels below then wait only on
+    // their own reads of Tm, one LDS round trip per level.
+    const int b8 = lane >> 3, cc = lane & 7;
+    const _Float16 *Ab = &A[8 * b8 * LDP + 8 * b8];
+    f16x4 a8[8][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const _Float16 *arow = &A[(16 * bb + i) * LDP + 16 * bb];
-            f16x4 av[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                if (4 * q4 < i) av[q4] = *(const f16x4 *)&arow[4 * q4];
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < i; ++j) part[j & 3] = fmaf((float)av[j >> 2][j & 3], x[j], part[j & 3]);
-            x[i] = ((i == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Tm[(16 * bb + i) * LDP + 16 * bb + cc] = (_Float16)(x[i] - (i == cc ? 1.f : 0.f));
+    for (int i = 0; i < 8; ++i) {
+        a8[i][0] = (i > 0) ? *(const f16x4 *)&Ab[i * LDP] : z4;
+        a8[i][1] = (i > 4) ? *(const f16x4 *)&Ab[i * LDP + 4] : z4;
     }
+    f16x4 a16[4], a32[2], a64[2][2];
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        f32x4 M[3];
+    for (int B = 0; B < 4; ++B) a16[B] = row4<LDP>(A, 16 * B, 16 * B, lane);
 #pragma unroll
-        for (int J = 0; J < 4 - d; ++J) {
-            const int I = J + d;
-            // M starts as A_IJ: lane (g, r) holds A[16I + 4g + e][16J + r]
-            const f16x4 aij = col4_tr<LDP>(A, 16 * I, 16 * J, lane);
+    for (int p = 0; p < 2; ++p) a32[p] = row4<LDP>(A, 16 * (2 * p + 1), 32 * p, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) M[J][e] = (float)aij[e];
+    for (int K = 0; K < 2; ++K)
 #pragma unroll
-            for (int K = J; K < I; ++K) {
-                const f16x4 a = *(const f16x4 *)&A[(16 * I + r) * LDP + 16 * K + 4 * g];
-                M[J] = mma_f16_block(M[J], a, col4_tr<LDP>(Tm, 16 * K, 16 * J, lane));
+        for (int L = 0; L < 2; ++L) a64[K][L] = row4<LDP>(A, 16 * (K + 2), 16 * L, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // 8 x 8
+    {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) {
+                const float a = (float)a8[i][j >> 2][j & 3];
+                if (j & 1) s1 = fmaf(a, x[j], s1);
+                else s0 = fmaf(a, x[j], s0);
             }
+            x[i] = ((i == cc) ? 1.f : 0.f) - (s0 + s1);
         }
-        // T_IJ = -T_II M, formed transposed as M^T T_II^T so that this lane
-        // holds row 16I + r, columns 16J + 4g .. + 3 and stores them at once
 #pragma unroll
-        for (int J = 0; J < 4 - d; ++J) {
-            const int I = J + d;
-            f16x4 tb = *(const f16x4 *)&Tm[(16 * I + r) * LDP + 16 * I + 4 * g];
+        for (int i = 0; i < 8; ++i) Tm[(8 * b8 + i) * LDP + 8 * b8 + cc] = (_Float16)(x[i] - (i == cc ? 1.f : 0.f));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 16 x 16: W = A21 T11 as the 16x16 product Atilde T8 (Atilde: A's
+    // lower-left quadrant of the block, T8: the two 8x8 inverses), then
+    // the quadrant -T8 W.  D-layout entry (4g + e, r) is in the lower-left
+    // quadrant when g >= 2 and r < 8; row entry (r, 4g + e) when r >= 8 and
+    // g < 2.
+    {
+        f16x4 tc[4], tr[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * g + e == r) tb[e] = (_Float16)1.f;  // T_II = I + strict(T_II)
-            // M enters as fp16 hi + lo parts, so T_II M keeps ~22 bits of M
-            f16x4 mh, ml;
+        for (int B = 0; B < 4; ++B) {
+            tc[B] = col4_tr<LDP>(Tm, 16 * B, 16 * B, lane);
+            tr[B] = row4<LDP>(Tm, 16 * B, 16 * B, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 W[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                mh[e] = (_Float16)M[J][e];
-                ml[e] = (_Float16)(M[J][e] - (float)mh[e]);
+        for (int B = 0; B < 4; ++B)
+            W[B] = mma_f16_block(zero4(), ll_row ? a16[B] : z4, plus_eye(ll_col ? z4 : tc[B], lane));
+#pragma unroll
+        for (int B = 0; B < 4; ++B) {
+            const f16x4 t8 = plus_eye(ll_row ? z4 : tr[B], lane);
+            f16x4 wh, wl;
+            split_hl(wh, wl, W[B]);
+            const f32x4 res = mma_f16_block(mma_f16_block(zero4(), wh, t8), wl, t8);
+            if (ll_row) *(f16x4 *)&Tm[(16 * B + r) * LDP + 16 * B + 4 * g] = -__builtin_convertvector(res, f16x4);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 32 x 32: blocks (1,0) and (3,2)
+    {
+        f16x4 tc[2], tr[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            tc[p] = col4_tr<LDP>(Tm, 32 * p, 32 * p, lane);
+            tr[p] = row4<LDP>(Tm, 32 * p + 16, 32 * p + 16, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 W[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) W[p] = mma_f16_block(zero4(), a32[p], plus_eye(tc[p], lane));
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const f16x4 ti = plus_eye(tr[p], lane);
+            f16x4 wh, wl;
+            split_hl(wh, wl, W[p]);
+            const f32x4 res = mma_f16_block(mma_f16_block(zero4(), wh, ti), wl, ti);
+            *(f16x4 *)&Tm[(32 * p + 16 + r) * LDP + 32 * p + 4 * g] = -__builtin_convertvector(res, f16x4);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 64 x 64: Z_KJ = A_K0 T_0J + A_K1 T_1J (K = 2, 3; J = 0, 1; T_01 is an
+    // upper tile, zero), then block (I, J) = -(T_I2 Z_2J + T_I3 Z_3J)
+    {
+        f16x4 tc[2][2], tr[2][2];
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int L = 0; L < 2; ++L) tc[J][L] = col4_tr<LDP>(Tm, 16 * L, 16 * J, lane);
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+#pragma unroll
+            for (int K = 0; K < 2; ++K) tr[I][K] = row4<LDP>(Tm, 16 * (I + 2), 16 * (K + 2), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 Z[2][2];
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+            const f16x8 b = cat8(J == 0 ? plus_eye(tc[J][0], lane) : tc[J][0], J == 1 ? plus_eye(tc[J][1], lane) : tc[J][1]);
+#pragma unroll
+            for (int K = 0; K < 2; ++K)
+                Z[K][J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(a64[K][0], a64[K][1]), b, zero4(), 0, 0, 0);
+        }
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+            const f16x8 bt = cat8(I == 0 ? plus_eye(tr[I][0], lane) : tr[I][0], I == 1 ? plus_eye(tr[I][1], lane) : tr[I][1]);
+#pragma unroll
+            for (int J = 0; J < 2; ++J) {
+                f16x4 h2, l2, h3, l3;
+                split_hl(h2, l2, Z[0][J]);
+                split_hl(h3, l3, Z[1][J]);
+                f32x4 res = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(h2, h3), bt, zero4(), 0, 0, 0);
+                res = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(l2, l3), bt, res, 0, 0, 0);
+                *(f16x4 *)&Tm[(16 * (I + 2) + r) * LDP + 16 * J + 4 * g] = -__builtin_convertvector(res, f16x4);
             }
-            const f32x4 res = mma_f16_block(mma_f16_block(zero4(), mh, tb), ml, tb);
-            f16x4 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (_Float16)(-res[e]);
-            *(f16x4 *)&Tm[(16 * I + r) * LDP + 16 * J + 4 * g] = out;
         }
     }
 }
