@@ -185,15 +185,27 @@ def bench_gdn(args, wl):
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k1_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    k2_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    if fused:
+        # one kernel per step: events around the whole timed region give its
+        # average launch duration without per-launch event gaps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(args.steps):
+            step(sets[i % len(sets)])
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k1_ms, k2_ms = e0.elapsed_time(e1) / args.steps, 0.0
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(sets[i % len(sets)], evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k1_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        k2_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms = wall * 1e3 / args.steps
     if fused:
         kernels = {"fused_kernel": k1_ms * 1e3}
@@ -576,8 +588,9 @@ def bench_layer(args, wl):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps; the GPU clock needs ~50 ms of load to settle")
     ap.add_argument("--workload", default="layer_bf16",
                     choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "decode2_bf16", "gdn2_bf16",
                              "layer_bwd_bf16", "gdn2_bwd_bf16", "layer_full_bf16"])
