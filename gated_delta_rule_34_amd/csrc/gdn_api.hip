@@ -99,6 +99,9 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const Range rg{g, ntok * 4}, rb{beta, ntok * 4}, rh0{h0, h0 ? nstate : 0};
     const Range ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0};
     const bool fused = dtype == GDN_BF16;
+    // the fused kernel moves q, k, v rows and output rows in 16-byte pieces
+    if (fused && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)))
+        return GDN_ERR_INVALID_ARG;
     const ChunkWs lay = chunk_ws(B, T, H);
     const Range rws{fused ? nullptr : ws, lay.total};
     // Outputs may not overlap inputs, each other or the workspace; ht may be exactly h0.
@@ -266,6 +269,7 @@ gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, con
         return GDN_ERR_INVALID_ARG;
     if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
     if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_INVALID_ARG;
     const size_t es = esize(dtype);
     const size_t ntok = (size_t)total_T * H;
     const size_t nstate = (size_t)N * H * Dk * Dv * sizeof(float);

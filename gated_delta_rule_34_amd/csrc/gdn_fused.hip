@@ -2,10 +2,10 @@
 // inputs on gfx950.
 //
 // One workgroup owns (batch b, head h, a 32-wide slice of value columns) and
-// walks the 64-token chunks of that head in order.  Its four waves split
-// into two roles that run concurrently on the four SIMDs of a CU:
+// walks the 64-token chunks of that head in order.  Its five waves run
+// concurrently, each in a role of its own:
 //
-//   consumers (waves 0, 1; 16 value columns each) -- the state chain of
+//   consumers (waves 1, 2; 16 value columns each) -- the state chain of
 //     chunk c, with their d_k x 16 slice of the state S resident in MFMA
 //     accumulators:
 //       X = K S, Y = Q S
@@ -13,24 +13,25 @@
 //       Vnew = R + (T - I) R           (= U - W S of the WY form)
 //       O = scale (diag(gamma) Y + diag(q.k) Vnew + strict(P) Vnew)
 //       S = gamma_C S + (K . 2^(G2_C - G2))^T Vnew
-//   producers (waves 2, 3) -- everything of chunk c + 1 that does not depend
-//     on the state, written to the other half of double-buffered LDS:
-//       wave 2: the chunk-local cumsum G2 = log2(e) cumsum(g) (so each decay is
-//         one exp2 of a non-positive difference), A = strictly-lower(
-//         diag(beta) K K^T . 2^(G2_i - G2_j)) on bf16 MFMA straight from the
-//         raw inputs, and T = (I + A)^-1 -- diagonal 16x16 blocks by forward
-//         substitution (one lane per column), off-diagonal blocks by
-//         T_IJ = -T_II sum_K A_IK T_KJ on MFMA;
-//       wave 3: P = (Q K^T) . 2^(G2_i - G2_j) (causal, diagonal kept apart in
-//         fp32), the decayed keys K . 2^(G2_C - G2) transposed, V, gamma,
-//         beta, and the fp16 copies of K and Q the consumers read.
-//   Both producers keep the raw inputs of the next two chunks in registers
-//   (loads for chunk c + 2 are issued while chunk c + 1 is processed).
+//   producers -- everything that does not depend on the state, written to
+//     the other half of double-buffered LDS:
+//       wave 4 (chunk c + 2): the chunk-local cumsum G2 = log2(e) cumsum(g)
+//         (so each decay is one exp2 of a non-positive difference) and
+//         A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j)) on bf16 MFMA
+//         straight from raw K rows it loads into registers;
+//       wave 0 (chunk c + 1): T = (I + A)^-1 by block doubling
+//         (unit_lower_inverse);
+//       wave 3 (chunk c + 1): P = (Q K^T) . 2^(G2_i - G2_j) (causal, diagonal
+//         kept apart in fp32), the decay of each key to the chunk end, V,
+//         gamma, beta, and the raw Q rows of chunk c + 2 (the A producer
+//         stores the raw K rows of its chunk).
+//   Producers that load keep the raw inputs of their next chunk in
+//   registers, loaded an iteration before they are used.  With waves placed
+//   on SIMDs in turn, the A producer shares a SIMD with the inverse, whose
+//   time is mostly LDS and MFMA latency.
 //
-// Per chunk the workgroup synchronises twice: after phase 1 (consumer X, Y,
-// R, Vnew | producer A, P tiles) and after phase 2 (consumer output and
-// state carry | producer inverse and staging).  Buffers written by the
-// producers in a phase are never the ones the consumers read in it.
+// Per chunk the workgroup synchronises once, at the end of the iteration.
+// Buffers written in an iteration are never the ones read in it.
 //
 // Precision: products of exact bf16 inputs (K K^T, Q K^T) run on bf16 MFMA;
 // the state reads K S and Q S run on bf16 MFMA with the fp32 state split
@@ -43,6 +44,8 @@
 
 namespace gdn {
 
+constexpr int kFusedThreads = 320;  // five waves
+
 template <int DK, int DV>
 struct FusedCfg {
     static constexpr int BV = 32;
@@ -54,11 +57,13 @@ struct FusedCfg {
 };
 
 // The raw K and Q rows of chunk c sit in buffer c % 3: they are written two
-// iterations ahead (chunk c + 2 in iteration c), read by both producers one
-// iteration ahead and by the consumers in iteration c.  Everything else the
-// consumers read for a chunk is double-buffered (index = chunk parity).  One
-// barrier per iteration separates every write from its reads.  A is private
-// to the inverse producer.
+// iterations ahead (chunk c + 2 in iteration c, K by the A producer, Q by the
+// P producer), read by the P producer one
+// iteration ahead and by the consumers in iteration c.  A of chunk c is
+// written in iteration c - 2 and inverted in iteration c - 1 (index = chunk
+// parity).  Everything else the consumers read for a chunk is
+// double-buffered (index = chunk parity).  One barrier per iteration
+// separates every write from its reads.
 template <int DK, int DV>
 struct FusedSmem {
     using C = FusedCfg<DK, DV>;
@@ -68,12 +73,11 @@ struct FusedSmem {
     alignas(16) _Float16 Tm[2][BT * C::LDP];
     alignas(16) uint16_t V[2][BT * C::LDV];
     alignas(16) float gam[2][BT];
-    alignas(16) float gs[2][BT];               // scale * gam
     alignas(16) float beta[2][BT];
     alignas(16) float diag[2][BT];             // scale * (q_i . k_i)
     alignas(16) float dk[2][BT];              // 2^(G2_last - G2_j): decay of key j to the chunk end
-    alignas(16) _Float16 A[BT * C::LDP];
-    alignas(16) float g2T[BT], betaT[BT];  // gate tables private to the inverse producer
+    alignas(16) _Float16 A[2][BT * C::LDP];
+    alignas(16) float g2A[BT], betaA[BT];  // gate tables private to the A producer
     alignas(16) float g2P[BT];             // ... and to the P producer
 };
 
@@ -138,25 +142,19 @@ __device__ __forceinline__ void finish_gates(float &gv, float &bv, const HeadArg
     bv = in ? bv : 0.f;
 }
 
-// Raw K and Q rows held in registers into kq-buffer `kb` in the paired-group
-// layout (the two 4-column halves of a register go to their stored groups).
-template <int DK, int DV>
-__device__ __forceinline__ void write_kq(FusedSmem<DK, DV> &sm, const ChunkRegs<DK / 32> &R, int kb, int lane) {
-    using C = FusedCfg<DK, DV>;
+// Raw rows held in registers (k or q of ChunkRegs) into a kq-buffer tile in
+// the paired-group layout (the two 4-column halves of a register go to
+// their stored groups).
+template <int DK>
+__device__ __forceinline__ void write_rows(uint16_t *dst, const uint4 (&src)[4][DK / 32], int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
+        for (int s = 0; s < DK / 32; ++s) {
             const int row = 16 * I + r, c0 = 32 * s + 8 * g;
-            uint16_t *q0 = &sm.Q[kb][tile_off_pg<DK>(row, pair_col(c0))];
-            uint16_t *q1 = &sm.Q[kb][tile_off_pg<DK>(row, pair_col(c0 + 4))];
-            uint16_t *k0 = &sm.K[kb][tile_off_pg<DK>(row, pair_col(c0))];
-            uint16_t *k1 = &sm.K[kb][tile_off_pg<DK>(row, pair_col(c0 + 4))];
-            *(uint2 *)q0 = make_uint2(R.q[I][s].x, R.q[I][s].y);
-            *(uint2 *)q1 = make_uint2(R.q[I][s].z, R.q[I][s].w);
-            *(uint2 *)k0 = make_uint2(R.k[I][s].x, R.k[I][s].y);
-            *(uint2 *)k1 = make_uint2(R.k[I][s].z, R.k[I][s].w);
+            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(src[I][s].x, src[I][s].y);
+            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(src[I][s].z, src[I][s].w);
         }
 }
 
@@ -180,32 +178,42 @@ __device__ __forceinline__ void lower_tiles(f32x4 (&acc)[10], const uint16_t *X,
     }
 }
 
-// ------------------------------------------------------- producer: A and T
-// Chunk c1 (its K rows in kq-buffer c1 % 3) into T - I of LDS half c1 & 1;
-// R holds the gates of chunk c1 and receives those of c1 + 1.
+// ------------------------------------------------------------ producer: A
+// Chunk c2 into A of LDS half c2 & 1, from the raw K rows and gates of
+// chunk c2 held in R, which also go to kq-buffer c2 % 3 for the P producer
+// and the consumers; R then receives those of chunk c2 + 1.  Both MFMA
+// operands are the same register fragments (row 16I + r, columns 32s + 8g
+// .. + 7), so K_J K_I^T needs no particular k-slot order.
 template <int DK, int DV>
-__device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int NT,
+__device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c2, int NT,
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    finish_gates(R.g, R.beta, ha, c1, lane);
-    sm.g2T[lane] = chunk_g2(R.g);
-    sm.betaT[lane] = R.beta;
-    load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
+    write_rows<DK>(sm.K[c2 % 3], R.k, lane);
+    finish_gates(R.g, R.beta, ha, c2, lane);
+    sm.g2A[lane] = chunk_g2(R.g);
+    sm.betaA[lane] = R.beta;
+    load_gates(R.g, R.beta, ha, min(c2 + 1, NT - 1), lane);
     // K_J K_I^T: this lane gets row i = 16I + r and columns j = 16J + 4g + e
     // of every tile, stored as 4 adjacent halves
     f32x4 acc[10];
-    const uint16_t *Kt = sm.K[c1 % 3];
-    lower_tiles<DK>(acc, Kt, Kt, lane);
+#pragma unroll
+    for (int t = 0; t < 10; ++t) acc[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+        for (int t = 0; t < 10; ++t) acc[t] = mma_bf16_raw(acc[t], R.k[tileJ(t)][s], R.k[tileI(t)][s]);
+    load_rows<DK>(R.k, ha.k, ha, min(c2 + 1, NT - 1), lane);
     float rowG2[4], rowB[4];
     f32x4 colG2[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        rowG2[I] = sm.g2T[16 * I + r];
-        rowB[I] = sm.betaT[16 * I + r];
-        colG2[I] = *(const f32x4 *)&sm.g2T[16 * I + 4 * g];
+        rowG2[I] = sm.g2A[16 * I + r];
+        rowB[I] = sm.betaA[16 * I + r];
+        colG2[I] = *(const f32x4 *)&sm.g2A[16 * I + 4 * g];
     }
     // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j))
+    _Float16 *A = sm.A[c2 & 1];
 #pragma unroll
     for (int tile = 0; tile < 10; ++tile) {
         const int I = tileI(tile), J = tileJ(tile);
@@ -217,15 +225,14 @@ __device__ __forceinline__ void produce_T(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
             const float val = acc[tile][e] * rowB[I] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
             hv[e] = (_Float16)((i > j) ? val : 0.f);
         }
-        *(f16x4 *)&sm.A[i * C::LDP + 16 * J + 4 * g] = hv;
+        *(f16x4 *)&A[i * C::LDP + 16 * J + 4 * g] = hv;
     }
-    unit_lower_inverse<C::LDP>(sm.A, sm.Tm[c1 & 1], lane);
 }
 
 // ------------------------------------------- producer: P and consumer inputs
 // Chunk c1: V, gate tables and P into LDS half c1 & 1 (P from the K and Q
 // rows in kq-buffer c1 % 3).  R holds V and the gates of chunk c1 and the raw
-// K, Q rows of chunk c1 + 1; those rows go to kq-buffer (c1 + 1) % 3 and R
+// Q rows of chunk c1 + 1; those rows go to kq-buffer (c1 + 1) % 3 and R
 // receives the rows of chunk c1 + 2, a full iteration before they are stored.
 template <int DK, int DV>
 __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int NT,
@@ -234,8 +241,8 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     const int r = lane & 15, g = lane >> 4;
     const int buf = c1 & 1;
     // first store everything that arrived during the previous iteration: the
-    // V tile, the gates and the raw rows of chunk c1 + 1 (when it is past the
-    // end, its buffer is written but never read)
+    // V tile, the gates and the raw Q rows of chunk c1 + 1 (when it is past
+    // the end, its buffer is written but never read)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
@@ -246,14 +253,12 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     sm.g2P[lane] = G2;
     const float gmv = __builtin_amdgcn_exp2f(G2);
     sm.gam[buf][lane] = gmv;
-    sm.gs[buf][lane] = scale * gmv;
     sm.beta[buf][lane] = R.beta;
-    write_kq(sm, R, (c1 + 1) % 3, lane);
+    write_rows<DK>(sm.Q[(c1 + 1) % 3], R.q, lane);
     // then fetch the next ones together (indices clamped to the last chunk)
     load_v<DV>(R.v, ha, min(c1 + 1, NT - 1), lane);
     load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
     load_rows<DK>(R.q, ha.q, ha, min(c1 + 2, NT - 1), lane);
-    load_rows<DK>(R.k, ha.k, ha, min(c1 + 2, NT - 1), lane);
     const float G2L = sm.g2P[BT - 1];
     sm.dk[buf][lane] = __builtin_amdgcn_exp2f(G2L - G2);
     // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
@@ -286,8 +291,8 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 // ---------------------------------------------------------------- consumers
 template <int DK, int DV>
 __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, int kb,
-                                        float *__restrict__ o,
-                                        const HeadArgs &ha, int chunk, int wave, int lane) {
+                                        float *__restrict__ o, const HeadArgs &ha, int chunk, int cw, float scale,
+                                        int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
     // X = K S and Y = Q S on bf16 MFMA: exact bf16 K, Q against the state
@@ -314,14 +319,14 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     // R = beta (V - gamma X); V[16I + 4g + e][this wave's column r] by
     // transpose loads of the row-major V tile
     f32x4 Rr[4];
-    const int cl = wave * 16 + r;
+    const int cl = cw * 16 + r;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
         const f32x4 bet = *(const f32x4 *)&sm.beta[buf][16 * I + 4 * g];
         const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)&sm.V[buf][(16 * I + 4 * g + (r >> 2)) * C::LDV + wave * 16 + 4 * (r & 3)]);
+            (lds_s16x4 *)&sm.V[buf][(16 * I + 4 * g + (r >> 2)) * C::LDV + cw * 16 + 4 * (r & 3)]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float vv = __uint_as_float(((uint32_t)(uint16_t)vt[e]) << 16);
@@ -344,22 +349,20 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         }
     }
     // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew), with scale folded
-    // into the gs, diag and P tables
+    // into the diag and P tables
     _Float16 vf[2][8];
     frag_from_acc(vf[0], Vn[0], Vn[1]);
     frag_from_acc(vf[1], Vn[2], Vn[3]);
     const int t0 = chunk * BT;
-    const int col = ha.vcol0 + cl;
     const bool full = t0 + BT <= ha.T;
-    float *obase = o + ((ha.tok0 + t0) * ha.H + ha.h) * (long)DV + col;
     const long ostride = (long)ha.H * DV;
     f32x4 O[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        const f32x4 gs = *(const f32x4 *)&sm.gs[buf][16 * I + 4 * g];
+        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
         const f32x4 dg = *(const f32x4 *)&sm.diag[buf][16 * I + 4 * g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[I][e] = gs[e] * Y[I][e] + dg[e] * Vn[I][e];
+        for (int e = 0; e < 4; ++e) O[I][e] = (scale * gm[e]) * Y[I][e] + dg[e] * Vn[I][e];
 #pragma unroll
         for (int s = 0; s <= (I >> 1); ++s) {
             _Float16 a[8];
@@ -367,20 +370,24 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             O[I] = mma_slab(O[I], a, vf[s]);
         }
     }
-    // row 16I + 4g + e of the chunk: the lane's base row 4g, plus a
-    // wave-uniform offset
-    float *ob = obase + (4 * g) * ostride;
-    if (full) {
+    // Stores: a 4 x 4 transpose within each quad of lanes (DPP quad
+    // permutations) gives lane (g, 4a + b) row 16I + 4g + b and columns
+    // 4a .. 4a + 3 of this wave's 16, so each row block is one 16-byte store
+    // per lane (four store instructions per chunk instead of sixteen).
+    const int qb = r & 3;
+    float *ob = o + ((ha.tok0 + t0 + 4 * g + qb) * ha.H + ha.h) * (long)DV + ha.vcol0 + cw * 16 + 4 * (r >> 2);
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I) {
+        f32x4 v = O[I], p;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ob[(16 * I + e) * ostride] = O[I][e];
-    } else {
+        for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0xB1, 0xf>(v[e]);  // from lane qb ^ 1
+        if (qb & 1) v = f32x4{p[1], v[1], p[3], v[3]};
+        else v = f32x4{v[0], p[0], v[2], p[2]};
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (t0 + 16 * I + 4 * g + e < ha.T) ob[(16 * I + e) * ostride] = O[I][e];
+        for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0x4E, 0xf>(v[e]);  // from lane qb ^ 2
+        if (qb & 2) v = f32x4{p[2], p[3], v[2], v[3]};
+        else v = f32x4{v[0], v[1], p[0], p[1]};
+        if (full || t0 + 16 * I + 4 * g + qb < ha.T) *(f32x4 *)&ob[16 * I * ostride] = v;
     }
     // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =
     // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
@@ -413,7 +420,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ k,
                                                        const uint16_t *__restrict__ v,
                                                        const float *__restrict__ gin,
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
 
     // The upper tiles (0,1) and (2,3) of P and T - I are read by the 32-wide
     // slabs of the consumers but never written: zero them once.
-    for (int idx = tid; idx < 2 * BT * C::LDP; idx += 256) {
+    for (int idx = tid; idx < 2 * BT * C::LDP; idx += kFusedThreads) {
         (&sm.P[0][0])[idx] = (_Float16)0.f;
         (&sm.Tm[0][0])[idx] = (_Float16)0.f;
     }
@@ -463,18 +470,20 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
     // Each role runs its own loop with the same barrier count (one per
     // iteration), so the registers of one role are never live in another.
     // Iteration c: consumers walk chunk c (LDS half c & 1, kq-buffer c % 3);
-    // producers prepare chunk c + 1, the P producer also stores the raw rows
-    // of chunk c + 2 and fetches chunk c + 3.
-    if (wave < 2) {
+    // the inverse and the P producer prepare chunk c + 1, the P producer also
+    // stores the raw rows of chunk c + 2 and fetches chunk c + 3; the A
+    // producer prepares chunk c + 2.
+    if (wave == 1 || wave == 2) {
+        const int cw = wave - 1;
         f32x4 S[C::NKB];
-        const int col = ha.vcol0 + wave * 16 + r;
+        const int col = ha.vcol0 + cw * 16 + r;
 #pragma unroll
         for (int m = 0; m < C::NKB; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c >= 0) consume(sm, S, c & 1, c % 3, o, ha, c, wave, lane);
+            if (c >= 0) consume(sm, S, c & 1, c % 3, o, ha, c, cw, scale, lane);
             __syncthreads();
         }
         if (ht) {
@@ -483,25 +492,34 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(const uint16_t *__restric
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
         }
-    } else if (wave == 2) {
-        ChunkRegs<C::NS> R;
-        if (NT > 0) load_gates(R.g, R.beta, ha, 0, lane);
+    } else if (wave == 0) {
         __syncthreads();
         for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) produce_T(sm, R, c + 1, NT, ha, lane);
+            if (c + 1 < NT) unit_lower_inverse<C::LDP>(sm.A[(c + 1) & 1], sm.Tm[(c + 1) & 1], lane);
+            __syncthreads();
+        }
+    } else if (wave == 4) {
+        // A of chunk 0 before the first barrier; then chunk c + 2 in iteration c
+        ChunkRegs<C::NS> R;
+        if (NT > 0) {
+            load_gates(R.g, R.beta, ha, 0, lane);
+            load_rows<DK>(R.k, k, ha, 0, lane);
+            produce_A(sm, R, 0, NT, ha, lane);
+        }
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c + 2 < NT) produce_A(sm, R, c + 2, NT, ha, lane);
             __syncthreads();
         }
     } else {
         ChunkRegs<C::NS> R;
-        // chunk 0's raw rows go to kq-buffer 0 before the first barrier;
+        // chunk 0's raw Q rows go to kq-buffer 0 before the first barrier;
         // chunk 1's wait in registers (an empty sequence loads nothing)
         if (NT > 0) {
-            load_rows<DK>(R.k, k, ha, 0, lane);
             load_rows<DK>(R.q, q, ha, 0, lane);
             load_v<DV>(R.v, ha, 0, lane);
             load_gates(R.g, R.beta, ha, 0, lane);
-            write_kq(sm, R, 0, lane);
-            load_rows<DK>(R.k, k, ha, min(1, NT - 1), lane);
+            write_rows<DK>(sm.Q[0], R.q, lane);
             load_rows<DK>(R.q, q, ha, min(1, NT - 1), lane);
         }
         __syncthreads();
@@ -517,7 +535,7 @@ static hipError_t launch_fused_t(const void *q, const void *k, const void *v, co
                                  const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H,
                                  float scale, hipStream_t st) {
     const long grid = (long)B * H * (DV / FusedCfg<DK, DV>::BV);
-    hipLaunchKernelGGL((fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t *)q,
+    hipLaunchKernelGGL((fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(kFusedThreads), 0, st, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, o, ht, cu_seqlens, T, H, scale);
     return hipGetLastError();
 }

@@ -81,7 +81,8 @@ size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dt
  *   ht     [B, H, Dk, Dv] fp32, nullable final state; may alias h0 exactly
  *   scale  read-out scale (1/sqrt(Dk) in the pages' layer)
  *   ws, ws_bytes  device workspace of at least gdn_chunk_fwd_workspace(...) bytes
- * No other aliasing between arguments is allowed.
+ * No other aliasing between arguments is allowed.  With bf16 inputs q, k, v
+ * and o must be 16-byte aligned (GDN_ERR_INVALID_ARG otherwise).
  */
 gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *g, const float *beta, const float *h0,

@@ -52,6 +52,24 @@ def test_sequence_lengths(T):
         _check(x, o, S)
 
 
+def test_bf16_output_must_be_16_byte_aligned():
+    """bf16 inputs run the fused kernel, which stores output rows in 16-byte
+    pieces: an output view 4 bytes off alignment is refused before any launch
+    (nothing written); a 16-byte-aligned view of the same buffer gives the
+    result of a fresh output tensor."""
+    import torch
+    x = gi.gdn_inputs(1, 70, 2, 64, 64, seed=77, dtype="bf16")
+    args = gdn_dev_args(x)
+    n = 70 * 2 * 64
+    buf = torch.zeros(n + 8, dtype=torch.float32, device=args[0].device)
+    with pytest.raises(RuntimeError, match="status 1"):
+        gdn.gdn_chunk_fwd(*args, scale=x["scale"], out=buf[1:1 + n].view(1, 70, 2, 64))
+    assert int(torch.count_nonzero(buf)) == 0
+    o, _ = gdn.gdn_chunk_fwd(*args, scale=x["scale"], out=buf[4:4 + n].view(1, 70, 2, 64))
+    ref, _ = _run(x)
+    np.testing.assert_array_equal(host(o), ref)
+
+
 def test_layer_shape_reduced_bf16():
     """Layer-shaped bf16 case (d=128) at reduced batch and length: 5 chunks + tail."""
     x = gi.gdn_inputs(2, 300, 4, 128, 128, seed=1001, dtype="bf16")
