@@ -461,13 +461,16 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
             Vn[I] = mma_slab(Vn[I], a, rf[s]);
         }
     }
-    // O = scale (Y + diag(P) Vnew + strict(P) Vnew)
+    // O = scale (Y + diag(P) Vnew + strict(P) Vnew); each row block leaves
+    // the MFMA as 4 rows of one column per lane and is stored, after a quad
+    // transpose, as 4 adjacent columns of one row (16 bytes per lane)
     _Float16 vf[2][8];
     frag_from_acc(vf[0], Vn[0], Vn[1]);
     frag_from_acc(vf[1], Vn[2], Vn[3]);
     const int t0 = chunk * BT;
     const bool full = t0 + BT <= hd.T;
-    float *obase = o + (hd.row0 + (long)t0 * hd.H) * DV + hd.vcol0 + cl;
+    const int qb = r & 3;
+    float *ob = o + (hd.row0 + (long)(t0 + 4 * g + qb) * hd.H) * DV + hd.vcol0 + wave * 16 + 4 * (r >> 2);
     const long ostride = (long)hd.H * DV;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -481,11 +484,8 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
             frag_rows(a, sm.P[buf], C::LDP, 16 * I, 32 * s, lane);
             acc = mma_slab(acc, a, vf[s]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ti = 16 * I + 4 * g + e;
-            if (full || t0 + ti < hd.T) obase[ti * ostride] = scale * acc[e];
-        }
+        const f32x4 v = quad_transpose(acc * scale, lane);
+        if (full || t0 + 16 * I + 4 * g + qb < hd.T) *(f32x4 *)&ob[16 * I * ostride] = v;
     }
     // S = Diag(Gamma_C) S + Khat^T Vnew, Khat^T by transpose loads, Vnew as fp16 hi + lo
     uint4 vh[2], vl[2];

@@ -192,6 +192,10 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const flo
     if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN_ERR_INVALID_ARG;
     if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
     if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    // the bf16 kernels move q, k, v, b, w rows and output rows in 16-byte pieces
+    if (dtype == GDN_BF16 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(b, 16) ||
+                              !aligned(w, 16) || !aligned(o, 16)))
+        return GDN_ERR_INVALID_ARG;
     const size_t es = esize(dtype);
     const size_t ntok = (size_t)B * T * H;
     const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);

@@ -378,15 +378,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     float *ob = o + ((ha.tok0 + t0 + 4 * g + qb) * ha.H + ha.h) * (long)DV + ha.vcol0 + cw * 16 + 4 * (r >> 2);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        f32x4 v = O[I], p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0xB1, 0xf>(v[e]);  // from lane qb ^ 1
-        if (qb & 1) v = f32x4{p[1], v[1], p[3], v[3]};
-        else v = f32x4{v[0], p[0], v[2], p[2]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0x4E, 0xf>(v[e]);  // from lane qb ^ 2
-        if (qb & 2) v = f32x4{p[2], p[3], v[2], v[3]};
-        else v = f32x4{v[0], v[1], p[0], p[1]};
+        const f32x4 v = quad_transpose(O[I], lane);
         if (full || t0 + 16 * I + 4 * g + qb < ha.T) *(f32x4 *)&ob[16 * I * ostride] = v;
     }
     // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =

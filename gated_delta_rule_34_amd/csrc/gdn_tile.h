@@ -162,6 +162,24 @@ __device__ __forceinline__ float dpp_f32(float x) {
                                                                  false));
 }
 
+// 4 x 4 transpose within each quad of lanes (DPP quad permutations): lane
+// 4a + b holds v[e] = M[e][b] of its quad's 4 x 4 block on entry and
+// M[b][e] on return.  Used to turn an MFMA accumulator tile (4 rows of one
+// column per lane) into 4 adjacent columns of one row per lane.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
+    const int b = lane & 3;
+    f32x4 p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0xB1, 0xf>(v[e]);  // from lane b ^ 1
+    if (b & 1) v = f32x4{p[1], v[1], p[3], v[3]};
+    else v = f32x4{v[0], p[0], v[2], p[2]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0x4E, 0xf>(v[e]);  // from lane b ^ 2
+    if (b & 2) v = f32x4{p[2], p[3], v[2], v[3]};
+    else v = f32x4{v[0], v[1], p[0], p[1]};
+    return v;
+}
+
 // log2(e) * chunk-local inclusive cumsum of g, one token per lane: an fp32
 // wave scan on DPP (shifts 1, 2, 4, 8 within each row of 16 lanes, then the
 // row totals broadcast by lane 15 and lane 31), no LDS round trip.

@@ -127,6 +127,8 @@ size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype d
  *   b          [B, T, H, Dk] dtype   erase gate (key channels)
  *   w          [B, T, H, Dv] dtype   write gate (value channels)
  *   h0, o, ht, scale, ws, ws_bytes, stream: as gdn_chunk_fwd.
+ * With bf16 inputs q, k, v, b, w and o must be 16-byte aligned
+ * (GDN_ERR_INVALID_ARG otherwise).
  */
 gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                           const float *log_alpha, const void *b, const void *w,

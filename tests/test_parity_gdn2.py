@@ -39,6 +39,24 @@ def test_head_sizes_ragged(dtype, Dk, Dv):
     _check(x, o, S)
 
 
+def test_bf16_output_must_be_16_byte_aligned():
+    """The bf16 walk stores output rows in 16-byte pieces: an output view 4
+    bytes off alignment is refused before any launch (nothing written); a
+    16-byte-aligned view of the same buffer gives the result of a fresh
+    output tensor."""
+    import torch
+    x = gi.gdn2_inputs(1, 70, 2, 64, 64, seed=78, dtype="bf16", h0=True)
+    args = [dev(x[n]) for n in NAMES]
+    n = 70 * 2 * 64
+    buf = torch.zeros(n + 8, dtype=torch.float32, device=args[0].device)
+    with pytest.raises(RuntimeError, match="status 1"):
+        gdn.gdn2_chunk_fwd(*args, scale=x["scale"], out=buf[1:1 + n].view(1, 70, 2, 64))
+    assert int(torch.count_nonzero(buf)) == 0
+    o, _ = gdn.gdn2_chunk_fwd(*args, scale=x["scale"], out=buf[4:4 + n].view(1, 70, 2, 64))
+    ref, _ = _run(x)
+    np.testing.assert_array_equal(host(o), ref)
+
+
 @pytest.mark.parametrize("T", [1, 16, 63, 64, 65, 130])
 def test_sequence_lengths(T):
     for dtype in ("fp32", "bf16"):
