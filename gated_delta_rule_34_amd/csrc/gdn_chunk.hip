@@ -159,7 +159,9 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
     }
 }
 
-template <class Pol, int DK, int DV, int BV>
+// OUT = false: only the state chain (entry states into ck, final state),
+// for the backward's recompute; Q, P and the output are skipped.
+template <class Pol, int DK, int DV, int BV, bool OUT>
 __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *__restrict__ q,
                                                       const typename Pol::in_t *__restrict__ k,
                                                       const typename Pol::in_t *__restrict__ v,
@@ -193,7 +195,8 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
 
     // The upper tiles (0,1) and (2,3) of sP are read by the 32-wide slabs of
     // the output product but never written: they hold zeros for the whole walk.
-    for (int idx = tid; idx < BT * LDP; idx += NTHR) sP[idx] = to_mt<mt>(0.f);
+    if constexpr (OUT)
+        for (int idx = tid; idx < BT * LDP; idx += NTHR) sP[idx] = to_mt<mt>(0.f);
 
     f32x4 S[NKB];
     const long sbase = bh * (long)DK * DV;
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
         }
         // Q, K rows, the value slice and T - I of the chunk into LDS (vector
         // loads, issued ahead of their stores)
-        stage_rows<DK, LDQ, NTHR>(sQ, q, b, h, t0, T, H, 0, DK, tid);
+        if constexpr (OUT) stage_rows<DK, LDQ, NTHR>(sQ, q, b, h, t0, T, H, 0, DK, tid);
         stage_rows<DK, LDQ, NTHR>(sK, k, b, h, t0, T, H, 0, DK, tid);
         stage_rows<BV, LDV, NTHR>(sV, v, b, h, t0, T, H, vt * BV, DV, tid);
         {
@@ -252,6 +255,7 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
             sKt[kc * LDKT + j] = to_mt<mt>((float)sK[j * LDQ + kc] * sDecK[j]);
         }
         // P^T tiles (K_J Q_I^T): lane gets P[16I + r][16J + 4g + e].
+        if constexpr (OUT)
         for (int tile = wave; tile < 10; tile += NW) {
             const int I = kTileI[tile], J = kTileJ[tile];
             f32x4 acc = zero4();
@@ -287,8 +291,10 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
                 mt a[8];
                 frag_rows(a, sK, LDQ, 16 * I, 32 * s, lane);
                 X[I] = mma_slab(X[I], a, sb);
-                frag_rows(a, sQ, LDQ, 16 * I, 32 * s, lane);
-                Y[I] = mma_slab(Y[I], a, sb);
+                if constexpr (OUT) {
+                    frag_rows(a, sQ, LDQ, 16 * I, 32 * s, lane);
+                    Y[I] = mma_slab(Y[I], a, sb);
+                }
             }
         }
         // R = beta (V - gamma X), fp32.
@@ -319,6 +325,7 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
         mt vf[2][8];
         frag_from_acc(vf[0], Vn[0], Vn[1]);
         frag_from_acc(vf[1], Vn[2], Vn[3]);
+        if constexpr (OUT)
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 acc;
@@ -396,9 +403,14 @@ static hipError_t launch_walk_t(const void *q, const void *k, const void *v, con
     const int NT = (T + BT - 1) / BT;
     const long grid = (long)B * H * (DV / BV);
     using in_t = typename Pol::in_t;
-    hipLaunchKernelGGL((walk_kernel<Pol, DK, DV, BV>), dim3((unsigned)grid), dim3(BV * 4), 0, st,
-                       (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, G2, Tinv, h0, o, ht, ck, T, H,
-                       NT, scale);
+    if (o)
+        hipLaunchKernelGGL((walk_kernel<Pol, DK, DV, BV, true>), dim3((unsigned)grid), dim3(BV * 4), 0, st,
+                           (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, G2, Tinv, h0, o, ht, ck, T, H,
+                           NT, scale);
+    else
+        hipLaunchKernelGGL((walk_kernel<Pol, DK, DV, BV, false>), dim3((unsigned)grid), dim3(BV * 4), 0, st,
+                           (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, G2, Tinv, h0, o, ht, ck, T, H,
+                           NT, scale);
     return hipGetLastError();
 }
 
