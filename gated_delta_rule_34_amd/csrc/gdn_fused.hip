@@ -348,6 +348,36 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             Vn[I] = mma_slab(Vn[I], a, rf[s]);
         }
     }
+    // The state carry comes first: it is what the next chunk waits for, and
+    // the output work below overlaps its MFMAs.
+    // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =
+    // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
+    // straight from the raw K tile by transpose loads, and d . Vnew enters as
+    // bf16 hi + lo parts.
+    uint4 dvh[2], dvl[2];
+    {
+        f32x4 dv[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 dd = *(const f32x4 *)&sm.dk[buf][16 * I + 4 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[I][e] = dd[e] * Vn[I][e];
+        }
+        hilo_frags<bf16x2>(dvh[0], dvl[0], dv[0], dv[1]);
+        hilo_frags<bf16x2>(dvh[1], dvl[1], dv[2], dv[3]);
+    }
+    const float gl = sm.gam[buf][BT - 1];
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m) {
+        f32x4 acc = S[m] * gl;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 a = frag_T_pg<DK>(sm.K[kb], 32 * s, 16 * m, lane);
+            acc = mma_bf16_raw(acc, a, dvh[s]);
+            acc = mma_bf16_raw(acc, a, dvl[s]);
+        }
+        S[m] = acc;
+    }
     // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew), with scale folded
     // into the diag and P tables
     _Float16 vf[2][8];
@@ -380,34 +410,6 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     for (int I = 0; I < 4; ++I) {
         const f32x4 v = quad_transpose(O[I], lane);
         if (full || t0 + 16 * I + 4 * g + qb < ha.T) *(f32x4 *)&ob[16 * I * ostride] = v;
-    }
-    // S = gamma_C S + (K . d)^T Vnew = gamma_C S + K^T (d . Vnew), d_j =
-    // 2^(G2_last - G2_j) <= 1: the decay scales the new values, K^T comes
-    // straight from the raw K tile by transpose loads, and d . Vnew enters as
-    // bf16 hi + lo parts.
-    uint4 dvh[2], dvl[2];
-    {
-        f32x4 dv[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const f32x4 dd = *(const f32x4 *)&sm.dk[buf][16 * I + 4 * g];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dv[I][e] = dd[e] * Vn[I][e];
-        }
-        hilo_frags<bf16x2>(dvh[0], dvl[0], dv[0], dv[1]);
-        hilo_frags<bf16x2>(dvh[1], dvl[1], dv[2], dv[3]);
-    }
-    const float gl = sm.gam[buf][BT - 1];
-#pragma unroll
-    for (int m = 0; m < C::NKB; ++m) {
-        f32x4 acc = S[m] * gl;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_pg<DK>(sm.K[kb], 32 * s, 16 * m, lane);
-            acc = mma_bf16_raw(acc, a, dvh[s]);
-            acc = mma_bf16_raw(acc, a, dvl[s]);
-        }
-        S[m] = acc;
     }
 }
 
