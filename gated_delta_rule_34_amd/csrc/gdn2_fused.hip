@@ -461,6 +461,26 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
             Vn[I] = mma_slab(Vn[I], a, rf[s]);
         }
     }
+    // The state carry comes first: it is what the next chunk waits for, and
+    // the output work below overlaps its MFMAs.
+    // S = Diag(Gamma_C) S + Khat^T Vnew, Khat^T by transpose loads, Vnew as fp16 hi + lo
+    uint4 vh[2], vl[2];
+    hilo_frags<f16x2>(vh[0], vl[0], Vn[0], Vn[1]);
+    hilo_frags<f16x2>(vh[1], vl[1], Vn[2], Vn[3]);
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m) {
+        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * m + 4 * g];
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = S[m][e] * gm[e];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            acc = mma_f16_raw(acc, a, vh[s]);
+            acc = mma_f16_raw(acc, a, vl[s]);
+        }
+        S[m] = acc;
+    }
     // O = scale (Y + diag(P) Vnew + strict(P) Vnew); each row block leaves
     // the MFMA as 4 rows of one column per lane and is stored, after a quad
     // transpose, as 4 adjacent columns of one row (16 bytes per lane)
@@ -486,24 +506,6 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
         }
         const f32x4 v = quad_transpose(acc * scale, lane);
         if (full || t0 + 16 * I + 4 * g + qb < hd.T) *(f32x4 *)&ob[16 * I * ostride] = v;
-    }
-    // S = Diag(Gamma_C) S + Khat^T Vnew, Khat^T by transpose loads, Vnew as fp16 hi + lo
-    uint4 vh[2], vl[2];
-    hilo_frags<f16x2>(vh[0], vl[0], Vn[0], Vn[1]);
-    hilo_frags<f16x2>(vh[1], vl[1], Vn[2], Vn[3]);
-#pragma unroll
-    for (int m = 0; m < C::NKB; ++m) {
-        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * m + 4 * g];
-        f32x4 acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = S[m][e] * gm[e];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
-            acc = mma_f16_raw(acc, a, vh[s]);
-            acc = mma_f16_raw(acc, a, vl[s]);
-        }
-        S[m] = acc;
     }
 }
 
