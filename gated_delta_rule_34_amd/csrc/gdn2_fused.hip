@@ -182,128 +182,152 @@ __device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int la
     }
 }
 
+// Persistent: workgroup w handles chunks w, w + gridDim.x, ...  The raw rows
+// and log-decays of its next chunk are fetched into registers as soon as the
+// current chunk is staged in LDS, so their latency overlaps the current
+// chunk's work.
 template <int DK>
 __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                          const float *__restrict__ la, const uint16_t *__restrict__ bg,
-                                                         char *__restrict__ ws, int T, int H, int NT) {
+                                                         char *__restrict__ ws, int T, int H, int NT, int nchunks) {
     using SM = Gdn2PrepSmem<DK>;
     using BL = Gdn2Blk<DK>;
     constexpr int NTH = 512;
     constexpr int LDR = SM::LDR, LDG = SM::LDG, LDP = SM::LDP, NG = SM::NG;
     constexpr int C8 = DK / 8;      // uint4 per row of a raw tile
     constexpr int RG = BT / NG;     // rows per cumsum group
-    __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const long cb = blockIdx.x;
-    const int c = (int)(cb % NT);
-    const long bh = cb / NT;
-    const int h = (int)(bh % H);
-    const long bb = bh / H;
-    const int t0 = c * BT;
-    const long row0 = (bb * T + t0) * H + h;  // token-head row of the chunk's first token
-    char *blk = ws + cb * (long)BL::BYTES;
-
-    // 1. raw rows (zero past T) and the per-channel cumsum of log alpha.  All
-    //    loads are issued before any is used; rows past T read the last token
-    //    (always in bounds) and are then zeroed.
     constexpr int NU = BT * C8 / NTH;  // uint4 per thread per raw tile
+    __shared__ SM sm;
+    const int tid0 = threadIdx.x;
+    const int ch = tid0 % DK, gr = tid0 / DK;  // cumsum: rows RG gr .. RG gr + RG - 1 of channel ch
     typedef __attribute__((ext_vector_type(4))) unsigned int v4u;  // native vectors stay in registers
     v4u kr[NU], qr[NU], br[NU];
-#pragma unroll
-    for (int x = 0; x < NU; ++x) {
-        const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
-        const int tr = min(t0 + row, T - 1) - t0;
-        const long off = (row0 + (long)tr * H) * DK + 8 * c8;
-        kr[x] = *(const v4u *)(k + off);
-        qr[x] = *(const v4u *)(q + off);
-        br[x] = *(const v4u *)(bg + off);
-    }
-    // thread (group gr, channel ch) scans rows RG gr .. RG gr + RG - 1 of its channel
-    const int ch = tid % DK, gr = tid / DK;
     float lv[RG];
-#pragma unroll
-    for (int x = 0; x < RG; ++x) {
-        const int tr = min(t0 + RG * gr + x, T - 1) - t0;
-        lv[x] = la[(row0 + (long)tr * H) * DK + ch];
-    }
-#pragma unroll
-    for (int x = 0; x < NU; ++x) {
-        const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
-        const bool in = t0 + row < T;
-        const v4u z = {0u, 0u, 0u, 0u};
-        *(v4u *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
-        *(v4u *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
-        *(v4u *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int x = 0; x < RG; ++x) {
-        acc += (t0 + RG * gr + x < T) ? lv[x] * 1.4426950408889634f : 0.f;
-        lv[x] = acc;
-    }
-    sm.part[gr][ch] = acc;
-    // the upper tiles of T - I and P are never written below
-    for (int u = tid; u < BT * LDP; u += NTH) {
-        sm.Tm[u] = (_Float16)0.f;
-        sm.P[u] = (_Float16)0.f;
-    }
-    __syncthreads();
-    {
-        float off = 0.f;
-        for (int x = 0; x < gr; ++x) off += sm.part[x][ch];
-#pragma unroll
-        for (int x = 0; x < RG; ++x) sm.G2[(RG * gr + x) * LDG + ch] = lv[x] + off;
-    }
-    __syncthreads();
 
-    // 2. A and P: waves 0..3 the diagonal blocks, waves 4..7 the 6 off-diagonal tiles
-    if (wave < 4) {
-        diag_block<DK>(sm, 16 * wave, lane);
-    } else {
-        offdiag_tile<DK>(sm, wave - 4, lane);
-        if (wave < 6) offdiag_tile<DK>(sm, wave, lane);
-    }
-    __syncthreads();
-
-    // 3. wave 0: T - I; the other waves: decayed operands, Gamma_C, P, diag P
-    if (wave == 0) {
-        unit_lower_inverse<LDP>(sm.A, sm.Tm, lane);
-    } else {
-        const int ot = tid - 64;  // 0 .. 447
-        for (int u = ot; u < BT * C8; u += NTH - 64) {
-            const int row = u / C8, c0 = 8 * (u % C8);
-            const uint4 kv = *(const uint4 *)&sm.k[row * LDR + c0];
-            const uint4 qv = *(const uint4 *)&sm.q[row * LDR + c0];
-            const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
-            const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
-            f16x8 eo, qo, ko;
+    // token-head row of a chunk's first token, and the chunk's first token
+    auto locate = [&](int cb, long &row0, int &t0) {  // 32-bit index math (cheap on the VALU)
+        const int bh = cb / NT;
+        t0 = (cb - bh * NT) * BT;
+        const int b = bh / H;
+        row0 = ((long)b * T + t0) * H + (bh - b * H);
+    };
+    // raw rows and log-decays of chunk cb into registers; rows past T read the
+    // last token (always in bounds) and are zeroed when staged
+    auto fetch = [&](int cb) {
+        long row0;
+        int t0;
+        locate(cb, row0, t0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
-                const float gam = __builtin_amdgcn_exp2f(G);
-                const float kf = bf16_to_f32(kk[e]);
-                eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
-                qo[e] = (_Float16)(bf16_to_f32(qq[e]) * gam);
-                ko[e] = (_Float16)(kf * __builtin_amdgcn_exp2f(GL - G));
+        for (int x = 0; x < NU; ++x) {
+            const int u = tid0 + NTH * x, row = u / C8, c8 = u % C8;
+            const int tr = min(t0 + row, T - 1) - t0;
+            const long off = (row0 + (long)tr * H) * DK + 8 * c8;
+            kr[x] = *(const v4u *)(k + off);
+            qr[x] = *(const v4u *)(q + off);
+            br[x] = *(const v4u *)(bg + off);
+        }
+#pragma unroll
+        for (int x = 0; x < RG; ++x) {
+            const int tr = min(t0 + RG * gr + x, T - 1) - t0;
+            lv[x] = la[(row0 + (long)tr * H) * DK + ch];
+        }
+    };
+
+    fetch(blockIdx.x);  // the grid never exceeds the chunk count
+    for (int cb = blockIdx.x; cb < nchunks; cb += gridDim.x) {
+        // The thread index passes through an opaque move each chunk, so that
+        // the many lane-derived LDS addresses below are formed where they are
+        // used instead of being hoisted out of the loop into registers.
+        int tid;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid0));
+        const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        long row0;
+        int t0;
+        locate(cb, row0, t0);
+        char *blk = ws + (long)cb * BL::BYTES;
+        // 1. raw rows (zero past T) and the per-channel cumsum of log alpha
+#pragma unroll
+        for (int x = 0; x < NU; ++x) {
+            const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
+            const bool in = t0 + row < T;
+            const v4u z = {0u, 0u, 0u, 0u};
+            *(v4u *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
+            *(v4u *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
+            *(v4u *)&sm.b[row * LDR + 8 * c8] = in ? br[x] : z;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < RG; ++x) {
+            acc += (t0 + RG * gr + x < T) ? lv[x] * 1.4426950408889634f : 0.f;
+            lv[x] = acc;
+        }
+        sm.part[gr][ch] = acc;
+        // the upper tiles of T - I and P are never written below
+        for (int u = tid; u < BT * LDP; u += NTH) {
+            sm.Tm[u] = (_Float16)0.f;
+            sm.P[u] = (_Float16)0.f;
+        }
+        __syncthreads();
+        {
+            float off = 0.f;
+            for (int x = 0; x < gr; ++x) off += sm.part[x][ch];
+#pragma unroll
+            for (int x = 0; x < RG; ++x) sm.G2[(RG * gr + x) * LDG + ch] = lv[x] + off;
+        }
+        // the registers are free: fetch the next chunk now
+        if (cb + gridDim.x < nchunks) fetch(cb + gridDim.x);
+        __syncthreads();
+
+        // 2. A and P: waves 0..3 the diagonal blocks, waves 4..7 the 6 off-diagonal tiles
+        if (wave < 4) {
+            diag_block<DK>(sm, 16 * wave, lane);
+        } else {
+            offdiag_tile<DK>(sm, wave - 4, lane);
+            if (wave < 6) offdiag_tile<DK>(sm, wave, lane);
+        }
+        __syncthreads();
+
+        // 3. wave 0: T - I; the other waves: decayed operands, Gamma_C, P, diag P
+        if (wave == 0) {
+            unit_lower_inverse<LDP>(sm.A, sm.Tm, lane);
+        } else {
+            const int ot = tid - 64;  // 0 .. 447
+            for (int u = ot; u < BT * C8; u += NTH - 64) {
+                const int row = u / C8, c0 = 8 * (u % C8);
+                const uint4 kv = *(const uint4 *)&sm.k[row * LDR + c0];
+                const uint4 qv = *(const uint4 *)&sm.q[row * LDR + c0];
+                const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
+                const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
+                f16x8 eo, qo, ko;
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
+                    const float gam = __builtin_amdgcn_exp2f(G);
+                    const float kf = bf16_to_f32(kk[e]);
+                    eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
+                    qo[e] = (_Float16)(bf16_to_f32(qq[e]) * gam);
+                    ko[e] = (_Float16)(kf * __builtin_amdgcn_exp2f(GL - G));
+                }
+                const long o = ((long)row * DK + c0) * 2;
+                *(f16x8 *)(blk + BL::E + o) = eo;
+                *(f16x8 *)(blk + BL::Q + o) = qo;
+                *(f16x8 *)(blk + BL::K + o) = ko;
             }
-            const long o = ((long)row * DK + c0) * 2;
-            *(f16x8 *)(blk + BL::E + o) = eo;
-            *(f16x8 *)(blk + BL::Q + o) = qo;
-            *(f16x8 *)(blk + BL::K + o) = ko;
+            for (int u = ot; u < BT * 8; u += NTH - 64) {
+                const int row = u >> 3, c0 = 8 * (u & 7);
+                *(uint4 *)(blk + BL::PM + (row * BT + c0) * 2) = *(const uint4 *)&sm.P[row * LDP + c0];
+            }
+            if (ot < BT) ((float *)(blk + BL::DG))[ot] = sm.dg[ot];
+            if (ot >= BT && ot < BT + DK)
+                ((float *)(blk + BL::GAM))[ot - BT] = __builtin_amdgcn_exp2f(sm.G2[(BT - 1) * LDG + ot - BT]);
         }
-        for (int u = ot; u < BT * 8; u += NTH - 64) {
+        __syncthreads();
+        // 4. T - I out
+        for (int u = tid; u < BT * 8; u += NTH) {
             const int row = u >> 3, c0 = 8 * (u & 7);
-            *(uint4 *)(blk + BL::PM + (row * BT + c0) * 2) = *(const uint4 *)&sm.P[row * LDP + c0];
+            *(uint4 *)(blk + BL::TM + (row * BT + c0) * 2) = *(const uint4 *)&sm.Tm[row * LDP + c0];
         }
-        if (ot < BT) ((float *)(blk + BL::DG))[ot] = sm.dg[ot];
-        if (ot >= BT && ot < BT + DK)
-            ((float *)(blk + BL::GAM))[ot - BT] = __builtin_amdgcn_exp2f(sm.G2[(BT - 1) * LDG + ot - BT]);
-    }
-    __syncthreads();
-    // 4. T - I out
-    for (int u = tid; u < BT * 8; u += NTH) {
-        const int row = u >> 3, c0 = 8 * (u & 7);
-        *(uint4 *)(blk + BL::TM + (row * BT + c0) * 2) = *(const uint4 *)&sm.Tm[row * LDP + c0];
+        __syncthreads();  // this chunk's LDS is read before the next one is staged
     }
 }
 
@@ -577,9 +601,16 @@ static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float 
                                       const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
                                       int H, float scale, hipStream_t st) {
     const int NT = (T + BT - 1) / BT;
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)((long)B * H * NT)), dim3(512), 0, st,
-                       (const uint16_t *)q, (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, T, H, NT);
-    hipError_t e = hipGetLastError();
+    const long nchunks = (long)B * H * NT;
+    // persistent prep: one workgroup per compute unit (its LDS allows one)
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long pgrid = nchunks < ncu ? nchunks : (ncu > 0 ? ncu : 1);
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)pgrid), dim3(512), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, T, H, NT, (int)nchunks);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long grid = (long)B * H * (DV / Gdn2WalkCfg<DK, DV>::BV);
     hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
