@@ -142,6 +142,16 @@ def test_gdn2_workload_full_size_sampled_heads():
         assert rel_err(S[b, h], rS[0, 0]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("Dk", [64, 128])
+def test_more_chunks_than_compute_units_ragged(Dk):
+    """B 3, H 8, T 1000 (15 whole chunks and a 40-token tail): 384 chunks, more
+    than one per compute unit, so the bf16 prep workgroups loop over several
+    chunks, ragged tails included; every head compared in full."""
+    x = gi.gdn2_inputs(3, 1000, 8, Dk, Dk, seed=310 + Dk, dtype="bf16", h0=True)
+    o, S = _run(x)
+    _check(x, o, S)
+
+
 def test_strong_decay_blocks_summed_directly():
     """Per-token log-decays near -20: within a 16-token block the channel decay
     spans far more than 2^100, so every diagonal block of the bf16 path takes
