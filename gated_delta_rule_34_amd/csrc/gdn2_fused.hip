@@ -337,7 +337,7 @@ struct Gdn2WalkCfg {
     static constexpr int BV = 32;
     static constexpr int NS = DK / 32;
     static constexpr int NKB = DK / 16;
-    static constexpr int LDK = RowTile<DK>::LD;
+    static constexpr int LDK = DK;   // paired-group rows (tile_off_pg), unpadded
     static constexpr int LDP = BT + 8;    // fp16 rows of T - I and P (16-byte aligned)
     static constexpr int LDV = BV + 8;   // bf16 rows of the v and w slices
     static constexpr int UT = BT * DK / 8 / 128;  // uint4 per loader thread per DK tile
@@ -346,7 +346,7 @@ struct Gdn2WalkCfg {
 template <int DK, int DV>
 struct Gdn2WalkSmem {
     using C = Gdn2WalkCfg<DK, DV>;
-    alignas(16) uint16_t E[2][BT * C::LDK];   // fp16 bits, swizzled rows (tile_off)
+    alignas(16) uint16_t E[2][BT * C::LDK];   // fp16 bits, paired-group layout (tile_off_pg)
     alignas(16) uint16_t Q[2][BT * C::LDK];
     alignas(16) uint16_t K[2][BT * C::LDK];
     alignas(16) _Float16 Tm[2][BT * C::LDP];
@@ -412,9 +412,14 @@ __device__ __forceinline__ void stage_store(Gdn2WalkSmem<DK, DV> &sm, const Gdn2
 #pragma unroll
     for (int x = 0; x < C::UT; ++x) {
         const int u = lt + 128 * x, row = u / C8, c0 = 8 * (u % C8);
-        *(u32x4 *)&sm.E[buf][tile_off<DK>(row, c0)] = R.e[x];
-        *(u32x4 *)&sm.Q[buf][tile_off<DK>(row, c0)] = R.q[x];
-        *(u32x4 *)&sm.K[buf][tile_off<DK>(row, c0)] = R.k[x];
+        // the two 4-column halves of each 16-byte piece go to their stored groups
+        const int lo = tile_off_pg<DK>(row, pair_col(c0)), hi = tile_off_pg<DK>(row, pair_col(c0 + 4));
+        *(uint2 *)&sm.E[buf][lo] = make_uint2(R.e[x].x, R.e[x].y);
+        *(uint2 *)&sm.E[buf][hi] = make_uint2(R.e[x].z, R.e[x].w);
+        *(uint2 *)&sm.Q[buf][lo] = make_uint2(R.q[x].x, R.q[x].y);
+        *(uint2 *)&sm.Q[buf][hi] = make_uint2(R.q[x].z, R.q[x].w);
+        *(uint2 *)&sm.K[buf][lo] = make_uint2(R.k[x].x, R.k[x].y);
+        *(uint2 *)&sm.K[buf][hi] = make_uint2(R.k[x].z, R.k[x].w);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -452,8 +457,8 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
         hilo_frags<f16x2>(shi, slo, S[2 * s], S[2 * s + 1]);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint4 ea = frag_rows_sw<DK>(sm.E[buf], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_sw<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+            const uint4 ea = frag_rows_pg<DK>(sm.E[buf], 16 * I, 32 * s, lane);
+            const uint4 qa = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
             X[I] = mma_f16_raw(X[I], ea, shi);
             Y[I] = mma_f16_raw(Y[I], qa, shi);
             X[I] = mma_f16_raw(X[I], ea, slo);
@@ -499,7 +504,7 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
         for (int e = 0; e < 4; ++e) acc[e] = S[m][e] * gm[e];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_sw<DK>(sm.K[buf], 32 * s, 16 * m, lane);
+            const uint4 a = frag_T_pg<DK>(sm.K[buf], 32 * s, 16 * m, lane);
             acc = mma_f16_raw(acc, a, vh[s]);
             acc = mma_f16_raw(acc, a, vl[s]);
         }
