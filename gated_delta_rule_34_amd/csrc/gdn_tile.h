@@ -36,34 +36,6 @@ __device__ __forceinline__ f32x4 mma_f16_block(f32x4 acc, const f16x4 &a, const 
 __device__ constexpr int tileI(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
 __device__ constexpr int tileJ(int t) { return t - tileI(t) * (tileI(t) + 1) / 2; }
 
-// A 64 x D tile of raw 16-bit values in LDS.  With D = 128 a row is 64
-// dwords (every row starts on bank 0), so column groups are XOR-swizzled
-// per row: 16-half segments by (row & 7), 8-half groups by bit 3 of the row.
-// The 8-byte fragment reads (16 rows x 2 column groups per half-wave) and
-// the transpose reads (8 rows x one 16-half segment) then each cover 64
-// distinct banks.  With D = 64 rows are padded instead.
-template <int D>
-struct RowTile {
-    static constexpr bool SWZ = D == 128;
-    static constexpr int LD = SWZ ? D : D + 8;  // row stride in halves
-};
-
-// Offset (in halves) of column `col` (a multiple of 4) of row `row`.
-template <int D>
-__device__ __forceinline__ int tile_off(int row, int col) {
-    if (RowTile<D>::SWZ) return row * RowTile<D>::LD + (col ^ (((row & 7) << 4) ^ (((row >> 3) & 1) << 3)));
-    return row * RowTile<D>::LD + col;
-}
-
-// A/B fragment of the 32-wide slab at column k0 of rows row0 .. row0 + 15.
-template <int D>
-__device__ __forceinline__ uint4 frag_rows_sw(const uint16_t *M, int row0, int k0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    const uint2 lo = *(const uint2 *)&M[tile_off<D>(row0 + r, k0 + 4 * g)];
-    const uint2 hi = *(const uint2 *)&M[tile_off<D>(row0 + r, k0 + 16 + 4 * g)];
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 // Paired-group column layout: within each 32-column slab the 4-column groups
@@ -98,26 +70,13 @@ __device__ __forceinline__ uint4 frag_rows_pg(const uint16_t *M, int row0, int k
 }
 
 // A fragment of the transpose (rows kc0 .. kc0 + 15 of M^T, slab of M rows
-// j0 .. j0 + 31) read from the row-major tile with the gfx950 LDS transpose
-// load: within each 16-lane group, lane j receives element (j % 4) of the
-// 8-byte chunks addressed by lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12.  Lane
-// (g, r) therefore addresses row j0 + 4g + r/4, columns kc0 + 4(r % 4), and
-// receives M[j0 + 4g + e][kc0 + r], e = 0..3.  Two such loads (j0 and
-// j0 + 16) make the 32-wide slab.
-template <int D>
-__device__ __forceinline__ uint4 frag_T_sw(const uint16_t *M, int j0, int kc0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const uint16_t *p0 = &M[tile_off<D>(j0 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
-    const uint16_t *p1 = &M[tile_off<D>(j0 + 16 + 4 * g + (r >> 2), kc0 + 4 * (r & 3))];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
-}
-
-// frag_T_sw for a paired-group tile (logical columns kc0 + 4(r % 4) .. + 3
-// are one stored 4-column group).
+// j0 .. j0 + 31) read from a row-major paired-group tile with the gfx950 LDS
+// transpose load: within each 16-lane group, lane j receives element (j % 4)
+// of the 8-byte chunks addressed by lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12.
+// Lane (g, r) therefore addresses row j0 + 4g + r/4, logical columns
+// kc0 + 4(r % 4) .. + 3 (one stored 4-column group), and receives
+// M[j0 + 4g + e][kc0 + r], e = 0..3.  Two such loads (j0 and j0 + 16) make
+// the 32-wide slab.
 template <int D>
 __device__ __forceinline__ uint4 frag_T_pg(const uint16_t *M, int j0, int kc0, int lane) {
     const int r = lane & 15, g = lane >> 4;
