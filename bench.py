@@ -305,6 +305,8 @@ def bench_gdn2(args, wl):
     kbytes = float(B) * T * H * ((3 * Dk + 2 * Dv) * esz + 4 * Dk + 4 * Dv) + B * H * Dk * Dv * 4.0
     achieved = kbytes / (kms * 1e-3) / 1e9
     flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
+    # bf16 inputs take the fused prep + walk pair, fp32 inputs the staged pair
+    kname = ("gdn2_prep_kernel+gdn2_walk_fused_kernel" if esz == 2 else "gdn2_intra_kernel+gdn2_walk_kernel")
     res = {
         "metric": "chunk gated delta rule-2 fwd tokens/s, T=4096 d=128",
         "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -313,7 +315,7 @@ def bench_gdn2(args, wl):
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
                    "inputs": x["dtype"], "kernels": "gdn2 intra-chunk stage + state walk",
                    "buffer_sets": args.sets, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gdn2_intra_kernel+gdn2_walk_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3, "traffic": None},
         "mfma": {"algorithmic_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,

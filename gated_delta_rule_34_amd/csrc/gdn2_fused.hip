@@ -68,6 +68,13 @@ struct Gdn2PrepSmem {
     alignas(16) float dg[BT];
 };
 
+// Four consecutive bf16 values (8 bytes, 8-byte aligned) as floats.
+__device__ __forceinline__ f32x4 bf16x4_at(const uint16_t *p) {
+    const uint2 u = *(const uint2 *)p;
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+
 // Largest |G2[x][c] - G2[a][c]| over the 16 rows x of the block at row a and
 // all channels: the size of the anchored factors in log2 units.
 template <int DK, int LDG>
@@ -100,13 +107,18 @@ __device__ __forceinline__ void diag_block(Gdn2PrepSmem<DK> &sm, int a, int lane
         for (int s = 0; s < DK / 32; ++s) {
             float fa[8], fq[8], fb[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
-                const float Ga = sm.G2[a * LDG + cc], Gi = sm.G2[i * LDG + cc];
-                const float ri = __builtin_amdgcn_exp2f(Gi - Ga), ki = bf16_to_f32(sm.k[i * LDR + cc]);
-                fa[e] = bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri;
-                fq[e] = bf16_to_f32(sm.q[i * LDR + cc]) * ri;
-                fb[e] = ki * __builtin_amdgcn_exp2f(Ga - Gi);
+            for (int h = 0; h < 2; ++h) {  // columns c0 .. c0 + 3, one read per row and array
+                const int c0 = 32 * s + 16 * h + 4 * g;
+                const f32x4 Ga = *(const f32x4 *)&sm.G2[a * LDG + c0], Gi = *(const f32x4 *)&sm.G2[i * LDG + c0];
+                const f32x4 kk = bf16x4_at(&sm.k[i * LDR + c0]), bb = bf16x4_at(&sm.b[i * LDR + c0]);
+                const f32x4 qq = bf16x4_at(&sm.q[i * LDR + c0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ri = __builtin_amdgcn_exp2f(Gi[e] - Ga[e]);
+                    fa[4 * h + e] = bb[e] * kk[e] * ri;
+                    fq[4 * h + e] = qq[e] * ri;
+                    fb[4 * h + e] = kk[e] * __builtin_amdgcn_exp2f(Ga[e] - Gi[e]);
+                }
             }
             accA = mma_slab(accA, fa, fb);
             accP = mma_slab(accP, fq, fb);
@@ -160,15 +172,19 @@ __device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int la
     for (int s = 0; s < DK / 32; ++s) {
         f16x8 fe, fq, fk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int cc = 32 * s + (e >> 2) * 16 + 4 * g + (e & 3);
-            const float Ga = sm.G2[a * LDG + cc];
-            const float ri = __builtin_amdgcn_exp2f(sm.G2[i * LDG + cc] - Ga);
-            const float kj = __builtin_amdgcn_exp2f(Ga - sm.G2[j * LDG + cc]);
-            const float ki = bf16_to_f32(sm.k[i * LDR + cc]);
-            fe[e] = (_Float16)(bf16_to_f32(sm.b[i * LDR + cc]) * ki * ri);
-            fq[e] = (_Float16)(bf16_to_f32(sm.q[i * LDR + cc]) * ri);
-            fk[e] = (_Float16)(bf16_to_f32(sm.k[j * LDR + cc]) * kj);
+        for (int h = 0; h < 2; ++h) {  // columns c0 .. c0 + 3, one read per row and array
+            const int c0 = 32 * s + 16 * h + 4 * g;
+            const f32x4 Ga = *(const f32x4 *)&sm.G2[a * LDG + c0], Gi = *(const f32x4 *)&sm.G2[i * LDG + c0];
+            const f32x4 Gj = *(const f32x4 *)&sm.G2[j * LDG + c0];
+            const f32x4 ki = bf16x4_at(&sm.k[i * LDR + c0]), bi = bf16x4_at(&sm.b[i * LDR + c0]);
+            const f32x4 qi = bf16x4_at(&sm.q[i * LDR + c0]), kj = bf16x4_at(&sm.k[j * LDR + c0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ri = __builtin_amdgcn_exp2f(Gi[e] - Ga[e]);
+                fe[4 * h + e] = (_Float16)(bi[e] * ki[e] * ri);
+                fq[4 * h + e] = (_Float16)(qi[e] * ri);
+                fk[4 * h + e] = (_Float16)(kj[e] * __builtin_amdgcn_exp2f(Ga[e] - Gj[e]));
+            }
         }
         accA = __builtin_amdgcn_mfma_f32_16x16x32_f16(fe, fk, accA, 0, 0, 0);
         accP = __builtin_amdgcn_mfma_f32_16x16x32_f16(fq, fk, accP, 0, 0, 0);
@@ -299,9 +315,13 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
                 const uint4 bv = *(const uint4 *)&sm.b[row * LDR + c0];
                 const uint16_t *kk = (const uint16_t *)&kv, *qq = (const uint16_t *)&qv, *bq = (const uint16_t *)&bv;
                 f16x8 eo, qo, ko;
-    #pragma unroll
+                const f32x4 G0 = *(const f32x4 *)&sm.G2[row * LDG + c0];
+                const f32x4 G1 = *(const f32x4 *)&sm.G2[row * LDG + c0 + 4];
+                const f32x4 L0 = *(const f32x4 *)&sm.G2[(BT - 1) * LDG + c0];
+                const f32x4 L1 = *(const f32x4 *)&sm.G2[(BT - 1) * LDG + c0 + 4];
+#pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float G = sm.G2[row * LDG + c0 + e], GL = sm.G2[(BT - 1) * LDG + c0 + e];
+                    const float G = e < 4 ? G0[e] : G1[e - 4], GL = e < 4 ? L0[e] : L1[e - 4];
                     const float gam = __builtin_amdgcn_exp2f(G);
                     const float kf = bf16_to_f32(kk[e]);
                     eo[e] = (_Float16)(bf16_to_f32(bq[e]) * kf * gam);
