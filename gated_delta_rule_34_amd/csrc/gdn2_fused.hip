@@ -471,30 +471,41 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-        uint4 shi, slo;
-        hilo_frags<f16x2>(shi, slo, S[2 * s], S[2 * s + 1]);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const uint4 ea = frag_rows_pg<DK>(sm.E[buf], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
-            X[I] = mma_f16_raw(X[I], ea, shi);
-            Y[I] = mma_f16_raw(Y[I], qa, shi);
-            X[I] = mma_f16_raw(X[I], ea, slo);
-            Y[I] = mma_f16_raw(Y[I], qa, slo);
-        }
-    }
-    // R = w . v - X
-    f32x4 Rr[4];
+    // w . v for this wave's 16 columns, read first so that the element reads
+    // hide under the products below
     const int cl = wave * 16 + r;
+    f32x4 wv[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
-            Rr[I][e] = bf16_to_f32(sm.W[buf][i * C::LDV + cl]) * bf16_to_f32(sm.V[buf][i * C::LDV + cl]) - X[I][e];
+            wv[I][e] = bf16_to_f32(sm.W[buf][i * C::LDV + cl]) * bf16_to_f32(sm.V[buf][i * C::LDV + cl]);
         }
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        uint4 shi, slo;
+        hilo_frags<f16x2>(shi, slo, S[2 * s], S[2 * s + 1]);
+        // all hi-part products, then all lo-part products: an accumulator's
+        // two updates are eight MFMAs apart
+        uint4 ea[4], qa[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            ea[I] = frag_rows_pg<DK>(sm.E[buf], 16 * I, 32 * s, lane);
+            qa[I] = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+            X[I] = mma_f16_raw(X[I], ea[I], shi);
+            Y[I] = mma_f16_raw(Y[I], qa[I], shi);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            X[I] = mma_f16_raw(X[I], ea[I], slo);
+            Y[I] = mma_f16_raw(Y[I], qa[I], slo);
+        }
+    }
+    // R = w . v - X
+    f32x4 Rr[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) Rr[I] = wv[I] - X[I];
     // Vnew = R + (T - I) R
     _Float16 rf[2][8];
     frag_from_acc(rf[0], Rr[0], Rr[1]);
@@ -655,3 +666,4 @@ hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la,
 }
 
 }  // namespace gdn
+

@@ -300,33 +300,49 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
+    // The gate tables and this wave's V columns (transpose loads of the
+    // row-major V tile: V[16I + 4g + e][column r]) are read first, so their
+    // latency hides under the products below.
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    f32x4 gmv[4], betv[4];
+    s16x4 vtv[4];
+    {
+        const int cl0 = cw * 16 + 4 * (r & 3);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            gmv[I] = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
+            betv[I] = *(const f32x4 *)&sm.beta[buf][16 * I + 4 * g];
+            vtv[I] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)&sm.V[buf][(16 * I + 4 * g + (r >> 2)) * C::LDV + cl0]);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
         uint4 uhi, ulo;
         hilo_frags<bf16x2>(uhi, ulo, S[2 * s], S[2 * s + 1]);
         const bf16x8 shi = __builtin_bit_cast(bf16x8, uhi), slo = __builtin_bit_cast(bf16x8, ulo);
+        // all hi-part products, then all lo-part products: an accumulator's
+        // two updates are eight MFMAs apart
+        bf16x8 kf[4], qf[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint4 ka = frag_rows_pg<DK>(sm.K[kb], 16 * I, 32 * s, lane);
-            const uint4 qa = frag_rows_pg<DK>(sm.Q[kb], 16 * I, 32 * s, lane);
-            const bf16x8 kb = __builtin_bit_cast(bf16x8, ka), qb = __builtin_bit_cast(bf16x8, qa);
-            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, shi, X[I], 0, 0, 0);
-            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, shi, Y[I], 0, 0, 0);
-            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, slo, X[I], 0, 0, 0);
-            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb, slo, Y[I], 0, 0, 0);
+            kf[I] = __builtin_bit_cast(bf16x8, frag_rows_pg<DK>(sm.K[kb], 16 * I, 32 * s, lane));
+            qf[I] = __builtin_bit_cast(bf16x8, frag_rows_pg<DK>(sm.Q[kb], 16 * I, 32 * s, lane));
+            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[I], shi, X[I], 0, 0, 0);
+            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], shi, Y[I], 0, 0, 0);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[I], slo, X[I], 0, 0, 0);
+            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], slo, Y[I], 0, 0, 0);
         }
     }
-    // R = beta (V - gamma X); V[16I + 4g + e][this wave's column r] by
-    // transpose loads of the row-major V tile
+    // R = beta (V - gamma X)
     f32x4 Rr[4];
-    const int cl = cw * 16 + r;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * I + 4 * g];
-        const f32x4 bet = *(const f32x4 *)&sm.beta[buf][16 * I + 4 * g];
-        const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)&sm.V[buf][(16 * I + 4 * g + (r >> 2)) * C::LDV + cw * 16 + 4 * (r & 3)]);
+        const f32x4 gm = gmv[I], bet = betv[I];
+        const s16x4 vt = vtv[I];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float vv = __uint_as_float(((uint32_t)(uint16_t)vt[e]) << 16);
