@@ -93,8 +93,9 @@ __device__ __forceinline__ float block_span(const float *G2, int a, int lane) {
 // Diagonal block (rows and columns a .. a + 15) of A and P, one wave.  When
 // every channel's decay within the block stays inside 2^(+-100) of row a, the
 // block is a product of factors anchored at a, e_i 2^(G2_i - G2_a) and
-// k_j 2^(G2_a - G2_j), on fp32 MFMA (exact fp32 operands, no overflow or
-// underflow of either factor); otherwise each entry is summed directly.
+// k_j 2^(G2_a - G2_j), formed in fp32 (no overflow or underflow of either
+// factor) and multiplied on bf16 MFMA as hi + lo parts; otherwise each entry
+// is summed directly.
 template <int DK>
 __device__ __forceinline__ void diag_block(Gdn2PrepSmem<DK> &sm, int a, int lane) {
     using SM = Gdn2PrepSmem<DK>;
@@ -120,8 +121,18 @@ __device__ __forceinline__ void diag_block(Gdn2PrepSmem<DK> &sm, int a, int lane
                     fb[4 * h + e] = kk[e] * __builtin_amdgcn_exp2f(Ga[e] - Gi[e]);
                 }
             }
-            accA = mma_slab(accA, fa, fb);
-            accP = mma_slab(accP, fq, fb);
+            // bf16 hi + lo parts of each factor; the products hi.hi, hi.lo
+            // and lo.hi keep about 16 bits of each factor with fp32's range
+            uint4 ah, al, qh, ql, bh, bl;
+            hilo_frags<bf16x2>(ah, al, f32x4{fa[0], fa[1], fa[2], fa[3]}, f32x4{fa[4], fa[5], fa[6], fa[7]});
+            hilo_frags<bf16x2>(qh, ql, f32x4{fq[0], fq[1], fq[2], fq[3]}, f32x4{fq[4], fq[5], fq[6], fq[7]});
+            hilo_frags<bf16x2>(bh, bl, f32x4{fb[0], fb[1], fb[2], fb[3]}, f32x4{fb[4], fb[5], fb[6], fb[7]});
+            accA = mma_bf16_raw(accA, ah, bh);
+            accP = mma_bf16_raw(accP, qh, bh);
+            accA = mma_bf16_raw(accA, ah, bl);
+            accP = mma_bf16_raw(accP, qh, bl);
+            accA = mma_bf16_raw(accA, al, bh);
+            accP = mma_bf16_raw(accP, ql, bh);
         }
         // lane holds [a + 4g + e][a + r]
 #pragma unroll
@@ -199,9 +210,9 @@ __device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int la
 }
 
 // Persistent: workgroup w handles chunks w, w + gridDim.x, ...  The raw rows
-// and log-decays of its next chunk are fetched into registers as soon as the
-// current chunk is staged in LDS, so their latency overlaps the current
-// chunk's work.
+// and log-decays of its next chunk are fetched into registers while the
+// current chunk's A and P tiles are formed, so their latency overlaps the
+// current chunk's work.
 template <int DK>
 __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                          const float *__restrict__ la, const uint16_t *__restrict__ bg,
@@ -290,17 +301,21 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
 #pragma unroll
             for (int x = 0; x < RG; ++x) sm.G2[(RG * gr + x) * LDG + ch] = lv[x] + off;
         }
-        // the registers are free: fetch the next chunk now
-        if (cb + gridDim.x < nchunks) fetch(cb + gridDim.x);
         __syncthreads();
 
-        // 2. A and P: waves 0..3 the diagonal blocks, waves 4..7 the 6 off-diagonal tiles
+        // 2. A and P: waves 0..3 the diagonal blocks, waves 4..7 the 6 off-diagonal tiles.
+        // The staging registers are free now, so the next chunk is fetched here:
+        // first by waves 4 and 5, which have two tiles each, and by the others
+        // after their tile, where they would otherwise wait at the barrier.
+        const bool more = cb + gridDim.x < nchunks, fetch_first = wave == 4 || wave == 5;
+        if (fetch_first && more) fetch(cb + gridDim.x);
         if (wave < 4) {
             diag_block<DK>(sm, 16 * wave, lane);
         } else {
             offdiag_tile<DK>(sm, wave - 4, lane);
             if (wave < 6) offdiag_tile<DK>(sm, wave, lane);
         }
+        if (!fetch_first && more) fetch(cb + gridDim.x);
         __syncthreads();
 
         // 3. wave 0: T - I; the other waves: decayed operands, Gamma_C, P, diag P
