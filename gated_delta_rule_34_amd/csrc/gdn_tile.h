@@ -121,6 +121,14 @@ __device__ __forceinline__ float dpp_f32(float x) {
                                                                  false));
 }
 
+// Value of `x` from another lane of the same quad (a DPP quad permutation,
+// where every lane has a source, so no old value is needed and the move can
+// fold into the instruction that uses it).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+
 // 4 x 4 transpose within each quad of lanes (DPP quad permutations): lane
 // 4a + b holds v[e] = M[e][b] of its quad's 4 x 4 block on entry and
 // M[b][e] on return.  Used to turn an MFMA accumulator tile (4 rows of one
@@ -129,11 +137,11 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
     const int b = lane & 3;
     f32x4 p;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0xB1, 0xf>(v[e]);  // from lane b ^ 1
+    for (int e = 0; e < 4; ++e) p[e] = quad_perm_f32<0xB1>(v[e]);  // from lane b ^ 1
     if (b & 1) v = f32x4{p[1], v[1], p[3], v[3]};
     else v = f32x4{v[0], p[0], v[2], p[2]};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = dpp_f32<0x4E, 0xf>(v[e]);  // from lane b ^ 2
+    for (int e = 0; e < 4; ++e) p[e] = quad_perm_f32<0x4E>(v[e]);  // from lane b ^ 2
     if (b & 2) v = f32x4{p[2], p[3], v[2], v[3]};
     else v = f32x4{v[0], v[1], p[0], p[1]};
     return v;
