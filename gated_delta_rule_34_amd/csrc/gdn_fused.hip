@@ -203,7 +203,6 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     for (int s = 0; s < C::NS; ++s)
 #pragma unroll
         for (int t = 0; t < 10; ++t) acc[t] = mma_bf16_raw(acc[t], R.k[tileJ(t)][s], R.k[tileI(t)][s]);
-    load_rows<DK>(R.k, ha.k, ha, min(c2 + 1, NT - 1), lane);
     float rowG2[4], rowB[4];
     f32x4 colG2[4];
 #pragma unroll
@@ -212,6 +211,9 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         rowB[I] = sm.betaA[16 * I + r];
         colG2[I] = *(const f32x4 *)&sm.g2A[16 * I + 4 * g];
     }
+    // The next chunk's rows overwrite the MFMA operands, so they are requested
+    // once those products have had time to read them.
+    load_rows<DK>(R.k, ha.k, ha, min(c2 + 1, NT - 1), lane);
     // A = strictly-lower(diag(beta) K K^T . 2^(G2_i - G2_j))
     _Float16 *A = sm.A[c2 & 1];
 #pragma unroll
