@@ -88,6 +88,124 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
+SETTLE_S = 0.25   # seconds of back-to-back steps before any timed region
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz, via torch.cuda.clock_rate) from a
+    background thread while the GPU is under load; None where unavailable."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.samples = []
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import torch
+        while not self._stop.is_set():
+            try:
+                self.samples.append(float(torch.cuda.clock_rate(0)))
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self):
+        import statistics
+        if not self.samples:
+            return None
+        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples), "samples": len(self.samples),
+                "source": "torch.cuda.clock_rate sampled every 20 ms during the settle phase and timed region"}
+
+
+def percentile(xs, p):
+    ys = sorted(xs)
+    if not ys:
+        return None
+    k = (len(ys) - 1) * p / 100.0
+    lo = int(k)
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
+
+
+def run_timed(step, sets, args, per_launch_min: int = 50):
+    """The timing protocol shared by every workload.
+
+    1. `args.warmup` untimed steps, then more back-to-back steps until at least
+       SETTLE_S seconds of load have run (the GPU clock needs ~50 ms of load to
+       settle), whatever --warmup says.
+    2. The timed region: exactly `args.steps` steps between two synchronisations,
+       with one HIP event pair on the current stream around all of them (wall
+       clock and event time).
+    3. A distribution pass outside the timed region: max(steps, 50) steps, each
+       between its own event pair, for the median / p10 / p90 of one step.
+    Returns a dict with ms_per_step (wall), event_ms_per_step and the stats."""
+    import torch
+    n = len(sets)
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        done = 0
+        for i in range(args.warmup):
+            step(sets[i % n])
+            done += 1
+        torch.cuda.synchronize()
+        while time.perf_counter() - t0 < SETTLE_S:
+            for _ in range(20):
+                step(sets[done % n])
+                done += 1
+            torch.cuda.synchronize()
+        settle_s = time.perf_counter() - t0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(args.steps):
+            step(sets[i % n])
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        event_ms = e0.elapsed_time(e1) / args.steps
+        m = max(args.steps, per_launch_min)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(m)]
+        for i in range(m):
+            evs[i][0].record()
+            step(sets[i % n])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+    per = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return {"ms_per_step": wall * 1e3 / args.steps, "event_ms_per_step": event_ms,
+            "settle": {"steps": done, "seconds": settle_s},
+            "step_us": {"median": percentile(per, 50), "p10": percentile(per, 10), "p90": percentile(per, 90),
+                        "n": m, "method": "one HIP event pair per step, outside the timed region"},
+            "device_clock": clk.summary()}
+
+
+def timing_fields(tm):
+    """JSON fields every workload reports from run_timed's result."""
+    return {"settle": tm["settle"], "step_us": tm["step_us"], "device_clock": tm["device_clock"],
+            "host_cpu": host_cpu_model()}
+
+
 def to_dev(a, dev):
     import numpy as np
     import torch
@@ -188,37 +306,26 @@ def bench_gdn(args, wl):
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
+    tm = run_timed(step, sets, args)
+    ms = tm["ms_per_step"]
     if fused:
-        # one kernel per step: events around the whole timed region give its
+        # one kernel per step: the event pair around the timed region gives its
         # average launch duration without per-launch event gaps
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(args.steps):
-            step(sets[i % len(sets)])
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        k1_ms, k2_ms = e0.elapsed_time(e1) / args.steps, 0.0
+        k1_ms, k2_ms = tm["event_ms_per_step"], 0.0
+        kernels = {"fused_kernel": k1_ms * 1e3}
     else:
+        # the two stages, each between events, in a pass of its own after the timed region
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        t0 = time.perf_counter()
         for i in range(args.steps):
             step(sets[i % len(sets)], evs[i])
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         k1_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
         k2_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms = wall * 1e3 / args.steps
-    if fused:
-        kernels = {"fused_kernel": k1_ms * 1e3}
-    else:
         kernels = {"intra_kernel": k1_ms * 1e3, "walk_kernel": k2_ms * 1e3}
     log(f"[bench] {args.steps} steps: {ms:.4f} ms/step wall; per launch (HIP events): " +
-        ", ".join(f"{k} {v:.1f} us" for k, v in kernels.items()))
+        ", ".join(f"{k} {v:.1f} us" for k, v in kernels.items()) +
+        f"; step median {tm['step_us']['median']:.1f} us (p10 {tm['step_us']['p10']:.1f}, "
+        f"p90 {tm['step_us']['p90']:.1f}); clock {tm['device_clock']}")
 
     tokens = B * T
     flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
@@ -246,11 +353,12 @@ def bench_gdn(args, wl):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if x["dtype"] == "bf16" else "f32",
+        "dtype": "bf16" if x["dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
                    "inputs": x["dtype"], "state_and_output": "fp32",
-                   "mfma": "f16 operands, fp32 accumulate" if x["dtype"] == "bf16" else "fp32",
+                   "mfma": ("bf16 operands (inputs, state hi + lo parts) and fp16 operands (T - I, P, new "
+                            "values), fp32 accumulate") if x["dtype"] == "bf16" else "fp32",
                    "h0": has_h0, "buffer_sets": args.sets, "parallelism": "single GPU",
                    "kernels": "single fused kernel" if fused else "intra-chunk stage + state walk"},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -261,6 +369,7 @@ def bench_gdn(args, wl):
                  "frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
                  "flop_model": "full-tile 2*64*(3*Dk+2*Dv)+6*Dk*Dv per token-head"},
         "kernels_us": kernels,
+        **timing_fields(tm),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
@@ -294,18 +403,9 @@ def bench_gdn2(args, wl):
         gdn.gdn2_chunk_fwd(*[s[n] for n in names], scale=x["scale"], workspace=ws, out=s["o"],
                            final_state=s["ht"])
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kms = e0.elapsed_time(e1) / args.steps
+    tm = run_timed(step, sets, args)
+    ms = tm["ms_per_step"]
+    kms = tm["event_ms_per_step"]
     esz = 2 if x["dtype"] == "bf16" else 4
     # q, k, b (Dk) and v, w (Dv) in the input dtype, log_alpha fp32, o fp32, final state
     kbytes = float(B) * T * H * ((3 * Dk + 2 * Dv) * esz + 4 * Dk + 4 * Dv) + B * H * Dk * Dv * 4.0
@@ -317,16 +417,18 @@ def bench_gdn2(args, wl):
         "metric": "chunk gated delta rule-2 fwd tokens/s, T=4096 d=128",
         "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16" if esz == 2 else "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
                    "inputs": x["dtype"], "kernels": "gdn2 intra-chunk stage + state walk",
                    "buffer_sets": args.sets, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3, "traffic": None},
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3,
+                     "traffic": read_traffic("gdn2_kernels", wl) if esz == 2 else None},
         "mfma": {"algorithmic_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
                  "frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
                  "flop_model": "full-tile 2*64*(3*Dk+2*Dv)+6*Dk*Dv per token-head"},
+        **timing_fields(tm),
     }
     if not args.no_cpu_baseline:
         args64 = [x[n + "_f64"] for n in names]
@@ -380,18 +482,9 @@ def bench_step(args, wl):
     def step(s):
         fn(*[s[n] for n in names], s["S"], scale=x["scale"], out=s["o"])
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kms = e0.elapsed_time(e1) / args.steps
+    tm = run_timed(step, sets, args)
+    ms = tm["ms_per_step"]
+    kms = tm["event_ms_per_step"]
     esz = 2 if x["dtype"] == "bf16" else 4
     # state read and written once, q, k, v, the gates, and o
     kbytes = float(B) * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * esz + spec["gate_bytes"](Dk, Dv, esz) + Dv * 4)
@@ -406,6 +499,7 @@ def bench_step(args, wl):
         "roofline": {"bound": "hbm", "kernel": spec["kernel"], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": kbytes,
                      "avg_launch_us": kms * 1e3, "traffic": read_traffic(spec["kernel"], wl)},
+        **timing_fields(tm),
     }
     if not args.no_cpu_baseline:
         args_f64 = [x[n + "_f64"] for n in names + ("S",)]
@@ -463,18 +557,9 @@ def bench_bwd(args, wl):
     def step(s):
         fn(*[s[n] for n in names], None, s["do"], s["dht"], scale=x["scale"], workspace=ws)
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kms = e0.elapsed_time(e1) / args.steps
+    tm = run_timed(step, sets, args)
+    ms = tm["ms_per_step"]
+    kms = tm["event_ms_per_step"]
     esz = 2 if x["dtype"] == "bf16" else 4
     # inputs q, k, v (and the gates), dO, dht read once; every gradient written once (fp32)
     per_tok = (2 * Dk + Dv) * esz + Dv * 4 + (2 * Dk + Dv) * 4 + spec["extra"](Dk, Dv, esz)
@@ -493,6 +578,7 @@ def bench_bwd(args, wl):
         "roofline": {"bound": "hbm", "kernel": f"{spec['fn']} (all stages)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3, "traffic": None},
+        **timing_fields(tm),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -544,15 +630,13 @@ def bench_layer(args, wl):
         if ev is not None:
             ev[3].record()
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
+    tm = run_timed(step, sets, args)
+    ms = tm["ms_per_step"]
+    # the three stages, each between events, in a pass of its own after the timed region
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
     seg = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
     th = float(B) * T * H
     stage_bytes = [th * (2 * (2 * Dk + Dv) * 2 + 16),                       # projections in, q k v out, gates
@@ -569,7 +653,7 @@ def bench_layer(args, wl):
         "metric": f"gated delta rule layer (prologue + chunked fwd + gated RMSNorm) tokens/s, T={T} d={Dk}",
         "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": BT,
                    "inputs": "bf16 projections", "kernels": "prologue, fused chunked forward, gated RMSNorm",
                    "buffer_sets": args.sets, "parallelism": "single GPU"},
@@ -578,6 +662,7 @@ def bench_layer(args, wl):
                      "algorithmic_bytes_per_launch": stage_bytes[dom], "avg_launch_us": seg[dom] * 1e3,
                      "traffic": None},
         "stages": stages,
+        **timing_fields(tm),
     }
     if not args.no_cpu_baseline:
         # the oracle's prologue and epilogue on one sequence of the workload

@@ -13,14 +13,18 @@
 //   O    = scale (Qhat S + P Vnew),       Qhat_i = Gamma_i . q_i
 //   S'   = Diag(Gamma_C) S + Khat^T Vnew, Khat_j = k_j . Gamma_C / Gamma_j
 //
-// prep kernel (one workgroup per (batch, head, chunk), all chunks in
-// parallel): the cumsum, Ehat, Qhat, Khat, Gamma_C, T - I = (I + A)^-1 - I and
-// the strict and diagonal parts of P, written as one block per chunk.
+// prep kernel (persistent: one workgroup per compute unit, looping over the
+// (batch, head, chunk) blocks, with the next chunk's raw rows and
+// log-decays fetched into registers while the current chunk is computed):
+// the cumsum, Ehat, Qhat, Khat, Gamma_C, T - I = (I + A)^-1 - I and the
+// strict and diagonal parts of P, written as one block per chunk.
 //   Off-diagonal 16x16 blocks of A and P are fp16 MFMA products of factors
 //   anchored at the first row a of the block row: (x_i e^{G_i - G_a}) and
 //   (k_j e^{G_a - G_j}), both at most 1 in size since j < a <= i.  Diagonal
-//   blocks use the same anchor on fp32 MFMA while the block's decay keeps
-//   both factors inside 2^(+-100), and are summed directly otherwise.
+//   blocks are anchored at their own first row, with the fp32 factors split
+//   into bf16 hi + lo parts on bf16 MFMA (hi.hi + hi.lo + lo.hi), while the
+//   block's decay keeps both factors inside 2^(+-100); otherwise they are
+//   summed directly.
 // walk kernel (one workgroup per (batch, head, 32 value columns)): two
 //   consumer waves carry the state in registers through the chunks, two
 //   loader waves stage the next chunk's block and value slices into LDS.

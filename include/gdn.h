@@ -39,6 +39,20 @@
  *     values are accepted but not guaranteed (exp2 of a positive difference
  *     may overflow).  beta, b, w are expected in [0, 1].
  *   - Results are bitwise reproducible for identical inputs, sizes and device.
+ *   - Operand range of the bf16 paths.  They round some intermediate values
+ *     to fp16 (11 significant bits, largest finite value 65,504) for the
+ *     matrix-core products: in gdn_chunk_fwd and gdn_chunk_fwd_varlen the
+ *     chunk residuals R = beta (v - gamma K S), the new values, T - I and P;
+ *     in gdn2_chunk_fwd also the decayed keys and queries and the state as
+ *     hi + lo parts.  With ||k_t|| <= 1, beta in [0, 1] and g <= 0 one has
+ *     |T - I| <= 1, |P| <= scale, and for every value column c
+ *       |R|, |new values| <= max_t |v_{t,c}| + sqrt(||h0[:, c]||^2 + sum_t beta_t v_{t,c}^2)
+ *     (each token grows the squared norm of a state column by at most
+ *     beta v^2); keep this below 32,768.  For Gated DeltaNet-2 keep the state
+ *     entries and |w . v| below 32,768.  Beyond that the output may hold inf
+ *     or NaN and no error is reported.  Magnitudes below 2^-14 fall into
+ *     fp16's subnormal range and lose precision, so v and h0 should not be
+ *     uniformly tiny (rms below about 2^-10).  The fp32 paths have fp32 range.
  */
 #ifndef GDN_H
 #define GDN_H

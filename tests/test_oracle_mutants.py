@@ -89,3 +89,46 @@ def test_pins_reject_mutant(tmp_path, monkeypatch, name, old, new):
         except AssertionError:
             caught.append(f.__name__)
     assert caught, f"no pin rejects mutant {name}"
+
+
+# Planted mistakes in a copy of the prologue oracle (oracle/prologue.py); each
+# must be rejected by a pin of tests/test_oracle_prologue.py.
+PROLOGUE_SRC = os.path.join(os.path.dirname(oracle.__file__), "prologue.py")
+PROLOGUE_MUTANTS = [
+    ("silu_negated_argument", "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))"),
+    ("sigmoid_negated_argument", "return 1.0 / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(x))"),
+    ("softplus_negated_argument", "return np.logaddexp(0.0, x)", "return np.logaddexp(0.0, -x)"),
+    ("beta_of_minus_b", "    beta = sigmoid(b)\n", "    beta = sigmoid(-b)\n"),
+    ("dt_bias_outside_softplus", "softplus(a + dt_bias[None, None, :])",
+     "(softplus(a) + dt_bias[None, None, :])"),
+    ("A_log_not_exponentiated", "g = -np.exp(A_log)[None, None, :]", "g = -A_log[None, None, :]"),
+    ("g_positive", "g = -np.exp(A_log)[None, None, :]", "g = np.exp(A_log)[None, None, :]"),
+    ("l2norm_eps_outside_root", "np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)",
+     "(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + eps)"),
+    ("conv_taps_reversed", "y[:, t] += w[:, j] * full[:, t + j]", "y[:, t] += w[:, CONV - 1 - j] * full[:, t + j]"),
+    ("v_without_silu", "v = silu(yv).reshape(B, T, H, Dv)", "v = yv.reshape(B, T, H, Dv)"),
+    ("q_not_normalised", "q = l2norm(silu(yq).reshape(B, T, H, Dk))", "q = silu(yq).reshape(B, T, H, Dk)"),
+    ("rmsnorm_sum_not_mean", "np.mean(o * o, axis=-1, keepdims=True)", "np.sum(o * o, axis=-1, keepdims=True)"),
+    ("rmsnorm_sigmoid_gate", "+ eps) * w * silu(z)\n", "+ eps) * w * sigmoid(z)\n"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PROLOGUE_MUTANTS, ids=[m[0] for m in PROLOGUE_MUTANTS])
+def test_prologue_pins_reject_mutant(tmp_path, name, old, new):
+    import importlib.util
+
+    from tests import test_oracle_prologue as ppins
+    text = open(PROLOGUE_SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / f"prologue_{name}.py"
+    path.write_text(text.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"prologue_{name}", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for f in ppins.PINS:
+        try:
+            f(mod)
+        except AssertionError:
+            caught.append(f.__name__)
+    assert caught, f"no prologue pin rejects mutant {name}"

@@ -130,16 +130,37 @@ def test_deterministic():
     assert (o1 == o2).all().item() and (S1 == S2).all().item()
 
 
-def test_gdn2_workload_full_size_sampled_heads():
-    """The GDN-2 workload at full size (B=4 H=8 T=4096 d=128, bf16); the oracle
-    checks 3 heads."""
+def test_gdn2_workload_full_size_every_head():
+    """The GDN-2 workload at full size (B=4 H=8 T=4096 d=128, bf16) in the
+    launch configuration the benchmark times; the oracle runs every head."""
     x = gi.workload("gdn2_bf16")
     o, S = _run(x)
-    for b, h in [(0, 0), (2, 5), (3, 7)]:
-        sub = [x[n + "_f64"][b:b + 1, :, h:h + 1] for n in NAMES[:6]]
-        ro, rS = oracle.gdn2_fwd(*sub, None, scale=x["scale"])
-        assert rel_err(o[b, :, h], ro[0, :, 0]) <= TOL["bf16"]
-        assert rel_err(S[b, h], rS[0, 0]) <= TOL["bf16"]
+    ro, rS = _ref(x)
+    eo, es = rel_err(o, ro), rel_err(S, rS)
+    ho = max(rel_err(o[b, :, h], ro[b, :, h]) for b in range(4) for h in range(8))
+    hs = max(rel_err(S[b, h], rS[b, h]) for b in range(4) for h in range(8))
+    print(f"gdn2_bf16: o err {eo:.3e}, S err {es:.3e}; worst head o {ho:.3e}, S {hs:.3e}")
+    assert max(eo, es, ho, hs) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("t", [0, 45, 64, 130])
+def test_causality_perturbation(dtype, t):
+    """Perturbing q, k, v, b and w of token t leaves every earlier output
+    bitwise unchanged and changes the output at t.  The log-decay of token t is
+    left as it is: on the bf16 path it decides, per 16-token diagonal block,
+    between the anchored product and the direct sum, so changing it may move
+    the rounding of the earlier rows of its block (not their exact value)."""
+    x = gi.gdn2_inputs(1, 200, 2, 128, 128, seed=330 + t, dtype=dtype, h0=True)
+    o1, S1 = _run(x)
+    y = {n: (np.array(a, copy=True) if isinstance(a, np.ndarray) else a) for n, a in x.items()}
+    pert = gi.gdn2_inputs(1, 200, 2, 128, 128, seed=340 + t, dtype=dtype)
+    for n in ("q", "k", "v", "b", "w"):
+        y[n][:, t] = pert[n][:, t]
+    o2, S2 = _run(y)
+    np.testing.assert_array_equal(o2[:, :t], o1[:, :t])
+    assert np.abs(o2[:, t] - o1[:, t]).max() > 0
+    assert np.abs(S2 - S1).max() > 0
 
 
 @pytest.mark.parametrize("Dk", [64, 128])
