@@ -88,7 +88,7 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-SETTLE_S = 0.25   # seconds of back-to-back steps before any timed region
+SETTLE_S = 0.25   # default seconds of back-to-back steps before any timed region
 
 
 def host_cpu_model() -> str:
@@ -152,7 +152,7 @@ def run_timed(step, sets, args, per_launch_min: int = 50):
     """The timing protocol shared by every workload.
 
     1. `args.warmup` untimed steps, then more back-to-back steps until at least
-       SETTLE_S seconds of load have run (the GPU clock needs ~50 ms of load to
+       --settle-ms of load have run (the GPU clock needs ~50 ms of load to
        settle), whatever --warmup says.
     2. The timed region: exactly `args.steps` steps between two synchronisations,
        with one HIP event pair on the current stream around all of them (wall
@@ -169,7 +169,7 @@ def run_timed(step, sets, args, per_launch_min: int = 50):
             step(sets[i % n])
             done += 1
         torch.cuda.synchronize()
-        while time.perf_counter() - t0 < SETTLE_S:
+        while time.perf_counter() - t0 < args.settle_ms * 1e-3:
             for _ in range(20):
                 step(sets[done % n])
                 done += 1
@@ -688,12 +688,14 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps; the GPU clock needs ~50 ms of load to settle")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the settle phase")
     ap.add_argument("--workload", default="layer_bf16",
                     choices=["layer_bf16", "long_bf16", "tiny_fp32", "decode_bf16", "decode2_bf16", "gdn2_bf16",
                              "layer_bwd_bf16", "gdn2_bwd_bf16", "layer_full_bf16"])
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                    help="milliseconds of back-to-back untimed steps before timing, on top of --warmup "
+                         "(the GPU clock needs ~50 ms of load to settle); 0 for short profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of MIB MiB (outside the timed region) "

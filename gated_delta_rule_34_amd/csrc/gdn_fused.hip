@@ -185,11 +185,11 @@ __device__ __forceinline__ void lower_tiles(f32x4 (&acc)[10], const uint16_t *X,
 // operands are the same register fragments (row 16I + r, columns 32s + 8g
 // .. + 7), so K_J K_I^T needs no particular k-slot order.
 template <int DK, int DV>
-__device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c2, int NT,
+__device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c2, int kb, int NT,
                                           const HeadArgs &ha, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    write_rows<DK>(sm.K[c2 % 3], R.k, lane);
+    write_rows<DK>(sm.K[kb], R.k, lane);
     finish_gates(R.g, R.beta, ha, c2, lane);
     sm.g2A[lane] = chunk_g2(R.g);
     sm.betaA[lane] = R.beta;
@@ -237,7 +237,7 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 // Q rows of chunk c1 + 1; those rows go to kq-buffer (c1 + 1) % 3 and R
 // receives the rows of chunk c1 + 2, a full iteration before they are stored.
 template <int DK, int DV>
-__device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int NT,
+__device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int kb, int NT,
                                           const HeadArgs &ha, float scale, int lane) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
@@ -256,7 +256,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     const float gmv = __builtin_amdgcn_exp2f(G2);
     sm.gam[buf][lane] = gmv;
     sm.beta[buf][lane] = R.beta;
-    write_rows<DK>(sm.Q[(c1 + 1) % 3], R.q, lane);
+    write_rows<DK>(sm.Q[(kb + 1) % 3], R.q, lane);
     // then fetch the next ones together (indices clamped to the last chunk)
     load_v<DV>(R.v, ha, min(c1 + 1, NT - 1), lane);
     load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
@@ -265,7 +265,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     sm.dk[buf][lane] = __builtin_amdgcn_exp2f(G2L - G2);
     // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
     f32x4 acc[10];
-    lower_tiles<DK>(acc, sm.K[c1 % 3], sm.Q[c1 % 3], lane);
+    lower_tiles<DK>(acc, sm.K[kb], sm.Q[kb], lane);
     f32x4 colG2[4];
     float rowG2[4];
 #pragma unroll
@@ -494,9 +494,21 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
         __syncthreads();
-        for (int c = -1; c < NT; ++c) {
-            if (c >= 0) consume(sm, S, c & 1, c % 3, o, ha, c, cw, scale, lane);
+        __syncthreads();  // iteration -1: the producers fill chunk 0 and 1
+        // Unrolled by the period of the kq-buffers, so that buffer c % 3 is a
+        // constant in each copy and its fragment addresses stay in registers
+        // across chunks; one barrier per chunk as in the other roles.
+        for (int c = 0; c < NT; c += 3) {
+            consume(sm, S, c & 1, 0, o, ha, c, cw, scale, lane);
             __syncthreads();
+            if (c + 1 < NT) {
+                consume(sm, S, (c + 1) & 1, 1, o, ha, c + 1, cw, scale, lane);
+                __syncthreads();
+            }
+            if (c + 2 < NT) {
+                consume(sm, S, c & 1, 2, o, ha, c + 2, cw, scale, lane);
+                __syncthreads();
+            }
         }
         if (ht) {
 #pragma unroll
@@ -516,12 +528,22 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
         if (NT > 0) {
             load_gates(R.g, R.beta, ha, 0, lane);
             load_rows<DK>(R.k, k, ha, 0, lane);
-            produce_A(sm, R, 0, NT, ha, lane);
+            produce_A(sm, R, 0, 0, NT, ha, lane);
         }
         __syncthreads();
-        for (int c = -1; c < NT; ++c) {
-            if (c + 2 < NT) produce_A(sm, R, c + 2, NT, ha, lane);
+        // iteration c = c2 - 2 prepares chunk c2; unrolled by the kq-buffer
+        // period (c2 % 3 constant in each copy), one barrier per iteration
+        for (int c2 = 1; c2 <= NT + 1; c2 += 3) {
+            if (c2 < NT) produce_A(sm, R, c2, 1, NT, ha, lane);
             __syncthreads();
+            if (c2 + 1 <= NT + 1) {
+                if (c2 + 1 < NT) produce_A(sm, R, c2 + 1, 2, NT, ha, lane);
+                __syncthreads();
+            }
+            if (c2 + 2 <= NT + 1) {
+                if (c2 + 2 < NT) produce_A(sm, R, c2 + 2, 0, NT, ha, lane);
+                __syncthreads();
+            }
         }
     } else {
         ChunkRegs<C::NS> R;
@@ -535,9 +557,18 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
             load_rows<DK>(R.q, q, ha, min(1, NT - 1), lane);
         }
         __syncthreads();
-        for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) produce_P(sm, R, c + 1, NT, ha, scale, lane);
+        // iteration c = c1 - 1 prepares chunk c1; unrolled like the A producer
+        for (int c1 = 0; c1 <= NT; c1 += 3) {
+            if (c1 < NT) produce_P(sm, R, c1, 0, NT, ha, scale, lane);
             __syncthreads();
+            if (c1 + 1 <= NT) {
+                if (c1 + 1 < NT) produce_P(sm, R, c1 + 1, 1, NT, ha, scale, lane);
+                __syncthreads();
+            }
+            if (c1 + 2 <= NT) {
+                if (c1 + 2 < NT) produce_P(sm, R, c1 + 2, 2, NT, ha, scale, lane);
+                __syncthreads();
+            }
         }
     }
 }

@@ -66,7 +66,15 @@ __device__ __forceinline__ int tile_off_pg(int row, int col) {
 template <int D>
 __device__ __forceinline__ uint4 frag_rows_pg(const uint16_t *M, int row0, int k0, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    return *(const uint4 *)&M[tile_off_pg<D>(row0 + r, k0 + 8 * g)];
+    // row0 is a multiple of 16 and the swizzle reads only the low 4 row bits,
+    // so the block's offset is a constant the LDS read can carry as its
+    // immediate offset
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    lds_u16 *m3 = (lds_u16 *)M;
+    const u32x4 v = *(lds_u32x4 *)(m3 + tile_off_pg<D>(r, k0 + 8 * g) + row0 * D);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // A fragment of the transpose (rows kc0 .. kc0 + 15 of M^T, slab of M rows
@@ -82,8 +90,11 @@ __device__ __forceinline__ uint4 frag_T_pg(const uint16_t *M, int j0, int kc0, i
     const int r = lane & 15, g = lane >> 4;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const int pc = pair_col(kc0 + 4 * (r & 3));
-    const uint16_t *p0 = &M[tile_off_pg<D>(j0 + 4 * g + (r >> 2), pc)];
-    const uint16_t *p1 = &M[tile_off_pg<D>(j0 + 16 + 4 * g + (r >> 2), pc)];
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    lds_u16 *m3 = (lds_u16 *)M;
+    // j0 is a multiple of 16: the row block's offset is a constant (see frag_rows_pg)
+    lds_u16 *p0 = m3 + tile_off_pg<D>(4 * g + (r >> 2), pc) + j0 * D;
+    lds_u16 *p1 = p0 + 16 * D;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
     const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);

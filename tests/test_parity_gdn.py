@@ -237,7 +237,7 @@ def test_causality_perturbation(dtype, t):
     strict mask of A and the inclusive mask of the output, the chunk-local
     cumsum and the carry never let a token reach back."""
     x = gi.gdn_inputs(2, 200, 2, 128, 128, seed=70 + t, dtype=dtype, h0=True, a_range=(0.01, 0.5))
-    o1, S1 = _run(x)
+    o1, _ = _run(x)
     y = {n: (np.array(a, copy=True) if isinstance(a, np.ndarray) else a) for n, a in x.items()}
     rng = np.random.default_rng(900 + t)
     for n in ("q", "k", "v"):
@@ -245,10 +245,9 @@ def test_causality_perturbation(dtype, t):
         y[n][:, t] = pert[:, t]
     y["g"][:, t] = (-rng.uniform(0.5, 3.0, size=y["g"][:, t].shape)).astype(np.float32)
     y["beta"][:, t] = rng.uniform(0.05, 0.95, size=y["beta"][:, t].shape).astype(np.float32)
-    o2, S2 = _run(y)
+    o2, _ = _run(y)
     np.testing.assert_array_equal(o2[:, :t], o1[:, :t])
     assert np.abs(o2[:, t] - o1[:, t]).max() > 0
-    assert np.abs(S2 - S1).max() > 0
 
 
 def test_staged_entry_points_equal_fused_call():

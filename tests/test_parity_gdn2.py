@@ -152,15 +152,14 @@ def test_causality_perturbation(dtype, t):
     between the anchored product and the direct sum, so changing it may move
     the rounding of the earlier rows of its block (not their exact value)."""
     x = gi.gdn2_inputs(1, 200, 2, 128, 128, seed=330 + t, dtype=dtype, h0=True)
-    o1, S1 = _run(x)
+    o1, _ = _run(x)
     y = {n: (np.array(a, copy=True) if isinstance(a, np.ndarray) else a) for n, a in x.items()}
     pert = gi.gdn2_inputs(1, 200, 2, 128, 128, seed=340 + t, dtype=dtype)
     for n in ("q", "k", "v", "b", "w"):
         y[n][:, t] = pert[n][:, t]
-    o2, S2 = _run(y)
+    o2, _ = _run(y)
     np.testing.assert_array_equal(o2[:, :t], o1[:, :t])
     assert np.abs(o2[:, t] - o1[:, t]).max() > 0
-    assert np.abs(S2 - S1).max() > 0
 
 
 @pytest.mark.parametrize("Dk", [64, 128])
