@@ -16,7 +16,7 @@ __all__ = [
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
     "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_prologue", "gdn_gated_rmsnorm",
-    "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace",
+    "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace", "gdn2_chunk_fwd_noalloc", "gdn2_chunk_fwd_noalloc_max_bytes",
     "GDN_F32", "GDN_BF16", "BT",
 ]
 
@@ -71,6 +71,10 @@ def load():
     lib.gdn2_chunk_bwd.argtypes = [_vp] * 16 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_prologue.restype = _i
     lib.gdn_prologue.argtypes = [_vp] * 17 + [_i] * 5 + [_vp]
+    lib.gdn2_chunk_fwd_noalloc.restype = _i
+    lib.gdn2_chunk_fwd_noalloc.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
+    lib.gdn2_chunk_fwd_noalloc_max_bytes.restype = _sz
+    lib.gdn2_chunk_fwd_noalloc_max_bytes.argtypes = []
     lib.gdn_gated_rmsnorm.restype = _i
     lib.gdn_gated_rmsnorm.argtypes = [_vp] * 4 + [ctypes.c_longlong, _i, _f, _vp]
     _lib = lib
@@ -385,6 +389,43 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, h0=None, scale=None, output_final_s
     _check(lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(h0), _ptr(o),
                               _ptr(ht), B, T, H, Dk, Dv, dt, float(scale), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(dev)), "gdn2_chunk_fwd")
+    return o, ht
+
+
+def gdn2_chunk_fwd_noalloc_max_bytes() -> int:
+    """Size of the library's fixed device workspace used by gdn2_chunk_fwd_noalloc."""
+    return int(load().gdn2_chunk_fwd_noalloc_max_bytes())
+
+
+def gdn2_chunk_fwd_noalloc(q, k, v, log_alpha, b, w, h0=None, scale=None, out=None, final_state=None):
+    """gdn2_chunk_fwd through the entry point that takes its workspace from the
+    library's fixed device array instead of an argument.  `out` (and
+    `final_state`, when the final state is wanted) should be preallocated by
+    callers that cannot allocate; otherwise they are allocated here with torch
+    (the C entry point itself allocates nothing).  Returns (o, ht or None)."""
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, Dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, Dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (B, T, H, Dk), torch.float32, dev)
+    _need(b, "b", (B, T, H, Dk), q.dtype, dev)
+    _need(w, "w", (B, T, H, Dv), q.dtype, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _need(o, "out", (B, T, H, Dv), torch.float32, dev)
+    ht = final_state
+    if ht is not None:
+        _need(ht, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    _check(load().gdn2_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(h0),
+                                         _ptr(o), _ptr(ht), B, T, H, Dk, Dv, dt, float(scale), _stream(dev)),
+           "gdn2_chunk_fwd_noalloc")
     return o, ht
 
 

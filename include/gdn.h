@@ -151,6 +151,31 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * gdn2_chunk_fwd_noalloc -- gdn2_chunk_fwd for callers that cannot allocate
+ * device memory at all (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * gdn2_chunk_fwd, without ws / ws_bytes: the workspace is a fixed device
+ * array inside the library, GDN2_NOALLOC_SCRATCH_BYTES (144 MiB) per GPU,
+ * held from the library's first use on that GPU until the process ends.  It
+ * holds gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype) bytes: with bf16
+ * inputs and Dk = 128 up to 2,277 chunk-heads (B * H * ceil(T / 64)), e.g.
+ * B = 4, H = 8, T = 4096.  Larger sizes return GDN_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing; its first call on a
+ * device looks up that device's copy of the array.  Every call on one GPU
+ * shares that copy, so calls that overlap on one GPU (several streams or
+ * host threads) race: the caller serialises them.
+ */
+#define GDN2_NOALLOC_SCRATCH_BYTES (144u * 1024u * 1024u)
+
+size_t gdn2_chunk_fwd_noalloc_max_bytes(void);
+
+gdn_status gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const void *b, const void *w,
+                                  const float *h0, float *o, float *ht,
+                                  int B, int T, int H, int Dk, int Dv, gdn_dtype dtype,
+                                  float scale, void *stream);
+
+/*
  * gdn_recurrent_step -- one decode token of Gated DeltaNet, state updated in
  * place (the per-token loop of the walkthrough's "Delta Rule" section):
  *   S <- exp(g) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = scale S^T q

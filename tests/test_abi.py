@@ -223,3 +223,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "lib_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         gdn.load()
+
+
+def test_noalloc_rejects_sizes_beyond_its_array():
+    """gdn2_chunk_fwd_noalloc refuses, on the host, sizes whose workspace exceeds
+    the fixed device array (fake pointers: nothing is launched or touched)."""
+    lib = gdn.load()
+    cap = lib.gdn2_chunk_fwd_noalloc_max_bytes()
+    assert cap == 144 << 20
+    B, T, H = 8, 8192, 8          # 8,192 chunk-heads of ~65 KB each
+    assert lib.gdn2_chunk_fwd_workspace(B, T, H, 128, 128, 1) > cap
+    a = [_p(FAKE + (i << 32)) for i in range(9)]
+    assert lib.gdn2_chunk_fwd_noalloc(*a, B, T, H, 128, 128, 1, 0.1, None) == 3
+    assert lib.gdn2_chunk_fwd_noalloc(*a, 0, T, H, 128, 128, 1, 0.1, None) == 1
+    assert lib.gdn2_chunk_fwd_noalloc(*a, 1, T, H, 96, 128, 1, 0.1, None) == 2
