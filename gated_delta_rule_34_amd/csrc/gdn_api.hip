@@ -52,6 +52,55 @@ bool sizes_ok(int B, int T, int H) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Chunk-parallel plan for the bf16 forward of a dense batch (gdn_fused.hip,
+// SegArgs).  The single kernel runs (Dv / 32) workgroups per head, one per
+// compute unit, each walking every chunk in order; when that fills less than
+// half of the 256 compute units, each sequence is cut into NS segments of L
+// chunks.  The walk launch runs 2 NS - 3 workgroup sets per head (one for
+// segment 0's end state, two per middle segment), so NS is the largest count
+// for which they fit the compute units in one round; the single kernel then
+// runs the NS segments of every head together.  NS = 0: no plan.
+struct SegPlan {
+    int NS, L;
+};
+
+constexpr int kPlanCUs = 256;  // compute units of the MI355X
+
+SegPlan seg_plan(int B, int T, int H, int Dk, int Dv) {
+    SegPlan p{0, 0};
+    if (Dk != Dv) return p;
+    const long sets = (long)B * H * (Dv / 32);   // workgroups of the single kernel
+    if (sets * 2 > kPlanCUs) return p;
+    const int NT = (T + kBT - 1) / kBT;
+    int ns = (int)((kPlanCUs / sets + 3) / 2);
+    if (ns > 16) ns = 16;
+    for (; ns >= 3; --ns) {
+        const int L = (NT + ns - 1) / ns;
+        if (L >= 8 && (ns - 1) * L < NT) {
+            p = SegPlan{ns, L};
+            return p;
+        }
+    }
+    return p;
+}
+
+// Workspace of the plan: Hin, Hout, M [B NS, H, D, D] fp32, then the B NS + 1
+// segment offsets (int32); each section 256-byte aligned.
+struct SegWs {
+    size_t hin, hout, m, cu, total;
+};
+
+SegWs seg_ws(int B, int H, int D, const SegPlan &p) {
+    const size_t st = align_up((size_t)B * p.NS * H * D * D * sizeof(float));
+    SegWs w;
+    w.hin = 0;
+    w.hout = st;
+    w.m = 2 * st;
+    w.cu = 3 * st;
+    w.total = w.cu + align_up(((size_t)B * p.NS + 1) * sizeof(int));
+    return w;
+}
+
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 }  // namespace
@@ -73,7 +122,10 @@ const char *gdn_status_string(gdn_status s) {
 // inputs take the two-stage path (intra-chunk stage, then the state walk).
 size_t gdn_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
     if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
-    if (dtype == GDN_BF16) return kAlign;
+    if (dtype == GDN_BF16) {
+        const SegPlan p = seg_plan(B, T, H, Dk, Dv);
+        return p.NS ? seg_ws(B, H, Dk, p).total : kAlign;
+    }
     return chunk_ws(B, T, H).total;
 }
 
@@ -103,7 +155,12 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (fused && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)))
         return GDN_ERR_INVALID_ARG;
     const ChunkWs lay = chunk_ws(B, T, H);
-    const Range rws{fused ? nullptr : ws, lay.total};
+    // bf16: the chunk-parallel scan when planned and the workspace holds it
+    const SegPlan plan = fused ? seg_plan(B, T, H, Dk, Dv) : SegPlan{0, 0};
+    const SegWs slay = plan.NS ? seg_ws(B, H, Dk, plan) : SegWs{0, 0, 0, 0, 0};
+    const size_t seg_bytes = slay.total;
+    const bool seg = plan.NS && ws && aligned(ws, kAlign) && ws_bytes >= seg_bytes;
+    const Range rws{fused ? (seg ? ws : nullptr) : ws, fused ? seg_bytes : lay.total};
     // Outputs may not overlap inputs, each other or the workspace; ht may be exactly h0.
     for (Range in : {rq, rk, rv, rg, rb, rh0, rws})
         if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
@@ -113,6 +170,14 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
             if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
     }
     hipStream_t st = (hipStream_t)stream;
+    if (seg) {
+        for (Range in : {rq, rk, rv, rg, rb, rh0})
+            if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
+        char *base = (char *)ws;
+        return from_hip(gdn::launch_fused_seg_bf16(q, k, v, g, beta, h0, o, ht, B, T, H, Dk, scale, plan.NS, plan.L,
+                                                   (float *)(base + slay.hin), (float *)(base + slay.hout),
+                                                   (float *)(base + slay.m), (int *)(base + slay.cu), st));
+    }
     if (fused)
         return from_hip(gdn::launch_fused_bf16(q, k, v, g, beta, h0, o, ht, nullptr, B, T, H, Dk, Dv, scale, st));
     if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;

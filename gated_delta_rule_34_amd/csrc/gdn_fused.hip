@@ -82,12 +82,12 @@ struct FusedSmem {
 };
 
 // Raw inputs of one chunk held by a producer lane (lane = (g, r)):
-// k/q rows 16I + r, columns 32s + 8g .. +7 as 8 bf16 in a uint4.
+// k/q rows 16I + r, columns 32s + 8g .. +7 as 8 bf16 in 16 bytes.
 template <int NS>
 struct ChunkRegs {
-    uint4 k[4][NS];
-    uint4 q[4][NS];
-    uint4 v[4];   // V tile rows 16p + lane/4, 8 columns at (lane%4)*8
+    u32x4 k[4][NS];
+    u32x4 q[4][NS];
+    u32x4 v[4];   // V tile rows 16p + lane/4, 8 columns at (lane%4)*8
     float g, beta;
 };
 
@@ -99,6 +99,38 @@ struct HeadArgs {
     const float *g, *beta;
     long tok0;
     int h, T, H, vcol0;
+    bool zero_v;  // walk with all values zero (a segment's transfer matrix)
+};
+
+// A long sequence in segments (chunk-parallel state scan).  Segment s of
+// sequence b holds chunks [s L, min((s + 1) L, NT)).  Per chunk the state map
+// is affine, S' = M_c S + N_c, so a segment's end state is M_s S_in + E_s, with
+// E_s its end state from a zero start and M_s the product of its M_c.
+//   walk launch (fused_walk_kernel): for segment 0 its end state from h0, for
+//     every middle segment 1 .. NS - 2 the output-free walks that give E_s and
+//     M_s (the identity columns walked with zero values); E_s goes to
+//     Hin[b NS + s + 1], M_s to M[b NS + s];
+//   scan (seg_scan_kernel): Hin[b NS] = h0, and Hin[b NS + s + 1] =
+//     M_s Hin[b NS + s] + E_s for s = 1 .. NS - 2, so Hin[b NS + s] is the true
+//     entry state of segment s; it also writes the segment offsets cu;
+//   then the ordinary single kernel runs the B NS segments as packed
+//     sequences (cu, initial states Hin, final states Hout) and the final
+//     state of each sequence is Hout[b NS + NS - 1].
+// Hin, Hout: [B NS, H, Dk, Dk] fp32; M: [B NS, H, Dk, Dk] fp32 (Dv = Dk here).
+struct SegArgs {
+    int L, NS;
+    float *Hin, *M;
+};
+
+// What one workgroup computes: the rows of its sequence, its initial state
+// (h0 rows of this head, or null for zeros; or the identity), where its final
+// state goes (or null), and its output (or null for a walk without output).
+struct WgJob {
+    HeadArgs ha;
+    const float *h0;
+    float *ht;
+    float *o;
+    bool ident;
 };
 
 // The loaders are branch-free, so the compiler can count the loads in
@@ -107,7 +139,7 @@ struct HeadArgs {
 // beta = g = 0 there (load_gates zeroes them) such rows add nothing to A,
 // T - I, the new values or the state, and their outputs are not stored.
 template <int DK>
-__device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16_t *__restrict__ src,
+__device__ __forceinline__ void load_rows(u32x4 (&dst)[4][DK / 32], const uint16_t *__restrict__ src,
                                           const HeadArgs &a, int chunk, int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -115,16 +147,16 @@ __device__ __forceinline__ void load_rows(uint4 (&dst)[4][DK / 32], const uint16
         const int t = min(chunk * BT + 16 * I + r, a.T - 1);
         const uint16_t *p = src + ((a.tok0 + t) * a.H + a.h) * (long)DK + 8 * g;
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) dst[I][s] = *(const uint4 *)(p + 32 * s);
+        for (int s = 0; s < DK / 32; ++s) dst[I][s] = *(const u32x4 *)(p + 32 * s);
     }
 }
 
 template <int DV>
-__device__ __forceinline__ void load_v(uint4 (&dst)[4], const HeadArgs &a, int chunk, int lane) {
+__device__ __forceinline__ void load_v(u32x4 (&dst)[4], const HeadArgs &a, int chunk, int lane) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int t = min(chunk * BT + 16 * p + (lane >> 2), a.T - 1);
-        dst[p] = *(const uint4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 + (lane & 3) * 8);
+        dst[p] = *(const u32x4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 + (lane & 3) * 8);
     }
 }
 
@@ -146,15 +178,15 @@ __device__ __forceinline__ void finish_gates(float &gv, float &bv, const HeadArg
 // the paired-group layout (the two 4-column halves of a register go to
 // their stored groups).
 template <int DK>
-__device__ __forceinline__ void write_rows(uint16_t *dst, const uint4 (&src)[4][DK / 32], int lane) {
+__device__ __forceinline__ void write_rows(uint16_t *dst, const u32x4 (&src)[4][DK / 32], int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
             const int row = 16 * I + r, c0 = 32 * s + 8 * g;
-            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(src[I][s].x, src[I][s].y);
-            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(src[I][s].z, src[I][s].w);
+            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0))] = make_uint2(src[I][s][0], src[I][s][1]);
+            *(uint2 *)&dst[tile_off_pg<DK>(row, pair_col(c0 + 4))] = make_uint2(src[I][s][2], src[I][s][3]);
         }
 }
 
@@ -236,7 +268,7 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 // rows in kq-buffer c1 % 3).  R holds V and the gates of chunk c1 and the raw
 // Q rows of chunk c1 + 1; those rows go to kq-buffer (c1 + 1) % 3 and R
 // receives the rows of chunk c1 + 2, a full iteration before they are stored.
-template <int DK, int DV>
+template <int DK, int DV, bool OUT, bool ZV>
 __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 32> &R, int c1, int kb, int NT,
                                           const HeadArgs &ha, float scale, int lane) {
     using C = FusedCfg<DK, DV>;
@@ -244,11 +276,14 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     const int buf = c1 & 1;
     // first store everything that arrived during the previous iteration: the
     // V tile, the gates and the raw Q rows of chunk c1 + 1 (when it is past
-    // the end, its buffer is written but never read)
+    // the end, its buffer is written but never read).  A walk with zero
+    // values (ZV) keeps the zeroed V buffers and loads no values.
+    if constexpr (!ZV) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
-        *(uint4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
+        for (int p = 0; p < 4; ++p) {
+            const int row = 16 * p + (lane >> 2), c0 = (lane & 3) * 8;
+            *(u32x4 *)&sm.V[buf][row * C::LDV + c0] = R.v[p];
+        }
     }
     finish_gates(R.g, R.beta, ha, c1, lane);
     const float G2 = chunk_g2(R.g);
@@ -256,13 +291,14 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     const float gmv = __builtin_amdgcn_exp2f(G2);
     sm.gam[buf][lane] = gmv;
     sm.beta[buf][lane] = R.beta;
-    write_rows<DK>(sm.Q[(kb + 1) % 3], R.q, lane);
+    if constexpr (OUT) write_rows<DK>(sm.Q[(kb + 1) % 3], R.q, lane);
     // then fetch the next ones together (indices clamped to the last chunk)
-    load_v<DV>(R.v, ha, min(c1 + 1, NT - 1), lane);
+    if constexpr (!ZV) load_v<DV>(R.v, ha, min(c1 + 1, NT - 1), lane);
     load_gates(R.g, R.beta, ha, min(c1 + 1, NT - 1), lane);
-    load_rows<DK>(R.q, ha.q, ha, min(c1 + 2, NT - 1), lane);
+    if constexpr (OUT) load_rows<DK>(R.q, ha.q, ha, min(c1 + 2, NT - 1), lane);
     const float G2L = sm.g2P[BT - 1];
     sm.dk[buf][lane] = __builtin_amdgcn_exp2f(G2L - G2);
+    if constexpr (!OUT) return;  // a walk without output needs no P
     // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
     f32x4 acc[10];
     lower_tiles<DK>(acc, sm.K[kb], sm.Q[kb], lane);
@@ -291,7 +327,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 }
 
 // ---------------------------------------------------------------- consumers
-template <int DK, int DV>
+template <int DK, int DV, bool OUT>
 __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, int kb,
                                         float *__restrict__ o, const HeadArgs &ha, int chunk, int cw, float scale,
                                         int lane) {
@@ -329,14 +365,16 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             kf[I] = __builtin_bit_cast(bf16x8, frag_rows_pg<DK>(sm.K[kb], 16 * I, 32 * s, lane));
-            qf[I] = __builtin_bit_cast(bf16x8, frag_rows_pg<DK>(sm.Q[kb], 16 * I, 32 * s, lane));
             X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[I], shi, X[I], 0, 0, 0);
-            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], shi, Y[I], 0, 0, 0);
+            if constexpr (OUT) {
+                qf[I] = __builtin_bit_cast(bf16x8, frag_rows_pg<DK>(sm.Q[kb], 16 * I, 32 * s, lane));
+                Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], shi, Y[I], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[I], slo, X[I], 0, 0, 0);
-            Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], slo, Y[I], 0, 0, 0);
+            if constexpr (OUT) Y[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[I], slo, Y[I], 0, 0, 0);
         }
     }
     // R = beta (V - gamma X)
@@ -396,6 +434,7 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
         }
         S[m] = acc;
     }
+    if constexpr (!OUT) return;  // a walk without output ends with the carry
     // O = scale (gamma Y + diag(q.k) Vnew + strict(P) Vnew), with scale folded
     // into the diag and P tables
     _Float16 vf[2][8];
@@ -431,8 +470,159 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
     }
 }
 
+// Consumer role: the state slice of this wave from the job's initial state (or
+// the identity columns of a transfer-matrix walk), the chunks in order, and
+// the final state to the job's destination.
+template <int DK, int DV, bool OUT>
+__device__ __forceinline__ void run_consumer(FusedSmem<DK, DV> &sm, const WgJob &job, int NT, int cw, float scale,
+                                             int lane) {
+    using C = FusedCfg<DK, DV>;
+    const int r = lane & 15, g = lane >> 4;
+    const HeadArgs &ha = job.ha;
+    f32x4 S[C::NKB];
+    const int col = ha.vcol0 + cw * 16 + r;
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * m + 4 * g + e;
+            S[m][e] = job.ident ? (row == col ? 1.f : 0.f) : (job.h0 ? job.h0[(long)row * DV + col] : 0.f);
+        }
+    __syncthreads();
+    __syncthreads();  // iteration -1: the producers fill chunk 0 and 1
+    // Unrolled by the period of the kq-buffers, so that buffer c % 3 is a
+    // constant in each copy and its fragment addresses stay in registers
+    // across chunks; one barrier per chunk as in the other roles.
+    for (int c = 0; c < NT; c += 3) {
+        consume<DK, DV, OUT>(sm, S, c & 1, 0, job.o, ha, c, cw, scale, lane);
+        __syncthreads();
+        if (c + 1 < NT) {
+            consume<DK, DV, OUT>(sm, S, (c + 1) & 1, 1, job.o, ha, c + 1, cw, scale, lane);
+            __syncthreads();
+        }
+        if (c + 2 < NT) {
+            consume<DK, DV, OUT>(sm, S, c & 1, 2, job.o, ha, c + 2, cw, scale, lane);
+            __syncthreads();
+        }
+    }
+    if (job.ht) {
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) job.ht[(long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
+    }
+}
+
+// P-producer role (see produce_P).
+template <int DK, int DV, bool OUT, bool ZV>
+__device__ __forceinline__ void run_p_producer(FusedSmem<DK, DV> &sm, const HeadArgs &ha, int NT, float scale,
+                                               int lane) {
+    using C = FusedCfg<DK, DV>;
+    ChunkRegs<C::NS> R;
+    // chunk 0's raw Q rows go to kq-buffer 0 before the first barrier;
+    // chunk 1's wait in registers (an empty sequence loads nothing)
+    if (NT > 0) {
+        if constexpr (!ZV) load_v<DV>(R.v, ha, 0, lane);
+        load_gates(R.g, R.beta, ha, 0, lane);
+        if constexpr (OUT) {
+            load_rows<DK>(R.q, ha.q, ha, 0, lane);
+            write_rows<DK>(sm.Q[0], R.q, lane);
+            load_rows<DK>(R.q, ha.q, ha, min(1, NT - 1), lane);
+        }
+    }
+    __syncthreads();
+    // iteration c = c1 - 1 prepares chunk c1; unrolled like the A producer
+    for (int c1 = 0; c1 <= NT; c1 += 3) {
+        if (c1 < NT) produce_P<DK, DV, OUT, ZV>(sm, R, c1, 0, NT, ha, scale, lane);
+        __syncthreads();
+        if (c1 + 1 <= NT) {
+            if (c1 + 1 < NT) produce_P<DK, DV, OUT, ZV>(sm, R, c1 + 1, 1, NT, ha, scale, lane);
+            __syncthreads();
+        }
+        if (c1 + 2 <= NT) {
+            if (c1 + 2 < NT) produce_P<DK, DV, OUT, ZV>(sm, R, c1 + 2, 2, NT, ha, scale, lane);
+            __syncthreads();
+        }
+    }
+}
+
+// What one workgroup computes.  Dense batch: (batch b, head h, 32 value
+// columns) over the whole sequence.  Packed sequences: the same for sequence
+// n of cu_seqlens.  Segmented (a long sequence split into segments whose
+// entry states come from a scan, see SegArgs): one segment of one head, either
+// in full (output and final state) or as an output-free walk that records the
+// segment's end state from a zero start (E) or its transfer matrix (M: zero
+// values, the identity as initial state).
+template <int DK, int DV, bool SEG>
+__device__ __forceinline__ WgJob decode_job(int L, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                            const float *gin, const float *betain, const float *h0, float *o,
+                                            float *ht, const int *cu_seqlens, int T, int H, const SegArgs &sg) {
+    using C = FusedCfg<DK, DV>;
+    constexpr int W = DV / C::BV;  // column slices per head
+    WgJob job;
+    HeadArgs &ha = job.ha;
+    ha.q = q; ha.k = k; ha.v = v; ha.g = gin; ha.beta = betain;
+    ha.H = H;
+    ha.zero_v = false;
+    job.ident = false;
+    job.o = o;
+    if constexpr (!SEG) {
+        const int vt = L % W;
+        const long bh = L / W;
+        ha.h = (int)(bh % H);
+        ha.vcol0 = vt * C::BV;
+        if (cu_seqlens) {
+            // packed sequences: T is the total token count; the bounds are clamped
+            // into [0, T] so that malformed offsets can never address out of range
+            const long n_seq = bh / H;
+            const int s0 = min(max(cu_seqlens[n_seq], 0), T);
+            const int s1 = min(max(cu_seqlens[n_seq + 1], s0), T);
+            ha.tok0 = s0;
+            ha.T = s1 - s0;
+        } else {
+            ha.tok0 = (bh / H) * (long)T;
+            ha.T = T;
+        }
+        const long sbase = bh * (long)DK * DV;
+        job.h0 = h0 ? h0 + sbase : nullptr;
+        job.ht = ht ? ht + sbase : nullptr;
+    } else {
+        // walk launch: per head, W workgroups for segment 0's end state, then
+        // 2 W per middle segment (W for E_s, W for M_s)
+        const int per_head = W + 2 * W * (sg.NS - 2);
+        const long bh = L / per_head;
+        const int j = L % per_head;
+        const long b = bh / H;
+        ha.h = (int)(bh % H);
+        job.o = nullptr;
+        job.h0 = nullptr;
+        int seg, slice;
+        if (j < W) {
+            seg = 0;
+            slice = j;
+            job.h0 = h0 ? h0 + bh * (long)DK * DV : nullptr;
+        } else {
+            const int kk = j - W;
+            seg = 1 + kk / (2 * W);
+            slice = kk % (2 * W);
+            if (slice >= W) {
+                slice -= W;
+                job.ident = true;
+                ha.zero_v = true;
+            }
+        }
+        job.ht = job.ident ? sg.M + ((b * sg.NS + seg) * H + ha.h) * (long)DK * DV
+                           : sg.Hin + ((b * sg.NS + seg + 1) * H + ha.h) * (long)DK * DV;
+        ha.vcol0 = slice * C::BV;
+        const int c0 = seg * sg.L;
+        ha.tok0 = b * (long)T + (long)c0 * BT;
+        ha.T = min(T, (c0 + sg.L) * BT) - c0 * BT;
+    }
+    return job;
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t *__restrict__ q,
+__global__ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ k,
                                                        const uint16_t *__restrict__ v,
                                                        const float *__restrict__ gin,
@@ -457,6 +647,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
     ha.h = (int)(bh % H);
     ha.H = H;
     ha.vcol0 = vt * C::BV;
+    ha.zero_v = false;
     if (cu_seqlens) {
         // packed sequences: T is the total token count; the bounds are clamped
         // into [0, T] so that malformed offsets can never address out of range
@@ -499,14 +690,14 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
         // constant in each copy and its fragment addresses stay in registers
         // across chunks; one barrier per chunk as in the other roles.
         for (int c = 0; c < NT; c += 3) {
-            consume(sm, S, c & 1, 0, o, ha, c, cw, scale, lane);
+            consume<DK, DV, true>(sm, S, c & 1, 0, o, ha, c, cw, scale, lane);
             __syncthreads();
             if (c + 1 < NT) {
-                consume(sm, S, (c + 1) & 1, 1, o, ha, c + 1, cw, scale, lane);
+                consume<DK, DV, true>(sm, S, (c + 1) & 1, 1, o, ha, c + 1, cw, scale, lane);
                 __syncthreads();
             }
             if (c + 2 < NT) {
-                consume(sm, S, c & 1, 2, o, ha, c + 2, cw, scale, lane);
+                consume<DK, DV, true>(sm, S, c & 1, 2, o, ha, c + 2, cw, scale, lane);
                 __syncthreads();
             }
         }
@@ -559,18 +750,172 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(const uint16_t 
         __syncthreads();
         // iteration c = c1 - 1 prepares chunk c1; unrolled like the A producer
         for (int c1 = 0; c1 <= NT; c1 += 3) {
-            if (c1 < NT) produce_P(sm, R, c1, 0, NT, ha, scale, lane);
+            if (c1 < NT) produce_P<DK, DV, true, false>(sm, R, c1, 0, NT, ha, scale, lane);
             __syncthreads();
             if (c1 + 1 <= NT) {
-                if (c1 + 1 < NT) produce_P(sm, R, c1 + 1, 1, NT, ha, scale, lane);
+                if (c1 + 1 < NT) produce_P<DK, DV, true, false>(sm, R, c1 + 1, 1, NT, ha, scale, lane);
                 __syncthreads();
             }
             if (c1 + 2 <= NT) {
-                if (c1 + 2 < NT) produce_P(sm, R, c1 + 2, 2, NT, ha, scale, lane);
+                if (c1 + 2 < NT) produce_P<DK, DV, true, false>(sm, R, c1 + 2, 2, NT, ha, scale, lane);
                 __syncthreads();
             }
         }
     }
+}
+
+
+// Producer role of the walk kernel: the A producer's work for chunk c + 2
+// (its K rows to the kq-buffer, A) and the output-free P producer's work for
+// chunk c + 1 (V unless the values are zero, the gate tables), in one wave.
+template <int DK, int DV, bool ZV>
+__device__ __forceinline__ void run_walk_producer(FusedSmem<DK, DV> &sm, const HeadArgs &ha, int NT, float scale,
+                                                  int lane) {
+    using C = FusedCfg<DK, DV>;
+    ChunkRegs<C::NS> RA, RP;
+    if (NT > 0) {
+        load_gates(RA.g, RA.beta, ha, 0, lane);
+        load_rows<DK>(RA.k, ha.k, ha, 0, lane);
+        if constexpr (!ZV) load_v<DV>(RP.v, ha, 0, lane);
+        load_gates(RP.g, RP.beta, ha, 0, lane);
+        produce_A(sm, RA, 0, 0, NT, ha, lane);
+    }
+    __syncthreads();
+    // iteration c = c2 - 2 (A of chunk c2, tables of chunk c2 - 1); unrolled
+    // by the kq-buffer period, one barrier per iteration
+    for (int c2 = 1; c2 <= NT + 1; c2 += 3) {
+        if (c2 < NT) produce_A(sm, RA, c2, 1, NT, ha, lane);
+        if (c2 - 1 < NT) produce_P<DK, DV, false, ZV>(sm, RP, c2 - 1, 0, NT, ha, scale, lane);
+        __syncthreads();
+        if (c2 + 1 <= NT + 1) {
+            if (c2 + 1 < NT) produce_A(sm, RA, c2 + 1, 2, NT, ha, lane);
+            if (c2 < NT) produce_P<DK, DV, false, ZV>(sm, RP, c2, 1, NT, ha, scale, lane);
+            __syncthreads();
+        }
+        if (c2 + 2 <= NT + 1) {
+            if (c2 + 2 < NT) produce_A(sm, RA, c2 + 2, 0, NT, ha, lane);
+            if (c2 + 1 < NT) produce_P<DK, DV, false, ZV>(sm, RP, c2 + 1, 2, NT, ha, scale, lane);
+            __syncthreads();
+        }
+    }
+}
+
+constexpr int kWalkThreads = 256;  // four waves
+
+// Output-free walks of the chunk-parallel scan (SegArgs): the consumers carry
+// the state (or the identity columns of a transfer matrix) through the
+// segment and store it at its end.  Four waves, one per SIMD: the inverse,
+// two consumers, and one producer for A and the gate tables.
+template <int DK, int DV>
+__global__ __launch_bounds__(kWalkThreads, 1) void fused_walk_kernel(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ k,
+                                                       const uint16_t *__restrict__ v,
+                                                       const float *__restrict__ gin,
+                                                       const float *__restrict__ betain,
+                                                       const float *__restrict__ h0, float *__restrict__ o,
+                                                       float *__restrict__ ht, int T, int H, float scale,
+                                                       SegArgs sg) {
+    using C = FusedCfg<DK, DV>;
+    static_assert(sizeof(FusedSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ FusedSmem<DK, DV> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Workgroup n runs on XCD n % 8; give the slices of one head consecutive
+    // ids on one XCD so they share its L2 for K.
+    const int n = blockIdx.x, nwg = gridDim.x;
+    const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
+    // Every role decodes the job itself, so that no part of it stays live
+    // across the role branch.
+#define GDN_JOB decode_job<DK, DV, true>(L, q, k, v, gin, betain, h0, o, ht, nullptr, T, H, sg)
+    {
+        const WgJob job = GDN_JOB;
+        // the upper tiles of T - I are read by the consumers but never written;
+        // a walk with zero values never stores V
+        for (int idx = tid; idx < 2 * BT * C::LDP; idx += kWalkThreads) (&sm.Tm[0][0])[idx] = (_Float16)0.f;
+        if (job.ha.zero_v)
+            for (int idx = tid; idx < 2 * BT * C::LDV; idx += kWalkThreads) (&sm.V[0][0])[idx] = 0;
+    }
+    if (wave == 1 || wave == 2) {
+        const WgJob job = GDN_JOB;
+        const int NT = (job.ha.T + BT - 1) / BT;
+        run_consumer<DK, DV, false>(sm, job, NT, wave - 1, scale, lane);
+    } else if (wave == 0) {
+        const WgJob job = GDN_JOB;
+        const int NT = (job.ha.T + BT - 1) / BT;
+        __syncthreads();
+        for (int c = -1; c < NT; ++c) {
+            if (c + 1 < NT) unit_lower_inverse<C::LDP>(sm.A[(c + 1) & 1], sm.Tm[(c + 1) & 1], lane);
+            __syncthreads();
+        }
+    } else {
+        const WgJob job = GDN_JOB;
+        const HeadArgs &ha = job.ha;
+        const int NT = (ha.T + BT - 1) / BT;
+        if (ha.zero_v) run_walk_producer<DK, DV, true>(sm, ha, NT, scale, lane);
+        else run_walk_producer<DK, DV, false>(sm, ha, NT, scale, lane);
+    }
+#undef GDN_JOB
+}
+
+// Scan over the segments of one head, for a 32-column slice of the state:
+// Hin[b NS] = h0 (zeros when null); S = Hin[b NS + 1]; for s = 1 .. NS - 2:
+// S = M_s S + Hin[b NS + s + 1] (which holds E_s), stored back.  fp32 FMA with
+// M_s and the slice staged in LDS.  Workgroup 0 also writes the segment
+// offsets cu[n] (n = b NS + s: b T + s L 64; cu[B NS] = B T).
+template <int D>
+__global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ Hin, const float *__restrict__ M,
+                                                       const float *__restrict__ h0, int *__restrict__ cu, int B,
+                                                       int T, int H, int NS, int L) {
+    constexpr int CW = 32;
+    __shared__ float sM[D * (D + 1)];
+    __shared__ float sS[D * CW];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0)
+        for (int n = tid; n <= B * NS; n += 256) {
+            const int bb = n / NS, sg = n % NS;
+            cu[n] = n == B * NS ? B * T : bb * T + min(sg * L * BT, T);
+        }
+    const int slice = blockIdx.x % (D / CW);
+    const long bh = blockIdx.x / (D / CW);
+    const long b = bh / H, h = bh % H;
+    const long hs = (long)D * D;
+    const int col = tid % CW, rg = tid / CW;  // 8 row groups of D / 8 rows
+    constexpr int RPT = D / 8;
+    float *H0 = Hin + ((b * NS + 0) * H + h) * hs;
+    for (int idx = tid; idx < D * CW; idx += 256) {
+        const long off = (long)(idx / CW) * D + slice * CW + idx % CW;
+        H0[off] = h0 ? h0[bh * hs + off] : 0.f;
+    }
+    float *E1 = Hin + ((b * NS + 1) * H + h) * hs;
+    for (int idx = tid; idx < D * CW; idx += 256) sS[idx] = E1[(long)(idx / CW) * D + slice * CW + idx % CW];
+    for (int sgm = 1; sgm <= NS - 2; ++sgm) {
+        const float *Ms = M + ((b * NS + sgm) * H + h) * hs;
+        float *Es = Hin + ((b * NS + sgm + 1) * H + h) * hs;
+        __syncthreads();
+        for (int idx = tid; idx < D * D; idx += 256) sM[(idx / D) * (D + 1) + idx % D] = Ms[idx];
+        __syncthreads();
+        float acc[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) acc[i] = Es[(long)(rg * RPT + i) * D + slice * CW + col];
+        for (int kk = 0; kk < D; ++kk) {
+            const float sv = sS[kk * CW + col];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) acc[i] = fmaf(sM[(rg * RPT + i) * (D + 1) + kk], sv, acc[i]);
+        }
+        __syncthreads();  // every thread has read sS
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            sS[(rg * RPT + i) * CW + col] = acc[i];
+            Es[(long)(rg * RPT + i) * D + slice * CW + col] = acc[i];
+        }
+    }
+}
+
+// Final state of each sequence: the last segment's, Hout[b NS + NS - 1] -> ht[b].
+__global__ __launch_bounds__(256) void seg_final_kernel(const float *__restrict__ Hout, float *__restrict__ ht,
+                                                        long per_seq, int NS) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    const long b = blockIdx.y;
+    if (i < per_seq) ht[b * per_seq + i] = Hout[(b * NS + NS - 1) * per_seq + i];
 }
 
 template <int DK, int DV>
@@ -581,6 +926,41 @@ static hipError_t launch_fused_t(const void *q, const void *k, const void *v, co
     hipLaunchKernelGGL((fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(kFusedThreads), 0, st, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, o, ht, cu_seqlens, T, H, scale);
     return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fused_seg_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                     const float *h0, float *o, float *ht, int B, int T, int H, float scale, int NS,
+                                     int L, float *Hin, float *Hout, float *M, int *cu, hipStream_t st) {
+    constexpr int W = D / FusedCfg<D, D>::BV;
+    const SegArgs sg{L, NS, Hin, M};
+    const long gridA = (long)B * H * (W + 2 * W * (NS - 2));
+    hipLaunchKernelGGL((fused_walk_kernel<D, D>), dim3((unsigned)gridA), dim3(kWalkThreads), 0, st,
+                       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, h0, (float *)nullptr,
+                       (float *)nullptr, T, H, scale, sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_scan_kernel<D>), dim3((unsigned)(B * H * (D / 32))), dim3(256), 0, st, Hin,
+                       (const float *)M, h0, cu, B, T, H, NS, L);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_fused_t<D, D>(q, k, v, g, beta, Hin, o, ht ? Hout : nullptr, cu, B * NS, B * T, H, scale, st);
+    if (e != hipSuccess || !ht) return e;
+    const long per_seq = (long)H * D * D;
+    hipLaunchKernelGGL(seg_final_kernel, dim3((unsigned)((per_seq + 255) / 256), (unsigned)B), dim3(256), 0, st,
+                       (const float *)Hout, ht, per_seq, NS);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_seg_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                 const float *h0, float *o, float *ht, int B, int T, int H, int D, float scale,
+                                 int NS, int L, float *Hin, float *Hout, float *M, int *cu, hipStream_t st) {
+    if (NS < 2) return hipErrorInvalidValue;
+    if (D == 64)
+        return launch_fused_seg_t<64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, NS, L, Hin, Hout, M, cu, st);
+    if (D == 128)
+        return launch_fused_seg_t<128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, NS, L, Hin, Hout, M, cu, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,

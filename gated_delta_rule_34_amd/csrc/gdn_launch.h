@@ -23,6 +23,17 @@ hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const 
                              const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H, int Dk,
                              int Dv, float scale, hipStream_t st);
 
+// The same forward over a dense batch as a chunk-parallel state scan (Dk =
+// Dv = D): each sequence in NS segments of L chunks; output-free walks give
+// every segment but the last its end state from its entry (segment 0) or from
+// zero, and its transfer matrix (middle segments); a scan gives every
+// segment's true entry state; then the single kernel runs all segments as
+// packed sequences.  Hin, Hout, M: [B NS, H, D, D] fp32, cu: B NS + 1 int32
+// (the caller's workspace).
+hipError_t launch_fused_seg_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                 const float *h0, float *o, float *ht, int B, int T, int H, int D, float scale,
+                                 int NS, int L, float *Hin, float *Hout, float *M, int *cu, hipStream_t st);
+
 // Gated DeltaNet-2, two stages: per-chunk prepared operands (decayed e, q
 // and k; Gamma_C; T - I; strict P; diag P), then the state walk.
 hipError_t launch_gdn2_intra(const void *q, const void *k, const float *la, const void *bg, void *Ehat, void *Qhat,

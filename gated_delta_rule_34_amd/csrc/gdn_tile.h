@@ -16,8 +16,15 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+// 16 bytes as a native vector: arrays of it stay in registers where arrays of
+// HIP's uint4 struct can be demoted to scratch
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 __device__ __forceinline__ f32x4 mma_bf16_raw(f32x4 acc, const uint4 &a, const uint4 &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16_raw(f32x4 acc, const u32x4 &a, const u32x4 &b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    acc, 0, 0, 0);
 }
@@ -69,7 +76,6 @@ __device__ __forceinline__ uint4 frag_rows_pg(const uint16_t *M, int row0, int k
     // row0 is a multiple of 16 and the swizzle reads only the low 4 row bits,
     // so the block's offset is a constant the LDS read can carry as its
     // immediate offset
-    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     typedef __attribute__((address_space(3))) const uint16_t lds_u16;
     typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
     lds_u16 *m3 = (lds_u16 *)M;

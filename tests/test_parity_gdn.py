@@ -250,6 +250,58 @@ def test_causality_perturbation(dtype, t):
     assert np.abs(o2[:, t] - o1[:, t]).max() > 0
 
 
+def _seq_path(x):
+    """The single-kernel path (a 256-byte workspace is too small for the scan)."""
+    import torch
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(*gdn_dev_args(x), scale=x["scale"], workspace=ws)
+    return host(o), host(ht)
+
+
+@pytest.mark.parametrize("B,T,H,D,h0", [(1, 3800, 2, 128, True), (1, 2000, 1, 64, True), (2, 1500, 3, 128, False),
+                                        (1, 4160, 4, 128, True)])
+def test_chunk_parallel_scan_parity(B, T, H, D, h0):
+    """Few heads and long sequences take the chunk-parallel scan (segments whose
+    entry states come from transfer matrices and a scan): parity with the
+    oracle on every element, and with the single-kernel path, at segment
+    counts from 3 to 8 with ragged last segments."""
+    import ctypes
+    lib = gdn.load()
+    assert lib.gdn_chunk_fwd_workspace(B, T, H, D, D, gdn.GDN_BF16) > 256, "scan not planned for this shape"
+    x = gi.gdn_inputs(B, T, H, D, D, seed=700 + T + H, dtype="bf16", h0=h0, a_range=(0.01, 0.5))
+    o, S = _run(x)
+    ref = oracle.gdn_fwd(*gdn_ref_args(x), scale=x["scale"])
+    eo, es = _check(x, o, S, ref)
+    o1, S1 = _seq_path(x)
+    eo1, es1 = _check(x, o1, S1, ref)
+    print(f"scan o {eo:.2e} S {es:.2e}; single kernel o {eo1:.2e} S {es1:.2e}")
+
+
+def test_chunk_parallel_scan_weak_decay_carry():
+    """Weak decay (the state survives whole segments, so the transfer matrices
+    and the scan carry real weight): parity with the oracle."""
+    x = gi.gdn_inputs(1, 3200, 2, 128, 128, seed=711, dtype="bf16", h0=True, a_range=(0.0005, 0.002))
+    o, S = _run(x)
+    _check(x, o, S)
+    x["g"][:] = 0.0
+    x["g_f64"][:] = 0.0
+    o, S = _run(x)
+    _check(x, o, S)
+
+
+def test_chunk_parallel_scan_deterministic_and_alias():
+    import torch
+    x = gi.gdn_inputs(1, 3000, 2, 128, 128, seed=712, dtype="bf16", h0=True, a_range=(0.01, 0.5))
+    q, k, v, g, beta, h0 = gdn_dev_args(x)
+    o1, S1 = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, scale=x["scale"])
+    o2, S2 = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, scale=x["scale"])
+    assert (o1 == o2).all().item() and (S1 == S2).all().item()
+    h0c = h0.clone()
+    o3, S3 = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0c, scale=x["scale"], final_state=h0c)
+    assert S3.data_ptr() == h0c.data_ptr()
+    assert (o3 == o1).all().item() and (S3 == S1).all().item()
+
+
 def test_staged_entry_points_equal_fused_call():
     """fp32: gdn_chunk_intra + gdn_chunk_walk enqueue exactly the work of gdn_chunk_fwd."""
     x = gi.gdn_inputs(2, 200, 3, 128, 128, seed=66, dtype="fp32", h0=True)
