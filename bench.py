@@ -135,7 +135,8 @@ class ClockSampler:
             return None
         return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
                 "max_mhz": max(self.samples), "samples": len(self.samples),
-                "source": "torch.cuda.clock_rate sampled every 20 ms during the settle phase and timed region"}
+                "source": "torch.cuda.clock_rate (amd-smi) sampled every 20 ms during the settle phase and "
+                          "timed region; it reads the SMI's clock, which need not be the shader clock"}
 
 
 def percentile(xs, p):
@@ -149,6 +150,7 @@ def percentile(xs, p):
 
 
 def run_timed(step, sets, args, per_launch_min: int = 50):
+    import gated_delta_rule_34_amd as gdn
     """The timing protocol shared by every workload.
 
     1. `args.warmup` untimed steps, then more back-to-back steps until at least
@@ -191,19 +193,26 @@ def run_timed(step, sets, args, per_launch_min: int = 50):
             evs[i][0].record()
             step(sets[i % n])
             evs[i][1].record()
+        # the shader clock right behind the launches, before the GPU idles
+        probe = gdn.clock_probe(nblocks=256, spin_us=2000)
         torch.cuda.synchronize()
     per = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    pc = probe.cpu().double()
+    mhz = sorted((100.0 * pc[:, 0] / pc[:, 1]).tolist())
+    shader_clock = {"median_mhz": mhz[len(mhz) // 2], "min_mhz": mhz[0], "max_mhz": mhz[-1], "workgroups": len(mhz),
+                    "method": "s_memtime cycles over 100 MHz s_memrealtime ticks in a 2 ms probe kernel enqueued "
+                              "right after the per-step launches"}
     return {"ms_per_step": wall * 1e3 / args.steps, "event_ms_per_step": event_ms,
             "settle": {"steps": done, "seconds": settle_s},
             "step_us": {"median": percentile(per, 50), "p10": percentile(per, 10), "p90": percentile(per, 90),
                         "n": m, "method": "one HIP event pair per step, outside the timed region"},
-            "device_clock": clk.summary()}
+            "device_clock": shader_clock, "smi_clock": clk.summary()}
 
 
 def timing_fields(tm):
     """JSON fields every workload reports from run_timed's result."""
     return {"settle": tm["settle"], "step_us": tm["step_us"], "device_clock": tm["device_clock"],
-            "host_cpu": host_cpu_model()}
+            "smi_clock": tm["smi_clock"], "host_cpu": host_cpu_model()}
 
 
 def to_dev(a, dev):
@@ -308,7 +317,13 @@ def bench_gdn(args, wl):
 
     tm = run_timed(step, sets, args)
     ms = tm["ms_per_step"]
-    if fused:
+    # few heads and a long sequence: the library plans the chunk-parallel scan
+    # (a workspace beyond 256 bytes), four launches per step
+    scan = fused and ws.numel() > 256
+    if scan:
+        k1_ms, k2_ms = tm["event_ms_per_step"], 0.0
+        kernels = {"chunk_parallel_step": k1_ms * 1e3}
+    elif fused:
         # one kernel per step: the event pair around the timed region gives its
         # average launch duration without per-launch event gaps
         k1_ms, k2_ms = tm["event_ms_per_step"], 0.0
@@ -331,7 +346,12 @@ def bench_gdn(args, wl):
     flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
     esz = 2 if x["dtype"] == "bf16" else 4
     has_h0 = x["h0"] is not None
-    if fused:
+    if scan:
+        # the whole step: output-free segment walks, the scan, the single kernel
+        # on the segments and the final-state copy
+        kname, kms = "fused_walk_kernel+seg_scan_kernel+fused_kernel+seg_final_kernel", k1_ms
+        kbytes = walk_algorithmic_bytes(B, T, H, Dk, Dv, esz, has_h0) + 4.0 * B * T * H
+    elif fused:
         kname, kms = "fused_kernel", k1_ms
         kbytes = walk_algorithmic_bytes(B, T, H, Dk, Dv, esz, has_h0) + 4.0 * B * T * H   # + g
     elif k2_ms >= k1_ms:
@@ -360,7 +380,8 @@ def bench_gdn(args, wl):
                    "mfma": ("bf16 operands (inputs, state hi + lo parts) and fp16 operands (T - I, P, new "
                             "values), fp32 accumulate") if x["dtype"] == "bf16" else "fp32",
                    "h0": has_h0, "buffer_sets": args.sets, "parallelism": "single GPU",
-                   "kernels": "single fused kernel" if fused else "intra-chunk stage + state walk"},
+                   "kernels": ("chunk-parallel state scan (segment walks, scan, single kernel on the segments)"
+                               if scan else "single fused kernel" if fused else "intra-chunk stage + state walk")},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3,

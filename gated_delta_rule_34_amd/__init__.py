@@ -17,6 +17,7 @@ __all__ = [
     "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_prologue", "gdn_gated_rmsnorm",
     "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace", "gdn2_chunk_fwd_noalloc", "gdn2_chunk_fwd_noalloc_max_bytes",
+    "clock_probe",
     "GDN_F32", "GDN_BF16", "BT",
 ]
 
@@ -75,6 +76,8 @@ def load():
     lib.gdn2_chunk_fwd_noalloc.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
     lib.gdn2_chunk_fwd_noalloc_max_bytes.restype = _sz
     lib.gdn2_chunk_fwd_noalloc_max_bytes.argtypes = []
+    lib.gdn_clock_probe.restype = _i
+    lib.gdn_clock_probe.argtypes = [_vp, _i, _i, _vp]
     lib.gdn_gated_rmsnorm.restype = _i
     lib.gdn_gated_rmsnorm.argtypes = [_vp] * 4 + [ctypes.c_longlong, _i, _f, _vp]
     _lib = lib
@@ -531,3 +534,13 @@ def gdn_gated_rmsnorm(o, z, weight, eps=1e-5, out=None):
     _check(load().gdn_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(weight), _ptr(y), rows, Dv, float(eps), _stream(dev)),
            "gdn_gated_rmsnorm")
     return y
+
+
+def clock_probe(nblocks=256, spin_us=2000, device="cuda"):
+    """Enqueue the clock probe (measurement aid) on torch's current stream and
+    return a device tensor [nblocks, 2] int64 of (shader cycles, 100 MHz ticks);
+    read it after the stream has run: clock_MHz = 100 * cycles / ticks."""
+    torch = _torch()
+    out = torch.zeros((nblocks, 2), dtype=torch.int64, device=device)
+    _check(load().gdn_clock_probe(_ptr(out), int(nblocks), int(spin_us), _stream(out.device)), "gdn_clock_probe")
+    return out

@@ -78,6 +78,7 @@ struct FusedSmem {
     alignas(16) float dk[2][BT];              // 2^(G2_last - G2_j): decay of key j to the chunk end
     alignas(16) _Float16 A[2][BT * C::LDP];
     alignas(16) float g2A[BT], betaA[BT];  // gate tables private to the A producer
+    alignas(16) float decA[BT];            // ... 2^(g2_j) = 2^(G2_j - G2_(j-1)), the decay of one token
     alignas(16) float g2P[BT];             // ... and to the P producer
 };
 
@@ -225,6 +226,7 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     finish_gates(R.g, R.beta, ha, c2, lane);
     sm.g2A[lane] = chunk_g2(R.g);
     sm.betaA[lane] = R.beta;
+    sm.decA[lane] = __builtin_amdgcn_exp2f(R.g * LOG2E);
     load_gates(R.g, R.beta, ha, min(c2 + 1, NT - 1), lane);
     // K_J K_I^T: this lane gets row i = 16I + r and columns j = 16J + 4g + e
     // of every tile, stored as 4 adjacent halves
@@ -235,12 +237,13 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     for (int s = 0; s < C::NS; ++s)
 #pragma unroll
         for (int t = 0; t < 10; ++t) acc[t] = mma_bf16_raw(acc[t], R.k[tileJ(t)][s], R.k[tileI(t)][s]);
-    float rowG2[4], rowB[4];
+    // beta_i 2^(G2_i - G2_j) = 2^(G2_i + log2(beta_i) - G2_j): beta enters the
+    // row's exponent (beta = 0 gives 2^-inf = 0)
+    float rowG2[4];
     f32x4 colG2[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        rowG2[I] = sm.g2A[16 * I + r];
-        rowB[I] = sm.betaA[16 * I + r];
+        rowG2[I] = sm.g2A[16 * I + r] + __builtin_amdgcn_logf(sm.betaA[16 * I + r]);
         colG2[I] = *(const f32x4 *)&sm.g2A[16 * I + 4 * g];
     }
     // The next chunk's rows overwrite the MFMA operands, so they are requested
@@ -253,11 +256,25 @@ __device__ __forceinline__ void produce_A(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
         const int I = tileI(tile), J = tileJ(tile);
         const int i = 16 * I + r;
         f16x4 hv;
+        if (I > J) {
+            // below the diagonal blocks (i > j always): one exp2 for the nearest
+            // of the 4 columns, then one token's decay per step to the left,
+            // 2^(G2_i - G2_(j-1)) = 2^(G2_i - G2_j) 2^(g2_j), all factors <= 1
+            const f32x4 dc = *(const f32x4 *)&sm.decA[16 * J + 4 * g];
+            float d = __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][3]);
+            hv[3] = (_Float16)(acc[tile][3] * d);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 16 * J + 4 * g + e;
-            const float val = acc[tile][e] * rowB[I] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
-            hv[e] = (_Float16)((i > j) ? val : 0.f);
+            for (int e = 2; e >= 0; --e) {
+                d *= dc[e + 1];
+                hv[e] = (_Float16)(acc[tile][e] * d);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * J + 4 * g + e;
+                const float val = acc[tile][e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+                hv[e] = (_Float16)((i > j) ? val : 0.f);
+            }
         }
         *(f16x4 *)&A[i * C::LDP + 16 * J + 4 * g] = hv;
     }
@@ -302,12 +319,14 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
     // P tiles: lane gets P[16I + r][16J + 4g + e] = scale (q_i . k_j) 2^(G2_i - G2_j)
     f32x4 acc[10];
     lower_tiles<DK>(acc, sm.K[kb], sm.Q[kb], lane);
+    // scale 2^(G2_i - G2_j) = 2^(G2_i + log2(scale) - G2_j)
+    const float lscale = __builtin_amdgcn_logf(scale);
     f32x4 colG2[4];
     float rowG2[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         colG2[I] = *(const f32x4 *)&sm.g2P[16 * I + 4 * g];
-        rowG2[I] = sm.g2P[16 * I + r];
+        rowG2[I] = sm.g2P[16 * I + r] + lscale;
     }
     _Float16 *P = sm.P[buf];
 #pragma unroll
@@ -318,8 +337,9 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 16 * J + 4 * g + e;
-            const float val = scale * acc[tile][e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
-            hv[e] = (_Float16)((i > j) ? val : 0.f);
+            const float val = acc[tile][e] * __builtin_amdgcn_exp2f(rowG2[I] - colG2[J][e]);
+            // below the diagonal blocks i > j always holds; only they are masked
+            hv[e] = (_Float16)((I > J || i > j) ? val : 0.f);
             if (I == J && i == j) sm.diag[buf][i] = scale * acc[tile][e];
         }
         *(f16x4 *)&P[i * C::LDP + 16 * J + 4 * g] = hv;

@@ -326,6 +326,18 @@ gdn_status gdn_prologue(const void *xq, const void *xk, const void *xv, const fl
 gdn_status gdn_gated_rmsnorm(const float *o, const void *z, const float *weight, void *y,
                              long long rows, int Dv, float eps, void *stream);
 
+/*
+ * gdn_clock_probe -- measurement aid, not part of the operation: enqueues
+ * nblocks single-wave workgroups that each spin for spin_us microseconds of
+ * real time and write two counts to out (device, 2 * nblocks uint64): the
+ * shader cycles (s_memtime) and the 100 MHz real-time ticks (s_memrealtime)
+ * that passed, so that clock_MHz = 100 * cycles / ticks.  Enqueued right
+ * after a run of kernels it reads the clock those kernels ran at.  Errors:
+ * GDN_ERR_INVALID_ARG (null out, nblocks outside 1..65536, spin_us outside
+ * 1..100000), GDN_ERR_HIP.  Asynchronous.
+ */
+gdn_status gdn_clock_probe(unsigned long long *out, int nblocks, int spin_us, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
