@@ -101,44 +101,6 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (MHz, via torch.cuda.clock_rate) from a
-    background thread while the GPU is under load; None where unavailable."""
-
-    def __init__(self, period_s: float = 0.02):
-        import threading
-        self.samples = []
-        self.period = period_s
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        import torch
-        while not self._stop.is_set():
-            try:
-                self.samples.append(float(torch.cuda.clock_rate(0)))
-            except Exception:
-                return
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        self._thread.join(timeout=5)
-
-    def summary(self):
-        import statistics
-        if not self.samples:
-            return None
-        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
-                "max_mhz": max(self.samples), "samples": len(self.samples),
-                "source": "torch.cuda.clock_rate (amd-smi) sampled every 20 ms during the settle phase and "
-                          "timed region; it reads the SMI's clock, which need not be the shader clock"}
-
-
 def percentile(xs, p):
     ys = sorted(xs)
     if not ys:
@@ -150,7 +112,6 @@ def percentile(xs, p):
 
 
 def run_timed(step, sets, args, per_launch_min: int = 50):
-    import gated_delta_rule_34_amd as gdn
     """The timing protocol shared by every workload.
 
     1. `args.warmup` untimed steps, then more back-to-back steps until at least
@@ -160,59 +121,61 @@ def run_timed(step, sets, args, per_launch_min: int = 50):
        with one HIP event pair on the current stream around all of them (wall
        clock and event time).
     3. A distribution pass outside the timed region: max(steps, 50) steps, each
-       between its own event pair, for the median / p10 / p90 of one step.
+       between its own event pair, for the median / p10 / p90 of one step,
+       followed at once by the library's clock probe, which reads the shader
+       clock before the GPU idles.
     Returns a dict with ms_per_step (wall), event_ms_per_step and the stats."""
     import torch
+    import gated_delta_rule_34_amd as gdn
     n = len(sets)
-    with ClockSampler() as clk:
-        t0 = time.perf_counter()
-        done = 0
-        for i in range(args.warmup):
-            step(sets[i % n])
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(args.warmup):
+        step(sets[i % n])
+        done += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < args.settle_ms * 1e-3:
+        for _ in range(20):
+            step(sets[done % n])
             done += 1
         torch.cuda.synchronize()
-        while time.perf_counter() - t0 < args.settle_ms * 1e-3:
-            for _ in range(20):
-                step(sets[done % n])
-                done += 1
-            torch.cuda.synchronize()
-        settle_s = time.perf_counter() - t0
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(args.steps):
-            step(sets[i % n])
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        event_ms = e0.elapsed_time(e1) / args.steps
-        m = max(args.steps, per_launch_min)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(m)]
-        for i in range(m):
-            evs[i][0].record()
-            step(sets[i % n])
-            evs[i][1].record()
-        # the shader clock right behind the launches, before the GPU idles
-        probe = gdn.clock_probe(nblocks=256, spin_us=2000)
-        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(sets[i % n])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = e0.elapsed_time(e1) / args.steps
+    m = max(args.steps, per_launch_min)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(m)]
+    for i in range(m):
+        evs[i][0].record()
+        step(sets[i % n])
+        evs[i][1].record()
+    probe = gdn.clock_probe(nblocks=256, spin_us=2000)
+    torch.cuda.synchronize()
     per = [a.elapsed_time(b) * 1e3 for a, b in evs]
     pc = probe.cpu().double()
     mhz = sorted((100.0 * pc[:, 0] / pc[:, 1]).tolist())
     shader_clock = {"median_mhz": mhz[len(mhz) // 2], "min_mhz": mhz[0], "max_mhz": mhz[-1], "workgroups": len(mhz),
                     "method": "s_memtime cycles over 100 MHz s_memrealtime ticks in a 2 ms probe kernel enqueued "
-                              "right after the per-step launches"}
+                              "right after the per-step launches (the clock just after the load, which can be "
+                              "above the clock under it)"}
     return {"ms_per_step": wall * 1e3 / args.steps, "event_ms_per_step": event_ms,
             "settle": {"steps": done, "seconds": settle_s},
             "step_us": {"median": percentile(per, 50), "p10": percentile(per, 10), "p90": percentile(per, 90),
                         "n": m, "method": "one HIP event pair per step, outside the timed region"},
-            "device_clock": shader_clock, "smi_clock": clk.summary()}
+            "device_clock": shader_clock}
 
 
 def timing_fields(tm):
     """JSON fields every workload reports from run_timed's result."""
     return {"settle": tm["settle"], "step_us": tm["step_us"], "device_clock": tm["device_clock"],
-            "smi_clock": tm["smi_clock"], "host_cpu": host_cpu_model()}
+            "host_cpu": host_cpu_model()}
 
 
 def to_dev(a, dev):
