@@ -57,15 +57,22 @@ __device__ __forceinline__ int pair_col(int c) {
 }
 
 // Offset (in halves) of stored column `col` of row `row` in a paired-group
-// tile (unpadded rows of D halves).  The 8-column units are XOR-swizzled by
-// row so that both the 16-byte fragment reads (16 rows, one 8-column unit
-// each) and the 8-byte transpose reads (4 rows x 4 alternate 4-column
-// groups) touch 64 distinct banks (64 banks of 4 bytes).
+// tile (unpadded rows of D halves).  The 16-byte units of a row are
+// XOR-swizzled by the row's low four bits.  gfx950's LDS (64 banks of 4 bytes)
+// serves a 16-byte read in four passes of 16 lanes, lanes (l >> 5, parity of
+// l >> 2) alike sharing a pass, and an 8-byte access in two passes of 32
+// contiguous lanes (both measured with the bank-conflict counters).  The
+// swizzle gives each pass of a fragment read (16 rows, one unit each) 16
+// distinct units, and each pass of a transpose read (8 rows x 4 units of one
+// half) or of a row store (16 rows x 2 units of one half) at most two lanes
+// per bank pair, which is the least those two can have: the paired-group
+// order puts all their 8-byte pieces in the same half of a unit.
 template <int D>
 __device__ __forceinline__ int tile_off_pg(int row, int col) {
     static_assert(D == 64 || D == 128, "head size");
-    if (D == 128) return row * D + (col ^ (((row & 3) << 5) | (((row >> 2) & 3) << 3)));
-    return row * D + (col ^ ((((row >> 1) & 1) << 5) | (((row >> 2) & 3) << 3)));
+    if (D == 128) return row * D + (col ^ (((row & 1) << 3) | (((row >> 3) & 1) << 4) | (((row >> 1) & 3) << 5)));
+    // 128-byte rows: row parity already picks the bank half
+    return row * D + (col ^ ((((row >> 1) & 1) << 3) | (((row >> 3) & 1) << 4) | (((row >> 2) & 1) << 5)));
 }
 
 // Fragment of the 32-wide slab at column k0 of rows row0 .. row0 + 15 of a
