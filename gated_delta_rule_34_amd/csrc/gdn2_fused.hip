@@ -28,6 +28,10 @@
 // walk kernel (one workgroup per (batch, head, 32 value columns)): two
 //   consumer waves carry the state in registers through the chunks, two
 //   loader waves stage the next chunk's block and value slices into LDS.
+// When the walk leaves at least half of the compute units idle, the chunks
+// run in time parts: the prep of part p and the walk of part p - 1 share one
+// launch (gdn2_pipe_kernel) on disjoint workgroups, and the state crosses the
+// launches in an fp32 carry in the workspace.
 //
 // Precision: Ehat, Qhat, Khat, T - I and P are fp16; the state enters K S and
 // Q S as fp16 hi + lo parts and Vnew enters the state update the same way;
@@ -213,14 +217,16 @@ __device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int la
     }
 }
 
-// Persistent: workgroup w handles chunks w, w + gridDim.x, ...  The raw rows
-// and log-decays of its next chunk are fetched into registers while the
-// current chunk's A and P tiles are formed, so their latency overlaps the
-// current chunk's work.
+// Persistent: over the chunks c0 .. c0 + nc - 1 of every (batch, head), in
+// the order idx = bh nc + (c - c0), workgroup w of nw handles idx = w, w + nw,
+// ...  The raw rows and log-decays of its next chunk are fetched into
+// registers while the current chunk's A and P tiles are formed, so their
+// latency overlaps the current chunk's work.
 template <int DK>
-__global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                         const float *__restrict__ la, const uint16_t *__restrict__ bg,
-                                                         char *__restrict__ ws, int T, int H, int NT, int nchunks) {
+__device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *__restrict__ q,
+                                         const uint16_t *__restrict__ k, const float *__restrict__ la,
+                                         const uint16_t *__restrict__ bg, char *__restrict__ ws, int T, int H, int NT,
+                                         int c0, int nc, int nidx, int w0, int nw) {
     using SM = Gdn2PrepSmem<DK>;
     using BL = Gdn2Blk<DK>;
     constexpr int NTH = 512;
@@ -228,13 +234,17 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
     constexpr int C8 = DK / 8;      // uint4 per row of a raw tile
     constexpr int RG = BT / NG;     // rows per cumsum group
     constexpr int NU = BT * C8 / NTH;  // uint4 per thread per raw tile
-    __shared__ SM sm;
     const int tid0 = threadIdx.x;
     const int ch = tid0 % DK, gr = tid0 / DK;  // cumsum: rows RG gr .. RG gr + RG - 1 of channel ch
     typedef __attribute__((ext_vector_type(4))) unsigned int v4u;  // native vectors stay in registers
     v4u kr[NU], qr[NU], br[NU];
     float lv[RG];
 
+    // the chunk (its index among all chunks: bh NT + c) of position idx
+    auto chunk_of = [&](int idx) {
+        const int bh = idx / nc;
+        return bh * NT + c0 + (idx - bh * nc);
+    };
     // token-head row of a chunk's first token, and the chunk's first token
     auto locate = [&](int cb, long &row0, int &t0) {  // 32-bit index math (cheap on the VALU)
         const int bh = cb / NT;
@@ -264,8 +274,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
         }
     };
 
-    fetch(blockIdx.x);  // the grid never exceeds the chunk count
-    for (int cb = blockIdx.x; cb < nchunks; cb += gridDim.x) {
+    fetch(chunk_of(w0));  // w0 < nidx: the grid never exceeds the chunk count
+    for (int idx = w0; idx < nidx; idx += nw) {
+        const int cb = chunk_of(idx);
         // The thread index passes through an opaque move each chunk, so that
         // the many lane-derived LDS addresses below are formed where they are
         // used instead of being hoisted out of the loop into registers.
@@ -311,15 +322,16 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
         // The staging registers are free now, so the next chunk is fetched here:
         // first by waves 4 and 5, which have two tiles each, and by the others
         // after their tile, where they would otherwise wait at the barrier.
-        const bool more = cb + gridDim.x < nchunks, fetch_first = wave == 4 || wave == 5;
-        if (fetch_first && more) fetch(cb + gridDim.x);
+        const bool more = idx + nw < nidx, fetch_first = wave == 4 || wave == 5;
+        const int cnext = more ? chunk_of(idx + nw) : 0;
+        if (fetch_first && more) fetch(cnext);
         if (wave < 4) {
             diag_block<DK>(sm, 16 * wave, lane);
         } else {
             offdiag_tile<DK>(sm, wave - 4, lane);
             if (wave < 6) offdiag_tile<DK>(sm, wave, lane);
         }
-        if (!fetch_first && more) fetch(cb + gridDim.x);
+        if (!fetch_first && more) fetch(cnext);
         __syncthreads();
 
         // 3. wave 0: T - I; the other waves: decayed operands, Gamma_C, P, diag P
@@ -368,6 +380,15 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restri
         }
         __syncthreads();  // this chunk's LDS is read before the next one is staged
     }
+}
+
+template <int DK>
+__global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                         const float *__restrict__ la, const uint16_t *__restrict__ bg,
+                                                         char *__restrict__ ws, int T, int H, int NT, int c0, int nc,
+                                                         int nidx) {
+    __shared__ Gdn2PrepSmem<DK> sm;
+    prep_run<DK>(sm, q, k, la, bg, ws, T, H, NT, c0, nc, nidx, blockIdx.x, gridDim.x);
 }
 
 // --------------------------------------------------------------- walk kernel
@@ -588,21 +609,19 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
     }
 }
 
+// The walk over chunks c0 .. c1 - 1 of one (batch, head, 32 value columns):
+// workgroup n of nwg.  Waves 0 and 1 carry the state, waves 2 and 3 stage the
+// blocks; any further waves of the workgroup only keep the barrier count.
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__restrict__ ws,
-                                                                  const uint16_t *__restrict__ v,
-                                                                  const uint16_t *__restrict__ wg,
-                                                                  const float *__restrict__ h0, float *__restrict__ o,
-                                                                  float *__restrict__ ht, int T, int H, int NT,
-                                                                  float scale) {
+__device__ __forceinline__ void walk_run(Gdn2WalkSmem<DK, DV> &sm, const char *__restrict__ ws,
+                                         const uint16_t *__restrict__ v, const uint16_t *__restrict__ wg,
+                                         const float *__restrict__ h0, float *__restrict__ o, float *__restrict__ ht,
+                                         int T, int H, int NT, float scale, int n, int nwg, int c0, int c1) {
     using C = Gdn2WalkCfg<DK, DV>;
-    static_assert(sizeof(Gdn2WalkSmem<DK, DV>) <= 160 * 1024, "LDS budget");
-    __shared__ Gdn2WalkSmem<DK, DV> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     constexpr int NTILE = DV / C::BV;
     // the column slices of one head get consecutive ids on one XCD (shared L2)
-    const int n = blockIdx.x, nwg = gridDim.x;
     const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
     const int vt = L % NTILE;
     const long bh = L / NTILE;
@@ -624,8 +643,8 @@ __global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__r
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[m][e] = h0 ? h0[sbase + (long)(16 * m + 4 * g + e) * DV + col] : 0.f;
         __syncthreads();
-        for (int c = -1; c < NT; ++c) {
-            if (c >= 0) gdn2_consume(sm, S, c & 1, o, hd, c, wave, scale, lane);
+        for (int c = c0 - 1; c < c1; ++c) {
+            if (c >= c0) gdn2_consume(sm, S, c & 1, o, hd, c, wave, scale, lane);
             __syncthreads();
         }
         if (ht) {
@@ -634,42 +653,128 @@ __global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__r
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ht[sbase + (long)(16 * m + 4 * g + e) * DV + col] = S[m][e];
         }
-    } else {
+    } else if (wave < 4) {
         // loaders: iteration c stores chunk c + 1 and fetches chunk c + 2
         const int lt = tid - 128;
         Gdn2Stage<DK> R;
-        stage_load<DK, DV>(R, hd, 0, lt);
+        stage_load<DK, DV>(R, hd, c0, lt);
         __syncthreads();
-        for (int c = -1; c < NT; ++c) {
-            if (c + 1 < NT) {
+        for (int c = c0 - 1; c < c1; ++c) {
+            if (c + 1 < c1) {
                 stage_store(sm, R, (c + 1) & 1, lt);
-                if (c + 2 < NT) stage_load<DK, DV>(R, hd, c + 2, lt);
+                if (c + 2 < c1) stage_load<DK, DV>(R, hd, c + 2, lt);
             }
             __syncthreads();
         }
+    } else {
+        __syncthreads();
+        for (int c = c0 - 1; c < c1; ++c) __syncthreads();
     }
 }
 
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__restrict__ ws,
+                                                                  const uint16_t *__restrict__ v,
+                                                                  const uint16_t *__restrict__ wg,
+                                                                  const float *__restrict__ h0, float *__restrict__ o,
+                                                                  float *__restrict__ ht, int T, int H, int NT,
+                                                                  int c0, int c1, float scale) {
+    static_assert(sizeof(Gdn2WalkSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ Gdn2WalkSmem<DK, DV> sm;
+    walk_run<DK, DV>(sm, ws, v, wg, h0, o, ht, T, H, NT, scale, blockIdx.x, gridDim.x, c0, c1);
+}
+
+// One launch of the pipelined forward: workgroups below nwalk walk chunks
+// wc0 .. wc1 - 1 (their blocks were prepared by an earlier launch), the rest
+// prepare the blocks of chunks pc0 .. pc0 + pnc - 1 for the next launch.  The
+// two parts share no memory, so no workgroup waits for another.
+template <int DK, int DV>
+union Gdn2PipeSmem {
+    Gdn2PrepSmem<DK> prep;
+    Gdn2WalkSmem<DK, DV> walk;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512, 1) void gdn2_pipe_kernel(const uint16_t *__restrict__ q,
+                                                            const uint16_t *__restrict__ k,
+                                                            const float *__restrict__ la,
+                                                            const uint16_t *__restrict__ bg, char *__restrict__ ws,
+                                                            const uint16_t *__restrict__ v,
+                                                            const uint16_t *__restrict__ wg,
+                                                            const float *__restrict__ h0, float *__restrict__ o,
+                                                            float *__restrict__ ht, int T, int H, int NT, float scale,
+                                                            int nwalk, int wc0, int wc1, int pc0, int pnc, int pidx) {
+    static_assert(sizeof(Gdn2PipeSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ Gdn2PipeSmem<DK, DV> sm;
+    const int n = blockIdx.x;
+    if (n < nwalk)
+        walk_run<DK, DV>(sm.walk, ws, v, wg, h0, o, ht, T, H, NT, scale, n, nwalk, wc0, wc1);
+    else
+        prep_run<DK>(sm.prep, q, k, la, bg, ws, T, H, NT, pc0, pnc, pidx, n - nwalk, gridDim.x - nwalk);
+}
+
 // ----------------------------------------------------------------- launchers
+// Workspace: the per-chunk blocks, then one fp32 state [B, H, Dk, Dv] that
+// carries the state between the launches of the pipelined form.
+static size_t gdn2_blocks_bytes(int B, int T, int H, int Dk) {
+    const size_t NT = (size_t)(T + BT - 1) / BT;
+    return ((size_t)B * H * NT * gdn2_fused_block_bytes(Dk) + 255) / 256 * 256;
+}
+
+size_t gdn2_fused_ws_bytes(int B, int T, int H, int Dk, int Dv) {
+    return gdn2_blocks_bytes(B, T, H, Dk) + ((size_t)B * H * Dk * Dv * sizeof(float) + 255) / 256 * 256;
+}
+
+// Number of time parts of the pipelined form: while the walk of part k runs
+// on its workgroups (one per compute unit), the other compute units prepare
+// the blocks of part k + 1 in the same launch.  Worth it when the walk leaves
+// at least half of the compute units idle and the parts stay a few chunks long.
+static int gdn2_parts(long walk_grid, int ncu, int NT) {
+    return (2 * walk_grid <= ncu && NT >= 8) ? 4 : 1;
+}
+
 template <int DK, int DV>
 static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float *la, const void *bg, const void *v,
                                       const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
                                       int H, float scale, hipStream_t st) {
     const int NT = (T + BT - 1) / BT;
-    const long nchunks = (long)B * H * NT;
-    // persistent prep: one workgroup per compute unit (its LDS allows one)
+    const int BH = B * H;
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const long pgrid = nchunks < ncu ? nchunks : (ncu > 0 ? ncu : 1);
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)pgrid), dim3(512), 0, st, (const uint16_t *)q,
-                       (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, T, H, NT, (int)nchunks);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long grid = (long)B * H * (DV / Gdn2WalkCfg<DK, DV>::BV);
-    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const char *)ws, (const uint16_t *)v, (const uint16_t *)wg, h0, o, ht, T, H, NT, scale);
+    if (ncu < 1) ncu = 1;
+    const long walk_grid = (long)BH * (DV / Gdn2WalkCfg<DK, DV>::BV);
+    const int K = gdn2_parts(walk_grid, ncu, NT);
+    auto bound = [&](int p) { return (int)((long)p * NT / K); };  // first chunk of part p
+    float *carry = (float *)((char *)ws + gdn2_blocks_bytes(B, T, H, DK));
+    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *b16 = (const uint16_t *)bg;
+    const uint16_t *v16 = (const uint16_t *)v, *w16 = (const uint16_t *)wg;
+    // part 0's blocks: a persistent prep on every compute unit (its LDS allows one per unit)
+    {
+        const int nc = bound(1) - bound(0);
+        const long nidx = (long)BH * nc;
+        const long pgrid = nidx < ncu ? nidx : ncu;
+        hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)pgrid), dim3(512), 0, st, q16, k16, la, b16,
+                           (char *)ws, T, H, NT, bound(0), nc, (int)nidx);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // walk part p - 1 beside the prep of part p; the state crosses the
+    // launches in `carry` (each workgroup reads and writes its own columns)
+    for (int p = 1; p < K; ++p) {
+        const int nc = bound(p + 1) - bound(p);
+        const long pidx = (long)BH * nc;
+        const long room = ncu - walk_grid;
+        const long pgrid = pidx < room ? pidx : room;
+        hipLaunchKernelGGL((gdn2_pipe_kernel<DK, DV>), dim3((unsigned)(walk_grid + pgrid)), dim3(512), 0, st, q16,
+                           k16, la, b16, (char *)ws, v16, w16, p == 1 ? h0 : carry, o, carry, T, H, NT, scale,
+                           (int)walk_grid, bound(p - 1), bound(p), bound(p), nc, (int)pidx);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV>), dim3((unsigned)walk_grid), dim3(256), 0, st,
+                       (const char *)ws, v16, w16, K == 1 ? h0 : carry, o, ht, T, H, NT, bound(K - 1), NT, scale);
     return hipGetLastError();
 }
 

@@ -224,15 +224,15 @@ struct Gdn2Ws {
     size_t e_off, q_off, k_off, gam_off, t_off, p_off, d_off, total;
 };
 
-static Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
+static Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, int Dv, gdn_dtype dt) {
     const size_t NT = (size_t)(T + kBT - 1) / kBT;
     const size_t chunks = (size_t)B * H * NT;
     const size_t mts = dt == GDN_BF16 ? 2 : 4;
     Gdn2Ws w;
     size_t off = 0;
-    if (dt == GDN_BF16) {  // one block of prepared operands per chunk (gdn2_fused.hip)
+    if (dt == GDN_BF16) {  // per-chunk blocks of prepared operands and a state carry (gdn2_fused.hip)
         w = Gdn2Ws{};
-        w.total = align_up(chunks * gdn::gdn2_fused_block_bytes(Dk));
+        w.total = align_up(gdn::gdn2_fused_ws_bytes(B, T, H, Dk, Dv));
         return w;
     }
     w.e_off = off; off += align_up(chunks * kBT * Dk * mts);
@@ -248,7 +248,7 @@ static Gdn2Ws gdn2_ws(int B, int T, int H, int Dk, gdn_dtype dt) {
 
 size_t gdn2_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype) {
     if (!sizes_ok(B, T, H) || !head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return 0;
-    return gdn2_ws(B, T, H, Dk, dtype).total;
+    return gdn2_ws(B, T, H, Dk, Dv, dtype).total;
 }
 
 gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
@@ -264,7 +264,7 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const flo
     const size_t es = esize(dtype);
     const size_t ntok = (size_t)B * T * H;
     const size_t nstate = (size_t)B * H * Dk * Dv * sizeof(float);
-    const Gdn2Ws lay = gdn2_ws(B, T, H, Dk, dtype);
+    const Gdn2Ws lay = gdn2_ws(B, T, H, Dk, Dv, dtype);
     const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es};
     const Range rla{log_alpha, ntok * Dk * 4}, rb{b, ntok * Dk * es}, rw{w, ntok * Dv * es};
     const Range rh0{h0, h0 ? nstate : 0}, ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0}, rws{ws, lay.total};

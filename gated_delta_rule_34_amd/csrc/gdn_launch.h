@@ -47,8 +47,12 @@ hipError_t launch_gdn2_walk(const void *Ehat, const void *Qhat, const void *Khat
 
 // Gated DeltaNet-2 for bf16 inputs: a parallel prep kernel writes one block
 // of prepared operands per chunk into ws (gdn2_fused_block_bytes(Dk) each),
-// then the walk kernel carries the state through the chunks.
+// then the walk kernel carries the state through the chunks; when the walk
+// leaves compute units idle, the sequence runs in time parts and the prep of
+// one part shares a launch with the walk of the previous one.  ws holds
+// gdn2_fused_ws_bytes() bytes.
 size_t gdn2_fused_block_bytes(int Dk);
+size_t gdn2_fused_ws_bytes(int B, int T, int H, int Dk, int Dv);
 hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la, const void *bg, const void *v,
                                   const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
                                   int H, int Dk, int Dv, float scale, hipStream_t st);

@@ -158,9 +158,10 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
  * array inside the library, GDN2_NOALLOC_SCRATCH_BYTES (144 MiB) per GPU,
  * held from the library's first use on that GPU until the process ends.  It
  * holds gdn2_chunk_fwd_workspace(B, T, H, Dk, Dv, dtype) bytes: with bf16
- * inputs and Dk = 128 up to 2,277 chunk-heads (B * H * ceil(T / 64)), e.g.
- * B = 4, H = 8, T = 4096.  Larger sizes return GDN_ERR_WORKSPACE before
- * anything is enqueued.  The call allocates nothing; its first call on a
+ * inputs and Dk = Dv = 128, 66,304 bytes per chunk-head
+ * (B * H * ceil(T / 64) of them) and 65,536 bytes per (batch, head), e.g.
+ * 137.9 MB for B = 4, H = 8, T = 4096.  Larger sizes return
+ * GDN_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing; its first call on a
  * device looks up that device's copy of the array.  Every call on one GPU
  * shares that copy, so calls that overlap on one GPU (several streams or
  * host threads) race: the caller serialises them.
