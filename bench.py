@@ -396,7 +396,7 @@ def bench_gdn2(args, wl):
     achieved = kbytes / (kms * 1e-3) / 1e9
     flops = gdn_flops_full_tile(B, T, H, Dk, Dv)
     # bf16 inputs take the fused prep + walk pair, fp32 inputs the staged pair
-    kname = ("gdn2_prep_kernel+gdn2_walk_fused_kernel" if esz == 2 else "gdn2_intra_kernel+gdn2_walk_kernel")
+    kname = ("gdn2_prep_kernel+gdn2_pipe_kernel+gdn2_walk_fused_kernel" if esz == 2 else "gdn2_intra_kernel+gdn2_walk_kernel")
     res = {
         "metric": "chunk gated delta rule-2 fwd tokens/s, T=4096 d=128",
         "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
