@@ -360,7 +360,7 @@ gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, con
 // entry state and the leaving-state gradient of every chunk, fp32
 // [B, H, NT, Dk, Dv] each.
 struct BwdWs {
-    size_t ck_off, dck_off, total;
+    size_t ck_off, dck_off, g2d_off, total;
 };
 
 static BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv) {
@@ -369,7 +369,8 @@ static BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv) {
     BwdWs w;
     w.ck_off = chunk_ws(B, T, H).total;
     w.dck_off = w.ck_off + st;
-    w.total = w.dck_off + st;
+    w.g2d_off = w.dck_off + st;  // fp64 gate sums [B, H, NT, 64]
+    w.total = w.g2d_off + align_up((size_t)B * H * NT * kBT * sizeof(double));
     return w;
 }
 
@@ -385,6 +386,8 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     if (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta) return GDN_ERR_INVALID_ARG;
     if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
     if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    // the bf16 recompute walk reads q, k, v rows in 16-byte pieces
+    if (dtype == GDN_BF16 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))) return GDN_ERR_INVALID_ARG;
     const BwdWs lay = bwd_ws(B, T, H, Dk, Dv);
     if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
     const size_t es = esize(dtype);
@@ -407,12 +410,19 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     float *G2 = (float *)(base + cw.g2_off), *Tinv = (float *)(base + cw.t_off);
     float *Sck = (float *)(base + lay.ck_off), *dSck = (float *)(base + lay.dck_off);
     const bool bf = dtype == GDN_BF16;
-    gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, bf, st, true));
+    double *G2d = (double *)(base + lay.g2d_off);
+    gdn_status s = from_hip(gdn::launch_intra(k, g, beta, G2, Tinv, B, T, H, Dk, bf, st, true, G2d));
     if (s != GDN_OK) return s;
-    s = from_hip(
-        gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, nullptr, nullptr, Sck, B, T, H, Dk, Dv, bf, scale, st, true));
+    // entry state of every chunk: for bf16 inputs the fused forward's walk
+    // (bf16 hi + lo state products, T - I and the residuals as fp16 hi + lo),
+    // else the staged fp32 walk
+    if (bf)
+        s = from_hip(gdn::launch_fused_states_bf16(q, k, v, g, beta, Tinv, h0, Sck, B, T, H, Dk, Dv, st));
+    else
+        s = from_hip(
+            gdn::launch_walk(q, k, v, beta, G2, Tinv, h0, nullptr, nullptr, Sck, B, T, H, Dk, Dv, bf, scale, st, true));
     if (s != GDN_OK) return s;
-    return from_hip(gdn::launch_bwd(q, k, v, beta, dO, dht, G2, Tinv, Sck, dSck, dq, dk, dv, dg, dbeta, dh0, B, T, H,
+    return from_hip(gdn::launch_bwd(q, k, v, beta, dO, dht, G2d, Tinv, Sck, dSck, dq, dk, dv, dg, dbeta, dh0, B, T, H,
                                     Dk, Dv, bf, scale, st));
 }
 

@@ -64,19 +64,20 @@ __device__ __forceinline__ float row16_sum(float x) {
 // Chunk inputs common to both backward kernels: Q, K rows (zero past T) and
 // the gate tables of chunk c.
 template <class Pol, int DK, int LDQ, int NTHR>
-__device__ __forceinline__ void load_chunk_qk(float *sQ, float *sK, float *sG2, float *sGam, float *sDec, float *sBeta,
+__device__ __forceinline__ void load_chunk_qk(float *sQ, float *sK, double *sG2, float *sGam, float *sDec, float *sBeta,
                                               const typename Pol::in_t *q, const typename Pol::in_t *k,
-                                              const float *beta, const float *G2ws, long b, int h, int c, long cb,
+                                              const float *beta, const double *G2ws, long b, int h, int c, long cb,
                                               int T, int H, int tid) {
     const int t0 = c * BT;
     stage_rows<DK, LDQ, NTHR>(sQ, q, b, h, t0, T, H, 0, DK, tid);
     stage_rows<DK, LDQ, NTHR>(sK, k, b, h, t0, T, H, 0, DK, tid);
     if (tid < BT) {
         const int t = t0 + tid;
-        const float G2 = G2ws[cb * BT + tid], G2L = G2ws[cb * BT + BT - 1];
+        // fp64 gate sums (see the intra stage): their differences are exact to fp32
+        const double G2 = G2ws[cb * BT + tid], G2L = G2ws[cb * BT + BT - 1];
         sG2[tid] = G2;
-        sGam[tid] = exp2f(G2);
-        sDec[tid] = exp2f(G2L - G2);
+        sGam[tid] = exp2f((float)G2);
+        sDec[tid] = exp2f((float)(G2L - G2));
         sBeta[tid] = (t < T) ? beta[(b * T + t) * H + h] : 0.f;
     }
 }
@@ -103,13 +104,14 @@ template <class Pol, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t *__restrict__ q,
                                                        const typename Pol::in_t *__restrict__ k,
                                                        const float *__restrict__ beta, const float *__restrict__ dO,
-                                                       const float *__restrict__ dht, const float *__restrict__ G2ws,
+                                                       const float *__restrict__ dht, const double *__restrict__ G2ws,
                                                        const float *__restrict__ Tws, float *__restrict__ dSck,
                                                        float *__restrict__ dh0, int T, int H, int NT, float scale) {
     constexpr int BV = 32, NTHR = 256, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
     __shared__ float sQ[BT * LDQ], sK[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
     __shared__ float sdO[BT * LDB], sdVn[BT * LDB], sdR[BT * LDB], sdS[DK * LDB];
-    __shared__ float sG2[BT], sGam[BT], sDec[BT], sBeta[BT], sGdO[BT], sBG[BT];
+    __shared__ double sG2[BT];
+    __shared__ float sGam[BT], sDec[BT], sBeta[BT], sGdO[BT], sBG[BT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     constexpr int NTILE = DV / BV;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e, j = 16 * J + r;
-                sP[i * LDC + j] = (j <= i) ? acc[e] * exp2f(sG2[i] - sG2[j]) : 0.f;
+                sP[i * LDC + j] = (j <= i) ? acc[e] * exp2f((float)(sG2[i] - sG2[j])) : 0.f;
             }
         }
         __syncthreads();
@@ -211,7 +213,8 @@ struct BwdChunkSmem {
     float P[BT * LDC];    // (Q K^T) . D, lower; after the column loop: dP . D
     float S[DK * LDW], dS[DK * LDW];                 // column slice of S and dS'
     float V[BT * LDW], dO[BT * LDW], R[BT * LDW], Vn[BT * LDW], dVn[BT * LDW];
-    float G2[BT], Gam[BT], Dec[BT], Beta[BT];
+    double G2[BT];
+    float Gam[BT], Dec[BT], Beta[BT];
     float dB[BT], dG[BT], colG[4][BT], red[256];
 };
 
@@ -219,7 +222,7 @@ template <class Pol, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const typename Pol::in_t *__restrict__ q, const typename Pol::in_t *__restrict__ k,
     const typename Pol::in_t *__restrict__ v, const float *__restrict__ beta, const float *__restrict__ dO,
-    const float *__restrict__ G2ws, const float *__restrict__ Tws, const float *__restrict__ Sck,
+    const double *__restrict__ G2ws, const float *__restrict__ Tws, const float *__restrict__ Sck,
     const float *__restrict__ dSck, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, int T, int H, int NT, float scale) {
     using SM = BwdChunkSmem<DK>;
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
-            sm.P[i * LDC + j] = (j <= i) ? acc[e] * exp2f(sm.G2[i] - sm.G2[j]) : 0.f;
+            sm.P[i * LDC + j] = (j <= i) ? acc[e] * exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
         }
     }
 
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
-            const float D = (j <= i) ? exp2f(sm.G2[i] - sm.G2[j]) : 0.f;
+            const float D = (j <= i) ? exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
             const float dAv = (j < i) ? dA[J][e] : 0.f;
             const float dPv = (j <= i) ? dP[J][e] : 0.f;
             const float Av = sm.Beta[i] * KK[e] * D, Pv = QK[e] * D;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 // ----------------------------------------------------------------- launchers
 template <class Pol, int DK, int DV>
 static hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const float *beta, const float *dO,
-                               const float *dht, const float *G2, const float *Tinv, const float *Sck, float *dSck,
+                               const float *dht, const double *G2, const float *Tinv, const float *Sck, float *dSck,
                                float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T,
                                int H, float scale, hipStream_t st) {
     using in_t = typename Pol::in_t;
@@ -469,7 +472,7 @@ static hipError_t launch_bwd_t(const void *q, const void *k, const void *v, cons
 }
 
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *beta, const float *dO,
-                      const float *dht, const float *G2, const float *Tinv, const float *Sck, float *dSck, float *dq,
+                      const float *dht, const double *G2, const float *Tinv, const float *Sck, float *dSck, float *dq,
                       float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv,
                       bool bf16, float scale, hipStream_t st) {
 #define GDN_BWD(P, DKv, DVv)                                                                                       \

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
                                                     const float *__restrict__ gin,
                                                     const float *__restrict__ betain,
                                                     float *__restrict__ G2out, float *__restrict__ Tout,
-                                                    int T, int H, int NT) {
+                                                    double *__restrict__ G2dout, int T, int H, int NT) {
     using mt = typename Pol::mt;
     constexpr int LDK = DK + 8;
     constexpr int LDA = 65;
@@ -48,7 +48,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
         mt k[BT * LDK];
         float t[BT * LDA];
     } u;
-    __shared__ float sG2[BT], sBeta[BT];
+    __shared__ float sBeta[BT];
+    // G2 in fp64: its differences G2_i - G2_j are then exact to fp32 however
+    // large the chunk's decay (an fp32 G2 of magnitude ~1000 carries an
+    // absolute error of ~6e-5 into every decay factor)
+    __shared__ double sG2[BT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -73,10 +77,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
             const double y = __shfl_up(x, off, 64);
             if (lane >= off) x += y;
         }
-        const float G2 = (float)(x * 1.4426950408889634);
+        const double G2 = x * 1.4426950408889634;
         sG2[lane] = G2;
         sBeta[lane] = bv;
-        G2out[chunk * BT + lane] = G2;
+        G2out[chunk * BT + lane] = (float)G2;
+        if (G2dout) G2dout[chunk * BT + lane] = G2;
     }
     for (int idx = tid; idx < BT * DK / 4; idx += 256) {
         const int row = idx / (DK / 4), col = (idx % (DK / 4)) * 4;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
             float val = 0.f;
-            if (i > j) val = acc[e] * sBeta[i] * exp2f(sG2[i] - sG2[j]);
+            if (i > j) val = acc[e] * sBeta[i] * exp2f((float)(sG2[i] - sG2[j]));
             sA[i * LDA + j] = val;
         }
     }
@@ -373,26 +378,26 @@ __global__ __launch_bounds__(BV * 4) void walk_kernel(const typename Pol::in_t *
 
 template <class Pol, int DK>
 static hipError_t launch_intra_t(const void *k, const float *g, const float *beta, float *G2, float *Tinv,
-                                 int B, int T, int H, hipStream_t st) {
+                                 double *G2d, int B, int T, int H, hipStream_t st) {
     const int NT = (T + BT - 1) / BT;
     const long grid = (long)B * H * NT;
     hipLaunchKernelGGL((intra_kernel<Pol, DK>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const typename Pol::in_t *)k, g, beta, G2, Tinv, T, H, NT);
+                       (const typename Pol::in_t *)k, g, beta, G2, Tinv, G2d, T, H, NT);
     return hipGetLastError();
 }
 
 hipError_t launch_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
-                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact) {
+                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact, double *G2d) {
     if (bf16 && exact) {
-        if (Dk == 64) return launch_intra_t<PolBF16F32, 64>(k, g, beta, G2, Tinv, B, T, H, st);
-        return launch_intra_t<PolBF16F32, 128>(k, g, beta, G2, Tinv, B, T, H, st);
+        if (Dk == 64) return launch_intra_t<PolBF16F32, 64>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
+        return launch_intra_t<PolBF16F32, 128>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
     }
     if (bf16) {
-        if (Dk == 64) return launch_intra_t<PolBF16, 64>(k, g, beta, G2, Tinv, B, T, H, st);
-        return launch_intra_t<PolBF16, 128>(k, g, beta, G2, Tinv, B, T, H, st);
+        if (Dk == 64) return launch_intra_t<PolBF16, 64>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
+        return launch_intra_t<PolBF16, 128>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
     }
-    if (Dk == 64) return launch_intra_t<PolF32, 64>(k, g, beta, G2, Tinv, B, T, H, st);
-    return launch_intra_t<PolF32, 128>(k, g, beta, G2, Tinv, B, T, H, st);
+    if (Dk == 64) return launch_intra_t<PolF32, 64>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
+    return launch_intra_t<PolF32, 128>(k, g, beta, G2, Tinv, G2d, B, T, H, st);
 }
 
 template <class Pol, int DK, int DV>

@@ -347,7 +347,7 @@ __device__ __forceinline__ void produce_P(FusedSmem<DK, DV> &sm, ChunkRegs<DK / 
 }
 
 // ---------------------------------------------------------------- consumers
-template <int DK, int DV, bool OUT>
+template <int DK, int DV, bool OUT, bool TLO = false>
 __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 16], int buf, int kb,
                                         float *__restrict__ o, const HeadArgs &ha, int chunk, int cw, float scale,
                                         int lane) {
@@ -409,10 +409,21 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             Rr[I][e] = bet[e] * (vv - gm[e] * X[I][e]);
         }
     }
-    // Vnew = R + (T - I) R
-    _Float16 rf[2][8];
+    // Vnew = R + (T - I) R.  TLO: T - I arrives as fp16 hi (Tm) + lo (the P
+    // buffer, free without output) parts and R enters as fp16 hi + lo parts,
+    // so the product keeps about 22 bits (hi.hi + hi.lo + lo.hi)
+    _Float16 rf[2][8], rl[2][8];
     frag_from_acc(rf[0], Rr[0], Rr[1]);
     frag_from_acc(rf[1], Rr[2], Rr[3]);
+    if constexpr (TLO) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                rl[s][e] = (_Float16)(Rr[2 * s][e] - (float)rf[s][e]);
+                rl[s][e + 4] = (_Float16)(Rr[2 * s + 1][e] - (float)rf[s][e + 4]);
+            }
+    }
     f32x4 Vn[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -422,6 +433,12 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
             _Float16 a[8];
             frag_rows(a, sm.Tm[buf], C::LDP, 16 * I, 32 * s, lane);
             Vn[I] = mma_slab(Vn[I], a, rf[s]);
+            if constexpr (TLO) {
+                _Float16 al[8];
+                frag_rows(al, sm.P[buf], C::LDP, 16 * I, 32 * s, lane);
+                Vn[I] = mma_slab(Vn[I], a, rl[s]);
+                Vn[I] = mma_slab(Vn[I], al, rf[s]);
+            }
         }
     }
     // The state carry comes first: it is what the next chunk waits for, and
@@ -493,14 +510,24 @@ __device__ __forceinline__ void consume(FusedSmem<DK, DV> &sm, f32x4 (&S)[DK / 1
 // Consumer role: the state slice of this wave from the job's initial state (or
 // the identity columns of a transfer-matrix walk), the chunks in order, and
 // the final state to the job's destination.
-template <int DK, int DV, bool OUT>
+template <int DK, int DV, bool OUT, bool ST = false, bool TLO = false>
 __device__ __forceinline__ void run_consumer(FusedSmem<DK, DV> &sm, const WgJob &job, int NT, int cw, float scale,
-                                             int lane) {
+                                             int lane, float *states = nullptr) {
     using C = FusedCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
     const HeadArgs &ha = job.ha;
     f32x4 S[C::NKB];
     const int col = ha.vcol0 + cw * 16 + r;
+    // ST: the state entering chunk c goes to states + c DK DV ([DK][DV], this
+    // wave's 16 columns), after a quad transpose as 16-byte row pieces
+    auto store_state = [&](int c) {
+        if constexpr (ST) {
+            float *dst = states + (long)c * DK * DV + ha.vcol0 + cw * 16 + 4 * (r >> 2);
+#pragma unroll
+            for (int m = 0; m < C::NKB; ++m)
+                *(f32x4 *)&dst[(long)(16 * m + 4 * g + (r & 3)) * DV] = quad_transpose(S[m], lane);
+        }
+    };
 #pragma unroll
     for (int m = 0; m < C::NKB; ++m)
 #pragma unroll
@@ -514,14 +541,17 @@ __device__ __forceinline__ void run_consumer(FusedSmem<DK, DV> &sm, const WgJob 
     // constant in each copy and its fragment addresses stay in registers
     // across chunks; one barrier per chunk as in the other roles.
     for (int c = 0; c < NT; c += 3) {
-        consume<DK, DV, OUT>(sm, S, c & 1, 0, job.o, ha, c, cw, scale, lane);
+        store_state(c);
+        consume<DK, DV, OUT, TLO>(sm, S, c & 1, 0, job.o, ha, c, cw, scale, lane);
         __syncthreads();
         if (c + 1 < NT) {
-            consume<DK, DV, OUT>(sm, S, (c + 1) & 1, 1, job.o, ha, c + 1, cw, scale, lane);
+            store_state(c + 1);
+            consume<DK, DV, OUT, TLO>(sm, S, (c + 1) & 1, 1, job.o, ha, c + 1, cw, scale, lane);
             __syncthreads();
         }
         if (c + 2 < NT) {
-            consume<DK, DV, OUT>(sm, S, c & 1, 2, job.o, ha, c + 2, cw, scale, lane);
+            store_state(c + 2);
+            consume<DK, DV, OUT, TLO>(sm, S, c & 1, 2, job.o, ha, c + 2, cw, scale, lane);
             __syncthreads();
         }
     }
@@ -876,6 +906,116 @@ __global__ __launch_bounds__(kWalkThreads, 1) void fused_walk_kernel(const uint1
 #undef GDN_JOB
 }
 
+// Producer of the states walk: the raw K rows of chunk c + 2 and the V tile
+// and gate tables of chunk c + 1 in iteration c (run_walk_producer without A:
+// the states walk reads T - I from memory).
+template <int DK, int DV>
+__device__ __forceinline__ void run_states_producer(FusedSmem<DK, DV> &sm, const HeadArgs &ha, int NT, int lane) {
+    using C = FusedCfg<DK, DV>;
+    ChunkRegs<C::NS> RA, RP;
+    // chunk c2's rows (in RA) to kq-buffer kb, then fetch chunk c2 + 1's
+    auto put_k = [&](int c2, int kb) {
+        write_rows<DK>(sm.K[kb], RA.k, lane);
+        load_rows<DK>(RA.k, ha.k, ha, min(c2 + 1, NT - 1), lane);
+    };
+    if (NT > 0) {
+        load_rows<DK>(RA.k, ha.k, ha, 0, lane);
+        load_v<DV>(RP.v, ha, 0, lane);
+        load_gates(RP.g, RP.beta, ha, 0, lane);
+        put_k(0, 0);
+    }
+    __syncthreads();
+    for (int c2 = 1; c2 <= NT + 1; c2 += 3) {
+        if (c2 < NT) put_k(c2, 1);
+        if (c2 - 1 < NT) produce_P<DK, DV, false, false>(sm, RP, c2 - 1, 0, NT, ha, 1.f, lane);
+        __syncthreads();
+        if (c2 + 1 <= NT + 1) {
+            if (c2 + 1 < NT) put_k(c2 + 1, 2);
+            if (c2 < NT) produce_P<DK, DV, false, false>(sm, RP, c2, 1, NT, ha, 1.f, lane);
+            __syncthreads();
+        }
+        if (c2 + 2 <= NT + 1) {
+            if (c2 + 2 < NT) put_k(c2 + 2, 0);
+            if (c2 + 1 < NT) produce_P<DK, DV, false, false>(sm, RP, c2 + 1, 2, NT, ha, 1.f, lane);
+            __syncthreads();
+        }
+    }
+}
+
+// T - I of chunk c + 1 from memory (fp32 [64][64] per chunk, this head's
+// chunks from Tw on) into LDS half (c + 1) & 1 in iteration c, as fp16 hi
+// (the T - I buffer) and lo (the P buffer) parts; the next chunk's is
+// fetched into registers meanwhile.
+template <int DK, int DV>
+__device__ __forceinline__ void run_tm_loader(FusedSmem<DK, DV> &sm, const float *__restrict__ Tw, int NT, int lane) {
+    using C = FusedCfg<DK, DV>;
+    constexpr int U = BT * BT / 4 / 64;  // 16-byte pieces per lane
+    f32x4 x[U];
+    auto fetch = [&](int c) {
+        const float *src = Tw + (long)c * BT * BT;
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = *(const f32x4 *)(src + 4 * (lane + 64 * u));
+    };
+    auto put = [&](int c) {
+        _Float16 *hi = sm.Tm[c & 1], *lo = sm.P[c & 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = 4 * (lane + 64 * u), row = idx / BT, col = idx % BT;
+            const f16x4 h = __builtin_convertvector(x[u], f16x4);
+            const f16x4 l = __builtin_convertvector(x[u] - __builtin_convertvector(h, f32x4), f16x4);
+            *(f16x4 *)&hi[row * C::LDP + col] = h;
+            *(f16x4 *)&lo[row * C::LDP + col] = l;
+        }
+    };
+    if (NT > 0) fetch(0);
+    __syncthreads();
+    for (int c = -1; c < NT; ++c) {
+        if (c + 1 < NT) {
+            put(c + 1);
+            if (c + 2 < NT) fetch(c + 2);
+        }
+        __syncthreads();
+    }
+}
+
+// The forward walk of every dense sequence, storing the state that enters each
+// chunk, states[b, h, c] ([DK][DV] fp32), and nothing else: the recompute of
+// a backward pass.  T - I comes from memory (Tws: fp32 [B, H, NT, 64, 64])
+// and enters the products as fp16 hi + lo parts, as do the residuals, so the
+// stored states keep the accuracy the backward needs.  Four waves, one per
+// SIMD: T - I loader, two consumers, K/V/gate producer.
+template <int DK, int DV>
+__global__ __launch_bounds__(kWalkThreads, 1) void fused_states_kernel(const uint16_t *__restrict__ q,
+                                                         const uint16_t *__restrict__ k,
+                                                         const uint16_t *__restrict__ v,
+                                                         const float *__restrict__ gin,
+                                                         const float *__restrict__ betain,
+                                                         const float *__restrict__ Tws,
+                                                         const float *__restrict__ h0, float *__restrict__ states,
+                                                         int T, int H) {
+    using C = FusedCfg<DK, DV>;
+    static_assert(sizeof(FusedSmem<DK, DV>) <= 160 * 1024, "LDS budget");
+    __shared__ FusedSmem<DK, DV> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = blockIdx.x, nwg = gridDim.x;
+    const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
+    const SegArgs none{};
+    const int NT = (T + BT - 1) / BT;
+    const long bh = L / (DV / C::BV);
+#define GDN_JOB decode_job<DK, DV, false>(L, q, k, v, gin, betain, h0, nullptr, nullptr, nullptr, T, H, none)
+    if (wave == 1 || wave == 2) {
+        const WgJob job = GDN_JOB;
+        run_consumer<DK, DV, false, true, true>(sm, job, NT, wave - 1, 1.f, lane,
+                                                states + bh * NT * (long)DK * DV);
+    } else if (wave == 0) {
+        run_tm_loader(sm, Tws + bh * NT * (long)BT * BT, NT, lane);
+    } else {
+        const WgJob job = GDN_JOB;
+        run_states_producer(sm, job.ha, NT, lane);
+    }
+#undef GDN_JOB
+}
+
 // Scan over the segments of one head, for a 32-column slice of the state:
 // Hin[b NS] = h0 (zeros when null); S = Hin[b NS + 1]; for s = 1 .. NS - 2:
 // S = M_s S + Hin[b NS + s + 1] (which holds E_s), stored back.  fp32 FMA with
@@ -980,6 +1120,25 @@ hipError_t launch_fused_seg_bf16(const void *q, const void *k, const void *v, co
         return launch_fused_seg_t<64>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, NS, L, Hin, Hout, M, cu, st);
     if (D == 128)
         return launch_fused_seg_t<128>(q, k, v, g, beta, h0, o, ht, B, T, H, scale, NS, L, Hin, Hout, M, cu, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_states_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                    const float *Tws, const float *h0, float *states, int B, int T, int H, int Dk,
+                                    int Dv, hipStream_t st) {
+#define GDN_STATES(DKv, DVv)                                                                                    \
+    if (Dk == DKv && Dv == DVv) {                                                                               \
+        const long grid = (long)B * H * (DVv / FusedCfg<DKv, DVv>::BV);                                         \
+        hipLaunchKernelGGL((fused_states_kernel<DKv, DVv>), dim3((unsigned)grid), dim3(kWalkThreads), 0, st,    \
+                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, Tws, h0, states, \
+                           T, H);                                                                                  \
+        return hipGetLastError();                                                                               \
+    }
+    GDN_STATES(64, 64);
+    GDN_STATES(64, 128);
+    GDN_STATES(128, 64);
+    GDN_STATES(128, 128);
+#undef GDN_STATES
     return hipErrorInvalidValue;
 }
 

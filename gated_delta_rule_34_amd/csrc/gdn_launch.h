@@ -7,8 +7,10 @@
 namespace gdn {
 
 // exact: fp32 operands also for bf16 inputs (used by the backward's recompute).
+// G2d (nullable): the gate sums also in fp64 [B, H, NT, 64] (for the backward).
 hipError_t launch_intra(const void *k, const float *g, const float *beta, float *G2, float *Tinv, int B,
-                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact = false);
+                        int T, int H, int Dk, bool bf16, hipStream_t st, bool exact = false,
+                        double *G2d = nullptr);
 
 // ck (nullable): entry state of every chunk, [B, H, NT, Dk, Dv] fp32; o may
 // then be null to skip the output.
@@ -19,6 +21,12 @@ hipError_t launch_walk(const void *q, const void *k, const void *v, const float 
 // Single-kernel chunked forward for bf16 inputs (no workspace).  With
 // cu_seqlens (device, B + 1 int32 offsets) the tensors hold B packed
 // sequences of T tokens in total; otherwise a dense [B, T, H, D] batch.
+// The forward walk of bf16 inputs storing only the state that enters every
+// chunk: states [B, H, ceil(T / 64), Dk, Dv] fp32 (a backward's recompute),
+// with T - I of every chunk from Tws (fp32 [B, H, ceil(T / 64), 64, 64]).
+hipError_t launch_fused_states_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                    const float *Tws, const float *h0, float *states, int B, int T, int H, int Dk,
+                                    int Dv, hipStream_t st);
 hipError_t launch_fused_bf16(const void *q, const void *k, const void *v, const float *g, const float *beta,
                              const float *h0, float *o, float *ht, const int *cu_seqlens, int B, int T, int H, int Dk,
                              int Dv, float scale, hipStream_t st);
@@ -69,7 +77,7 @@ hipError_t launch_step2(const void *q, const void *k, const void *v, const float
 // (dS' of every chunk into dSck, dh0) and the per-chunk gradients, given the
 // intra stage (G2, T - I) and the entry state of every chunk (Sck).
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *beta, const float *dO,
-                      const float *dht, const float *G2, const float *Tinv, const float *Sck, float *dSck, float *dq,
+                      const float *dht, const double *G2, const float *Tinv, const float *Sck, float *dSck, float *dq,
                       float *dk, float *dv, float *dg, float *dbeta, float *dh0, int B, int T, int H, int Dk, int Dv,
                       bool bf16, float scale, hipStream_t st);
 

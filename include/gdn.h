@@ -232,19 +232,23 @@ gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, con
  * Backward of gdn_chunk_fwd (training): gradients of
  * L = sum(dO . o) + sum(dht . ht) with respect to every input, by reverse-mode
  * differentiation of the chunk equations of the forward (WY form over 64-token
- * chunks, the chunked-kernel section of the walkthrough): a reverse walk over
- * the chunks carries the state gradient, then every chunk is recomputed and
- * differentiated in parallel.  fp32 arithmetic throughout.
+ * chunks, the chunked-kernel section of the walkthrough): a forward walk
+ * recomputes the state entering every chunk, a reverse walk over the chunks
+ * carries the state gradient, then every chunk is recomputed and
+ * differentiated in parallel.  fp32 arithmetic, except that with bf16 inputs
+ * the forward walk is the bf16 forward's (its state products on bf16 hi + lo
+ * parts, new values in fp16), whose states carry about 16 significant bits;
+ * q, k and v must then be 16-byte aligned.
  *   inputs  as gdn_chunk_fwd (h0 nullable), dO [B, T, H, Dv] fp32,
  *           dht [B, H, Dk, Dv] fp32 or NULL (no gradient on the final state)
  *   outputs dq, dk [B, T, H, Dk], dv [B, T, H, Dv], dg, dbeta [B, T, H],
  *           dh0 [B, H, Dk, Dv] or NULL, all fp32
  *   ws      gdn_chunk_bwd_workspace() bytes, 256-byte aligned, caller-owned
- * Errors: GDN_ERR_INVALID_ARG for null required pointers, bad sizes or any
- * output overlapping an input, another output or the workspace;
- * GDN_ERR_UNSUPPORTED for head sizes other than 64 and 128 or an unknown
- * dtype; GDN_ERR_WORKSPACE for a missing, misaligned or short workspace;
- * GDN_ERR_HIP if a launch fails.  Asynchronous on `stream`.
+ * Errors: GDN_ERR_INVALID_ARG for null required pointers, bad sizes,
+ * misaligned bf16 q, k, v or any output overlapping an input, another output
+ * or the workspace; GDN_ERR_UNSUPPORTED for head sizes other than 64 and 128
+ * or an unknown dtype; GDN_ERR_WORKSPACE for a missing, misaligned or short
+ * workspace; GDN_ERR_HIP if a launch fails.  Asynchronous on `stream`.
  */
 size_t gdn_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
 

@@ -4,9 +4,16 @@ the forward), element by element.  The backward runs in fp32 on exact inputs
 (bf16 inputs are exact in fp32), so both input types are held to the same bar
 (max |diff| / rms of the oracle gradient): 1e-4 for dq, dk, dv, dbeta, dh0,
 and 1e-3 for dg.  dg is a within-chunk reverse sum of differences of row and
-column sums of much larger terms; the same chunk equations evaluated in plain
-fp32 (numpy) already reach 1.3e-4 on it at d = 128, against about 1e-5 for
-the other gradients."""
+column sums of much larger terms.
+
+The bars stand on the float32 floor of the same chunk equations
+(tests/fp32_bwd_eval.py, every product in float32; tests/test_fp32_floor.py).
+At the full layer workload (T = 4096, the state gradient carried through 64
+chunks, the maximum over 4096 x 128 entries of a head) that floor is, worst
+head of 64: dq 7.9e-6, dk 9.9e-5, dv 7.3e-5, dg 5.3e-5, dbeta 4.7e-5, dh0
+2.0e-6 (`python -m tests.fp32_bwd_eval`), so the full-size test holds each
+head to about 8x that (TOL_FULL); the GPU measures dq 2.3e-5, dk 9.9e-5, dv
+7.5e-5, dg 1.9e-4, dbeta 5.0e-5 and dh0 9.5e-6 there."""
 import numpy as np
 import pytest
 
@@ -19,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 TOL_BWD = {"dq": 1e-4, "dk": 1e-4, "dv": 1e-4, "dg": 1e-3, "dbeta": 1e-4, "dh0": 1e-4}
+TOL_FULL = {"dq": 1e-4, "dk": 8e-4, "dv": 6e-4, "dg": 1e-3, "dbeta": 4e-4, "dh0": 1e-4}
 
 
 def _case(B, T, H, Dk, Dv, seed, dtype, h0=True, dht=True):
@@ -84,15 +92,15 @@ def test_bwd_deterministic():
         assert np.array_equal(u, w)
 
 
-def test_bwd_layer_shape_sampled_heads():
-    """B=2 H=8 T=1024 d=128 bf16 (layer-shaped, shorter); the oracle checks 2 heads."""
-    x = _case(2, 1024, 8, 128, 128, seed=643, dtype="bf16")
+def test_bwd_layer_workload_full_size_every_head():
+    """B=8 H=8 T=4096 d=128 bf16 (the layer workload, with h0 and dht): every
+    gradient of every head against the oracle, element by element, each head
+    to the full-size bars (TOL_FULL)."""
+    x = _case(8, 4096, 8, 128, 128, seed=643, dtype="bf16")
     got = _gpu(x)
-    for bb, hh in [(0, 3), (1, 6)]:
-        sub = {n: x[n + "_f64"][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "g", "beta")}
-        ref = oracle.gdn_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], x["h0_f64"][bb:bb + 1, hh:hh + 1],
-                             x["do"][bb:bb + 1, :, hh:hh + 1].astype(np.float64),
-                             x["dht"][bb:bb + 1, hh:hh + 1].astype(np.float64), scale=x["scale"])
-        mine = [got[0][bb:bb + 1, :, hh:hh + 1], got[1][bb:bb + 1, :, hh:hh + 1], got[2][bb:bb + 1, :, hh:hh + 1],
-                got[3][bb:bb + 1, :, hh:hh + 1], got[4][bb:bb + 1, :, hh:hh + 1], got[5][bb:bb + 1, hh:hh + 1]]
-        _check(mine, ref)
+    ref = _ref(x)
+    B, H = x["h0"].shape[:2]
+    for name, a, b in zip(GRADS, got, ref):
+        heads = [(a[i, j], b[i, j]) if name == "dh0" else (a[i, :, j], b[i, :, j]) for i in range(B) for j in range(H)]
+        worst = max(rel_err(u, w) for u, w in heads)
+        assert worst <= TOL_FULL[name], f"{name}: worst head rel err {worst:.3e} > {TOL_FULL[name]}"
