@@ -12,8 +12,9 @@ same inputs:
   the full workload (T = 4096, the state gradient carried through 64 chunks,
   the maximum over 4096 x 128 entries per head): fp32 reaches 1.4e-5 (dq),
   1.6e-4 (dk), 1.5e-4 (dv), 3.0e-4 (dw), 3.6e-4 (dlog_alpha) and 4.9e-4 (db)
-  on the two checked heads, so the bars there are 1e-4, 1.5e-3, 1.5e-3,
-  2.5e-3, 3e-3 and 4e-3."""
+  on two heads, so the bars there are 1e-4, 1.5e-3, 1.5e-3, 2.5e-3, 3e-3
+  and 4e-3.  Every head of the workload is checked; the GPU's worst heads
+  measure 2.5e-5, 3.5e-4, 3.4e-4, 4.6e-4, 8.8e-4 and 1.5e-3."""
 import numpy as np
 import pytest
 
@@ -91,19 +92,19 @@ def test_bwd2_deterministic():
         np.testing.assert_array_equal(u, v)
 
 
-def test_bwd2_full_workload_sampled_heads():
-    """The GDN-2 workload shape (B 4, T 4096, H 8, d 128) in one call; the
-    oracle checks two whole heads of it (every gradient of those heads)."""
+def test_bwd2_full_workload_every_head():
+    """The GDN-2 workload shape (B 4, T 4096, H 8, d 128) in one call; every
+    gradient of every head against the oracle, each head to TOL_FULL."""
     x = gi.workload("gdn2_bf16")
     rng = np.random.default_rng(960)
     B, T, H, Dk, Dv = x["B"], x["T"], x["H"], x["Dk"], x["Dv"]
     x["do"] = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
     x["dht"] = rng.standard_normal((B, H, Dk, Dv)).astype(np.float32)
     got = _gpu(x)
-    for b, h in ((0, 0), (B - 1, H - 1)):
-        sub = {n + "_f64": x[n + "_f64"][b:b + 1, :, h:h + 1] for n in NAMES}
-        ref = oracle.gdn2_bwd(*[sub[n + "_f64"] for n in NAMES], None, x["do"][b:b + 1, :, h:h + 1].astype(np.float64),
-                              x["dht"][b:b + 1, h:h + 1].astype(np.float64), scale=x["scale"])
-        for name, a, r in zip(GRADS[:6], got[:6], ref[:6]):
-            e = rel_err(a[b:b + 1, :, h:h + 1], r)
-            assert e <= TOL_FULL[name], f"head ({b},{h}) {name}: rel err {e:.3e}"
+    ref = oracle.gdn2_bwd(*[x[n + "_f64"] for n in NAMES], None, x["do"].astype(np.float64),
+                          x["dht"].astype(np.float64), scale=x["scale"])
+    for name, a, r in zip(GRADS[:6], got[:6], ref[:6]):
+        for b in range(B):
+            for h in range(H):
+                e = rel_err(a[b, :, h], r[b, :, h])
+                assert e <= TOL_FULL[name], f"head ({b},{h}) {name}: rel err {e:.3e}"
