@@ -99,6 +99,115 @@ __device__ __forceinline__ void stage_tm(float *dst, const float *src, int tid) 
     }
 }
 
+// The raw inputs of one chunk of the reverse walk, held in registers from
+// the iteration before the one that stages them (their loads then have a
+// whole iteration to arrive).  Rows past T read the last token and are
+// zeroed when staged.
+template <class In, int DK, int BV, int NTHR>
+struct WalkRegs {
+    static constexpr int W = sizeof(In) / 2;          // 16-byte pieces per 8 inputs
+    static constexpr int UQ = BT * DK / 8 / NTHR;     // 8-input groups per thread (Q, K rows)
+    static constexpr int UT = BT * BT / 4 / NTHR;     // float4 per thread (T - I)
+    static constexpr int UD = BT * BV / 8 / NTHR;     // 8-float groups per thread (dO)
+    uint4 q[UQ][W], k[UQ][W];
+    float4 t[UT];
+    float4 d[UD][2];
+    double g2, g2L;
+    float beta;
+};
+
+template <class In, int DK, int BV, int NTHR>
+__device__ __forceinline__ void walk_fetch(WalkRegs<In, DK, BV, NTHR> &R, const In *q, const In *k, const float *beta,
+                                           const float *dO, const double *G2ws, const float *Tws, long b, int h,
+                                           int c, long cb, int T, int H, int vcol0, int DV, int tid) {
+    using WR = WalkRegs<In, DK, BV, NTHR>;
+    const int t0 = c * BT;
+#pragma unroll
+    for (int u = 0; u < WR::UQ; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+        const long off = ((b * T + min(t0 + row, T - 1)) * H + h) * (long)DK + c8;
+#pragma unroll
+        for (int w = 0; w < WR::W; ++w) {
+            R.q[u][w] = *(const uint4 *)((const char *)(q + off) + 16 * w);
+            R.k[u][w] = *(const uint4 *)((const char *)(k + off) + 16 * w);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < WR::UT; ++u) R.t[u] = *(const float4 *)(Tws + cb * BT * BT + 4 * (tid + NTHR * u));
+#pragma unroll
+    for (int u = 0; u < WR::UD; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (BV / 8), c8 = 8 * (idx % (BV / 8));
+        const float *p = dO + ((b * T + min(t0 + row, T - 1)) * H + h) * (long)DV + vcol0 + c8;
+        R.d[u][0] = *(const float4 *)p;
+        R.d[u][1] = *(const float4 *)(p + 4);
+    }
+    if (tid < BT) {
+        R.g2 = G2ws[cb * BT + tid];
+        R.g2L = G2ws[cb * BT + BT - 1];
+        R.beta = beta[(b * T + min(t0 + tid, T - 1)) * H + h];
+    }
+}
+
+// Eight inputs of a 16-byte piece (bf16) or two (fp32) as floats.
+__device__ __forceinline__ void raw8(float (&x)[8], const uint4 (&u)[1]) {
+    const uint32_t w[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void raw8(float (&x)[8], const uint4 (&u)[2]) {
+    const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
+}
+
+template <class In, int DK, int BV, int NTHR, int LDQ, int LDC, int LDB>
+__device__ __forceinline__ void walk_stage(const WalkRegs<In, DK, BV, NTHR> &R, float *sQ, float *sK, float *sTm,
+                                           float *sdO, double *sG2, float *sGam, float *sDec, float *sBeta, int c,
+                                           int T, int tid) {
+    using WR = WalkRegs<In, DK, BV, NTHR>;
+    const int t0 = c * BT;
+#pragma unroll
+    for (int u = 0; u < WR::UQ; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+        const bool in = t0 + row < T;
+        float xq[8], xk[8];
+        raw8(xq, R.q[u]);
+        raw8(xk, R.k[u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sQ[row * LDQ + c8 + e] = in ? xq[e] : 0.f;
+            sK[row * LDQ + c8 + e] = in ? xk[e] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < WR::UT; ++u) {
+        const int idx = 4 * (tid + NTHR * u), row = idx / BT, col = idx % BT;
+        sTm[row * LDC + col] = R.t[u].x;
+        sTm[row * LDC + col + 1] = R.t[u].y;
+        sTm[row * LDC + col + 2] = R.t[u].z;
+        sTm[row * LDC + col + 3] = R.t[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < WR::UD; ++u) {
+        const int idx = tid + NTHR * u, row = idx / (BV / 8), c8 = 8 * (idx % (BV / 8));
+        const bool in = t0 + row < T;
+        const float x[8] = {R.d[u][0].x, R.d[u][0].y, R.d[u][0].z, R.d[u][0].w,
+                            R.d[u][1].x, R.d[u][1].y, R.d[u][1].z, R.d[u][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sdO[row * LDB + c8 + e] = in ? x[e] : 0.f;
+    }
+    if (tid < BT) {
+        // fp64 gate sums (see the intra stage): their differences are exact to fp32
+        sG2[tid] = R.g2;
+        sGam[tid] = exp2f((float)R.g2);
+        sDec[tid] = exp2f((float)(R.g2L - R.g2));
+        sBeta[tid] = (t0 + tid < T) ? R.beta : 0.f;
+    }
+}
+
 // --------------------------------------------------------- reverse state walk
 template <class Pol, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t *__restrict__ q,
@@ -127,11 +236,13 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
         sdS[row * LDB + col] = dht ? dht[sbase + (long)row * DV + vcol0 + col] : 0.f;
     }
     for (int idx = tid; idx < BT * LDC; idx += NTHR) sP[idx] = 0.f;  // upper tiles stay zero
+    using In = typename Pol::in_t;
+    WalkRegs<In, DK, BV, NTHR> R;
+    walk_fetch<In, DK, BV, NTHR>(R, q, k, beta, dO, G2ws, Tws, b, h, NT - 1, bh * NT + NT - 1, T, H, vcol0, DV, tid);
     __syncthreads();
 
     for (int c = NT - 1; c >= 0; --c) {
         const long cb = bh * NT + c;
-        const int t0 = c * BT;
         // gradient of the state leaving chunk c, for the per-chunk stage
 #pragma unroll
         for (int u = 0; u < DK * BV / 4 / NTHR; ++u) {
@@ -139,9 +250,10 @@ __global__ __launch_bounds__(256) void bwd_walk_kernel(const typename Pol::in_t 
             const float *p = &sdS[row * LDB + col];
             *(float4 *)(dSck + cb * DK * DV + (long)row * DV + vcol0 + col) = make_float4(p[0], p[1], p[2], p[3]);
         }
-        load_chunk_qk<Pol, DK, LDQ, NTHR>(sQ, sK, sG2, sGam, sDec, sBeta, q, k, beta, G2ws, b, h, c, cb, T, H, tid);
-        stage_tm<LDC, NTHR>(sTm, Tws + cb * BT * BT, tid);
-        stage_rows<BV, LDB, NTHR>(sdO, dO, b, h, t0, T, H, vcol0, DV, tid);
+        // this chunk's inputs arrived during the previous iteration; the next
+        // chunk's (c - 1) are requested now
+        walk_stage<In, DK, BV, NTHR, LDQ, LDC, LDB>(R, sQ, sK, sTm, sdO, sG2, sGam, sDec, sBeta, c, T, tid);
+        if (c > 0) walk_fetch<In, DK, BV, NTHR>(R, q, k, beta, dO, G2ws, Tws, b, h, c - 1, cb - 1, T, H, vcol0, DV, tid);
         __syncthreads();
         if (tid < BT) {
             sGdO[tid] = sGam[tid];               // B-row scale of (gamma Q)^T dO
