@@ -26,6 +26,8 @@
 //   4. bwd_chunk_kernel: one workgroup per (batch, head, chunk) recomputes
 //      the chunk and produces its dq, dk, dv, dbeta, dg, looping over the
 //      value columns 16 at a time
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -573,9 +575,15 @@ static hipError_t launch_bwd_t(const void *q, const void *k, const void *v, cons
                                int H, float scale, hipStream_t st) {
     using in_t = typename Pol::in_t;
     const int NT = (T + BT - 1) / BT;
-    hipLaunchKernelGGL((bwd_walk_kernel<Pol, DK, DV>), dim3((unsigned)((long)B * H * (DV / 32))), dim3(256), 0, st,
-                       (const in_t *)q, (const in_t *)k, beta, dO, dht, G2, Tinv, dSck, dh0, T, H, NT, scale);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if constexpr (std::is_same<in_t, uint16_t>::value) {
+        // bf16 inputs: the fused reverse walk (gdn_bwd_fused.hip)
+        e = launch_bwd_walk_fused(q, k, beta, dO, dht, G2, Tinv, dSck, dh0, B, T, H, DK, DV, scale, st);
+    } else {
+        hipLaunchKernelGGL((bwd_walk_kernel<Pol, DK, DV>), dim3((unsigned)((long)B * H * (DV / 32))), dim3(256), 0,
+                           st, (const in_t *)q, (const in_t *)k, beta, dO, dht, G2, Tinv, dSck, dh0, T, H, NT, scale);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_chunk_kernel<Pol, DK, DV>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
                        (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, dO, G2, Tinv, Sck, dSck, dq, dk, dv,

@@ -73,6 +73,12 @@ hipError_t launch_step2(const void *q, const void *k, const void *v, const float
                         const void *wg, float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                         hipStream_t st);
 
+// The reverse state walk of the GDN backward for bf16 inputs in one fused
+// kernel (gdn_bwd_fused.hip): dS' of every chunk into dSck, dh0 (nullable).
+hipError_t launch_bwd_walk_fused(const void *q, const void *k, const float *beta, const float *dO, const float *dht,
+                                 const double *G2, const float *Tinv, float *dSck, float *dh0, int B, int T, int H,
+                                 int Dk, int Dv, float scale, hipStream_t st);
+
 // Backward of the chunked GDN forward (gdn_bwd.hip): the reverse state walk
 // (dS' of every chunk into dSck, dh0) and the per-chunk gradients, given the
 // intra stage (G2, T - I) and the entry state of every chunk (Sck).
