@@ -33,6 +33,8 @@
 
 namespace gdn {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v;
+
 // acc (the 16x16 tile at rows i0, columns j0 of C) += A B over k in [0, K):
 // A(i, k) = A[i * sar + k * sac], B(k, j) = B[k * sbr + j * sbc] (LDS, fp32),
 // optionally B(k, j) * ks[k].  Lane (g, r) ends with C[i0 + 4g + e][j0 + r].
@@ -50,6 +52,34 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float *A, int sar, in
         float b = pb[k0 * sbr];
         if (ks) b *= ks[k0 + g];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// acc (the 16x16 tile at rows i0, columns j0 of C) += A B^T over k in
+// [0, K) for fp32 LDS rows A[i][k] = A[i * lda + k], B[j][k] = B[j * ldb + k]
+// whose values are bf16 numbers (bf16 inputs staged in fp32): one bf16 MFMA
+// per 32 k instead of eight fp32 ones, the same result up to fp32 summation
+// order.  Lane (g, r) gives both operands k-slots 8g .. 8g + 7 of its row.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+template <int K>
+__device__ __forceinline__ f32x4 tile_mma_bf16rows(f32x4 acc, const float *A, int lda, const float *B, int ldb, int i0,
+                                                   int j0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float *pa = A + (i0 + r) * lda + 8 * g;
+    const float *pb = B + (j0 + r) * ldb + 8 * g;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const float4 a0 = *(const float4 *)(pa + k0), a1 = *(const float4 *)(pa + k0 + 4);
+        const float4 b0 = *(const float4 *)(pb + k0), b1 = *(const float4 *)(pb + k0 + 4);
+        const uint4 ua = make_uint4(pack_bf16_exact(a0.x, a0.y), pack_bf16_exact(a0.z, a0.w),
+                                    pack_bf16_exact(a1.x, a1.y), pack_bf16_exact(a1.z, a1.w));
+        const uint4 ub = make_uint4(pack_bf16_exact(b0.x, b0.y), pack_bf16_exact(b0.z, b0.w),
+                                    pack_bf16_exact(b1.x, b1.y), pack_bf16_exact(b1.z, b1.w));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, ua), __builtin_bit_cast(bf16x8v, ub),
+                                                      acc, 0, 0, 0);
     }
     return acc;
 }
@@ -341,6 +371,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     float *__restrict__ dg, float *__restrict__ dbeta, int T, int H, int NT, float scale) {
     using SM = BwdChunkSmem<DK>;
     constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 256, NM = DK / 16;
+    // bf16 inputs: Q and K hold bf16 numbers, so their products run on bf16 MFMA
+    constexpr bool kExact = std::is_same<typename Pol::in_t, uint16_t>::value;
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -363,7 +395,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     // P = (Q K^T) . D, lower with the diagonal (all 16 tiles, upper ones zero)
     for (int tile = wave; tile < 16; tile += 4) {
         const int TI = tile >> 2, TJ = tile & 3;
-        const f32x4 acc = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * TI, 16 * TJ, lane);
+        f32x4 acc;
+        if constexpr (kExact) acc = tile_mma_bf16rows<DK>(zero4(), sm.Q, LDQ, sm.K, LDQ, 16 * TI, 16 * TJ, lane);
+        else acc = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * TI, 16 * TJ, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
@@ -474,8 +508,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     float colp[4][4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        const f32x4 KK = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
-        const f32x4 QK = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
+        f32x4 KK, QK;
+        if constexpr (kExact) {
+            KK = tile_mma_bf16rows<DK>(zero4(), sm.K, LDQ, sm.K, LDQ, 16 * I, 16 * J, lane);
+            QK = tile_mma_bf16rows<DK>(zero4(), sm.Q, LDQ, sm.K, LDQ, 16 * I, 16 * J, lane);
+        } else {
+            KK = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
+            QK = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.K, 1, LDQ, nullptr, 16 * I, 16 * J, lane);
+        }
         const int j = 16 * J + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
