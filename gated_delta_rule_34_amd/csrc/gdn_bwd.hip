@@ -34,6 +34,8 @@
 namespace gdn {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v;
+// 16 bytes as a native vector (arrays of HIP's uint4 struct can be demoted to scratch)
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4b;
 
 // acc (the 16x16 tile at rows i0, columns j0 of C) += A B over k in [0, K):
 // A(i, k) = A[i * sar + k * sac], B(k, j) = B[k * sbr + j * sbc] (LDS, fp32),
@@ -141,7 +143,7 @@ struct WalkRegs {
     static constexpr int UQ = BT * DK / 8 / NTHR;     // 8-input groups per thread (Q, K rows)
     static constexpr int UT = BT * BT / 4 / NTHR;     // float4 per thread (T - I)
     static constexpr int UD = BT * BV / 8 / NTHR;     // 8-float groups per thread (dO)
-    uint4 q[UQ][W], k[UQ][W];
+    u32x4b q[UQ][W], k[UQ][W];
     float4 t[UT];
     float4 d[UD][2];
     double g2, g2L;
@@ -160,8 +162,8 @@ __device__ __forceinline__ void walk_fetch(WalkRegs<In, DK, BV, NTHR> &R, const 
         const long off = ((b * T + min(t0 + row, T - 1)) * H + h) * (long)DK + c8;
 #pragma unroll
         for (int w = 0; w < WR::W; ++w) {
-            R.q[u][w] = *(const uint4 *)((const char *)(q + off) + 16 * w);
-            R.k[u][w] = *(const uint4 *)((const char *)(k + off) + 16 * w);
+            R.q[u][w] = *(const u32x4b *)((const char *)(q + off) + 16 * w);
+            R.k[u][w] = *(const u32x4b *)((const char *)(k + off) + 16 * w);
         }
     }
 #pragma unroll
@@ -181,16 +183,16 @@ __device__ __forceinline__ void walk_fetch(WalkRegs<In, DK, BV, NTHR> &R, const 
 }
 
 // Eight inputs of a 16-byte piece (bf16) or two (fp32) as floats.
-__device__ __forceinline__ void raw8(float (&x)[8], const uint4 (&u)[1]) {
-    const uint32_t w[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
+__device__ __forceinline__ void raw8(float (&x)[8], const u32x4b (&u)[1]) {
+    const uint32_t w[4] = {u[0][0], u[0][1], u[0][2], u[0][3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[2 * e] = __uint_as_float(w[e] << 16);
         x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
 }
-__device__ __forceinline__ void raw8(float (&x)[8], const uint4 (&u)[2]) {
-    const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+__device__ __forceinline__ void raw8(float (&x)[8], const u32x4b (&u)[2]) {
+    const uint32_t w[8] = {u[0][0], u[0][1], u[0][2], u[0][3], u[1][0], u[1][1], u[1][2], u[1][3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
 }
@@ -363,7 +365,7 @@ struct BwdChunkSmem {
 };
 
 template <class Pol, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
     const typename Pol::in_t *__restrict__ q, const typename Pol::in_t *__restrict__ k,
     const typename Pol::in_t *__restrict__ v, const float *__restrict__ beta, const float *__restrict__ dO,
     const double *__restrict__ G2ws, const float *__restrict__ Tws, const float *__restrict__ Sck,
@@ -412,19 +414,42 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     for (int j = 0; j < 4; ++j) dA[j] = dP[j] = zero4();
     float dGC = 0.f;  // <dS', S> over the slices this thread loaded
 
+    // The next slice's S, dS', V and dO are requested into registers while
+    // the current one is worked on, then staged after the barrier.
+    using In = typename Pol::in_t;
+    constexpr int US = DK * CW / 4 / NTHR;   // float4 of S (and of dS') per thread
+    constexpr int WV = sizeof(In) / 2;       // 16-byte pieces per 8 values of v
+    static_assert(BT * CW / 8 == NTHR / 2, "one 8-value piece of v or dO per thread");
+    float4 xs[US], xd[US], xo[2];
+    u32x4b xv[WV];
+    const int prow = (tid & (NTHR / 2 - 1)) / (CW / 8), pc8 = 8 * (tid % (CW / 8));  // this thread's v/dO piece
+    const int pt = min(t0 + prow, T - 1);
+    auto fetch_slice = [&](int cc) {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
+            const long off = cb * DK * DV + (long)row * DV + cc + col;
+            xs[u] = *(const float4 *)(Sck + off);
+            xd[u] = *(const float4 *)(dSck + off);
+        }
+        if (tid < NTHR / 2) {
+            const In *pv = v + ((b * T + pt) * H + h) * (long)DV + cc + pc8;
+#pragma unroll
+            for (int w = 0; w < WV; ++w) xv[w] = *(const u32x4b *)((const char *)pv + 16 * w);
+        } else {
+            const float *po = dO + ((b * T + pt) * H + h) * (long)DV + cc + pc8;
+            xo[0] = *(const float4 *)po;
+            xo[1] = *(const float4 *)(po + 4);
+        }
+    };
+    // (fp32 inputs fetch each slice just before staging it: the prefetch's
+    // registers would not fit beside theirs)
+    if constexpr (kExact) fetch_slice(0);
+
     for (int c0 = 0; c0 < DV; c0 += CW) {
         __syncthreads();  // previous slice fully consumed
+        if constexpr (!kExact) fetch_slice(c0);
         {
-            // S and dS' slices: DK x CW fp32, 4 columns per thread and pass
-            constexpr int US = DK * CW / 4 / NTHR;
-            float4 xs[US], xd[US];
-#pragma unroll
-            for (int u = 0; u < US; ++u) {
-                const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
-                const long off = cb * DK * DV + (long)row * DV + c0 + col;
-                xs[u] = *(const float4 *)(Sck + off);
-                xd[u] = *(const float4 *)(dSck + off);
-            }
 #pragma unroll
             for (int u = 0; u < US; ++u) {
                 const int idx = 4 * (tid + NTHR * u), row = idx / CW, col = idx % CW;
@@ -433,9 +458,19 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
                 pd[0] = xd[u].x; pd[1] = xd[u].y; pd[2] = xd[u].z; pd[3] = xd[u].w;
                 dGC += xs[u].x * xd[u].x + xs[u].y * xd[u].y + xs[u].z * xd[u].z + xs[u].w * xd[u].w;
             }
+            const bool in = t0 + prow < T;  // rows past T are zero
+            float x8[8];
+            if (tid < NTHR / 2) {
+                raw8(x8, xv);
+            } else {
+                x8[0] = xo[0].x; x8[1] = xo[0].y; x8[2] = xo[0].z; x8[3] = xo[0].w;
+                x8[4] = xo[1].x; x8[5] = xo[1].y; x8[6] = xo[1].z; x8[7] = xo[1].w;
+            }
+            float *dst = (tid < NTHR / 2 ? sm.V : sm.dO) + prow * LDW + pc8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = in ? x8[e] : 0.f;
         }
-        if (tid < BT * CW / 8) stage_rows<CW, LDW, BT * CW / 8>(sm.V, v, b, h, t0, T, H, c0, DV, tid);
-        else if (tid < BT * CW / 4) stage_rows<CW, LDW, BT * CW / 8>(sm.dO, dO, b, h, t0, T, H, c0, DV, tid - BT * CW / 8);
+        if (kExact && c0 + CW < DV) fetch_slice(c0 + CW);
         __syncthreads();
         // KS, QS, R for rows of block I
         const f32x4 KS = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
