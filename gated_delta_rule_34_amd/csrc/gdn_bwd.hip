@@ -66,6 +66,14 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float *A, int sar, in
 __device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
     return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
+// a, b rounded to bf16 (nearest even) in the low and high halves
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 template <int K>
 __device__ __forceinline__ f32x4 tile_mma_bf16rows(f32x4 acc, const float *A, int lda, const float *B, int ldb, int i0,
                                                    int j0, int lane) {
@@ -84,6 +92,32 @@ __device__ __forceinline__ f32x4 tile_mma_bf16rows(f32x4 acc, const float *A, in
                                                       acc, 0, 0, 0);
     }
     return acc;
+}
+
+// Eight floats as 2 or 3 bf16 parts (hi + lo ~16 bits, hi + mid + lo ~24
+// bits), packed in k-slot order for a bf16 MFMA operand.
+__device__ __forceinline__ void split_8(u32x4b (&out)[2], const float (&x)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t h = pack_bf16_rne(x[2 * p], x[2 * p + 1]);
+        out[0][p] = h;
+        out[1][p] = pack_bf16_rne(x[2 * p] - bf16_lo(h), x[2 * p + 1] - bf16_hi(h));
+    }
+}
+__device__ __forceinline__ void split_8(u32x4b (&out)[3], const float (&x)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t h = pack_bf16_rne(x[2 * p], x[2 * p + 1]);
+        const float r0 = x[2 * p] - bf16_lo(h), r1 = x[2 * p + 1] - bf16_hi(h);
+        const uint32_t m = pack_bf16_rne(r0, r1);
+        out[0][p] = h;
+        out[1][p] = m;
+        out[2][p] = pack_bf16_rne(r0 - bf16_lo(m), r1 - bf16_hi(m));
+    }
+}
+__device__ __forceinline__ f32x4 mma_bf16v(f32x4 acc, const u32x4b &a, const u32x4b &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b), acc,
+                                                   0, 0, 0);
 }
 
 // Sum over the 16 lanes of a lane group (the columns of a tile row).
@@ -584,12 +618,58 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
     // dk = diag(beta) dAs K + dAs^T diag(beta) K + dPs^T Q + diag(dec) dKd - diag(beta gamma) dkR
     // dq = scale diag(gamma) dqs + dPs K
     float tdec[4] = {0.f, 0.f, 0.f, 0.f};  // sum_m dKd_im K_im for the 4 rows of this lane
+    // bf16 inputs: the four products on bf16 MFMA.  Their left operands (dA.D,
+    // its transpose with beta, dP.D transposed and not) are split once into
+    // bf16 parts (three for dP.D, which feeds dq, two for the others); K and Q
+    // are bf16 numbers.  Lane (g, r): row 16I + r, k-slots 32 kb + 8g .. + 7.
+    u32x4b a1[2][2], a2[2][2], a3[2][2], a4[2][3];
+    if constexpr (kExact) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float x1[8], x2[8], x3[8], x4[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 16 * I + r, j = 32 * kb + 8 * g + e;
+                x1[e] = sm.Tm[i * LDC + j];
+                x2[e] = sm.Tm[j * LDC + i] * sm.Beta[j];
+                x3[e] = sm.P[j * LDC + i];
+                x4[e] = sm.P[i * LDC + j];
+            }
+            split_8(a1[kb], x1);
+            split_8(a2[kb], x2);
+            split_8(a3[kb], x3);
+            split_8(a4[kb], x4);
+        }
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const f32x4 t1 = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
-        const f32x4 t2 = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sm.K, LDQ, 1, sm.Beta, 16 * I, 16 * m, lane);
-        const f32x4 t3 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sm.Q, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
-        const f32x4 t4 = tile_mma<BT>(zero4(), sm.P, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+        f32x4 t1, t2, t3, t4;
+        if constexpr (kExact) {
+            t1 = t2 = t3 = t4 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float xk[8], xq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * kb + 8 * g + e;
+                    xk[e] = sm.K[j * LDQ + 16 * m + r];
+                    xq[e] = sm.Q[j * LDQ + 16 * m + r];
+                }
+                const u32x4b bk = {pack_bf16_exact(xk[0], xk[1]), pack_bf16_exact(xk[2], xk[3]),
+                                   pack_bf16_exact(xk[4], xk[5]), pack_bf16_exact(xk[6], xk[7])};
+                const u32x4b bq = {pack_bf16_exact(xq[0], xq[1]), pack_bf16_exact(xq[2], xq[3]),
+                                   pack_bf16_exact(xq[4], xq[5]), pack_bf16_exact(xq[6], xq[7])};
+                t1 = mma_bf16v(mma_bf16v(t1, a1[kb][0], bk), a1[kb][1], bk);
+                t2 = mma_bf16v(mma_bf16v(t2, a2[kb][0], bk), a2[kb][1], bk);
+                t3 = mma_bf16v(mma_bf16v(t3, a3[kb][0], bq), a3[kb][1], bq);
+                t4 = mma_bf16v(mma_bf16v(mma_bf16v(t4, a4[kb][0], bk), a4[kb][1], bk), a4[kb][2], bk);
+            }
+        } else {
+            t1 = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+            t2 = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sm.K, LDQ, 1, sm.Beta, 16 * I, 16 * m, lane);
+            t3 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sm.Q, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+            t4 = tile_mma<BT>(zero4(), sm.P, LDC, 1, sm.K, LDQ, 1, nullptr, 16 * I, 16 * m, lane);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e, col = 16 * m + r;
