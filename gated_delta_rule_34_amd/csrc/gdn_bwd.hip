@@ -120,6 +120,39 @@ __device__ __forceinline__ f32x4 mma_bf16v(f32x4 acc, const u32x4b &a, const u32
                                                    0, 0, 0);
 }
 
+// acc += A B over k in [0, K), A = fp32 LDS rows holding bf16 numbers (row
+// stride lda), B given as NP bf16 parts per 32-deep block (k-slots
+// 32 kb + 8g .. + 7 of this lane's column).
+template <int K, int NP>
+__device__ __forceinline__ f32x4 mma_rows_parts(f32x4 acc, const float *A, int lda, int i0,
+                                                const u32x4b (&bp)[K / 32][NP], int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float *pa = A + (i0 + r) * lda + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+        const float4 a0 = *(const float4 *)(pa + 32 * kb), a1 = *(const float4 *)(pa + 32 * kb + 4);
+        const u32x4b ua = {pack_bf16_exact(a0.x, a0.y), pack_bf16_exact(a0.z, a0.w), pack_bf16_exact(a1.x, a1.y),
+                           pack_bf16_exact(a1.z, a1.w)};
+#pragma unroll
+        for (int q = 0; q < NP; ++q) acc = mma_bf16v(acc, ua, bp[kb][q]);
+    }
+    return acc;
+}
+
+// Column col of a [K][ld] fp32 LDS matrix as NP bf16 parts per 32-deep
+// block, k-slots 32 kb + 8g .. + 7.
+template <int K, int NP>
+__device__ __forceinline__ void col_parts(u32x4b (&bp)[K / 32][NP], const float *M, int ld, int col, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = M[(32 * kb + 8 * g + e) * ld + col];
+        split_8(bp[kb], x);
+    }
+}
+
 // Sum over the 16 lanes of a lane group (the columns of a tile row).
 __device__ __forceinline__ float row16_sum(float x) {
     x += __shfl_xor(x, 1);
@@ -507,8 +540,17 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
         if (kExact && c0 + CW < DV) fetch_slice(c0 + CW);
         __syncthreads();
         // KS, QS, R for rows of block I
-        const f32x4 KS = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
-        const f32x4 QS = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
+        f32x4 KS, QS;
+        if constexpr (kExact) {
+            // K, Q exact in bf16; the S slice as bf16 hi + lo
+            u32x4b sp[DK / 32][2];
+            col_parts<DK, 2>(sp, sm.S, LDW, r, lane);
+            KS = mma_rows_parts<DK, 2>(zero4(), sm.K, LDQ, 16 * I, sp, lane);
+            QS = mma_rows_parts<DK, 2>(zero4(), sm.Q, LDQ, 16 * I, sp, lane);
+        } else {
+            KS = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
+            QS = tile_mma<DK>(zero4(), sm.Q, LDQ, 1, sm.S, LDW, 1, nullptr, 16 * I, 0, lane);
+        }
         f32x4 Rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -521,7 +563,15 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
         {
             const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, nullptr, 16 * I, 0, lane);
             const f32x4 b1 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, nullptr, 16 * I, 0, lane);
-            const f32x4 b2 = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, nullptr, 16 * I, 0, lane);
+            f32x4 b2;
+            if constexpr (kExact) {
+                // K exact; dS' as three bf16 parts (K dS' carries the state gradient)
+                u32x4b dp[DK / 32][3];
+                col_parts<DK, 3>(dp, sm.dS, LDW, r, lane);
+                b2 = mma_rows_parts<DK, 3>(zero4(), sm.K, LDQ, 16 * I, dp, lane);
+            } else {
+                b2 = tile_mma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, nullptr, 16 * I, 0, lane);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
