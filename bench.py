@@ -49,7 +49,7 @@ KERNEL_SOURCES = {
     "step_kernel": ("gdn_step.hip", "gdn_device.h"),
     "step2_kernel": ("gdn_step.hip", "gdn_device.h"),
     "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
-    "gdn_bwd": ("gdn_bwd.hip", "gdn_chunk.hip", "gdn_device.h"),
+    "gdn_bwd": ("gdn_bwd.hip", "gdn_bwd_fused.hip", "gdn_fused.hip", "gdn_chunk.hip", "gdn_tile.h", "gdn_device.h"),
     "prologue_kernel": ("gdn_prologue.hip", "gdn_device.h"),
     "gdn2_bwd": ("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn_device.h"),
 }
