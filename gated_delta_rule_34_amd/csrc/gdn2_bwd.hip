@@ -30,6 +30,8 @@
 //   gdn2_bwd_key_kernel: one workgroup per (chunk, 64 key channels): the
 //     decay-weighted contractions with exact per-channel exponentials, then
 //     dq, dk, db and dlog_alpha.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -514,6 +516,189 @@ __global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
     }
 }
 
+// Key side for bf16 inputs: one lane per key channel, one wave per 64
+// channels, one workgroup per chunk.  The channel's key and log-decay rows
+// live in the lane's registers (the key as packed bf16 pairs), so the
+// per-channel exponentials need no LDS; only dA and dP, shared by every
+// channel, are staged in LDS and read as broadcast 4 x 4 blocks.
+//
+// Rows are visited in 4-row blocks from the last block back.  For block
+// rows i >= i0 and earlier columns j < i0 the decay is split at the block's
+// first row, D_ijc = 2^(G_ic - G_i0c) 2^(G_i0c - G_jc), both factors at most
+// 1, so one exponential per (j, channel) serves the 4 x 4 block on both
+// sides; inside the diagonal block every D_ijc is exact.  When block ib is
+// reached every row i >= its rows has already added its column-side terms,
+// so the block's rows are finished there: dq, db, dk and, because rows come
+// in reverse order, the reverse cumulative sum giving dlog_alpha.
+template <int DK>
+__global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ la,
+    const uint16_t *__restrict__ bg, const float *__restrict__ dEh, const float *__restrict__ dQh,
+    const float *__restrict__ dKh, const float *__restrict__ srow, const float *__restrict__ dAws,
+    const float *__restrict__ dPws, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dla,
+    float *__restrict__ db, int T, int H, int NT) {
+    constexpr int NB = BT / 4;
+    __shared__ f32x4 sA[BT * BT / 4], sP[BT * BT / 4];  // dA, dP rows of the chunk, 4 columns per entry
+    const int tid = threadIdx.x;
+    const long cb = blockIdx.x;
+    const int c = (int)(cb % NT);
+    const long bh = cb / NT;
+    const int h = (int)(bh % H);
+    const long b = bh / H;
+    const int t0 = c * BT;
+    const int nrows = min(BT, T - t0);
+    const long ob = cb * (long)BT * DK;
+    const long rs = (long)H * DK;                             // token stride of a [B, T, H, DK] tensor
+    const long gbase = ((b * T + t0) * H + h) * (long)DK + tid;  // this channel at row 0 of the chunk
+
+    {
+        constexpr int U = BT * BT / 4 / DK;
+        f32x4 xa[U], xp[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xa[u] = *(const f32x4 *)(dAws + cb * BT * BT + 4 * (tid + DK * u));
+            xp[u] = *(const f32x4 *)(dPws + cb * BT * BT + 4 * (tid + DK * u));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            sA[tid + DK * u] = xa[u];
+            sP[tid + DK * u] = xp[u];
+        }
+    }
+    // the channel's key (bf16 pairs) and log2(e) * chunk-local cumsum of the
+    // log-decay (fp64 running sum, as in the intra stage)
+    uint32_t K2[BT / 2];
+    float G[BT];
+    {
+        uint16_t kr[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const bool in = j < nrows;
+            kr[j] = in ? k[gbase + j * rs] : (uint16_t)0;
+            G[j] = in ? la[gbase + j * rs] : 0.f;
+        }
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            acc += G[j];
+            G[j] = (float)(acc * 1.4426950408889634);
+        }
+#pragma unroll
+        for (int j = 0; j < BT / 2; ++j) K2[j] = (uint32_t)kr[2 * j] | ((uint32_t)kr[2 * j + 1] << 16);
+    }
+    auto Kf = [&](int j) -> float {
+        return __uint_as_float((j & 1) ? (K2[j >> 1] & 0xffff0000u) : (K2[j >> 1] << 16));
+    };
+    const float GL = G[BT - 1];
+    // the last row's G also enters Khat (sum_j dKhat . Khat) and the
+    // Gam_last . S term of S' (sum_v dS' . S): a constant in every dlog_alpha
+    float run = __builtin_amdgcn_exp2f(GL) * srow[cb * DK + tid];
+#pragma unroll
+    for (int j = 0; j < BT; ++j)
+        run += dKh[ob + (long)j * DK + tid] * Kf(j) * __builtin_amdgcn_exp2f(GL - G[j]);
+    float cs[BT];  // column sums: sum_i D_ij (dA_ij e_i + dP_ij q_i) of this channel
+#pragma unroll
+    for (int j = 0; j < BT; ++j) cs[j] = 0.f;
+    __syncthreads();
+
+#pragma unroll 1
+    for (int ib = NB - 1; ib >= 0; --ib) {
+        const int i0 = 4 * ib;
+        // this block's rows of the register arrays (every later row block has
+        // already added its terms to the column sums cur)
+        float Gi[4], Ki[4], cur[4], Bi[4], Qi[4], Ei[4], a[4], Et[4], Qt[4], xE[4], xQ[4], xK[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Gi[x] = Ki[x] = cur[x] = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            const bool sel = jb == ib;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                Gi[x] = sel ? G[4 * jb + x] : Gi[x];
+                Ki[x] = sel ? Kf(4 * jb + x) : Ki[x];
+                cur[x] = sel ? cs[4 * jb + x] : cur[x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const bool in = i0 + x < nrows;
+            const long off = gbase + (i0 + x) * rs;
+            Bi[x] = in ? bf16_to_f32(bg[off]) : 0.f;
+            Qi[x] = in ? bf16_to_f32(q[off]) : 0.f;
+            const long wo = ob + (long)(i0 + x) * DK + tid;
+            xE[x] = dEh[wo];
+            xQ[x] = dQh[wo];
+            xK[x] = dKh[wo];
+            Ei[x] = Bi[x] * Ki[x];
+            a[x] = __builtin_amdgcn_exp2f(Gi[x] - Gi[0]);
+            Et[x] = Ei[x] * a[x];
+            Qt[x] = Qi[x] * a[x];
+        }
+        float rA[4] = {0.f, 0.f, 0.f, 0.f}, rP[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < NB - 1; ++jb) {
+            const int j0 = 4 * jb;
+            if (jb < ib) {
+                float f[4], km[4], t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    f[y] = __builtin_amdgcn_exp2f(Gi[0] - G[j0 + y]);
+                    km[y] = Kf(j0 + y) * f[y];
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const f32x4 A4 = sA[(i0 + x) * (BT / 4) + jb], P4 = sP[(i0 + x) * (BT / 4) + jb];
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        rA[x] = fmaf(A4[y], km[y], rA[x]);
+                        rP[x] = fmaf(P4[y], km[y], rP[x]);
+                        t[y] = fmaf(A4[y], Et[x], fmaf(P4[y], Qt[x], t[y]));
+                    }
+                }
+#pragma unroll
+                for (int y = 0; y < 4; ++y) cs[j0 + y] = fmaf(f[y], t[y], cs[j0 + y]);
+            }
+        }
+        // diagonal block, exact decays; then the block's rows are complete
+        {
+            float rAd[4], rPd[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const f32x4 A4 = sA[(i0 + x) * (BT / 4) + ib], P4 = sP[(i0 + x) * (BT / 4) + ib];
+                rAd[x] = 0.f;
+                rPd[x] = 0.f;
+#pragma unroll
+                for (int y = 0; y <= x; ++y) {
+                    const float d = (y == x) ? 1.f : __builtin_amdgcn_exp2f(Gi[x] - Gi[y]);
+                    const float kd = Ki[y] * d;
+                    if (y < x) rAd[x] = fmaf(A4[y], kd, rAd[x]);
+                    rPd[x] = fmaf(P4[y], kd, rPd[x]);
+                    const float tv = (y < x) ? fmaf(A4[y], Ei[x], P4[y] * Qi[x]) : P4[y] * Qi[x];
+                    cur[y] = fmaf(d, tv, cur[y]);
+                }
+            }
+#pragma unroll
+            for (int x = 3; x >= 0; --x) {
+                const float ra = fmaf(a[x], rA[x], rAd[x]), rp = fmaf(a[x], rP[x], rPd[x]);
+                const float cc = cur[x];
+                const float gam = __builtin_amdgcn_exp2f(Gi[x]), dec = __builtin_amdgcn_exp2f(GL - Gi[x]);
+                const float de = fmaf(gam, xE[x], ra);
+                const float dqv = fmaf(gam, xQ[x], rp);
+                const float tk = xK[x] * Ki[x] * dec;
+                const float dg = Ei[x] * ra + Qi[x] * rp - Ki[x] * cc + gam * Ei[x] * xE[x] + gam * Qi[x] * xQ[x] - tk;
+                run += dg;
+                if (i0 + x < nrows) {
+                    const long off = gbase + (i0 + x) * rs;
+                    dq[off] = dqv;
+                    db[off] = de * Ki[x];
+                    dk[off] = cc + dec * xK[x] + de * Bi[x];
+                    dla[off] = run;
+                }
+            }
+        }
+    }
+}
+
 // ----------------------------------------------------------------- launcher
 template <class Pol, int DK, int DV>
 static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v, const float *la, const void *bg,
@@ -534,9 +719,14 @@ static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v,
                        H, NT, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn2_bwd_key_kernel<Pol, DK>), dim3((unsigned)(heads * NT * (DK / 64))), dim3(256), 0, st,
-                       (const in_t *)q, (const in_t *)k, la, (const in_t *)bg, Eh, Qh, Kh, GamC, Tws, Pws, dq, dk, dla,
-                       db, T, H, NT);
+    if (std::is_same<in_t, uint16_t>::value)
+        hipLaunchKernelGGL((gdn2_bwd_key_lane_kernel<DK>), dim3((unsigned)(heads * NT)), dim3(DK), 0, st,
+                           (const uint16_t *)q, (const uint16_t *)k, la, (const uint16_t *)bg, Eh, Qh, Kh, GamC,
+                           Tws, Pws, dq, dk, dla, db, T, H, NT);
+    else
+        hipLaunchKernelGGL((gdn2_bwd_key_kernel<Pol, DK>), dim3((unsigned)(heads * NT * (DK / 64))), dim3(256), 0,
+                           st, (const in_t *)q, (const in_t *)k, la, (const in_t *)bg, Eh, Qh, Kh, GamC, Tws, Pws, dq,
+                           dk, dla, db, T, H, NT);
     return hipGetLastError();
 }
 
