@@ -479,6 +479,8 @@ static hipError_t launch_gdn2_recompute_t(const void *q, const void *k, const fl
     using in_t = typename Pol::in_t;
     hipError_t e = launch_gdn2_intra_t<Pol, DK>(q, k, la, bg, Eh, Qh, Kh, GamC, Tinv, P, D, B, T, H, st);
     if (e != hipSuccess) return e;
+    if (std::is_same<in_t, uint16_t>::value)
+        return launch_gdn2_states_bf16(Eh, Kh, Tinv, GamC, v, wg, h0, ck, B, T, H, DK, DV, st);
     const int NT = (T + BT - 1) / BT;
     hipLaunchKernelGGL((gdn2_walk_kernel<Pol, DK, DV, BV, false>), dim3((unsigned)((long)B * H * (DV / BV))), dim3(BV * 4),
                        0, st, (const float *)Eh, (const float *)Qh, (const float *)Kh, GamC, Tinv, P, D,

@@ -91,6 +91,11 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *
 // (gdn2_chunk.hip; intra operands into Eh .. D, chunk entry states into ck),
 // then the reverse walk and the per-chunk gradients (gdn2_bwd.hip), which
 // overwrite Eh, Qh, Kh, GamC, Tinv and P with their gradients.
+// Entry state of every chunk of the GDN-2 forward from the intra stage's
+// fp32 operands (bf16 v and w), on split 16-bit MFMA operands.
+hipError_t launch_gdn2_states_bf16(const float *Eh, const float *Kh, const float *Tws, const float *GamC,
+                                   const void *v, const void *w, const float *h0, float *ck, int B, int T, int H,
+                                   int Dk, int Dv, hipStream_t st);
 hipError_t launch_gdn2_recompute(const void *q, const void *k, const float *la, const void *bg, const void *v,
                                  const void *wg, const float *h0, float *Eh, float *Qh, float *Kh, float *GamC,
                                  float *Tinv, float *P, float *D, float *ck, int B, int T, int H, int Dk, int Dv,
