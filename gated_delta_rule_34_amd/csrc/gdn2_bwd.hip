@@ -123,92 +123,135 @@ __device__ constexpr int lJ(int t) { return t - lI(t) * (lI(t) + 1) / 2; }
 }  // namespace
 
 // ------------------------------------------------------- reverse state walk
+// One workgroup per (batch, head, 16 state-gradient columns), four waves.
+// The next chunk's operands are requested into registers while the current
+// chunk is worked on, and stored into LDS at the top of the next iteration.
+template <int DK>
+struct Gdn2WalkPf {
+    static constexpr int UE = BT * DK / 4 / 256, UT = BT * BT / 4 / 256;
+    f32x4 k[UE], q[UE], e[UE], t[UT], p[UT], o, gam;
+    float dg[UT];
+};
+
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void gdn2_bwd_walk_kernel(
+__global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
     const float *__restrict__ Eh, const float *__restrict__ Qh, const float *__restrict__ Kh,
     const float *__restrict__ GamC, const float *__restrict__ Tws, const float *__restrict__ Pws,
     const float *__restrict__ Dws, const float *__restrict__ dO, const float *__restrict__ dht,
     float *__restrict__ dSck, float *__restrict__ dh0, int T, int H, int NT, float scale) {
-    constexpr int BV = 32, NTHR = 256, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
-    __shared__ float sA[BT * LDQ], sQ[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
+    constexpr int BV = 16, NTHR = 256, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
+    using PF = Gdn2WalkPf<DK>;
+    __shared__ float sK[BT * LDQ], sQ[BT * LDQ], sE[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
     __shared__ float sdO[BT * LDB], sdDl[BT * LDB], sdR[BT * LDB], sdS[DK * LDB], sGam[DK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     constexpr int NTILE = DV / BV;
-    const int vt = blockIdx.x % NTILE;
-    const long bh = blockIdx.x / NTILE;
+    const int n = blockIdx.x, nwg = gridDim.x;
+    // the column slices of one head get consecutive ids on one XCD (shared L2)
+    const int L = (nwg % 8 == 0) ? (n % 8) * (nwg / 8) + n / 8 : n;
+    const int vt = L % NTILE;
+    const long bh = L / NTILE;
     const int h = (int)(bh % H);
     const long b = bh / H;
     const int vcol0 = vt * BV;
     const long sbase = bh * (long)DK * DV;
 
+    PF pf;
+    auto fetch = [&](int c) {
+        const long cb = bh * NT + c;
+        const long ob = cb * (long)BT * DK;
+#pragma unroll
+        for (int u = 0; u < PF::UE; ++u) {
+            pf.k[u] = *(const f32x4 *)(Kh + ob + 4 * (tid + NTHR * u));
+            pf.q[u] = *(const f32x4 *)(Qh + ob + 4 * (tid + NTHR * u));
+            pf.e[u] = *(const f32x4 *)(Eh + ob + 4 * (tid + NTHR * u));
+        }
+#pragma unroll
+        for (int u = 0; u < PF::UT; ++u) {
+            pf.t[u] = *(const f32x4 *)(Tws + cb * BT * BT + 4 * (tid + NTHR * u));
+            pf.p[u] = *(const f32x4 *)(Pws + cb * BT * BT + 4 * (tid + NTHR * u));
+            pf.dg[u] = Dws[cb * BT + ((4 * (tid + NTHR * u)) >> 6)];
+        }
+        {   // dO: 64 rows x 16 columns, one f32x4 per thread
+            const int row = tid >> 2, col = 4 * (tid & 3);
+            const int t = c * BT + row;
+            pf.o = (t < T) ? *(const f32x4 *)(dO + ((b * T + t) * H + h) * (long)DV + vcol0 + col) : zero4();
+        }
+        pf.gam = (tid < DK / 4) ? *(const f32x4 *)(GamC + cb * DK + 4 * tid) : zero4();
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int u = 0; u < PF::UE; ++u) {
+            const int idx = 4 * (tid + NTHR * u), row = idx / DK, col = idx % DK;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sK[row * LDQ + col + e] = pf.k[u][e];
+                sQ[row * LDQ + col + e] = pf.q[u][e];
+                sE[row * LDQ + col + e] = pf.e[u][e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PF::UT; ++u) {
+            const int idx = 4 * (tid + NTHR * u), i = idx >> 6, j = idx & 63;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sTm[i * LDC + j + e] = pf.t[u][e];
+                sP[i * LDC + j + e] = (j + e < i) ? pf.p[u][e] : (j + e == i ? pf.dg[u] : 0.f);
+            }
+        }
+        {
+            const int row = tid >> 2, col = 4 * (tid & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sdO[row * LDB + col + e] = pf.o[e];
+        }
+        if (tid < DK / 4) *(f32x4 *)&sGam[4 * tid] = pf.gam;
+    };
+
     for (int idx = tid; idx < DK * BV; idx += NTHR) {
         const int row = idx / BV, col = idx % BV;
         sdS[row * LDB + col] = dht ? dht[sbase + (long)row * DV + vcol0 + col] : 0.f;
     }
+    if (NT > 0) fetch(NT - 1);
     __syncthreads();
     for (int c = NT - 1; c >= 0; --c) {
         const long cb = bh * NT + c;
-        const long ob = cb * (long)BT * DK;
         // gradient of the state leaving chunk c, for the per-chunk stages
         for (int idx = tid; idx < DK * BV / 4; idx += NTHR) {
             const int row = (4 * idx) / BV, col = (4 * idx) % BV;
             const float *p = &sdS[row * LDB + col];
-            *(float4 *)(dSck + cb * DK * DV + (long)row * DV + vcol0 + col) = make_float4(p[0], p[1], p[2], p[3]);
+            *(f32x4 *)(dSck + cb * DK * DV + (long)row * DV + vcol0 + col) = (f32x4){p[0], p[1], p[2], p[3]};
         }
-        stage_block<DK, LDQ, NTHR>(sA, Kh + ob, tid);
-        stage_block<DK, LDQ, NTHR>(sQ, Qh + ob, tid);
-        stage_tp<LDC>(sTm, sP, Tws + cb * BT * BT, Pws + cb * BT * BT, Dws + cb * BT, tid);
+        put();
+        if (c > 0) fetch(c - 1);
+        __syncthreads();
+        // dDl = scale P^T dO + Khat dS' (row block I = wave)
         {
-            constexpr int UO = BT * BV / 4 / NTHR;
-            float4 xo[UO];
+            const int I = wave;
+            const f32x4 a1 = tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 0, lane);
+            const f32x4 a2 = tmma<DK>(zero4(), sK, LDQ, 1, sdS, LDB, 1, 16 * I, 0, lane);
 #pragma unroll
-            for (int u = 0; u < UO; ++u) {
-                const int idx = 4 * (tid + NTHR * u), row = idx / BV, col = idx % BV;
-                const int t = min(c * BT + row, T - 1);
-                xo[u] = *(const float4 *)(dO + ((b * T + t) * H + h) * (long)DV + vcol0 + col);
-            }
-#pragma unroll
-            for (int u = 0; u < UO; ++u) {
-                const int idx = 4 * (tid + NTHR * u), row = idx / BV, col = idx % BV;
-                const bool in = c * BT + row < T;
-                float *p = &sdO[row * LDB + col];
-                p[0] = in ? xo[u].x : 0.f; p[1] = in ? xo[u].y : 0.f;
-                p[2] = in ? xo[u].z : 0.f; p[3] = in ? xo[u].w : 0.f;
-            }
-        }
-        for (int idx = tid; idx < DK; idx += NTHR) sGam[idx] = GamC[cb * DK + idx];
-        __syncthreads();
-        // dDl = scale P^T dO + Khat dS' (8 tiles of 64 x 32)
-        for (int tile = wave; tile < 8; tile += 4) {
-            const int I = tile >> 1, J = tile & 1;
-            const f32x4 a1 = tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 16 * J, lane);
-            const f32x4 a2 = tmma<DK>(zero4(), sA, LDQ, 1, sdS, LDB, 1, 16 * I, 16 * J, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sdDl[(16 * I + 4 * g + e) * LDB + 16 * J + r] = scale * a1[e] + a2[e];
+            for (int e = 0; e < 4; ++e) sdDl[(16 * I + 4 * g + e) * LDB + r] = scale * a1[e] + a2[e];
         }
         __syncthreads();
-        // dR = dDl + (T - I)^T dDl; Ehat replaces Khat in LDS meanwhile
-        for (int tile = wave; tile < 8; tile += 4) {
-            const int I = tile >> 1, J = tile & 1;
-            const f32x4 a = tmma<BT>(zero4(), sTm, 1, LDC, sdDl, LDB, 1, 16 * I, 16 * J, lane);
+        // dR = dDl + (T - I)^T dDl
+        {
+            const int I = wave;
+            const f32x4 a = tmma<BT>(zero4(), sTm, 1, LDC, sdDl, LDB, 1, 16 * I, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
-                sdR[i * LDB + 16 * J + r] = sdDl[i * LDB + 16 * J + r] + a[e];
+                sdR[i * LDB + r] = sdDl[i * LDB + r] + a[e];
             }
         }
-        stage_block<DK, LDQ, NTHR>(sA, Eh + ob, tid);
         __syncthreads();
-        // dS = Gam_C . dS' + scale Qhat^T dO - Ehat^T dR  (DK/16 x 2 tiles)
-        for (int tile = wave; tile < (DK / 16) * 2; tile += 4) {
-            const int M = tile >> 1, J = tile & 1;
-            const f32x4 a1 = tmma<BT>(zero4(), sQ, 1, LDQ, sdO, LDB, 1, 16 * M, 16 * J, lane);
-            const f32x4 a2 = tmma<BT>(zero4(), sA, 1, LDQ, sdR, LDB, 1, 16 * M, 16 * J, lane);
+        // dS = Gam_C . dS' + scale Qhat^T dO - Ehat^T dR  (DK / 16 row blocks)
+        for (int M = wave; M < DK / 16; M += 4) {
+            const f32x4 a1 = tmma<BT>(zero4(), sQ, 1, LDQ, sdO, LDB, 1, 16 * M, 0, lane);
+            const f32x4 a2 = tmma<BT>(zero4(), sE, 1, LDQ, sdR, LDB, 1, 16 * M, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = 16 * M + 4 * g + e;
-                float *d = &sdS[m * LDB + 16 * J + r];
+                float *d = &sdS[m * LDB + r];
                 *d = sGam[m] * *d + scale * a1[e] - a2[e];
             }
         }
@@ -710,7 +753,7 @@ static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v,
     using in_t = typename Pol::in_t;
     const int NT = (T + BT - 1) / BT;
     const long heads = (long)B * H;
-    hipLaunchKernelGGL((gdn2_bwd_walk_kernel<DK, DV>), dim3((unsigned)(heads * (DV / 32))), dim3(256), 0, st, Eh,
+    hipLaunchKernelGGL((gdn2_bwd_walk_kernel<DK, DV>), dim3((unsigned)(heads * (DV / 16))), dim3(256), 0, st, Eh,
                        Qh, Kh, GamC, Tws, Pws, Dws, dO, dht, dSck, dh0, T, H, NT, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

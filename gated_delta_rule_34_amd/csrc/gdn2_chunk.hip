@@ -72,21 +72,65 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
     const int t0 = c * BT;
 
     // 1. load the chunk (rows past T are zero, log-decay 0)
-    for (int idx = tid; idx < BT * DK; idx += 256) {
-        const int row = idx / DK, col = idx % DK;
-        const int t = t0 + row;
-        float kv = 0.f, qv = 0.f, bv = 0.f, lv = 0.f;
-        if (t < T) {
-            const long off = ((b * T + t) * H + h) * (long)DK + col;
-            kv = load_elem(k + off);
-            qv = load_elem(q + off);
-            bv = load_elem(bg + off);
-            lv = la[off];
+    if constexpr (std::is_same<typename Pol::in_t, uint16_t>::value) {
+        // bf16 inputs: every 16-byte piece of the chunk requested before the
+        // first LDS store (8 channels of q, k, b and 4 of the log-decay each)
+        typedef __attribute__((ext_vector_type(4))) unsigned int u32x4i;
+        constexpr int UP = BT * DK / 8 / 256, UL = BT * DK / 4 / 256;
+        u32x4i xk[UP], xq[UP], xb[UP];
+        f32x4 xl[UL];
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+            const int p = tid + 256 * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
+            const int t = t0 + row;
+            const long off = ((b * T + t) * H + h) * (long)DK + c0;
+            const bool in = t < T;
+            const u32x4i z = {0u, 0u, 0u, 0u};
+            xk[u] = in ? *(const u32x4i *)(k + off) : z;
+            xq[u] = in ? *(const u32x4i *)(q + off) : z;
+            xb[u] = in ? *(const u32x4i *)(bg + off) : z;
         }
-        sm.u.in.K[row * LD + col] = kv;
-        sm.u.in.Q[row * LD + col] = qv;
-        sm.u.in.E[row * LD + col] = bv * kv;
-        sm.G2[row * LD + col] = lv;
+#pragma unroll
+        for (int u = 0; u < UL; ++u) {
+            const int p = tid + 256 * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
+            const int t = t0 + row;
+            xl[u] = (t < T) ? *(const f32x4 *)(la + ((b * T + t) * H + h) * (long)DK + c0) : zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+            const int p = tid + 256 * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = 16 * (e & 1);
+                const float kv = bf16_to_f32((uint16_t)(xk[u][e >> 1] >> sh));
+                sm.u.in.K[row * LD + c0 + e] = kv;
+                sm.u.in.Q[row * LD + c0 + e] = bf16_to_f32((uint16_t)(xq[u][e >> 1] >> sh));
+                sm.u.in.E[row * LD + c0 + e] = bf16_to_f32((uint16_t)(xb[u][e >> 1] >> sh)) * kv;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UL; ++u) {
+            const int p = tid + 256 * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.G2[row * LD + c0 + e] = xl[u][e];
+        }
+    } else {
+        for (int idx = tid; idx < BT * DK; idx += 256) {
+            const int row = idx / DK, col = idx % DK;
+            const int t = t0 + row;
+            float kv = 0.f, qv = 0.f, bv = 0.f, lv = 0.f;
+            if (t < T) {
+                const long off = ((b * T + t) * H + h) * (long)DK + col;
+                kv = load_elem(k + off);
+                qv = load_elem(q + off);
+                bv = load_elem(bg + off);
+                lv = la[off];
+            }
+            sm.u.in.K[row * LD + col] = kv;
+            sm.u.in.Q[row * LD + col] = qv;
+            sm.u.in.E[row * LD + col] = bv * kv;
+            sm.G2[row * LD + col] = lv;
+        }
     }
     __syncthreads();
     // 2. chunk-local cumsum per channel (fp64 running sum), times log2(e)

@@ -464,6 +464,10 @@ gdn_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const flo
         return GDN_ERR_INVALID_ARG;
     if (!sizes_ok(B, T, H)) return GDN_ERR_INVALID_ARG;
     if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    // the bf16 path moves q, k, b, log_alpha, v and w rows in 16-byte pieces
+    if (dtype == GDN_BF16 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(b, 16) ||
+                              !aligned(w, 16) || !aligned(log_alpha, 16)))
+        return GDN_ERR_INVALID_ARG;
     const Bwd2Ws lay = bwd2_ws(B, T, H, Dk, Dv);
     if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
     const size_t es = esize(dtype);

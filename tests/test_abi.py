@@ -177,6 +177,8 @@ def test_gdn2_bwd_workspace_and_validation():
     assert f(ptrs=p[:9] + [p[0]] + p[10:]) == 1       # dq overlaps q
     assert f(ptrs=p[:10] + [p[9]] + p[11:]) == 1      # dk overlaps dq
     assert f(w=p[3]) == 1                             # workspace overlaps log_alpha
+    assert f(ptrs=[p[0] + 2] + p[1:]) == 1            # bf16 q not 16-byte aligned
+    assert f(ptrs=p[:3] + [p[3] + 4] + p[4:]) == 1    # bf16 path: log_alpha not 16-byte aligned
 
 
 def test_prologue_rejects_bad_arguments():
