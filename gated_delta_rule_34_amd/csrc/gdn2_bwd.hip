@@ -644,6 +644,24 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
     for (int j = 0; j < BT; ++j) cs[j] = 0.f;
     __syncthreads();
 
+    // the global rows of the next block (erase gate, query, dEhat, dQhat,
+    // dKhat) are requested one block ahead
+    uint16_t nb[4], nq[4];
+    float nE[4], nQ[4], nK[4];
+    auto fetch_rows = [&](int r0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const bool in = r0 + x < nrows;
+            const long off = gbase + (r0 + x) * rs;
+            nb[x] = in ? bg[off] : (uint16_t)0;
+            nq[x] = in ? q[off] : (uint16_t)0;
+            const long wo = ob + (long)(r0 + x) * DK + tid;
+            nE[x] = dEh[wo];
+            nQ[x] = dQh[wo];
+            nK[x] = dKh[wo];
+        }
+    };
+    fetch_rows(BT - 4);
 #pragma unroll 1
     for (int ib = NB - 1; ib >= 0; --ib) {
         const int i0 = 4 * ib;
@@ -664,14 +682,15 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
         }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const bool in = i0 + x < nrows;
-            const long off = gbase + (i0 + x) * rs;
-            Bi[x] = in ? bf16_to_f32(bg[off]) : 0.f;
-            Qi[x] = in ? bf16_to_f32(q[off]) : 0.f;
-            const long wo = ob + (long)(i0 + x) * DK + tid;
-            xE[x] = dEh[wo];
-            xQ[x] = dQh[wo];
-            xK[x] = dKh[wo];
+            Bi[x] = bf16_to_f32(nb[x]);
+            Qi[x] = bf16_to_f32(nq[x]);
+            xE[x] = nE[x];
+            xQ[x] = nQ[x];
+            xK[x] = nK[x];
+        }
+        if (ib > 0) fetch_rows(i0 - 4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
             Ei[x] = Bi[x] * Ki[x];
             a[x] = __builtin_amdgcn_exp2f(Gi[x] - Gi[0]);
             Et[x] = Ei[x] * a[x];
