@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "gdn2_kernels": ("gdn2_fused.hip", "gdn_tile.h", "gdn_device.h"),
     "gdn_bwd": ("gdn_bwd.hip", "gdn_bwd_fused.hip", "gdn_fused.hip", "gdn_chunk.hip", "gdn_tile.h", "gdn_device.h"),
     "prologue_kernel": ("gdn_prologue.hip", "gdn_device.h"),
-    "gdn2_bwd": ("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn_device.h"),
+    "gdn2_bwd": ("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn2_states.hip", "gdn_tile.h", "gdn_device.h"),
 }
 
 
@@ -556,8 +556,10 @@ def bench_bwd(args, wl):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "inputs": x["dtype"],
-                   "gradients": "fp32", "stages": "fp32 forward recompute with chunk entry states, reverse state "
-                                                 "walk, per-chunk gradients", "buffer_sets": args.sets,
+                   "gradients": "fp32", "stages": "forward recompute of the chunk entry states, reverse state "
+                                                 "walk, per-chunk gradients; products on split bf16/fp16 "
+                                                 "MFMA operands or fp32 MFMA, fp32 accumulation",
+                   "buffer_sets": args.sets,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": f"{spec['fn']} (all stages)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
