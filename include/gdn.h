@@ -265,16 +265,19 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
  * differentiation of the GDN-2 chunk equations (the WY form with the channel
  * decay inside both factors of every product, "NVIDIA AI lanza Gated
  * DeltaNet-2", sections "Regla-2 del Delta cerrado" and on chunked training):
- * an fp32 forward recompute stores every chunk's entry state, a reverse walk
+ * a forward recompute stores every chunk's entry state, a reverse walk
  * carries the state gradient, then every chunk is differentiated in parallel
  * (the decay-weighted contractions with exact per-channel exponentials).
- * fp32 arithmetic throughout.
+ * fp32 accumulation throughout; with bf16 inputs the recompute's products
+ * take their fp32 operands as bf16 or fp16 hi + lo parts (about 16 and 22
+ * bits), and q, k, v, b, w and log_alpha must be 16-byte aligned.
  *   inputs  as gdn2_chunk_fwd (h0 nullable), dO [B, T, H, Dv] fp32,
  *           dht [B, H, Dk, Dv] fp32 or NULL (no gradient on the final state)
  *   outputs dq, dk, dlog_alpha, db [B, T, H, Dk], dv, dw [B, T, H, Dv],
  *           dh0 [B, H, Dk, Dv] or NULL, all fp32
  *   ws      gdn2_chunk_bwd_workspace() bytes, 256-byte aligned, caller-owned
- * Errors as gdn_chunk_bwd.  Asynchronous on `stream`.
+ * Errors as gdn_chunk_bwd (GDN_ERR_INVALID_ARG also for a misaligned bf16
+ * input).  Asynchronous on `stream`.
  */
 size_t gdn2_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv, gdn_dtype dtype);
 
