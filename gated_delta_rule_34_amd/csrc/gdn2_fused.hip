@@ -507,41 +507,53 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
                                              float scale, int lane) {
     using C = Gdn2WalkCfg<DK, DV>;
     const int r = lane & 15, g = lane >> 4;
-    // X = Ehat S, Y = Qhat S with the state as fp16 hi + lo
+    // X = Ehat S, Y = Qhat S with the state as fp16 hi + lo.  Every fragment
+    // of the chunk is requested first and the w . v elements after them, so
+    // the 64 MFMAs run back to back behind one wait on the LDS.
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Y[I] = zero4();
-    // w . v for this wave's 16 columns, read first so that the element reads
-    // hide under the products below
+    uint4 ea[C::NS][4], qa[C::NS][4];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            ea[s][I] = frag_rows_pg<DK>(sm.E[buf], 16 * I, 32 * s, lane);
+            qa[s][I] = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
+        }
     const int cl = wave * 16 + r;
-    f32x4 wv[4];
+    uint16_t wr[4][4], vr[4][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * g + e;
-            wv[I][e] = bf16_to_f32(sm.W[buf][i * C::LDV + cl]) * bf16_to_f32(sm.V[buf][i * C::LDV + cl]);
+            wr[I][e] = sm.W[buf][i * C::LDV + cl];
+            vr[I][e] = sm.V[buf][i * C::LDV + cl];
         }
+    uint4 shi[C::NS], slo[C::NS];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) hilo_frags<f16x2>(shi[s], slo[s], S[2 * s], S[2 * s + 1]);
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-        uint4 shi, slo;
-        hilo_frags<f16x2>(shi, slo, S[2 * s], S[2 * s + 1]);
         // all hi-part products, then all lo-part products: an accumulator's
         // two updates are eight MFMAs apart
-        uint4 ea[4], qa[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            ea[I] = frag_rows_pg<DK>(sm.E[buf], 16 * I, 32 * s, lane);
-            qa[I] = frag_rows_pg<DK>(sm.Q[buf], 16 * I, 32 * s, lane);
-            X[I] = mma_f16_raw(X[I], ea[I], shi);
-            Y[I] = mma_f16_raw(Y[I], qa[I], shi);
+            X[I] = mma_f16_raw(X[I], ea[s][I], shi[s]);
+            Y[I] = mma_f16_raw(Y[I], qa[s][I], shi[s]);
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            X[I] = mma_f16_raw(X[I], ea[I], slo);
-            Y[I] = mma_f16_raw(Y[I], qa[I], slo);
+            X[I] = mma_f16_raw(X[I], ea[s][I], slo[s]);
+            Y[I] = mma_f16_raw(Y[I], qa[s][I], slo[s]);
         }
     }
+    f32x4 wv[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[I][e] = bf16_to_f32(wr[I][e]) * bf16_to_f32(vr[I][e]);
     // R = w . v - X
     f32x4 Rr[4];
 #pragma unroll
@@ -567,19 +579,23 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
     uint4 vh[2], vl[2];
     hilo_frags<f16x2>(vh[0], vl[0], Vn[0], Vn[1]);
     hilo_frags<f16x2>(vh[1], vl[1], Vn[2], Vn[3]);
+    uint4 ka[C::NKB][2];
+#pragma unroll
+    for (int m = 0; m < C::NKB; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ka[m][s] = frag_T_pg<DK>(sm.K[buf], 32 * s, 16 * m, lane);
 #pragma unroll
     for (int m = 0; m < C::NKB; ++m) {
         const f32x4 gm = *(const f32x4 *)&sm.gam[buf][16 * m + 4 * g];
-        f32x4 acc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = S[m][e] * gm[e];
+        for (int e = 0; e < 4; ++e) S[m][e] *= gm[e];
+    }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint4 a = frag_T_pg<DK>(sm.K[buf], 32 * s, 16 * m, lane);
-            acc = mma_f16_raw(acc, a, vh[s]);
-            acc = mma_f16_raw(acc, a, vl[s]);
-        }
-        S[m] = acc;
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m) S[m] = mma_f16_raw(S[m], ka[m][s], vh[s]);
+#pragma unroll
+        for (int m = 0; m < C::NKB; ++m) S[m] = mma_f16_raw(S[m], ka[m][s], vl[s]);
     }
     // O = scale (Y + diag(P) Vnew + strict(P) Vnew); each row block leaves
     // the MFMA as 4 rows of one column per lane and is stored, after a quad
