@@ -744,30 +744,36 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
         if (r == 0) sm.dG[i] -= tj;
         tdec[e] = (r == 0) ? tj : 0.f;
     }
-    sm.red[tid] = tdec[0] + tdec[1] + tdec[2] + tdec[3];
-    __syncthreads();
-    if (tid == 0) {
-        float tsum = 0.f;
-        for (int x = 0; x < NTHR; ++x) tsum += sm.red[x];
-        sm.dG[BT - 1] += tsum;
+    // the Kd terms' total and sum_v dS' . S (both enter the last row's dG):
+    // wave sums on shuffles, then the four waves' partials
+    float tv = tdec[0] + tdec[1] + tdec[2] + tdec[3], sv = dGC;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        tv += __shfl_xor(tv, off, 64);
+        sv += __shfl_xor(sv, off, 64);
+    }
+    if (lane == 0) {
+        sm.red[wave] = tv;
+        sm.red[4 + wave] = sv;
     }
     __syncthreads();
-    sm.red[tid] = dGC;
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int x = 0; x < NTHR; ++x) s += sm.red[x];
-        sm.dG[BT - 1] += sm.Gam[BT - 1] * s;
-        // dG_j -= column sums; dg = reverse cumulative sum of dG within the chunk
-        float acc = 0.f;
-        for (int i = BT - 1; i >= 0; --i) {
-            const float dGi = sm.dG[i] - (sm.colG[0][i] + sm.colG[1][i] + sm.colG[2][i] + sm.colG[3][i]);
-            acc += dGi;
-            const int t = t0 + i;
-            if (t < T) {
-                dg[(b * T + t) * H + h] = acc;
-                dbeta[(b * T + t) * H + h] = sm.dB[i];
-            }
+    if (wave == 0) {
+        // dG_j -= column sums; dg = reverse cumulative sum of dG within the
+        // chunk, one row per lane (a suffix scan on shuffles)
+        const int i = lane;
+        float x = sm.dG[i] - (sm.colG[0][i] + sm.colG[1][i] + sm.colG[2][i] + sm.colG[3][i]);
+        if (i == BT - 1)
+            x += (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) +
+                 sm.Gam[BT - 1] * (sm.red[4] + sm.red[5] + sm.red[6] + sm.red[7]);
+#pragma unroll
+        for (int off = 1; off < BT; off <<= 1) {
+            const float y = __shfl_down(x, off, 64);
+            if (i + off < BT) x += y;
+        }
+        const int t = t0 + i;
+        if (t < T) {
+            dg[(b * T + t) * H + h] = x;
+            dbeta[(b * T + t) * H + h] = sm.dB[i];
         }
     }
 }
