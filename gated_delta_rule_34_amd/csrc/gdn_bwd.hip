@@ -778,6 +778,424 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(
     }
 }
 
+// ------------------------------------------- per-chunk gradients, bf16 inputs
+// The same chunk equations as bwd_chunk_kernel on eight waves in two groups
+// of four, so every SIMD runs two waves: each 32-column step of the value
+// columns gives the groups 16 columns each for the per-column products (R,
+// Vnew, dVnew, dR), and then each group accumulates half of the output tiles
+// (dA and dP for two of the four column blocks, dq, dk and dKd terms for
+// half of the key blocks) over all 32 columns, reading both groups' slice
+// buffers.  The epilogue is split the same way.  Q and K are kept as raw
+// bf16 rows (they are bf16 numbers), which makes room for the two groups'
+// slice buffers.
+template <int DK>
+struct BwdChunk2Smem {
+    static constexpr int LDQ = DK + 8, LDC = BT + 1, CW = 16, LDW = CW + 1;
+    alignas(16) uint16_t Q[BT * LDQ], K[BT * LDQ];   // raw bf16 rows
+    float Tm[BT * LDC];   // T - I; after the column loop: dA . D
+    float P[BT * LDC];    // (Q K^T) . D, lower; after the column loop: dP . D
+    struct Slices {
+        float S[DK * LDW], dS[DK * LDW];
+        float V[BT * LDW], dO[BT * LDW], R[BT * LDW], Vn[BT * LDW], dVn[BT * LDW];
+    };
+    Slices sl[2];  // one per group
+    double G2[BT];
+    float Gam[BT], Dec[BT], Beta[BT];
+    float dB[2][BT], dG[2][BT], colG[4][BT], red[16];
+};
+
+// acc += A B^T over k in [0, K) for raw bf16 rows A[i][k], B[j][k]: one
+// 16-byte read per operand and 32 k (lane (g, r): row r, k-slots 8g .. + 7).
+template <int K>
+__device__ __forceinline__ f32x4 tile_mma_raw(f32x4 acc, const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                                              int i0, int j0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *pa = A + (i0 + r) * lda + 8 * g, *pb = B + (j0 + r) * ldb + 8 * g;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32)
+        acc = mma_bf16v(acc, *(const u32x4b *)(pa + k0), *(const u32x4b *)(pb + k0));
+    return acc;
+}
+
+// acc += A B over k in [0, K), A = raw bf16 rows, B as NP bf16 parts per 32 k.
+template <int K, int NP>
+__device__ __forceinline__ f32x4 mma_raw_parts(f32x4 acc, const uint16_t *A, int lda, int i0,
+                                               const u32x4b (&bp)[K / 32][NP], int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *pa = A + (i0 + r) * lda + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+        const u32x4b ua = *(const u32x4b *)(pa + 32 * kb);
+#pragma unroll
+        for (int q = 0; q < NP; ++q) acc = mma_bf16v(acc, ua, bp[kb][q]);
+    }
+    return acc;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ beta, const float *__restrict__ dO, const double *__restrict__ G2ws,
+    const float *__restrict__ Tws, const float *__restrict__ Sck, const float *__restrict__ dSck,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
+    float *__restrict__ dbeta, int T, int H, int NT, float scale) {
+    using SM = BwdChunk2Smem<DK>;
+    constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 512, GT = 256, NM = DK / 16;
+    static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int gi = wave >> 2, gt = tid & (GT - 1);  // group and thread within the group
+    const long cb = blockIdx.x;
+    const int c = (int)(cb % NT);
+    const long bh = cb / NT;
+    const int h = (int)(bh % H);
+    const long b = bh / H;
+    const int t0 = c * BT;
+    const int I = wave & 3;  // this wave's 16-row block of every chunk-row product
+    typename SM::Slices &sl = sm.sl[gi];
+
+    // Q and K raw rows (zero past T), gate tables, T - I
+    {
+        constexpr int U = BT * DK / 8 / NTHR;
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const int idx = tid + NTHR * x, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+            const int t = min(t0 + row, T - 1);
+            const long off = ((b * T + t) * H + h) * (long)DK + c8;
+            const bool in = t0 + row < T;
+            const u32x4b z = {0u, 0u, 0u, 0u};
+            const u32x4b xq = *(const u32x4b *)(q + off), xk = *(const u32x4b *)(k + off);
+            *(u32x4b *)&sm.Q[row * LDQ + c8] = in ? xq : z;
+            *(u32x4b *)&sm.K[row * LDQ + c8] = in ? xk : z;
+        }
+    }
+    if (tid < BT) {
+        const int t = t0 + tid;
+        const double G2 = G2ws[cb * BT + tid], G2L = G2ws[cb * BT + BT - 1];
+        sm.G2[tid] = G2;
+        sm.Gam[tid] = exp2f((float)G2);
+        sm.Dec[tid] = exp2f((float)(G2L - G2));
+        sm.Beta[tid] = (t < T) ? beta[(b * T + t) * H + h] : 0.f;
+    }
+    stage_tm<LDC, NTHR>(sm.Tm, Tws + cb * BT * BT, tid);
+    if (tid < 2 * BT) {
+        sm.dB[tid / BT][tid % BT] = 0.f;
+        sm.dG[tid / BT][tid % BT] = 0.f;
+    }
+    __syncthreads();
+    // P = (Q K^T) . D, lower with the diagonal (all 16 tiles, upper ones zero)
+    for (int tile = wave; tile < 16; tile += 8) {
+        const int TI = tile >> 2, TJ = tile & 3;
+        const f32x4 acc = tile_mma_raw<DK>(zero4(), sm.Q, LDQ, sm.K, LDQ, 16 * TI, 16 * TJ, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
+            sm.P[i * LDC + j] = (j <= i) ? acc[e] * exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
+        }
+    }
+
+    // this group's output tiles: column blocks J = 2 gi + jj of dA and dP,
+    // key blocks m = MH gi + mm of the DK-wide products
+    constexpr int MH = NM / 2;
+    f32x4 dqs[MH], dkR[MH], dKd[MH], dA[2], dP[2];
+#pragma unroll
+    for (int m = 0; m < MH; ++m) dqs[m] = dkR[m] = dKd[m] = zero4();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dA[j] = dP[j] = zero4();
+    float dGC = 0.f;  // <dS', S> over the slices this thread loaded
+
+    // the group's next 16 columns of S, dS', V and dO, requested into
+    // registers while the current ones are worked on
+    constexpr int US = DK * CW / 4 / GT;
+    static_assert(BT * CW / 8 == GT / 2, "one 8-value piece of v or dO per thread");
+    f32x4 xs[US], xd[US], xo[2];
+    u32x4b xv;
+    const int prow = (gt & (GT / 2 - 1)) / (CW / 8), pc8 = 8 * (gt % (CW / 8));
+    const int pt = min(t0 + prow, T - 1);
+    auto fetch_slice = [&](int cc) {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const int idx = 4 * (gt + GT * u), row = idx / CW, col = idx % CW;
+            const long off = cb * DK * DV + (long)row * DV + cc + col;
+            xs[u] = *(const f32x4 *)(Sck + off);
+            xd[u] = *(const f32x4 *)(dSck + off);
+        }
+        if (gt < GT / 2) {
+            xv = *(const u32x4b *)(v + ((b * T + pt) * H + h) * (long)DV + cc + pc8);
+        } else {
+            const float *po = dO + ((b * T + pt) * H + h) * (long)DV + cc + pc8;
+            xo[0] = *(const f32x4 *)po;
+            xo[1] = *(const f32x4 *)(po + 4);
+        }
+    };
+    fetch_slice(16 * gi);
+
+    for (int c0 = 0; c0 < DV; c0 += 2 * CW) {
+        const int cg = c0 + CW * gi;  // this group's first column
+        __syncthreads();  // previous slice fully consumed
+        {
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int idx = 4 * (gt + GT * u), row = idx / CW, col = idx % CW;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sl.S[row * LDW + col + e] = xs[u][e];
+                    sl.dS[row * LDW + col + e] = xd[u][e];
+                    dGC += xs[u][e] * xd[u][e];
+                }
+            }
+            const bool in = t0 + prow < T;  // rows past T are zero
+            float x8[8];
+            if (gt < GT / 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x8[2 * e] = __uint_as_float(xv[e] << 16);
+                    x8[2 * e + 1] = __uint_as_float(xv[e] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x8[e] = xo[0][e];
+                    x8[e + 4] = xo[1][e];
+                }
+            }
+            float *dst = (gt < GT / 2 ? sl.V : sl.dO) + prow * LDW + pc8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = in ? x8[e] : 0.f;
+        }
+        if (c0 + 2 * CW < DV) fetch_slice(cg + 2 * CW);
+        __syncthreads();
+        // KS, QS, R for rows of block I: K, Q exact in bf16; the S slice as bf16 hi + lo
+        f32x4 KS, QS;
+        {
+            u32x4b sp[DK / 32][2];
+            col_parts<DK, 2>(sp, sl.S, LDW, r, lane);
+            KS = mma_raw_parts<DK, 2>(zero4(), sm.K, LDQ, 16 * I, sp, lane);
+            QS = mma_raw_parts<DK, 2>(zero4(), sm.Q, LDQ, 16 * I, sp, lane);
+        }
+        f32x4 Rr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            Rr[e] = sm.Beta[i] * (sl.V[i * LDW + r] - sm.Gam[i] * KS[e]);
+            sl.R[i * LDW + r] = Rr[e];
+        }
+        __syncthreads();
+        // Vn = R + (T - I) R;  dVn = scale P^T dO + Kd dS' (K exact; dS' as three bf16 parts)
+        {
+            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sl.R, LDW, 1, nullptr, 16 * I, 0, lane);
+            const f32x4 b1 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sl.dO, LDW, 1, nullptr, 16 * I, 0, lane);
+            u32x4b dp[DK / 32][3];
+            col_parts<DK, 3>(dp, sl.dS, LDW, r, lane);
+            const f32x4 b2 = mma_raw_parts<DK, 3>(zero4(), sm.K, LDQ, 16 * I, dp, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                sl.Vn[i * LDW + r] = Rr[e] + a[e];
+                sl.dVn[i * LDW + r] = scale * b1[e] + sm.Dec[i] * b2[e];
+            }
+        }
+        __syncthreads();
+        // dR = dVn + (T - I)^T dVn; dv; the row sums of dbeta and dG (per group)
+        f32x4 dRr;
+        {
+            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sl.dVn, LDW, 1, nullptr, 16 * I, 0, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                const int t = t0 + i;
+                dRr[e] = sl.dVn[i * LDW + r] + a[e];
+                if (t < T) dv[((b * T + t) * H + h) * (long)DV + cg + r] = sm.Beta[i] * dRr[e];
+                const float vb = sl.V[i * LDW + r] - sm.Gam[i] * KS[e];
+                const float pb = row16_sum(dRr[e] * vb);
+                const float pg = row16_sum(-sm.Beta[i] * sm.Gam[i] * dRr[e] * KS[e] +
+                                           scale * sm.Gam[i] * sl.dO[i * LDW + r] * QS[e]);
+                if (r == 0) {
+                    sm.dB[gi][i] += pb;
+                    sm.dG[gi][i] += pg;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sl.R[(16 * I + 4 * g + e) * LDW + r] = dRr[e];
+        __syncthreads();
+        // accumulate this group's tiles of dA, dP (64 x 64) and the DK-wide
+        // products for rows of block I, over both groups' 16 columns
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int J = 2 * gi + jj;
+            f32x4 x = zero4(), y = zero4();
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const typename SM::Slices &o = sm.sl[hh];
+                x = tile_mma<CW>(x, o.R, LDW, 1, o.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
+                y = tile_mma<CW>(y, o.dO, LDW, 1, o.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
+            }
+            dA[jj] -= x;
+            dP[jj] += y * scale;
+        }
+#pragma unroll
+        for (int mm = 0; mm < MH; ++mm) {
+            const int m = MH * gi + mm;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const typename SM::Slices &o = sm.sl[hh];
+                dqs[mm] = tile_mma<CW>(dqs[mm], o.dO, LDW, 1, o.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+                dkR[mm] = tile_mma<CW>(dkR[mm], o.R, LDW, 1, o.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+                dKd[mm] = tile_mma<CW>(dKd[mm], o.Vn, LDW, 1, o.dS, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+            }
+        }
+    }
+    __syncthreads();  // every wave is done with Tm, P and the slices
+
+    float tdec[4] = {0.f, 0.f, 0.f, 0.f};  // sum over this group's m of dKd_im K_im for the 4 rows of this lane
+    {
+        // dA, dP on their supports (this group's column blocks); A, P and the K K^T terms
+        float colp[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int J = 2 * gi + jj;
+            const f32x4 KK = tile_mma_raw<DK>(zero4(), sm.K, LDQ, sm.K, LDQ, 16 * I, 16 * J, lane);
+            const f32x4 QK = tile_mma_raw<DK>(zero4(), sm.Q, LDQ, sm.K, LDQ, 16 * I, 16 * J, lane);
+            const int j = 16 * J + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e;
+                const float D = (j <= i) ? exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
+                const float dAv = (j < i) ? dA[jj][e] : 0.f;
+                const float dPv = (j <= i) ? dP[jj][e] : 0.f;
+                const float Av = sm.Beta[i] * KK[e] * D, Pv = QK[e] * D;
+                const float w = dAv * Av + dPv * Pv;
+                const float pb = row16_sum(dAv * D * KK[e]);
+                const float pg = row16_sum(w);
+                if (r == 0) {
+                    sm.dB[gi][i] += pb;
+                    sm.dG[gi][i] += pg;
+                }
+                colp[jj][e] = w;
+                sm.Tm[i * LDC + j] = dAv * D;  // dA . D
+                sm.P[i * LDC + j] = dPv * D;   // dP . D
+            }
+        }
+        // column sums of dA . A + dP . P: lanes of column j = 16J + r
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            float x = colp[jj][0] + colp[jj][1] + colp[jj][2] + colp[jj][3];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            if (g == 0) sm.colG[I][16 * (2 * gi + jj) + r] = x;
+        }
+    }
+    __syncthreads();
+    {
+        // dk = diag(beta) dAs K + dAs^T diag(beta) K + dPs^T Q + diag(dec) dKd - diag(beta gamma) dkR
+        // dq = scale diag(gamma) dqs + dPs K, on bf16 MFMA: the left operands
+        // split once into bf16 parts (three for dP.D, two for the others)
+        u32x4b a1[2][2], a2[2][2], a3[2][2], a4[2][3];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float x1[8], x2[8], x3[8], x4[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 16 * I + r, j = 32 * kb + 8 * g + e;
+                x1[e] = sm.Tm[i * LDC + j];
+                x2[e] = sm.Tm[j * LDC + i] * sm.Beta[j];
+                x3[e] = sm.P[j * LDC + i];
+                x4[e] = sm.P[i * LDC + j];
+            }
+            split_8(a1[kb], x1);
+            split_8(a2[kb], x2);
+            split_8(a3[kb], x3);
+            split_8(a4[kb], x4);
+        }
+#pragma unroll
+        for (int mm = 0; mm < MH; ++mm) {
+            const int m = MH * gi + mm;
+            f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                uint32_t wk[8], wq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * kb + 8 * g + e;
+                    wk[e] = sm.K[j * LDQ + 16 * m + r];
+                    wq[e] = sm.Q[j * LDQ + 16 * m + r];
+                }
+                const u32x4b bk = {wk[0] | (wk[1] << 16), wk[2] | (wk[3] << 16), wk[4] | (wk[5] << 16),
+                                   wk[6] | (wk[7] << 16)};
+                const u32x4b bq = {wq[0] | (wq[1] << 16), wq[2] | (wq[3] << 16), wq[4] | (wq[5] << 16),
+                                   wq[6] | (wq[7] << 16)};
+                t1 = mma_bf16v(mma_bf16v(t1, a1[kb][0], bk), a1[kb][1], bk);
+                t2 = mma_bf16v(mma_bf16v(t2, a2[kb][0], bk), a2[kb][1], bk);
+                t3 = mma_bf16v(mma_bf16v(t3, a3[kb][0], bq), a3[kb][1], bq);
+                t4 = mma_bf16v(mma_bf16v(mma_bf16v(t4, a4[kb][0], bk), a4[kb][1], bk), a4[kb][2], bk);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e, col = 16 * m + r;
+                const int t = t0 + i;
+                const float kim = bf16_to_f32(sm.K[i * LDQ + col]);
+                tdec[e] = fmaf(dKd[mm][e], kim, tdec[e]);
+                const float dkv = sm.Beta[i] * t1[e] + t2[e] + t3[e] + sm.Dec[i] * dKd[mm][e] -
+                                  sm.Beta[i] * sm.Gam[i] * dkR[mm][e];
+                const float dqv = scale * sm.Gam[i] * dqs[mm][e] + t4[e];
+                if (t < T) {
+                    const long off = ((b * T + t) * H + h) * (long)DK + col;
+                    dk[off] = dkv;
+                    dq[off] = dqv;
+                }
+            }
+        }
+        // Kd terms of dG: t_j = dec_j (dKd_j . k_j) leaves row j and enters the last row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            const float tj = row16_sum(tdec[e]) * sm.Dec[i];
+            if (r == 0) sm.dG[gi][i] -= tj;
+            tdec[e] = (r == 0) ? tj : 0.f;
+        }
+    }
+    // the Kd terms' total and sum_v dS' . S (both enter the last row's dG):
+    // wave sums on shuffles, then the eight waves' partials
+    float tv = tdec[0] + tdec[1] + tdec[2] + tdec[3], sv = dGC;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        tv += __shfl_xor(tv, off, 64);
+        sv += __shfl_xor(sv, off, 64);
+    }
+    if (lane == 0) {
+        sm.red[wave] = tv;
+        sm.red[8 + wave] = sv;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // dG_j -= column sums; dg = reverse cumulative sum of dG within the
+        // chunk, one row per lane (a suffix scan on shuffles)
+        const int i = lane;
+        float x = sm.dG[0][i] + sm.dG[1][i] - (sm.colG[0][i] + sm.colG[1][i] + sm.colG[2][i] + sm.colG[3][i]);
+        if (i == BT - 1) {
+            float ts = 0.f, ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                ts += sm.red[w];
+                ss += sm.red[8 + w];
+            }
+            x += ts + sm.Gam[BT - 1] * ss;
+        }
+#pragma unroll
+        for (int off = 1; off < BT; off <<= 1) {
+            const float y = __shfl_down(x, off, 64);
+            if (i + off < BT) x += y;
+        }
+        const int t = t0 + i;
+        if (t < T) {
+            dg[(b * T + t) * H + h] = x;
+            dbeta[(b * T + t) * H + h] = sm.dB[0][i] + sm.dB[1][i];
+        }
+    }
+}
+
 // ----------------------------------------------------------------- launchers
 template <class Pol, int DK, int DV>
 static hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const float *beta, const float *dO,
@@ -796,9 +1214,14 @@ static hipError_t launch_bwd_t(const void *q, const void *k, const void *v, cons
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chunk_kernel<Pol, DK, DV>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
-                       (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, dO, G2, Tinv, Sck, dSck, dq, dk, dv,
-                       dg, dbeta, T, H, NT, scale);
+    if constexpr (std::is_same<in_t, uint16_t>::value)
+        hipLaunchKernelGGL((bwd_chunk2_kernel<DK, DV>), dim3((unsigned)((long)B * H * NT)), dim3(512), 0, st,
+                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, beta, dO, G2, Tinv, Sck,
+                           dSck, dq, dk, dv, dg, dbeta, T, H, NT, scale);
+    else
+        hipLaunchKernelGGL((bwd_chunk_kernel<Pol, DK, DV>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
+                           (const in_t *)q, (const in_t *)k, (const in_t *)v, beta, dO, G2, Tinv, Sck, dSck, dq, dk,
+                           dv, dg, dbeta, T, H, NT, scale);
     return hipGetLastError();
 }
 
