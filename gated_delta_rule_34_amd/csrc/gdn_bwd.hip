@@ -905,8 +905,9 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
     for (int j = 0; j < 2; ++j) dA[j] = dP[j] = zero4();
     float dGC = 0.f;  // <dS', S> over the slices this thread loaded
 
-    // the group's next 16 columns of S, dS', V and dO, requested into
-    // registers while the current ones are worked on
+    // the group's 16 columns of S, dS', V and dO (fetched at the top of each
+    // step: with two waves per SIMD the other wave hides the latency, and a
+    // prefetch's registers would spill)
     constexpr int US = DK * CW / 4 / GT;
     static_assert(BT * CW / 8 == GT / 2, "one 8-value piece of v or dO per thread");
     f32x4 xs[US], xd[US], xo[2];
@@ -929,10 +930,9 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
             xo[1] = *(const f32x4 *)(po + 4);
         }
     };
-    fetch_slice(16 * gi);
-
     for (int c0 = 0; c0 < DV; c0 += 2 * CW) {
         const int cg = c0 + CW * gi;  // this group's first column
+        fetch_slice(cg);
         __syncthreads();  // previous slice fully consumed
         {
 #pragma unroll
@@ -964,7 +964,6 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) dst[e] = in ? x8[e] : 0.f;
         }
-        if (c0 + 2 * CW < DV) fetch_slice(cg + 2 * CW);
         __syncthreads();
         // KS, QS, R for rows of block I: K, Q exact in bf16; the S slice as bf16 hi + lo
         f32x4 KS, QS;
