@@ -277,14 +277,17 @@ struct Gdn2BwdValueSmem {
 };
 
 template <class Pol, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
+__global__ __launch_bounds__(512, 1) void gdn2_bwd_value_kernel(
     const typename Pol::in_t *__restrict__ v, const typename Pol::in_t *__restrict__ wg,
     const float *__restrict__ dO, const float *__restrict__ Sck, const float *__restrict__ dSck,
     float *__restrict__ Eh, float *__restrict__ Qh, float *__restrict__ Kh, float *__restrict__ GamC,
     float *__restrict__ Tws, float *__restrict__ Pws, const float *__restrict__ Dws, float *__restrict__ dv,
     float *__restrict__ dw, int T, int H, int NT, float scale) {
     using SM = Gdn2BwdValueSmem<DK>;
-    constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 256, NM = DK / 16;
+    // eight waves: waves 0..3 form the per-column row products of each slice
+    // (row block I = wave); all eight accumulate, each half of the output
+    // tiles; the slices are staged by the first 256 threads
+    constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 256, NM = DK / 16, MH = NM / 2;
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -295,24 +298,28 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
     const long b = bh / H;
     const int t0 = c * BT;
     const long ob = cb * (long)BT * DK;
-    const int I = wave;  // this wave's 16-row block of every 64-row product
+    const int I = wave & 3;  // this wave's 16-row block of every 64-row product
+    const int gi = wave >> 2;  // half of the DK-wide output tiles (key blocks MH gi ..)
+    const bool rowp = wave < 4, st = tid < NTHR;
 
-    stage_block<DK, LDQ, NTHR>(sm.E, Eh + ob, tid);
-    stage_block<DK, LDQ, NTHR>(sm.K, Kh + ob, tid);
-    stage_tp<LDC>(sm.Tm, sm.P, Tws + cb * BT * BT, Pws + cb * BT * BT, Dws + cb * BT, tid);
+    if (st) {
+        stage_block<DK, LDQ, NTHR>(sm.E, Eh + ob, tid);
+        stage_block<DK, LDQ, NTHR>(sm.K, Kh + ob, tid);
+        stage_tp<LDC>(sm.Tm, sm.P, Tws + cb * BT * BT, Pws + cb * BT * BT, Dws + cb * BT, tid);
+    }
     // accumulators over the value columns: the lower tiles of dA and dP owned
-    // by this wave (tiles t = wave, wave + 4, wave + 8), and row block I of
-    // dEhat, dQhat, dKhat (NM tiles each); sum_v dS' . S per key channel
-    f32x4 aA[3], aP[3], aE[NM], aQ[NM], aK[NM];
+    // by this wave (tiles t = wave, wave + 8), and key blocks MH gi .. of row
+    // block I of dEhat, dQhat, dKhat; sum_v dS' . S per key channel
+    f32x4 aA[2], aP[2], aE[MH], aQ[MH], aK[MH];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) aA[u] = aP[u] = zero4();
+    for (int u = 0; u < 2; ++u) aA[u] = aP[u] = zero4();
 #pragma unroll
-    for (int m = 0; m < NM; ++m) aE[m] = aQ[m] = aK[m] = zero4();
+    for (int m = 0; m < MH; ++m) aE[m] = aQ[m] = aK[m] = zero4();
     float srow = 0.f;
 
     for (int v0 = 0; v0 < DV; v0 += CW) {
         __syncthreads();  // the previous slice's readers are done
-        {
+        if (st) {
             constexpr int US = DK * CW / 4 / NTHR;
             float4 xs[US], xd[US];
 #pragma unroll
@@ -330,16 +337,18 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
                 pd[0] = xd[u].x; pd[1] = xd[u].y; pd[2] = xd[u].z; pd[3] = xd[u].w;
             }
         }
-        stage_cols16<LDW>(sm.V, v, b, h, t0, T, H, v0, DV, tid);
-        stage_cols16<LDW>(sm.W, wg, b, h, t0, T, H, v0, DV, tid);
-        stage_cols16<LDW>(sm.dO, dO, b, h, t0, T, H, v0, DV, tid);
+        if (st) {
+            stage_cols16<LDW>(sm.V, v, b, h, t0, T, H, v0, DV, tid);
+            stage_cols16<LDW>(sm.W, wg, b, h, t0, T, H, v0, DV, tid);
+            stage_cols16<LDW>(sm.dO, dO, b, h, t0, T, H, v0, DV, tid);
+        }
         __syncthreads();
         if (tid < DK) {
 #pragma unroll
             for (int j = 0; j < CW; ++j) srow += sm.dS[tid * LDW + j] * sm.S[tid * LDW + j];
         }
         // R = Z - Ehat S (row block I)
-        {
+        if (rowp) {
             const f32x4 a = tmma<DK>(zero4(), sm.E, LDQ, 1, sm.S, LDW, 1, 16 * I, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
         }
         __syncthreads();
         // Dl = R + (T - I) R; dDl = scale P^T dO + Khat dS'
-        {
+        if (rowp) {
             const f32x4 a = tmma<BT>(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, 16 * I, 0, lane);
             const f32x4 a1 = tmma<BT>(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, 16 * I, 0, lane);
             const f32x4 a2 = tmma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, 16 * I, 0, lane);
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
         }
         __syncthreads();
         // dR = dDl + (T - I)^T dDl; dv = dR . w, dw = dR . v
-        {
+        if (rowp) {
             const f32x4 a = tmma<BT>(zero4(), sm.Tm, 1, LDC, sm.dDl, LDW, 1, 16 * I, 0, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -380,26 +389,27 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
         __syncthreads();
         // dA += -dR Dl^T, dP += scale dO Dl^T on this wave's lower tiles
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int t = wave + 4 * u;
+        for (int u = 0; u < 2; ++u) {
+            const int t = wave + 8 * u;
             if (t < 10) {
                 const int TI = lI(t), TJ = lJ(t);
                 aA[u] = tmma<CW>(aA[u], sm.dR, LDW, 1, sm.Dl, 1, LDW, 16 * TI, 16 * TJ, lane);
                 aP[u] = tmma<CW>(aP[u], sm.dO, LDW, 1, sm.Dl, 1, LDW, 16 * TI, 16 * TJ, lane);
             }
         }
-        // dEhat += -dR S^T, dQhat += scale dO S^T, dKhat += Dl dS'^T (row block I)
+        // dEhat += -dR S^T, dQhat += scale dO S^T, dKhat += Dl dS'^T (row block I, this half's key blocks)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            aE[m] = tmma<CW>(aE[m], sm.dR, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
-            aQ[m] = tmma<CW>(aQ[m], sm.dO, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
-            aK[m] = tmma<CW>(aK[m], sm.Dl, LDW, 1, sm.dS, 1, LDW, 16 * I, 16 * m, lane);
+        for (int mm = 0; mm < MH; ++mm) {
+            const int m = MH * gi + mm;
+            aE[mm] = tmma<CW>(aE[mm], sm.dR, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
+            aQ[mm] = tmma<CW>(aQ[mm], sm.dO, LDW, 1, sm.S, 1, LDW, 16 * I, 16 * m, lane);
+            aK[mm] = tmma<CW>(aK[mm], sm.Dl, LDW, 1, sm.dS, 1, LDW, 16 * I, 16 * m, lane);
         }
     }
     __syncthreads();  // every read of this chunk's operands is done: overwrite them
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int t = wave + 4 * u;
+    for (int u = 0; u < 2; ++u) {
+        const int t = wave + 8 * u;
         if (t < 10) {
             const int TI = lI(t), TJ = lJ(t);
 #pragma unroll
@@ -411,13 +421,13 @@ __global__ __launch_bounds__(256) void gdn2_bwd_value_kernel(
         }
     }
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int mm = 0; mm < MH; ++mm)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const long idx = ob + (long)(16 * I + 4 * g + e) * DK + 16 * m + r;
-            Eh[idx] = -aE[m][e];
-            Qh[idx] = scale * aQ[m][e];
-            Kh[idx] = aK[m][e];
+            const long idx = ob + (long)(16 * I + 4 * g + e) * DK + 16 * (MH * gi + mm) + r;
+            Eh[idx] = -aE[mm][e];
+            Qh[idx] = scale * aQ[mm][e];
+            Kh[idx] = aK[mm][e];
         }
     if (tid < DK) GamC[cb * DK + tid] = srow;
 }
@@ -776,7 +786,7 @@ static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v,
                        Qh, Kh, GamC, Tws, Pws, Dws, dO, dht, dSck, dh0, T, H, NT, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn2_bwd_value_kernel<Pol, DK, DV>), dim3((unsigned)(heads * NT)), dim3(256), 0, st,
+    hipLaunchKernelGGL((gdn2_bwd_value_kernel<Pol, DK, DV>), dim3((unsigned)(heads * NT)), dim3(512), 0, st,
                        (const in_t *)v, (const in_t *)wg, dO, Sck, dSck, Eh, Qh, Kh, GamC, Tws, Pws, Dws, dv, dw, T,
                        H, NT, scale);
     e = hipGetLastError();
