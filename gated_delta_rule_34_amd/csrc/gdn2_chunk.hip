@@ -52,7 +52,7 @@ struct Gdn2IntraSmem {
 };
 
 template <class Pol, int DK>
-__global__ __launch_bounds__(256) void gdn2_intra_kernel(
+__global__ __launch_bounds__(512) void gdn2_intra_kernel(
     const typename Pol::in_t *__restrict__ q, const typename Pol::in_t *__restrict__ k,
     const float *__restrict__ la, const typename Pol::in_t *__restrict__ bg,
     typename Pol::mt *__restrict__ Ehat, typename Pol::mt *__restrict__ Qhat, typename Pol::mt *__restrict__ Khat,
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
     int T, int H, int NT) {
     using mt = typename Pol::mt;
     using SM = Gdn2IntraSmem<Pol, DK>;
+    constexpr int NTH = 512;  // eight waves
     constexpr int LD = SM::LD, LDA = SM::LDA;
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -76,12 +77,12 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
         // bf16 inputs: every 16-byte piece of the chunk requested before the
         // first LDS store (8 channels of q, k, b and 4 of the log-decay each)
         typedef __attribute__((ext_vector_type(4))) unsigned int u32x4i;
-        constexpr int UP = BT * DK / 8 / 256, UL = BT * DK / 4 / 256;
+        constexpr int UP = BT * DK / 8 / NTH, UL = BT * DK / 4 / NTH;
         u32x4i xk[UP], xq[UP], xb[UP];
         f32x4 xl[UL];
 #pragma unroll
         for (int u = 0; u < UP; ++u) {
-            const int p = tid + 256 * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
+            const int p = tid + NTH * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
             const int t = t0 + row;
             const long off = ((b * T + t) * H + h) * (long)DK + c0;
             const bool in = t < T;
@@ -92,13 +93,13 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
         }
 #pragma unroll
         for (int u = 0; u < UL; ++u) {
-            const int p = tid + 256 * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
+            const int p = tid + NTH * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
             const int t = t0 + row;
             xl[u] = (t < T) ? *(const f32x4 *)(la + ((b * T + t) * H + h) * (long)DK + c0) : zero4();
         }
 #pragma unroll
         for (int u = 0; u < UP; ++u) {
-            const int p = tid + 256 * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
+            const int p = tid + NTH * u, row = p / (DK / 8), c0 = 8 * (p % (DK / 8));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sh = 16 * (e & 1);
@@ -110,12 +111,12 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
         }
 #pragma unroll
         for (int u = 0; u < UL; ++u) {
-            const int p = tid + 256 * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
+            const int p = tid + NTH * u, row = p / (DK / 4), c0 = 4 * (p % (DK / 4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.G2[row * LD + c0 + e] = xl[u][e];
         }
     } else {
-        for (int idx = tid; idx < BT * DK; idx += 256) {
+        for (int idx = tid; idx < BT * DK; idx += NTH) {
             const int row = idx / DK, col = idx % DK;
             const int t = t0 + row;
             float kv = 0.f, qv = 0.f, bv = 0.f, lv = 0.f;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
     __syncthreads();
     // 3. decayed operands for the walk
     const long obase = chunk * (long)BT * DK;
-    for (int idx = tid; idx < BT * DK; idx += 256) {
+    for (int idx = tid; idx < BT * DK; idx += NTH) {
         const int row = idx / DK, col = idx % DK;
         const float G = sm.G2[row * LD + col], GL = sm.G2[(BT - 1) * LD + col];
         const float gam = exp2f(G);
@@ -154,15 +155,15 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
         if (row == 0) GamC[chunk * DK + col] = exp2f(GL);
     }
     // 4a. zero the diagonal blocks of A (the VALU pass fills their lower part)
-    for (int idx = tid; idx < 4 * 256; idx += 256) {
+    for (int idx = tid; idx < 4 * 256; idx += NTH) {
         const int blk = idx >> 8, i = (idx >> 4) & 15, j = idx & 15;
         sm.A[(16 * blk + i) * LDA + 16 * blk + j] = 0.f;
     }
     float *Pc = Pout + chunk * (BT * BT);
-    for (int idx = tid; idx < BT * BT; idx += 256) Pc[idx] = 0.f;
+    for (int idx = tid; idx < BT * BT; idx += NTH) Pc[idx] = 0.f;
     __syncthreads();
     // 4b. off-diagonal blocks of A and P on MFMA with anchored decay factors
-    for (int job = wave; job < 12; job += 4) {
+    for (int job = wave; job < 12; job += 8) {
         const int tile = job % 6;
         const bool isP = job >= 6;
         const int I = t2I(tile), J = t2J(tile);
@@ -189,12 +190,12 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
             else sm.A[i * LDA + j] = acc[e];
         }
     }
-    // 4c. diagonal blocks exactly on the VALU: 4 threads per row, each a
-    // quarter of the channels, reduced across the 4 lanes.
+    // 4c. diagonal blocks exactly on the VALU: 8 threads per row, each an
+    // eighth of the channels, reduced across the 8 lanes.
     {
-        const int i = tid >> 2, qq = tid & 3;
+        const int i = tid >> 3, qq = tid & 7;
         const int blk0 = (i >> 4) * 16;
-        constexpr int CQ = DK / 4;
+        constexpr int CQ = DK / 8;
         float* Dc = Dout + chunk * BT;
         for (int j = blk0; j < blk0 + 16; ++j) {
             float pa = 0.f, pp = 0.f;
@@ -207,8 +208,10 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
             }
             pa += __shfl_xor(pa, 1, 64);
             pa += __shfl_xor(pa, 2, 64);
+            pa += __shfl_xor(pa, 4, 64);
             pp += __shfl_xor(pp, 1, 64);
             pp += __shfl_xor(pp, 2, 64);
+            pp += __shfl_xor(pp, 4, 64);
             if (qq == 0 && j <= i) {
                 if (j < i) {
                     sm.A[i * LDA + j] = pa;
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(256) void gdn2_intra_kernel(
         __syncthreads();
     }
     float *Tc = Tout + chunk * (BT * BT);
-    for (int idx = tid; idx < BT * BT; idx += 256) {
+    for (int idx = tid; idx < BT * BT; idx += NTH) {
         const int i = idx >> 6, j = idx & 63;
         Tc[idx] = (i > j) ? sm.u.Tm[i * LDA + j] : 0.f;
     }
@@ -455,7 +458,7 @@ static hipError_t launch_gdn2_intra_t(const void *q, const void *k, const float 
     using in_t = typename Pol::in_t;
     using mt = typename Pol::mt;
     const int NT = (T + BT - 1) / BT;
-    hipLaunchKernelGGL((gdn2_intra_kernel<Pol, DK>), dim3((unsigned)((long)B * H * NT)), dim3(256), 0, st,
+    hipLaunchKernelGGL((gdn2_intra_kernel<Pol, DK>), dim3((unsigned)((long)B * H * NT)), dim3(512), 0, st,
                        (const in_t *)q, (const in_t *)k, la, (const in_t *)bg, (mt *)Ehat, (mt *)Qhat, (mt *)Khat,
                        GamC, Tinv, P, D, T, H, NT);
     return hipGetLastError();
