@@ -123,23 +123,24 @@ __device__ constexpr int lJ(int t) { return t - lI(t) * (lI(t) + 1) / 2; }
 }  // namespace
 
 // ------------------------------------------------------- reverse state walk
-// One workgroup per (batch, head, 16 state-gradient columns), four waves.
+// One workgroup per (batch, head, 16 state-gradient columns), eight waves
+// (the row-block products on waves 0..3, the DK-wide ones on all eight).
 // The next chunk's operands are requested into registers while the current
 // chunk is worked on, and stored into LDS at the top of the next iteration.
 template <int DK>
 struct Gdn2WalkPf {
-    static constexpr int UE = BT * DK / 4 / 256, UT = BT * BT / 4 / 256;
+    static constexpr int UE = BT * DK / 4 / 512, UT = BT * BT / 4 / 512;
     f32x4 k[UE], q[UE], e[UE], t[UT], p[UT], o, gam;
     float dg[UT];
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
+__global__ __launch_bounds__(512, 1) void gdn2_bwd_walk_kernel(
     const float *__restrict__ Eh, const float *__restrict__ Qh, const float *__restrict__ Kh,
     const float *__restrict__ GamC, const float *__restrict__ Tws, const float *__restrict__ Pws,
     const float *__restrict__ Dws, const float *__restrict__ dO, const float *__restrict__ dht,
     float *__restrict__ dSck, float *__restrict__ dh0, int T, int H, int NT, float scale) {
-    constexpr int BV = 16, NTHR = 256, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
+    constexpr int BV = 16, NTHR = 512, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
     using PF = Gdn2WalkPf<DK>;
     __shared__ float sK[BT * LDQ], sQ[BT * LDQ], sE[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
     __shared__ float sdO[BT * LDB], sdDl[BT * LDB], sdR[BT * LDB], sdS[DK * LDB], sGam[DK];
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
             pf.p[u] = *(const f32x4 *)(Pws + cb * BT * BT + 4 * (tid + NTHR * u));
             pf.dg[u] = Dws[cb * BT + ((4 * (tid + NTHR * u)) >> 6)];
         }
-        {   // dO: 64 rows x 16 columns, one f32x4 per thread
+        if (tid < 256) {   // dO: 64 rows x 16 columns, one f32x4 per thread
             const int row = tid >> 2, col = 4 * (tid & 3);
             const int t = c * BT + row;
             pf.o = (t < T) ? *(const f32x4 *)(dO + ((b * T + t) * H + h) * (long)DV + vcol0 + col) : zero4();
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
                 sP[i * LDC + j + e] = (j + e < i) ? pf.p[u][e] : (j + e == i ? pf.dg[u] : 0.f);
             }
         }
-        {
+        if (tid < 256) {
             const int row = tid >> 2, col = 4 * (tid & 3);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sdO[row * LDB + col + e] = pf.o[e];
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
         if (c > 0) fetch(c - 1);
         __syncthreads();
         // dDl = scale P^T dO + Khat dS' (row block I = wave)
-        {
+        if (wave < 4) {
             const int I = wave;
             const f32x4 a1 = tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 0, lane);
             const f32x4 a2 = tmma<DK>(zero4(), sK, LDQ, 1, sdS, LDB, 1, 16 * I, 0, lane);
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
         }
         __syncthreads();
         // dR = dDl + (T - I)^T dDl
-        {
+        if (wave < 4) {
             const int I = wave;
             const f32x4 a = tmma<BT>(zero4(), sTm, 1, LDC, sdDl, LDB, 1, 16 * I, 0, lane);
 #pragma unroll
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_bwd_walk_kernel(
         }
         __syncthreads();
         // dS = Gam_C . dS' + scale Qhat^T dO - Ehat^T dR  (DK / 16 row blocks)
-        for (int M = wave; M < DK / 16; M += 4) {
+        for (int M = wave; M < DK / 16; M += 8) {
             const f32x4 a1 = tmma<BT>(zero4(), sQ, 1, LDQ, sdO, LDB, 1, 16 * M, 0, lane);
             const f32x4 a2 = tmma<BT>(zero4(), sE, 1, LDQ, sdR, LDB, 1, 16 * M, 0, lane);
 #pragma unroll
@@ -782,7 +783,7 @@ static hipError_t launch_gdn2_bwd_t(const void *q, const void *k, const void *v,
     using in_t = typename Pol::in_t;
     const int NT = (T + BT - 1) / BT;
     const long heads = (long)B * H;
-    hipLaunchKernelGGL((gdn2_bwd_walk_kernel<DK, DV>), dim3((unsigned)(heads * (DV / 16))), dim3(256), 0, st, Eh,
+    hipLaunchKernelGGL((gdn2_bwd_walk_kernel<DK, DV>), dim3((unsigned)(heads * (DV / 16))), dim3(512), 0, st, Eh,
                        Qh, Kh, GamC, Tws, Pws, Dws, dO, dht, dSck, dh0, T, H, NT, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
