@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) void gdn2_bwd_key_kernel(
 // so the block's rows are finished there: dq, db, dk and, because rows come
 // in reverse order, the reverse cumulative sum giving dlog_alpha.
 template <int DK>
-__global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
+__global__ __launch_bounds__(DK, 2) void gdn2_bwd_key_lane_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ la,
     const uint16_t *__restrict__ bg, const float *__restrict__ dEh, const float *__restrict__ dQh,
     const float *__restrict__ dKh, const float *__restrict__ srow, const float *__restrict__ dAws,
@@ -593,6 +593,11 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
     float *__restrict__ db, int T, int H, int NT) {
     constexpr int NB = BT / 4;
     __shared__ f32x4 sA[BT * BT / 4], sP[BT * BT / 4];  // dA, dP rows of the chunk, 4 columns per entry
+    // column sums sum_i D_ij (dA_ij e_i + dP_ij q_i) of each lane's channel:
+    // a per-lane array (row stride BT + 4 words, so a 16-byte access of 16
+    // lanes covers the 64 banks once)
+    constexpr int LDCS = BT + 4;
+    __shared__ float sC[DK * LDCS];
     const int tid = threadIdx.x;
     const long cb = blockIdx.x;
     const int c = (int)(cb % NT);
@@ -624,21 +629,31 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
     uint32_t K2[BT / 2];
     float G[BT];
     {
-        uint16_t kr[BT];
-#pragma unroll
-        for (int j = 0; j < BT; ++j) {
-            const bool in = j < nrows;
-            kr[j] = in ? k[gbase + j * rs] : (uint16_t)0;
-            G[j] = in ? la[gbase + j * rs] : 0.f;
-        }
+        // rows past T read the last row (always in bounds) and are zeroed by a
+        // select, so every load is issued without a branch or a wait; two
+        // halves of 32 rows keep the raw key registers few
         double acc = 0.0;
 #pragma unroll
-        for (int j = 0; j < BT; ++j) {
-            acc += G[j];
-            G[j] = (float)(acc * 1.4426950408889634);
-        }
+        for (int h2 = 0; h2 < 2; ++h2) {
+            uint16_t kr[BT / 2];
 #pragma unroll
-        for (int j = 0; j < BT / 2; ++j) K2[j] = (uint32_t)kr[2 * j] | ((uint32_t)kr[2 * j + 1] << 16);
+            for (int x = 0; x < BT / 2; ++x) {
+                const int j = (BT / 2) * h2 + x;
+                const long off = gbase + min(j, nrows - 1) * rs;
+                kr[x] = k[off];
+                G[j] = la[off];
+            }
+#pragma unroll
+            for (int x = 0; x < BT / 2; ++x) {
+                const int j = (BT / 2) * h2 + x;
+                kr[x] = j < nrows ? kr[x] : (uint16_t)0;
+                acc += j < nrows ? G[j] : 0.f;
+                G[j] = (float)(acc * 1.4426950408889634);
+            }
+#pragma unroll
+            for (int x = 0; x < BT / 4; ++x)
+                K2[(BT / 4) * h2 + x] = (uint32_t)kr[2 * x] | ((uint32_t)kr[2 * x + 1] << 16);
+        }
     }
     auto Kf = [&](int j) -> float {
         return __uint_as_float((j & 1) ? (K2[j >> 1] & 0xffff0000u) : (K2[j >> 1] << 16));
@@ -648,11 +663,16 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
     // Gam_last . S term of S' (sum_v dS' . S): a constant in every dlog_alpha
     float run = __builtin_amdgcn_exp2f(GL) * srow[cb * DK + tid];
 #pragma unroll
-    for (int j = 0; j < BT; ++j)
-        run += dKh[ob + (long)j * DK + tid] * Kf(j) * __builtin_amdgcn_exp2f(GL - G[j]);
-    float cs[BT];  // column sums: sum_i D_ij (dA_ij e_i + dP_ij q_i) of this channel
+    for (int j0 = 0; j0 < BT; j0 += 16) {  // 16 rows of loads in flight at a time
+        float dk16[16];
 #pragma unroll
-    for (int j = 0; j < BT; ++j) cs[j] = 0.f;
+        for (int x = 0; x < 16; ++x) dk16[x] = dKh[ob + (long)(j0 + x) * DK + tid];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) run += dk16[x] * Kf(j0 + x) * __builtin_amdgcn_exp2f(GL - G[j0 + x]);
+    }
+    float *cs = sC + tid * LDCS;
+#pragma unroll
+    for (int j = 0; j < BT; j += 4) *(f32x4 *)&cs[j] = zero4();
     __syncthreads();
 
     // the global rows of the next block (erase gate, query, dEhat, dQhat,
@@ -662,14 +682,18 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
     auto fetch_rows = [&](int r0) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const bool in = r0 + x < nrows;
-            const long off = gbase + (r0 + x) * rs;
-            nb[x] = in ? bg[off] : (uint16_t)0;
-            nq[x] = in ? q[off] : (uint16_t)0;
+            const long off = gbase + min(r0 + x, nrows - 1) * rs;
+            nb[x] = bg[off];
+            nq[x] = q[off];
             const long wo = ob + (long)(r0 + x) * DK + tid;
             nE[x] = dEh[wo];
             nQ[x] = dQh[wo];
             nK[x] = dKh[wo];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            nb[x] = r0 + x < nrows ? nb[x] : (uint16_t)0;
+            nq[x] = r0 + x < nrows ? nq[x] : (uint16_t)0;
         }
     };
     fetch_rows(BT - 4);
@@ -680,7 +704,7 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
         // already added its terms to the column sums cur)
         float Gi[4], Ki[4], cur[4], Bi[4], Qi[4], Ei[4], a[4], Et[4], Qt[4], xE[4], xQ[4], xK[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) Gi[x] = Ki[x] = cur[x] = 0.f;
+        for (int x = 0; x < 4; ++x) Gi[x] = Ki[x] = 0.f;
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             const bool sel = jb == ib;
@@ -688,8 +712,12 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
             for (int x = 0; x < 4; ++x) {
                 Gi[x] = sel ? G[4 * jb + x] : Gi[x];
                 Ki[x] = sel ? Kf(4 * jb + x) : Ki[x];
-                cur[x] = sel ? cs[4 * jb + x] : cur[x];
             }
+        }
+        {
+            const f32x4 c4 = *(const f32x4 *)&cs[i0];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) cur[x] = c4[x];
         }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -728,8 +756,10 @@ __global__ __launch_bounds__(DK) void gdn2_bwd_key_lane_kernel(
                         t[y] = fmaf(A4[y], Et[x], fmaf(P4[y], Qt[x], t[y]));
                     }
                 }
+                f32x4 c4 = *(const f32x4 *)&cs[j0];
 #pragma unroll
-                for (int y = 0; y < 4; ++y) cs[j0 + y] = fmaf(f[y], t[y], cs[j0 + y]);
+                for (int y = 0; y < 4; ++y) c4[y] = fmaf(f[y], t[y], c4[y]);
+                *(f32x4 *)&cs[j0] = c4;
             }
         }
         // diagonal block, exact decays; then the block's rows are complete
