@@ -275,6 +275,7 @@ struct Gdn2BwdValueSmem {
     float S[DK * LDW], dS[DK * LDW];  // column slice of the entry state and of dS'
     float dO[BT * LDW], R[BT * LDW], Dl[BT * LDW], dDl[BT * LDW], dR[BT * LDW];
     float W[BT * LDW], V[BT * LDW];
+    f32x4 xp[4][2][64];  // the second wave group's partial row products (per row block and lane)
 };
 
 template <class Pol, int DK, int DV>
@@ -285,9 +286,10 @@ __global__ __launch_bounds__(512, 1) void gdn2_bwd_value_kernel(
     float *__restrict__ Tws, float *__restrict__ Pws, const float *__restrict__ Dws, float *__restrict__ dv,
     float *__restrict__ dw, int T, int H, int NT, float scale) {
     using SM = Gdn2BwdValueSmem<DK>;
-    // eight waves: waves 0..3 form the per-column row products of each slice
-    // (row block I = wave); all eight accumulate, each half of the output
-    // tiles; the slices are staged by the first 256 threads
+    // eight waves in two groups of four: each group forms half (by k range)
+    // of the per-column row products of a slice for row block I = wave & 3,
+    // and accumulates half of the output tiles; the slices are staged by the
+    // first 256 threads
     constexpr int LDQ = SM::LDQ, LDC = SM::LDC, CW = SM::CW, LDW = SM::LDW, NTHR = 256, NM = DK / 16, MH = NM / 2;
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void gdn2_bwd_value_kernel(
     const long ob = cb * (long)BT * DK;
     const int I = wave & 3;  // this wave's 16-row block of every 64-row product
     const int gi = wave >> 2;  // half of the DK-wide output tiles (key blocks MH gi ..)
-    const bool rowp = wave < 4, st = tid < NTHR;
+    const bool st = tid < NTHR;
 
     if (st) {
         stage_block<DK, LDQ, NTHR>(sm.E, Eh + ob, tid);
@@ -348,42 +350,68 @@ __global__ __launch_bounds__(512, 1) void gdn2_bwd_value_kernel(
 #pragma unroll
             for (int j = 0; j < CW; ++j) srow += sm.dS[tid * LDW + j] * sm.S[tid * LDW + j];
         }
+        // The row-block products split their k range between the wave groups:
+        // group 1 leaves its partial sums in xp, group 0 adds them and stores.
         // R = Z - Ehat S (row block I)
-        if (rowp) {
-            const f32x4 a = tmma<DK>(zero4(), sm.E, LDQ, 1, sm.S, LDW, 1, 16 * I, 0, lane);
+        {
+            constexpr int KH = DK / 2;
+            const f32x4 a = tmma<KH>(zero4(), sm.E + KH * gi, LDQ, 1, sm.S + KH * gi * LDW, LDW, 1, 16 * I, 0, lane);
+            if (gi == 1) sm.xp[I][0][lane] = a;
+            __syncthreads();
+            if (gi == 0) {
+                const f32x4 at = a + sm.xp[I][0][lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * g + e;
-                sm.R[i * LDW + r] = sm.W[i * LDW + r] * sm.V[i * LDW + r] - a[e];
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * g + e;
+                    sm.R[i * LDW + r] = sm.W[i * LDW + r] * sm.V[i * LDW + r] - at[e];
+                }
             }
         }
         __syncthreads();
         // Dl = R + (T - I) R; dDl = scale P^T dO + Khat dS'
-        if (rowp) {
-            const f32x4 a = tmma<BT>(zero4(), sm.Tm, LDC, 1, sm.R, LDW, 1, 16 * I, 0, lane);
-            const f32x4 a1 = tmma<BT>(zero4(), sm.P, 1, LDC, sm.dO, LDW, 1, 16 * I, 0, lane);
-            const f32x4 a2 = tmma<DK>(zero4(), sm.K, LDQ, 1, sm.dS, LDW, 1, 16 * I, 0, lane);
+        {
+            constexpr int BH = BT / 2, KH = DK / 2;
+            const f32x4 a = tmma<BH>(zero4(), sm.Tm + BH * gi, LDC, 1, sm.R + BH * gi * LDW, LDW, 1, 16 * I, 0, lane);
+            const f32x4 a1 = tmma<BH>(zero4(), sm.P + BH * gi * LDC, 1, LDC, sm.dO + BH * gi * LDW, LDW, 1, 16 * I, 0,
+                                      lane);
+            const f32x4 a2 = tmma<KH>(zero4(), sm.K + KH * gi, LDQ, 1, sm.dS + KH * gi * LDW, LDW, 1, 16 * I, 0, lane);
+            const f32x4 d = scale * a1 + a2;
+            if (gi == 1) {
+                sm.xp[I][0][lane] = a;
+                sm.xp[I][1][lane] = d;
+            }
+            __syncthreads();
+            if (gi == 0) {
+                const f32x4 at = a + sm.xp[I][0][lane], dt = d + sm.xp[I][1][lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * g + e;
-                sm.Dl[i * LDW + r] = sm.R[i * LDW + r] + a[e];
-                sm.dDl[i * LDW + r] = scale * a1[e] + a2[e];
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * g + e;
+                    sm.Dl[i * LDW + r] = sm.R[i * LDW + r] + at[e];
+                    sm.dDl[i * LDW + r] = dt[e];
+                }
             }
         }
         __syncthreads();
         // dR = dDl + (T - I)^T dDl; dv = dR . w, dw = dR . v
-        if (rowp) {
-            const f32x4 a = tmma<BT>(zero4(), sm.Tm, 1, LDC, sm.dDl, LDW, 1, 16 * I, 0, lane);
+        {
+            constexpr int BH = BT / 2;
+            const f32x4 a = tmma<BH>(zero4(), sm.Tm + BH * gi * LDC, 1, LDC, sm.dDl + BH * gi * LDW, LDW, 1, 16 * I, 0,
+                                     lane);
+            if (gi == 1) sm.xp[I][0][lane] = a;
+            __syncthreads();
+            if (gi == 0) {
+                const f32x4 at = a + sm.xp[I][0][lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * g + e;
-                const float x = sm.dDl[i * LDW + r] + a[e];
-                sm.dR[i * LDW + r] = x;
-                const int t = t0 + i;
-                if (t < T) {
-                    const long off = ((b * T + t) * H + h) * (long)DV + v0 + r;
-                    dv[off] = x * sm.W[i * LDW + r];
-                    dw[off] = x * sm.V[i * LDW + r];
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * g + e;
+                    const float x = sm.dDl[i * LDW + r] + at[e];
+                    sm.dR[i * LDW + r] = x;
+                    const int t = t0 + i;
+                    if (t < T) {
+                        const long off = ((b * T + t) * H + h) * (long)DV + v0 + r;
+                        dv[off] = x * sm.W[i * LDW + r];
+                        dw[off] = x * sm.V[i * LDW + r];
+                    }
                 }
             }
         }
