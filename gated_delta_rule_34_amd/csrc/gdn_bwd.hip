@@ -832,6 +832,21 @@ __device__ __forceinline__ f32x4 mma_raw_parts(f32x4 acc, const uint16_t *A, int
     return acc;
 }
 
+// acc += A B^T for A and B given as bf16 parts of one 32-deep block (the
+// first parts the largest): the products of total order at most one
+// (a0 b0, a0 b1, a1 b0) or two (also a0 b2, a1 b1, a2 b0), smallest first.
+__device__ __forceinline__ f32x4 mma_parts2(f32x4 acc, const u32x4b *a, const u32x4b *b) {
+    acc = mma_bf16v(acc, a[1], b[0]);
+    acc = mma_bf16v(acc, a[0], b[1]);
+    return mma_bf16v(acc, a[0], b[0]);
+}
+__device__ __forceinline__ f32x4 mma_parts3(f32x4 acc, const u32x4b *a, const u32x4b *b) {
+    acc = mma_bf16v(acc, a[2], b[0]);
+    acc = mma_bf16v(acc, a[1], b[1]);
+    acc = mma_bf16v(acc, a[0], b[2]);
+    return mma_parts2(acc, a, b);
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -1020,29 +1035,41 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         for (int e = 0; e < 4; ++e) sl.R[(16 * I + 4 * g + e) * LDW + r] = dRr[e];
         __syncthreads();
         // accumulate this group's tiles of dA, dP (64 x 64) and the DK-wide
-        // products for rows of block I, over both groups' 16 columns
+        // products for rows of block I over both groups' 16 columns, as one
+        // 32-deep bf16 MFMA block: lane (g, r) takes k-slots 8g .. 8g + 7,
+        // columns 8 (g & 1) .. + 7 of group g >> 1's slice.  The fp32
+        // operands enter as bf16 parts: two on each side of dR Vn^T, dO S^T
+        // and dR S^T, three on each side of dO Vn^T and Vn dS'^T, keeping the
+        // part products of total order at most one (two parts) or two (three).
+        {
+            const typename SM::Slices &o = sm.sl[g >> 1];
+            const int kc = 8 * (g & 1);
+            auto parts_of_row = [&](auto &out, const float *M, int row) {
+                float x[8];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int J = 2 * gi + jj;
-            f32x4 x = zero4(), y = zero4();
+                for (int e = 0; e < 8; ++e) x[e] = M[row * LDW + kc + e];
+                split_8(out, x);
+            };
+            u32x4b ar[2], ao[3], av[3];
+            parts_of_row(ar, o.R, 16 * I + r);
+            parts_of_row(ao, o.dO, 16 * I + r);
+            parts_of_row(av, o.Vn, 16 * I + r);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const typename SM::Slices &o = sm.sl[hh];
-                x = tile_mma<CW>(x, o.R, LDW, 1, o.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
-                y = tile_mma<CW>(y, o.dO, LDW, 1, o.Vn, 1, LDW, nullptr, 16 * I, 16 * J, lane);
+            for (int jj = 0; jj < 2; ++jj) {
+                u32x4b bv[3];
+                parts_of_row(bv, o.Vn, 16 * (2 * gi + jj) + r);
+                dA[jj] -= mma_parts2(zero4(), ar, bv);
+                dP[jj] += mma_parts3(zero4(), ao, bv) * scale;
             }
-            dA[jj] -= x;
-            dP[jj] += y * scale;
-        }
 #pragma unroll
-        for (int mm = 0; mm < MH; ++mm) {
-            const int m = MH * gi + mm;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const typename SM::Slices &o = sm.sl[hh];
-                dqs[mm] = tile_mma<CW>(dqs[mm], o.dO, LDW, 1, o.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
-                dkR[mm] = tile_mma<CW>(dkR[mm], o.R, LDW, 1, o.S, 1, LDW, nullptr, 16 * I, 16 * m, lane);
-                dKd[mm] = tile_mma<CW>(dKd[mm], o.Vn, LDW, 1, o.dS, 1, LDW, nullptr, 16 * I, 16 * m, lane);
+            for (int mm = 0; mm < MH; ++mm) {
+                const int m = MH * gi + mm;
+                u32x4b bs[2], bd[3];
+                parts_of_row(bs, o.S, 16 * m + r);
+                parts_of_row(bd, o.dS, 16 * m + r);
+                dqs[mm] = mma_parts2(dqs[mm], ao, bs);
+                dkR[mm] = mma_parts2(dkR[mm], ar, bs);
+                dKd[mm] = mma_parts3(dKd[mm], av, bd);
             }
         }
     }

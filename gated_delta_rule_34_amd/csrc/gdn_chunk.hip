@@ -6,7 +6,8 @@
 //    * chunk-local cumsum of g, times log2(e), so every decay below is one
 //      exp2 of a non-positive difference (GatedDeltaNet walkthrough,
 //      yfxerp.com, chunked-kernel section: cumsum scaled by 1.44269504);
-//    * A = strictly-lower( diag(beta) K K^T  .  2^(G2_i - G2_j) ) on MFMA;
+//    * A = strictly-lower( diag(beta) K K^T  .  2^(G2_i - G2_j) ) on MFMA
+//      (bf16 MFMA for bf16 keys, whose products are exact);
 //    * T = (I + A)^-1: the four 16x16 diagonal blocks by forward
 //      substitution (one lane per column), the off-diagonal blocks by
 //      block forward substitution T_IJ = -T_II sum_K A_IK T_KJ on fp32 MFMA.
@@ -25,10 +26,14 @@
 //    The value columns of the state evolve independently, so each wave owns
 //    16 columns and runs the whole chain in registers; only the per-chunk
 //    inputs (Q, K, decayed K^T, P) are shared through LDS.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8c;
 
 // The 10 lower-triangular 16x16 tiles (I >= J) of a 64x64 chunk matrix.
 __constant__ int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
@@ -44,8 +49,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
     constexpr int LDK = DK + 8;
     constexpr int LDA = 65;
     __shared__ float sA[BT * LDA];
-    __shared__ union {
+    // bf16 keys stay raw bf16 rows (their products are exact on bf16 MFMA)
+    constexpr bool RAW = std::is_same<typename Pol::in_t, uint16_t>::value && std::is_same<mt, float>::value;
+    __shared__ union alignas(16) {
         mt k[BT * LDK];
+        uint16_t kraw[BT * LDK];
         float t[BT * LDA];
     } u;
     __shared__ float sBeta[BT];
@@ -86,14 +94,20 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
     for (int idx = tid; idx < BT * DK / 4; idx += 256) {
         const int row = idx / (DK / 4), col = (idx % (DK / 4)) * 4;
         const int t = t0 + row;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < T) {
-            const typename Pol::in_t *p = kin + ((b * T + t) * H + h) * (long)DK + col;
+        if constexpr (RAW) {
+            uint2 x = make_uint2(0u, 0u);
+            if (t < T) x = *(const uint2 *)(kin + ((b * T + t) * H + h) * (long)DK + col);
+            *(uint2 *)&u.kraw[row * LDK + col] = x;
+        } else {
+            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            if (t < T) {
+                const typename Pol::in_t *p = kin + ((b * T + t) * H + h) * (long)DK + col;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = load_elem(p + e);
+                for (int e = 0; e < 4; ++e) x[e] = load_elem(p + e);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u.k[row * LDK + col + e] = to_mt<mt>(x[e]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u.k[row * LDK + col + e] = to_mt<mt>(x[e]);
     }
     __syncthreads();
 
@@ -103,10 +117,18 @@ __global__ __launch_bounds__(256) void intra_kernel(const typename Pol::in_t *__
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < DK; kk += 32) {
-            mt a[8], bb[8];
-            frag_rows(a, u.k, LDK, 16 * I, kk, lane);
-            frag_rows(bb, u.k, LDK, 16 * J, kk, lane);
-            acc = mma_slab(acc, a, bb);
+            if constexpr (RAW) {
+                // one 16-byte read per operand (lane (g, r): k-slots 8g .. + 7)
+                // and one exact bf16 MFMA per 32 k
+                const bf16x8c a = *(const bf16x8c *)&u.kraw[(16 * I + r) * LDK + kk + 8 * g];
+                const bf16x8c bb = *(const bf16x8c *)&u.kraw[(16 * J + r) * LDK + kk + 8 * g];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc, 0, 0, 0);
+            } else {
+                mt a[8], bb[8];
+                frag_rows(a, u.k, LDK, 16 * I, kk, lane);
+                frag_rows(bb, u.k, LDK, 16 * J, kk, lane);
+                acc = mma_slab(acc, a, bb);
+            }
         }
         const int j = 16 * J + r;
 #pragma unroll

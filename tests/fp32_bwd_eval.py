@@ -12,9 +12,12 @@ elementwise steps stay in float64 (the GPU forms the gate sums in fp64 and
 takes the decay factors from their differences).
 
     python -m tests.fp32_bwd_eval            # the layer workload, every head
+    python -m tests.fp32_bwd_eval --plan     # the same with the bf16 part plan
 
 prints, per gradient, the worst over the 64 heads of max|diff| / rms against
-the fp64 oracle (about 90 s on 8 processes)."""
+the fp64 oracle (about 90 s on 8 processes).  With --plan the five products
+that the per-chunk kernel accumulates over the value columns take that
+kernel's bf16 part splits (BF16_ACCUM_PLAN) instead of float32."""
 import numpy as np
 
 from oracle import chunked as ch
@@ -25,9 +28,54 @@ def _mm(a, b):
     return (np.asarray(a, np.float32) @ np.asarray(b, np.float32)).astype(np.float64)
 
 
-def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64):
+def _bf16(x):
+    """Round float32 values to bfloat16 (nearest, ties to even), kept as float32."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _parts(x, n):
+    """x (float32) as n bfloat16 parts, largest first: each part rounds what
+    the earlier ones leave."""
+    rest = np.asarray(x, np.float32).copy()
+    out = []
+    for _ in range(n):
+        h = _bf16(rest)
+        out.append(h.astype(np.float64))
+        rest = (rest - h).astype(np.float32)
+    return out
+
+
+def mm_parts(n):
+    """A product on bf16 MFMA with both float32 operands split into n bf16
+    parts, keeping the part products of total order below n (3 of 4 for two
+    parts, 6 of 9 for three), each accumulated into a float32 result."""
+    def f(a, b):
+        pa, pb = _parts(a, n), _parts(b, n)
+        acc = np.zeros((pa[0].shape[0], pb[0].shape[1]), np.float32)
+        for i, x in enumerate(pa):
+            for j, y in enumerate(pb):
+                if i + j < n:
+                    acc = (acc + (x @ y).astype(np.float32)).astype(np.float32)
+        return acc.astype(np.float64)
+    return f
+
+
+# The per-chunk GPU kernel's plan for its five products accumulated over the
+# value columns (both operands float32 values): dR Vn^T, dO S^T and dR S^T
+# with two parts on each side, dO Vn^T and Vn dS'^T with three.
+BF16_ACCUM_PLAN = {"dA": mm_parts(2), "dP": mm_parts(3), "dkR": mm_parts(2), "dqs": mm_parts(2),
+                   "dKd": mm_parts(3)}
+
+
+def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64, prods=None):
     """dq, dk, dv, dg, dbeta, dS0 of one head with float32 products.  Entry
-    states come from the fp64 chunked forward."""
+    states come from the fp64 chunked forward.  `prods` may replace the
+    products accumulated over the value columns (keys dA, dP, dkR, dqs, dKd)
+    by other roundings, such as BF16_ACCUM_PLAN."""
+    pr = dict(prods or {})
+    mmx = lambda name, a, b: pr.get(name, _mm)(a, b)
     T, Dk = q.shape
     Dv = v.shape[1]
     starts = []
@@ -58,13 +106,13 @@ def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64):
         # reverse mode through the chunk, dS the gradient of the state leaving it
         dVn = scale * _mm(P.T, dOc) + dec[:, None] * _mm(K, dS)
         dR = dVn + _mm(TmI.T, dVn)
-        dA = -np.tril(_mm(dR, Vn.T), -1)
-        dP = scale * np.tril(_mm(dOc, Vn.T))
+        dA = -np.tril(mmx('dA', dR, Vn.T), -1)
+        dP = scale * np.tril(mmx('dP', dOc, Vn.T))
         dS_in = gam[-1] * dS + scale * _mm((gam[:, None] * Q).T, dOc) - _mm(((bc * gam)[:, None] * K).T, dR)
         dG = np.zeros(n)
         dv[s:e] = bc[:, None] * dR
         db[s:e] += np.sum(dR * (V - gam[:, None] * KS), axis=1)
-        dk[s:e] -= (bc * gam)[:, None] * _mm(dR, S.T)
+        dk[s:e] -= (bc * gam)[:, None] * mmx('dkR', dR, S.T)
         dG -= bc * gam * np.sum(dR * KS, axis=1)
         dAs = dA * D
         db[s:e] += np.sum(dAs * KK, axis=1)
@@ -76,10 +124,10 @@ def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64):
         dk[s:e] += _mm(dPs.T, Q)
         dPP = dP * P
         dG += dPP.sum(axis=1) - dPP.sum(axis=0)
-        dq[s:e] += scale * gam[:, None] * _mm(dOc, S.T)
+        dq[s:e] += scale * gam[:, None] * mmx('dqs', dOc, S.T)
         dG += scale * gam * np.sum(dOc * _mm(Q, S), axis=1)
         dG[-1] += gam[-1] * np.sum(dS * S)
-        dKd = _mm(Vn, dS.T)
+        dKd = mmx('dKd', Vn, dS.T)
         dk[s:e] += dec[:, None] * dKd
         t = np.sum(dKd * K * dec[:, None], axis=1)
         dG[-1] += t.sum()
@@ -89,7 +137,7 @@ def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64):
     return dq, dk, dv, dg, db, dS
 
 
-def per_head_errors(x, do, dht):
+def per_head_errors(x, do, dht, prods=None):
     """[heads, 6] of max|diff| / rms (dq, dk, dv, dg, dbeta, dh0) for every
     (batch, head) of generator output x against the fp64 chunked oracle."""
     B, T, H = x["g"].shape
@@ -100,7 +148,7 @@ def per_head_errors(x, do, dht):
             S0 = x["h0_f64"][b, h] if x["h0_f64"] is not None else np.zeros((args[0].shape[1], args[2].shape[1]))
             dST = None if dht is None else dht[b, h]
             ref = ch.gdn_chunk_bwd_head(*args, S0, do[b, :, h], dST, x["scale"])
-            got = bwd_head_fp32(*args, S0, do[b, :, h], dST, x["scale"])
+            got = bwd_head_fp32(*args, S0, do[b, :, h], dST, x["scale"], prods=prods)
             out.append([float(np.abs(a - r).max() / max(np.sqrt(np.mean(r * r)), 1e-300)) for a, r in zip(got, ref)])
     return np.array(out)
 
@@ -121,19 +169,22 @@ def _layer_workload():
 
 
 def _one(args):
-    b, h = args
+    b, h, plan = args
     x, do, dht = _layer_workload()
     sub = {n: x[n][b:b + 1, :, h:h + 1] for n in x if n.endswith("_f64") and x[n] is not None and x[n].ndim >= 3
            and n != "h0_f64"}
     sub["h0_f64"] = x["h0_f64"][b:b + 1, h:h + 1]
     sub["g"] = x["g"][b:b + 1, :, h:h + 1]
     sub["scale"] = x["scale"]
-    return per_head_errors(sub, do[b:b + 1, :, h:h + 1], dht[b:b + 1, h:h + 1])[0]
+    return per_head_errors(sub, do[b:b + 1, :, h:h + 1], dht[b:b + 1, h:h + 1],
+                           prods=BF16_ACCUM_PLAN if plan else None)[0]
 
 
 if __name__ == "__main__":
     import multiprocessing as mp
+    import sys
+    plan = "--plan" in sys.argv[1:]
     with mp.Pool(8) as pool:
-        errs = np.array(pool.map(_one, [(b, h) for b in range(8) for h in range(8)]))
+        errs = np.array(pool.map(_one, [(b, h, plan) for b in range(8) for h in range(8)]))
     for i, name in enumerate(("dq", "dk", "dv", "dg", "dbeta", "dh0")):
         print(f"{name}: worst head {errs[:, i].max():.2e}, median {np.median(errs[:, i]):.2e}")

@@ -103,4 +103,5 @@ def test_bwd_layer_workload_full_size_every_head():
     for name, a, b in zip(GRADS, got, ref):
         heads = [(a[i, j], b[i, j]) if name == "dh0" else (a[i, :, j], b[i, :, j]) for i in range(B) for j in range(H)]
         worst = max(rel_err(u, w) for u, w in heads)
+        print(f"{name}: worst head rel err {worst:.2e} (bar {TOL_FULL[name]:.0e})")
         assert worst <= TOL_FULL[name], f"{name}: worst head rel err {worst:.3e} > {TOL_FULL[name]}"
