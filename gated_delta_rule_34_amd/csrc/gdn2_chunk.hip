@@ -22,8 +22,10 @@
 //    diag(P).  The off-diagonal 16x16 blocks of A and P run on MFMA with the
 //    decay split at an anchor row a (the first row of the block row):
 //    2^(G2_i - G2_j) = 2^(G2_i - G2_a) 2^(G2_a - G2_j), both factors <= 1
-//    because j < a <= i.  The diagonal 16x16 blocks have no such anchor and
-//    are summed exactly in fp32 on the VALU.
+//    because j < a <= i.  The diagonal 16x16 blocks are anchored at their
+//    own first row (one factor at most 1, the other at least 1) while the
+//    block's decay stays inside 2^(+-100), and otherwise summed directly in
+//    fp32 on the VALU.
 //  gdn2_walk_kernel (one workgroup per (b, h, 32 value columns)) walks the
 //    chunks with the state slice in MFMA accumulators, like the Gated
 //    DeltaNet walk, on the prepared operands.
@@ -50,6 +52,77 @@ struct Gdn2IntraSmem {
     float G2[BT * LD];
     float A[BT * LDA];
 };
+
+// Diagonal block (rows and columns a .. a + 15) of A and P, one wave.  The
+// factors are anchored at the block's own first row: e_i 2^(G2_i - G2_a) and
+// q_i 2^(G2_i - G2_a), at most 1 in size, against k_j 2^(G2_a - G2_j), at
+// least 1.  While every channel's decay within the block stays inside
+// 2^(+-100) of row a both are fp32 numbers with no overflow or underflow and
+// the block is their product on fp32 MFMA; otherwise each entry is summed
+// directly with its own exponentials.
+template <class Pol, int DK>
+__device__ __forceinline__ void gdn2_intra_diag(Gdn2IntraSmem<Pol, DK> &sm, int a, int lane, float *__restrict__ Pc,
+                                                float *__restrict__ Dc) {
+    using SM = Gdn2IntraSmem<Pol, DK>;
+    constexpr int LD = SM::LD, LDA = SM::LDA;
+    const int r = lane & 15, g = lane >> 4;
+    float span = 0.f;
+    for (int c = lane; c < DK; c += 64) {
+        const float ga = sm.G2[a * LD + c];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) span = fmaxf(span, fabsf(sm.G2[(a + x) * LD + c] - ga));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+    if (span < 100.f) {
+        f32x4 accA = zero4(), accP = zero4();
+        const int i = a + r;  // this lane's A-operand row and B-operand column
+#pragma unroll
+        for (int kk = 0; kk < DK; kk += 32) {
+            float fa[8], fq[8], fb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cc = kk + (e >> 2) * 16 + 4 * g + (e & 3);
+                const float Ga = sm.G2[a * LD + cc], Gi = sm.G2[i * LD + cc];
+                const float ri = exp2f(Gi - Ga);
+                fa[e] = sm.u.in.E[i * LD + cc] * ri;
+                fq[e] = sm.u.in.Q[i * LD + cc] * ri;
+                fb[e] = sm.u.in.K[i * LD + cc] * exp2f(Ga - Gi);
+            }
+            accA = mma_slab(accA, fa, fb);
+            accP = mma_slab(accP, fq, fb);
+        }
+        // lane holds [a + 4g + e][a + r]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = 4 * g + e;
+            if (r < ii) {
+                sm.A[(a + ii) * LDA + a + r] = accA[e];
+                Pc[(a + ii) * BT + a + r] = accP[e];
+            } else if (r == ii) {
+                Dc[a + ii] = accP[e];
+            }
+        }
+    } else {
+        for (int pr = lane; pr < 256; pr += 64) {
+            const int il = pr >> 4, jl = pr & 15;
+            if (jl > il) continue;
+            const int i = a + il, j = a + jl;
+            float pa = 0.f, pp = 0.f;
+            for (int cc = 0; cc < DK; ++cc) {
+                const float kd = sm.u.in.K[j * LD + cc] * exp2f(sm.G2[i * LD + cc] - sm.G2[j * LD + cc]);
+                pa = fmaf(sm.u.in.E[i * LD + cc], kd, pa);
+                pp = fmaf(sm.u.in.Q[i * LD + cc], kd, pp);
+            }
+            if (jl < il) {
+                sm.A[i * LDA + j] = pa;
+                Pc[i * BT + j] = pp;
+            } else {
+                Dc[i] = pp;
+            }
+        }
+    }
+}
 
 template <class Pol, int DK>
 __global__ __launch_bounds__(512) void gdn2_intra_kernel(
@@ -154,7 +227,7 @@ __global__ __launch_bounds__(512) void gdn2_intra_kernel(
         Khat[obase + idx] = to_mt<mt>(sm.u.in.K[row * LD + col] * exp2f(GL - G));
         if (row == 0) GamC[chunk * DK + col] = exp2f(GL);
     }
-    // 4a. zero the diagonal blocks of A (the VALU pass fills their lower part)
+    // 4a. zero the diagonal blocks of A (the diagonal jobs fill their lower part)
     for (int idx = tid; idx < 4 * 256; idx += NTH) {
         const int blk = idx >> 8, i = (idx >> 4) & 15, j = idx & 15;
         sm.A[(16 * blk + i) * LDA + 16 * blk + j] = 0.f;
@@ -162,10 +235,20 @@ __global__ __launch_bounds__(512) void gdn2_intra_kernel(
     float *Pc = Pout + chunk * (BT * BT);
     for (int idx = tid; idx < BT * BT; idx += NTH) Pc[idx] = 0.f;
     __syncthreads();
-    // 4b. off-diagonal blocks of A and P on MFMA with anchored decay factors
-    for (int job = wave; job < 12; job += 8) {
-        const int tile = job % 6;
-        const bool isP = job >= 6;
+    // 4b. A and P on fp32 MFMA with anchored decay factors.  Jobs 0 .. 3 are
+    // the diagonal blocks (A and P together, gdn2_intra_diag), jobs 4 .. 15
+    // the six off-diagonal tiles of A and of P, anchored at the first row a
+    // of their block row: 2^(G2_i - G2_j) = 2^(G2_i - G2_a) 2^(G2_a - G2_j),
+    // both factors <= 1 because j < a <= i.  Waves w and w + 4 share a SIMD
+    // and get equal work (a diagonal block costs about one and a half tiles).
+    float *Dc = Dout + chunk * BT;
+    for (int job = wave; job < 16; job += 8) {
+        if (job < 4) {
+            gdn2_intra_diag<Pol, DK>(sm, 16 * job, lane, Pc, Dc);
+            continue;
+        }
+        const int tile = (job - 4) % 6;
+        const bool isP = job - 4 >= 6;
         const int I = t2I(tile), J = t2J(tile);
         const int a = 16 * I;  // anchor row
         const float *src = isP ? sm.u.in.Q : sm.u.in.E;
@@ -188,38 +271,6 @@ __global__ __launch_bounds__(512) void gdn2_intra_kernel(
             const int i = 16 * I + 4 * g + e, j = 16 * J + r;
             if (isP) Pc[i * BT + j] = acc[e];
             else sm.A[i * LDA + j] = acc[e];
-        }
-    }
-    // 4c. diagonal blocks exactly on the VALU: 8 threads per row, each an
-    // eighth of the channels, reduced across the 8 lanes.
-    {
-        const int i = tid >> 3, qq = tid & 7;
-        const int blk0 = (i >> 4) * 16;
-        constexpr int CQ = DK / 8;
-        float* Dc = Dout + chunk * BT;
-        for (int j = blk0; j < blk0 + 16; ++j) {
-            float pa = 0.f, pp = 0.f;
-            if (j <= i) {
-                for (int cc = qq * CQ; cc < (qq + 1) * CQ; ++cc) {
-                    const float kd = sm.u.in.K[j * LD + cc] * exp2f(sm.G2[i * LD + cc] - sm.G2[j * LD + cc]);
-                    pa = fmaf(sm.u.in.E[i * LD + cc], kd, pa);
-                    pp = fmaf(sm.u.in.Q[i * LD + cc], kd, pp);
-                }
-            }
-            pa += __shfl_xor(pa, 1, 64);
-            pa += __shfl_xor(pa, 2, 64);
-            pa += __shfl_xor(pa, 4, 64);
-            pp += __shfl_xor(pp, 1, 64);
-            pp += __shfl_xor(pp, 2, 64);
-            pp += __shfl_xor(pp, 4, 64);
-            if (qq == 0 && j <= i) {
-                if (j < i) {
-                    sm.A[i * LDA + j] = pa;
-                    Pc[i * BT + j] = pp;
-                } else {
-                    Dc[i] = pp;
-                }
-            }
         }
     }
     __syncthreads();

@@ -1038,9 +1038,10 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         // products for rows of block I over both groups' 16 columns, as one
         // 32-deep bf16 MFMA block: lane (g, r) takes k-slots 8g .. 8g + 7,
         // columns 8 (g & 1) .. + 7 of group g >> 1's slice.  The fp32
-        // operands enter as bf16 parts: two on each side of dR Vn^T, dO S^T
-        // and dR S^T, three on each side of dO Vn^T and Vn dS'^T, keeping the
-        // part products of total order at most one (two parts) or two (three).
+        // operands enter as bf16 parts: two on each side of dR Vn^T and
+        // dR S^T, three on each side of dO Vn^T, dO S^T and Vn dS'^T, keeping
+        // the part products of total order at most one (two parts) or two
+        // (three).
         {
             const typename SM::Slices &o = sm.sl[g >> 1];
             const int kc = 8 * (g & 1);
@@ -1064,10 +1065,10 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
 #pragma unroll
             for (int mm = 0; mm < MH; ++mm) {
                 const int m = MH * gi + mm;
-                u32x4b bs[2], bd[3];
+                u32x4b bs[3], bd[3];
                 parts_of_row(bs, o.S, 16 * m + r);
                 parts_of_row(bd, o.dS, 16 * m + r);
-                dqs[mm] = mma_parts2(dqs[mm], ao, bs);
+                dqs[mm] = mma_parts3(dqs[mm], ao, bs);
                 dkR[mm] = mma_parts2(dkR[mm], ar, bs);
                 dKd[mm] = mma_parts3(dKd[mm], av, bd);
             }

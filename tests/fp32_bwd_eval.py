@@ -63,9 +63,9 @@ def mm_parts(n):
 
 
 # The per-chunk GPU kernel's plan for its five products accumulated over the
-# value columns (both operands float32 values): dR Vn^T, dO S^T and dR S^T
-# with two parts on each side, dO Vn^T and Vn dS'^T with three.
-BF16_ACCUM_PLAN = {"dA": mm_parts(2), "dP": mm_parts(3), "dkR": mm_parts(2), "dqs": mm_parts(2),
+# value columns (both operands float32 values): dR Vn^T and dR S^T with two
+# parts on each side, dO Vn^T, dO S^T and Vn dS'^T with three.
+BF16_ACCUM_PLAN = {"dA": mm_parts(2), "dP": mm_parts(3), "dkR": mm_parts(2), "dqs": mm_parts(3),
                    "dKd": mm_parts(3)}
 
 

@@ -85,6 +85,17 @@ def test_bwd2_weak_decay_long_carry():
     _check(_gpu(x), _ref(x))
 
 
+def test_bwd2_one_channel_strong_decay_mixed_blocks():
+    """One channel decays by e^-40 per token inside one chunk only: the intra
+    stage sums that chunk's diagonal blocks directly and takes the anchored
+    product for every other block, in the same call (fp32 inputs, whose
+    recompute walk runs on the intra stage's fp32 operands)."""
+    x = _case(1, 256, 2, 128, 128, seed=960, dtype="fp32")
+    x["log_alpha"][0, 64:128, :, 5] = -40.0
+    x["log_alpha_f64"] = x["log_alpha"].astype(np.float64)
+    _check(_gpu(x), _ref(x))
+
+
 def test_bwd2_deterministic():
     x = _case(1, 200, 2, 128, 128, seed=950, dtype="bf16")
     a, b = _gpu(x), _gpu(x)
