@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
+from tests import fp32_bwd2_eval
 from tests.fp32_bwd_eval import BF16_ACCUM_PLAN, mm_parts, per_head_errors
 
 TOL_BWD = (1e-4, 1e-4, 1e-4, 1e-3, 1e-4, 1e-4)   # dq, dk, dv, dg, dbeta, dh0 (tests/test_parity_bwd.py)
@@ -61,3 +62,22 @@ def test_two_parts_for_dO_Vn_would_lose_dq(T, D, seed):
     floor = per_head_errors(*case).max(axis=0)
     errs = per_head_errors(*case, prods=dict(BF16_ACCUM_PLAN, dP=mm_parts(2))).max(axis=0)
     assert errs[0] >= 5 * floor[0], f"dq: {errs[0]:.2e} against the floor {floor[0]:.2e}"
+
+
+# GDN-2 (tests/test_parity_bwd2.py): the same check for its ragged-case bars
+TOL_BWD2 = (1e-4, 1e-4, 1e-4, 1e-3, 5e-4, 1e-4, 1e-4)   # dq, dk, dv, dlog_alpha, db, dw, dh0
+
+
+@pytest.mark.parametrize("B,T,Dk,Dv,seed", [(2, 150, 64, 64, 1028), (2, 150, 128, 128, 1156), (2, 150, 64, 128, 1092),
+                                            (1, 200, 128, 128, 1120), (1, 65, 128, 128, 985)])
+def test_gdn2_fp32_evaluation_is_below_the_bars(B, T, Dk, Dv, seed):
+    """tests/fp32_bwd2_eval.py on the GDN-2 backward's ragged cases (their
+    shapes and seeds): every gradient of the float32 evaluation stays under
+    half its bar."""
+    x = gi.gdn2_inputs(B, T, 2, Dk, Dv, seed=seed, dtype="bf16", h0=True)
+    rng = np.random.default_rng(seed + 7)
+    do = rng.standard_normal((B, T, 2, Dv)).astype(np.float32).astype(np.float64)
+    dht = rng.standard_normal((B, 2, Dk, Dv)).astype(np.float32).astype(np.float64)
+    errs = fp32_bwd2_eval.per_head_errors(x, do, dht).max(axis=0)
+    for name, e, bar in zip(fp32_bwd2_eval.GRADS, errs, TOL_BWD2):
+        assert e <= bar / 2, f"{name}: fp32 evaluation {e:.2e} > {bar / 2:.2e}"
