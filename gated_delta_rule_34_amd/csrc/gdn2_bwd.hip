@@ -143,7 +143,8 @@ __global__ __launch_bounds__(512, 1) void gdn2_bwd_walk_kernel(
     constexpr int BV = 16, NTHR = 512, LDQ = DK + 4, LDC = BT + 1, LDB = BV + 1;
     using PF = Gdn2WalkPf<DK>;
     __shared__ float sK[BT * LDQ], sQ[BT * LDQ], sE[BT * LDQ], sTm[BT * LDC], sP[BT * LDC];
-    __shared__ float sdO[BT * LDB], sdDl[BT * LDB], sdR[BT * LDB], sdS[DK * LDB], sGam[DK];
+    __shared__ float sdO[BT * LDB], sdDl[BT * LDB], sdS[DK * LDB], sGam[DK];
+    __shared__ __attribute__((aligned(16))) float sdR[BT * LDB];  // also the f32x4 partial sums of dDl
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     constexpr int NTILE = DV / BV;
@@ -225,13 +226,28 @@ __global__ __launch_bounds__(512, 1) void gdn2_bwd_walk_kernel(
         put();
         if (c > 0) fetch(c - 1);
         __syncthreads();
-        // dDl = scale P^T dO + Khat dS' (row block I = wave)
-        if (wave < 4) {
-            const int I = wave;
-            const f32x4 a1 = tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 0, lane);
-            const f32x4 a2 = tmma<DK>(zero4(), sK, LDQ, 1, sdS, LDB, 1, 16 * I, 0, lane);
+        // dDl = scale P^T dO + Khat dS' (row block I = wave & 3), split so that
+        // both wave groups issue 24 MFMAs: waves 0..3 take Khat dS' over the
+        // first 3/4 of the key channels, waves 4..7 scale P^T dO and the last
+        // quarter, leaving their partial sums in sdR (free until dR is formed)
+        {
+            constexpr int KX = DK - DK / 4;
+            const int I = wave & 3;
+            f32x4 *xp = (f32x4 *)sdR;  // [4][64]: 4 KB within sdR's 64 x 17 floats
+            f32x4 a;
+            if (wave < 4) {
+                a = tmma<KX>(zero4(), sK, LDQ, 1, sdS, LDB, 1, 16 * I, 0, lane);
+            } else {
+                a = scale * tmma<BT>(zero4(), sP, 1, LDC, sdO, LDB, 1, 16 * I, 0, lane);
+                a = tmma<DK - KX>(a, sK + KX, LDQ, 1, sdS + KX * LDB, LDB, 1, 16 * I, 0, lane);
+                xp[64 * I + lane] = a;
+            }
+            __syncthreads();
+            if (wave < 4) {
+                const f32x4 t = a + xp[64 * I + lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sdDl[(16 * I + 4 * g + e) * LDB + r] = scale * a1[e] + a2[e];
+                for (int e = 0; e < 4; ++e) sdDl[(16 * I + 4 * g + e) * LDB + r] = t[e];
+            }
         }
         __syncthreads();
         // dR = dDl + (T - I)^T dDl
