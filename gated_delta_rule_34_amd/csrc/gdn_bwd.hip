@@ -792,8 +792,19 @@ template <int DK>
 struct BwdChunk2Smem {
     static constexpr int LDQ = DK + 8, LDC = BT + 1, CW = 16, LDW = CW + 1;
     alignas(16) uint16_t Q[BT * LDQ], K[BT * LDQ];   // raw bf16 rows
-    float Tm[BT * LDC];   // T - I; after the column loop: dA . D
-    float P[BT * LDC];    // (Q K^T) . D, lower; after the column loop: dP . D
+    // T - I as two bf16 parts and P = (Q K^T) . D (lower) as three, 64 x 64
+    // planes in the layout of plane_off; after the column loop the same bytes
+    // hold dA . D and dP . D in fp32
+    union {
+        struct {
+            alignas(16) uint16_t T[2][BT * BT];
+            alignas(16) uint16_t P[3][BT * BT];
+        } pl;
+        struct {
+            float Tm[BT * LDC];
+            float P[BT * LDC];
+        } ep;
+    } tp;
     struct Slices {
         float S[DK * LDW], dS[DK * LDW];
         float V[BT * LDW], dO[BT * LDW], R[BT * LDW], Vn[BT * LDW], dVn[BT * LDW];
@@ -847,6 +858,57 @@ __device__ __forceinline__ f32x4 mma_parts3(f32x4 acc, const u32x4b *a, const u3
     return mma_parts2(acc, a, b);
 }
 
+// Element (row, col) of a 64 x 64 bf16 plane: 16-byte units XOR-swizzled by
+// the row's low three bits, so that 16 lanes reading one unit of 16 rows, or
+// a transpose load's 4 rows x 4 chunks, spread over the banks.
+__device__ __forceinline__ int plane_off(int row, int col) {
+    return row * BT + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
+}
+
+// acc += A B for row block i0 of a product over the 64 rows of a chunk: A
+// given as NP bf16 planes, B an fp32 LDS slice (row stride LDW, column r of
+// the lane) split into NP parts on the fly, over the 32-deep blocks
+// kb0 .. kb1 - 1 (uniform over the wave; the others are zero for the
+// triangular A).  TRANS: A(i, k) = plane[k][i], read with the gfx950 LDS
+// transpose load, which hands lane (g, r) rows 4g + e and 16 + 4g + e of
+// the block (e = 0..3) of column i0 + r; otherwise A(i, k) = plane[i][k],
+// k-slots 8g .. 8g + 7 in one 16-byte read.
+template <int NP, bool TRANS, int LDW>
+__device__ __forceinline__ f32x4 mma_planes(f32x4 acc, const uint16_t (*pl)[BT * BT], const float *B, int i0, int kb0,
+                                            int kb1, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    typedef __attribute__((ext_vector_type(4))) short s16x4b;
+    typedef __attribute__((address_space(3))) s16x4b lds_s16x4b;
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16c;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb < kb0 || kb >= kb1) continue;
+        u32x4b pa[NP], pb[NP];
+        float xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = TRANS ? 32 * kb + (e >> 2) * 16 + 4 * g + (e & 3) : 32 * kb + 8 * g + e;
+            xb[e] = B[k * LDW + r];
+        }
+        split_8(pb, xb);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            if (TRANS) {
+                lds_u16c *m3 = (lds_u16c *)pl[p];
+                const int rr = 32 * kb + 4 * g + (r >> 2), cc = i0 + 4 * (r & 3);
+                const s16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b *)(m3 + plane_off(rr, cc)));
+                const s16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b *)(m3 + plane_off(rr + 16, cc)));
+                const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+                pa[p] = (u32x4b){ulo.x, ulo.y, uhi.x, uhi.y};
+            } else {
+                pa[p] = *(const u32x4b *)&pl[p][plane_off(i0 + r, 32 * kb + 8 * g)];
+            }
+        }
+        acc = NP == 2 ? mma_parts2(acc, pa, pb) : mma_parts3(acc, pa, pb);
+    }
+    return acc;
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -893,7 +955,23 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         sm.Dec[tid] = exp2f((float)(G2L - G2));
         sm.Beta[tid] = (t < T) ? beta[(b * T + t) * H + h] : 0.f;
     }
-    stage_tm<LDC, NTHR>(sm.Tm, Tws + cb * BT * BT, tid);
+    {
+        // T - I (strictly lower, fp32) as two bf16 parts
+        constexpr int U = BT * BT / 4 / NTHR;
+        const float *src = Tws + cb * BT * BT;
+        f32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = *(const f32x4 *)(src + 4 * (tid + NTHR * u));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = 4 * (tid + NTHR * u), row = idx / BT, col = idx % BT;
+            const uint32_t h0 = pack_bf16_rne(x[u][0], x[u][1]), h1 = pack_bf16_rne(x[u][2], x[u][3]);
+            const uint32_t l0 = pack_bf16_rne(x[u][0] - bf16_lo(h0), x[u][1] - bf16_hi(h0));
+            const uint32_t l1 = pack_bf16_rne(x[u][2] - bf16_lo(h1), x[u][3] - bf16_hi(h1));
+            *(uint2 *)&sm.tp.pl.T[0][plane_off(row, col)] = make_uint2(h0, h1);
+            *(uint2 *)&sm.tp.pl.T[1][plane_off(row, col)] = make_uint2(l0, l1);
+        }
+    }
     if (tid < 2 * BT) {
         sm.dB[tid / BT][tid % BT] = 0.f;
         sm.dG[tid / BT][tid % BT] = 0.f;
@@ -906,7 +984,16 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * TI + 4 * g + e, j = 16 * TJ + r;
-            sm.P[i * LDC + j] = (j <= i) ? acc[e] * exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
+            const float pv = (j <= i) ? acc[e] * exp2f((float)(sm.G2[i] - sm.G2[j])) : 0.f;
+            // three bf16 parts (the low halves of packed conversions)
+            const uint32_t h = pack_bf16_rne(pv, 0.f);
+            const float r1 = pv - bf16_lo(h);
+            const uint32_t m = pack_bf16_rne(r1, 0.f);
+            const uint32_t l = pack_bf16_rne(r1 - bf16_lo(m), 0.f);
+            const int o = plane_off(i, j);
+            sm.tp.pl.P[0][o] = (uint16_t)h;
+            sm.tp.pl.P[1][o] = (uint16_t)m;
+            sm.tp.pl.P[2][o] = (uint16_t)l;
         }
     }
 
@@ -998,8 +1085,11 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         __syncthreads();
         // Vn = R + (T - I) R;  dVn = scale P^T dO + Kd dS' (K exact; dS' as three bf16 parts)
         {
-            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, LDC, 1, sl.R, LDW, 1, nullptr, 16 * I, 0, lane);
-            const f32x4 b1 = tile_mma<BT>(zero4(), sm.P, 1, LDC, sl.dO, LDW, 1, nullptr, 16 * I, 0, lane);
+            // (T - I) R on two bf16 parts per side, P^T dO on three; row block I of
+            // the strictly lower T - I reaches k < 32 only for I < 2, and of the
+            // upper P^T k >= 32 only for I >= 2
+            const f32x4 a = mma_planes<2, false, LDW>(zero4(), sm.tp.pl.T, sl.R, 16 * I, 0, I < 2 ? 1 : 2, lane);
+            const f32x4 b1 = mma_planes<3, true, LDW>(zero4(), sm.tp.pl.P, sl.dO, 16 * I, I < 2 ? 0 : 1, 2, lane);
             u32x4b dp[DK / 32][3];
             col_parts<DK, 3>(dp, sl.dS, LDW, r, lane);
             const f32x4 b2 = mma_raw_parts<DK, 3>(zero4(), sm.K, LDQ, 16 * I, dp, lane);
@@ -1014,7 +1104,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         // dR = dVn + (T - I)^T dVn; dv; the row sums of dbeta and dG (per group)
         f32x4 dRr;
         {
-            const f32x4 a = tile_mma<BT>(zero4(), sm.Tm, 1, LDC, sl.dVn, LDW, 1, nullptr, 16 * I, 0, lane);
+            const f32x4 a = mma_planes<2, true, LDW>(zero4(), sm.tp.pl.T, sl.dVn, 16 * I, I < 2 ? 0 : 1, 2, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * g + e;
@@ -1101,8 +1191,8 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
                     sm.dG[gi][i] += pg;
                 }
                 colp[jj][e] = w;
-                sm.Tm[i * LDC + j] = dAv * D;  // dA . D
-                sm.P[i * LDC + j] = dPv * D;   // dP . D
+                sm.tp.ep.Tm[i * LDC + j] = dAv * D;  // dA . D
+                sm.tp.ep.P[i * LDC + j] = dPv * D;   // dP . D
             }
         }
         // column sums of dA . A + dP . P: lanes of column j = 16J + r
@@ -1126,10 +1216,10 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 16 * I + r, j = 32 * kb + 8 * g + e;
-                x1[e] = sm.Tm[i * LDC + j];
-                x2[e] = sm.Tm[j * LDC + i] * sm.Beta[j];
-                x3[e] = sm.P[j * LDC + i];
-                x4[e] = sm.P[i * LDC + j];
+                x1[e] = sm.tp.ep.Tm[i * LDC + j];
+                x2[e] = sm.tp.ep.Tm[j * LDC + i] * sm.Beta[j];
+                x3[e] = sm.tp.ep.P[j * LDC + i];
+                x4[e] = sm.tp.ep.P[i * LDC + j];
             }
             split_8(a1[kb], x1);
             split_8(a2[kb], x2);

@@ -62,18 +62,19 @@ def mm_parts(n):
     return f
 
 
-# The per-chunk GPU kernel's plan for its five products accumulated over the
-# value columns (both operands float32 values): dR Vn^T and dR S^T with two
-# parts on each side, dO Vn^T, dO S^T and Vn dS'^T with three.
+# The per-chunk GPU kernel's bf16 part plan for its products of two float32
+# operands: of the five accumulated over the value columns, dR Vn^T and dR S^T
+# take two parts on each side, dO Vn^T, dO S^T and Vn dS'^T three; of the row
+# products, (T - I) R and (T - I)^T dVn take two, P^T dO three.
 BF16_ACCUM_PLAN = {"dA": mm_parts(2), "dP": mm_parts(3), "dkR": mm_parts(2), "dqs": mm_parts(3),
-                   "dKd": mm_parts(3)}
+                   "dKd": mm_parts(3), "TR": mm_parts(2), "PdO": mm_parts(3), "TdVn": mm_parts(2)}
 
 
 def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64, prods=None):
     """dq, dk, dv, dg, dbeta, dS0 of one head with float32 products.  Entry
     states come from the fp64 chunked forward.  `prods` may replace the
-    products accumulated over the value columns (keys dA, dP, dkR, dqs, dKd)
-    by other roundings, such as BF16_ACCUM_PLAN."""
+    products of two float32 operands (keys dA, dP, dkR, dqs, dKd, TR, PdO,
+    TdVn) by other roundings, such as BF16_ACCUM_PLAN."""
     pr = dict(prods or {})
     mmx = lambda name, a, b: pr.get(name, _mm)(a, b)
     T, Dk = q.shape
@@ -100,12 +101,12 @@ def bwd_head_fp32(q, k, v, g, beta, S0, dO, dST, scale, C=64, prods=None):
         TmI = Tm - np.eye(n)
         KS = _mm(K, S)
         R = bc[:, None] * (V - gam[:, None] * KS)
-        Vn = R + _mm(TmI, R)
+        Vn = R + mmx('TR', TmI, R)
         P = _mm(Q, K.T) * D
         dec = np.exp(G[-1] - G)
         # reverse mode through the chunk, dS the gradient of the state leaving it
-        dVn = scale * _mm(P.T, dOc) + dec[:, None] * _mm(K, dS)
-        dR = dVn + _mm(TmI.T, dVn)
+        dVn = scale * mmx('PdO', P.T, dOc) + dec[:, None] * _mm(K, dS)
+        dR = dVn + mmx('TdVn', TmI.T, dVn)
         dA = -np.tril(mmx('dA', dR, Vn.T), -1)
         dP = scale * np.tril(mmx('dP', dOc, Vn.T))
         dS_in = gam[-1] * dS + scale * _mm((gam[:, None] * Q).T, dOc) - _mm(((bc * gam)[:, None] * K).T, dR)

@@ -42,10 +42,11 @@ def test_fp32_evaluation_is_below_the_bars(T, D, seed):
 
 @pytest.mark.parametrize("T,D,seed", CASES)
 def test_bf16_part_plan_is_below_the_bars(T, D, seed):
-    """The per-chunk kernel accumulates dR Vn^T and dR S^T from two bf16
-    parts per operand and dO Vn^T, dO S^T, Vn dS'^T from three; evaluated
-    with those roundings, every gradient stays under half its bar, and dq
-    within twice the float32 floor."""
+    """The per-chunk kernel forms dR Vn^T, dR S^T, (T - I) R and
+    (T - I)^T dVn from two bf16 parts per operand and dO Vn^T, dO S^T,
+    Vn dS'^T, P^T dO from three; evaluated with those roundings, every
+    gradient stays under half its bar, and dq within twice the float32
+    floor."""
     case = _case(T, D, seed)
     floor = per_head_errors(*case).max(axis=0)
     errs = per_head_errors(*case, prods=BF16_ACCUM_PLAN).max(axis=0)
