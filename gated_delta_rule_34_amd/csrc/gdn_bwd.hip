@@ -909,6 +909,19 @@ __device__ __forceinline__ f32x4 mma_planes(f32x4 acc, const uint16_t (*pl)[BT *
     return acc;
 }
 
+// Two LDS transpose loads (at p and p + step elements) of 16-bit rows as one
+// 8-element MFMA operand.
+__device__ __forceinline__ u32x4b tr_rows16(const uint16_t *p, int step) {
+    typedef __attribute__((ext_vector_type(4))) short s16x4c;
+    typedef __attribute__((address_space(3))) s16x4c lds_s16x4c;
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16d;
+    lds_u16d *m3 = (lds_u16d *)p;
+    const s16x4c lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4c *)m3);
+    const s16x4c hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4c *)(m3 + step));
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return (u32x4b){ulo.x, ulo.y, uhi.x, uhi.y};
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -1209,13 +1222,16 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
         // dk = diag(beta) dAs K + dAs^T diag(beta) K + dPs^T Q + diag(dec) dKd - diag(beta gamma) dkR
         // dq = scale diag(gamma) dqs + dPs K, on bf16 MFMA: the left operands
         // split once into bf16 parts (three for dP.D, two for the others)
+        // k-slots of lane (g, r) in each 32-deep block: rows 4g + e and
+        // 16 + 4g + e (e = 0..3), the order in which the LDS transpose load
+        // hands out the K and Q columns below
         u32x4b a1[2][2], a2[2][2], a3[2][2], a4[2][3];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             float x1[8], x2[8], x3[8], x4[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int i = 16 * I + r, j = 32 * kb + 8 * g + e;
+                const int i = 16 * I + r, j = 32 * kb + (e >> 2) * 16 + 4 * g + (e & 3);
                 x1[e] = sm.tp.ep.Tm[i * LDC + j];
                 x2[e] = sm.tp.ep.Tm[j * LDC + i] * sm.Beta[j];
                 x3[e] = sm.tp.ep.P[j * LDC + i];
@@ -1232,17 +1248,12 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk2_kernel(
             f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                uint32_t wk[8], wq[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * kb + 8 * g + e;
-                    wk[e] = sm.K[j * LDQ + 16 * m + r];
-                    wq[e] = sm.Q[j * LDQ + 16 * m + r];
-                }
-                const u32x4b bk = {wk[0] | (wk[1] << 16), wk[2] | (wk[3] << 16), wk[4] | (wk[5] << 16),
-                                   wk[6] | (wk[7] << 16)};
-                const u32x4b bq = {wq[0] | (wq[1] << 16), wq[2] | (wq[3] << 16), wq[4] | (wq[5] << 16),
-                                   wq[6] | (wq[7] << 16)};
+                // columns 16m .. 16m + 15 of K and Q by transpose loads: lane (g, r)
+                // addresses row 32kb + 4g + r/4 (+ 16), columns 16m + 4(r % 4) .. + 3,
+                // and receives column 16m + r of rows 4g + e (+ 16) of the block
+                const int jr = 32 * kb + 4 * g + (r >> 2), jc = 16 * m + 4 * (r & 3);
+                const u32x4b bk = tr_rows16(sm.K + jr * LDQ + jc, 16 * LDQ);
+                const u32x4b bq = tr_rows16(sm.Q + jr * LDQ + jc, 16 * LDQ);
                 t1 = mma_bf16v(mma_bf16v(t1, a1[kb][0], bk), a1[kb][1], bk);
                 t2 = mma_bf16v(mma_bf16v(t2, a2[kb][0], bk), a2[kb][1], bk);
                 t3 = mma_bf16v(mma_bf16v(t3, a3[kb][0], bq), a3[kb][1], bq);
