@@ -1,5 +1,8 @@
-// gdn_bwd.hip -- backward of the chunked Gated DeltaNet forward on gfx950
-// (fp32 arithmetic throughout; bf16 inputs are exact in fp32).
+// gdn_bwd.hip -- backward of the chunked Gated DeltaNet forward on gfx950.
+// fp32 inputs: fp32 arithmetic on fp32 MFMA.  bf16 inputs: fp32 values and
+// accumulation, with the products on bf16 MFMA, exact where an operand is a
+// bf16 input and otherwise on bf16 parts (hi + lo, or hi + mid + lo where
+// the product needs fp32's precision) of the fp32 operands.
 //
 // Chunk equations (the chunked form of the GatedDeltaNet walkthrough's
 // recurrence, section on the chunked Triton kernels): in a chunk with entry
@@ -20,12 +23,14 @@
 // Stages (all chunks of all heads):
 //   1. the forward's intra stage: G2 = log2(e) G and T - I per chunk
 //   2. the forward walk, writing the entry state of every chunk
-//   3. bwd_walk_kernel: dS' chunk by chunk from the last one back (state
+//   3. bwd_walk_kernel (bf16 inputs: bwd_walk_fused_kernel in
+//      gdn_bwd_fused.hip): dS' chunk by chunk from the last one back (state
 //      columns are independent, so one workgroup owns 32 of them), written
 //      per chunk; dh0 is the gradient entering the first chunk
-//   4. bwd_chunk_kernel: one workgroup per (batch, head, chunk) recomputes
-//      the chunk and produces its dq, dk, dv, dbeta, dg, looping over the
-//      value columns 16 at a time
+//   4. bwd_chunk_kernel (bf16 inputs: bwd_chunk2_kernel, eight waves in two
+//      groups): one workgroup per (batch, head, chunk) recomputes the chunk
+//      and produces its dq, dk, dv, dbeta, dg, looping over the value
+//      columns 16 (32) at a time
 #include <type_traits>
 
 #include "gdn_device.h"
