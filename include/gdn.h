@@ -235,10 +235,13 @@ gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, con
  * chunks, the chunked-kernel section of the walkthrough): a forward walk
  * recomputes the state entering every chunk, a reverse walk over the chunks
  * carries the state gradient, then every chunk is recomputed and
- * differentiated in parallel.  fp32 arithmetic, except that with bf16 inputs
- * the forward walk is the bf16 forward's (its state products on bf16 hi + lo
- * parts, new values in fp16), whose states carry about 16 significant bits;
- * q, k and v must then be 16-byte aligned.
+ * differentiated in parallel.  fp32 values and accumulation throughout.  With
+ * fp32 inputs the products run on fp32 MFMA.  With bf16 inputs they run on
+ * bf16 or fp16 MFMA: exact where an operand is a bf16 input, and otherwise on
+ * hi + lo (about 16 bits) or hi + mid + lo (about 24 bits) parts of the fp32
+ * operands, chosen per product so that every gradient stays near the error of
+ * the same equations with fp32 products; q, k and v must then be 16-byte
+ * aligned.
  *   inputs  as gdn_chunk_fwd (h0 nullable), dO [B, T, H, Dv] fp32,
  *           dht [B, H, Dk, Dv] fp32 or NULL (no gradient on the final state)
  *   outputs dq, dk [B, T, H, Dk], dv [B, T, H, Dv], dg, dbeta [B, T, H],
