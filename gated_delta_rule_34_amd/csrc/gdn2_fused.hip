@@ -263,14 +263,14 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
             const int u = tid0 + NTH * x, row = u / C8, c8 = u % C8;
             const int tr = min(t0 + row, T - 1) - t0;
             const long off = (row0 + (long)tr * H) * DK + 8 * c8;
-            kr[x] = *(const v4u *)(k + off);
-            qr[x] = *(const v4u *)(q + off);
-            br[x] = *(const v4u *)(bg + off);
+            kr[x] = __builtin_nontemporal_load((const v4u *)(k + off));
+            qr[x] = __builtin_nontemporal_load((const v4u *)(q + off));
+            br[x] = __builtin_nontemporal_load((const v4u *)(bg + off));
         }
 #pragma unroll
         for (int x = 0; x < RG; ++x) {
             const int tr = min(t0 + RG * gr + x, T - 1) - t0;
-            lv[x] = la[(row0 + (long)tr * H) * DK + ch];
+            lv[x] = __builtin_nontemporal_load(&la[(row0 + (long)tr * H) * DK + ch]);
         }
     };
 
@@ -460,8 +460,8 @@ __device__ __forceinline__ void stage_load(Gdn2Stage<DK> &R, const Gdn2Head &hd,
         const int t = chunk * BT + row;
         const long off = (hd.row0 + (long)t * hd.H) * DV + hd.vcol0 + 8 * c4;
         const bool in = t < hd.T;
-        R.v[x] = in ? *(const u32x4 *)(hd.v + off) : (u32x4){0u, 0u, 0u, 0u};
-        R.w[x] = in ? *(const u32x4 *)(hd.w + off) : (u32x4){0u, 0u, 0u, 0u};
+        R.v[x] = in ? __builtin_nontemporal_load((const u32x4 *)(hd.v + off)) : (u32x4){0u, 0u, 0u, 0u};
+        R.w[x] = in ? __builtin_nontemporal_load((const u32x4 *)(hd.w + off)) : (u32x4){0u, 0u, 0u, 0u};
     }
 }
 

@@ -157,7 +157,7 @@ __device__ __forceinline__ void load_v(u32x4 (&dst)[4], const HeadArgs &a, int c
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int t = min(chunk * BT + 16 * p + (lane >> 2), a.T - 1);
-        dst[p] = *(const u32x4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 + (lane & 3) * 8);
+        dst[p] = __builtin_nontemporal_load((const u32x4 *)(a.v + ((a.tok0 + t) * a.H + a.h) * (long)DV + a.vcol0 + (lane & 3) * 8));
     }
 }
 
