@@ -15,6 +15,7 @@ __all__ = [
     "lib_path", "load", "status_string",
     "gdn_chunk_fwd", "gdn_chunk_intra", "gdn_chunk_walk", "gdn2_chunk_fwd", "gdn_recurrent_step",
     "gdn2_recurrent_step", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace", "gdn_chunk_fwd_varlen",
+    "gdn2_chunk_fwd_varlen", "gdn2_chunk_fwd_varlen_workspace",
     "gdn_chunk_fwd_workspace", "gdn2_chunk_fwd_workspace", "gdn_prologue", "gdn_gated_rmsnorm",
     "gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace", "gdn2_chunk_fwd_noalloc", "gdn2_chunk_fwd_noalloc_max_bytes",
     "clock_probe",
@@ -60,6 +61,10 @@ def load():
     lib.gdn_recurrent_step.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _vp]
     lib.gdn_chunk_fwd_varlen.restype = _i
     lib.gdn_chunk_fwd_varlen.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
+    lib.gdn2_chunk_fwd_varlen_workspace.restype = _sz
+    lib.gdn2_chunk_fwd_varlen_workspace.argtypes = [_i] * 6
+    lib.gdn2_chunk_fwd_varlen.restype = _i
+    lib.gdn2_chunk_fwd_varlen.argtypes = [_vp] * 10 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.gdn_chunk_bwd_workspace.restype = _sz
     lib.gdn_chunk_bwd_workspace.argtypes = [_i] * 6
     lib.gdn_chunk_bwd.restype = _i
@@ -211,6 +216,46 @@ def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, outp
     _check(load().gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0),
                                        _ptr(o), _ptr(ht), N, total_T, H, Dk, Dv, dt, float(scale), _stream(dev)),
            "gdn_chunk_fwd_varlen")
+    return o, ht
+
+
+def gdn2_chunk_fwd_varlen_workspace(N, total_T, H, Dk, Dv, dtype_code):
+    return load().gdn2_chunk_fwd_varlen_workspace(N, total_T, H, Dk, Dv, dtype_code)
+
+
+def gdn2_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, h0=None, scale=None, output_final_state=True,
+                          workspace=None):
+    """Gated DeltaNet-2 forward over packed variable-length sequences.  q, k, b
+    [total_T,H,Dk] and v, w [total_T,H,Dv] bf16 (a leading batch dim of 1 is accepted),
+    log_alpha [total_T,H,Dk] fp32, cu_seqlens int32 [N+1] on the device, h0 [N,H,Dk,Dv]
+    fp32 or None.  Returns (o [total_T,H,Dv] fp32, ht [N,H,Dk,Dv] or None)."""
+    torch = _torch()
+    if q.dim() == 4:
+        q, k, v, log_alpha, b, w = q[0], k[0], v[0], log_alpha[0], b[0], w[0]
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    dt = _dtype_code(q)
+    for t, name, d in ((q, "q", Dk), (k, "k", Dk), (v, "v", Dv), (b, "b", Dk), (w, "w", Dv)):
+        _need(t, name, (total_T, H, d), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (total_T, H, Dk), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (N, H, Dk, Dv), torch.float32, dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = torch.empty((total_T, H, Dv), dtype=torch.float32, device=dev)
+    ht = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    lib = load()
+    need = lib.gdn2_chunk_fwd_varlen_workspace(N, total_T, H, Dk, Dv, dt)
+    if need == 0:
+        _check(2, "gdn2_chunk_fwd_varlen_workspace")
+    ws = workspace if workspace is not None else _workspace(need, dev)[1]
+    _check(lib.gdn2_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                     _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht), N, total_T, H, Dk, Dv, dt,
+                                     float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)),
+           "gdn2_chunk_fwd_varlen")
     return o, ht
 
 

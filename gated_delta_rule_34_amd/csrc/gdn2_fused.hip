@@ -57,6 +57,18 @@ struct Gdn2Blk {
 
 size_t gdn2_fused_block_bytes(int Dk) { return Dk == 64 ? Gdn2Blk<64>::BYTES : Gdn2Blk<128>::BYTES; }
 
+// Packed variable-length sequences.  The chunks of all sequences are numbered
+// g = 0 .. NC - 1 in sequence order and the block of (head h, chunk g) is
+// block h NC + g of the workspace.  seq[n] = {first token, tokens walked,
+// first chunk number, 0} of sequence n (seq[N].z = chunks in use); tab[g] =
+// the sequence of chunk g, or N for the unused numbers at the end.  seq null:
+// a dense batch.
+struct Gdn2Var {
+    const int4 *seq;
+    const int *tab;
+    int N, NC;
+};
+
 
 // --------------------------------------------------------------- prep kernel
 template <int DK>
@@ -222,11 +234,11 @@ __device__ __forceinline__ void offdiag_tile(Gdn2PrepSmem<DK> &sm, int t, int la
 // ...  The raw rows and log-decays of its next chunk are fetched into
 // registers while the current chunk's A and P tiles are formed, so their
 // latency overlaps the current chunk's work.
-template <int DK>
+template <int DK, bool VAR>
 __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *__restrict__ q,
                                          const uint16_t *__restrict__ k, const float *__restrict__ la,
                                          const uint16_t *__restrict__ bg, char *__restrict__ ws, int T, int H, int NT,
-                                         int c0, int nc, int nidx, int w0, int nw) {
+                                         int c0, int nc, int nidx, int w0, int nw, const Gdn2Var var) {
     using SM = Gdn2PrepSmem<DK>;
     using BL = Gdn2Blk<DK>;
     constexpr int NTH = 512;
@@ -245,23 +257,40 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
         const int bh = idx / nc;
         return bh * NT + c0 + (idx - bh * nc);
     };
-    // token-head row of a chunk's first token, and the chunk's first token
-    auto locate = [&](int cb, long &row0, int &t0) {  // 32-bit index math (cheap on the VALU)
+    // token-head row of a chunk's first token, the chunk's first token within
+    // its sequence and the sequence's length
+    auto locate = [&](int cb, long &row0, int &t0, int &Tc) {  // 32-bit index math (cheap on the VALU)
+        if constexpr (VAR) {  // packed sequences: cb = h NC + g
+            const int h = cb / var.NC, gc = cb - h * var.NC;
+            const int n = var.tab[gc];
+            if (n >= var.N) {  // an unused chunk number: token 0 of head h, into its own block
+                row0 = h;
+                t0 = 0;
+                Tc = 1;
+                return;
+            }
+            const int4 sq = var.seq[n];
+            t0 = (gc - sq.z) * BT;
+            Tc = sq.y;
+            row0 = ((long)sq.x + t0) * H + h;
+            return;
+        }
         const int bh = cb / NT;
         t0 = (cb - bh * NT) * BT;
         const int b = bh / H;
         row0 = ((long)b * T + t0) * H + (bh - b * H);
+        Tc = T;
     };
     // raw rows and log-decays of chunk cb into registers; rows past T read the
     // last token (always in bounds) and are zeroed when staged
     auto fetch = [&](int cb) {
         long row0;
-        int t0;
-        locate(cb, row0, t0);
+        int t0, Tc;
+        locate(cb, row0, t0, Tc);
 #pragma unroll
         for (int x = 0; x < NU; ++x) {
             const int u = tid0 + NTH * x, row = u / C8, c8 = u % C8;
-            const int tr = min(t0 + row, T - 1) - t0;
+            const int tr = min(t0 + row, Tc - 1) - t0;
             const long off = (row0 + (long)tr * H) * DK + 8 * c8;
             kr[x] = __builtin_nontemporal_load((const v4u *)(k + off));
             qr[x] = __builtin_nontemporal_load((const v4u *)(q + off));
@@ -269,7 +298,7 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
         }
 #pragma unroll
         for (int x = 0; x < RG; ++x) {
-            const int tr = min(t0 + RG * gr + x, T - 1) - t0;
+            const int tr = min(t0 + RG * gr + x, Tc - 1) - t0;
             lv[x] = __builtin_nontemporal_load(&la[(row0 + (long)tr * H) * DK + ch]);
         }
     };
@@ -284,14 +313,14 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
         asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid0));
         const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         long row0;
-        int t0;
-        locate(cb, row0, t0);
+        int t0, Tc;
+        locate(cb, row0, t0, Tc);
         char *blk = ws + (long)cb * BL::BYTES;
         // 1. raw rows (zero past T) and the per-channel cumsum of log alpha
 #pragma unroll
         for (int x = 0; x < NU; ++x) {
             const int u = tid + NTH * x, row = u / C8, c8 = u % C8;
-            const bool in = t0 + row < T;
+            const bool in = t0 + row < Tc;
             const v4u z = {0u, 0u, 0u, 0u};
             *(v4u *)&sm.k[row * LDR + 8 * c8] = in ? kr[x] : z;
             *(v4u *)&sm.q[row * LDR + 8 * c8] = in ? qr[x] : z;
@@ -300,7 +329,7 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
         float acc = 0.f;
 #pragma unroll
         for (int x = 0; x < RG; ++x) {
-            acc += (t0 + RG * gr + x < T) ? lv[x] * 1.4426950408889634f : 0.f;
+            acc += (t0 + RG * gr + x < Tc) ? lv[x] * 1.4426950408889634f : 0.f;
             lv[x] = acc;
         }
         sm.part[gr][ch] = acc;
@@ -382,13 +411,13 @@ __device__ __forceinline__ void prep_run(Gdn2PrepSmem<DK> &sm, const uint16_t *_
     }
 }
 
-template <int DK>
+template <int DK, bool VAR>
 __global__ __launch_bounds__(512) void gdn2_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                          const float *__restrict__ la, const uint16_t *__restrict__ bg,
                                                          char *__restrict__ ws, int T, int H, int NT, int c0, int nc,
-                                                         int nidx) {
+                                                         int nidx, Gdn2Var var) {
     __shared__ Gdn2PrepSmem<DK> sm;
-    prep_run<DK>(sm, q, k, la, bg, ws, T, H, NT, c0, nc, nidx, blockIdx.x, gridDim.x);
+    prep_run<DK, VAR>(sm, q, k, la, bg, ws, T, H, NT, c0, nc, nidx, blockIdx.x, gridDim.x, var);
 }
 
 // --------------------------------------------------------------- walk kernel
@@ -628,11 +657,12 @@ __device__ __forceinline__ void gdn2_consume(Gdn2WalkSmem<DK, DV> &sm, f32x4 (&S
 // The walk over chunks c0 .. c1 - 1 of one (batch, head, 32 value columns):
 // workgroup n of nwg.  Waves 0 and 1 carry the state, waves 2 and 3 stage the
 // blocks; any further waves of the workgroup only keep the barrier count.
-template <int DK, int DV>
+template <int DK, int DV, bool VAR>
 __device__ __forceinline__ void walk_run(Gdn2WalkSmem<DK, DV> &sm, const char *__restrict__ ws,
                                          const uint16_t *__restrict__ v, const uint16_t *__restrict__ wg,
                                          const float *__restrict__ h0, float *__restrict__ o, float *__restrict__ ht,
-                                         int T, int H, int NT, float scale, int n, int nwg, int c0, int c1) {
+                                         int T, int H, int NT, float scale, int n, int nwg, int c0, int c1,
+                                         const Gdn2Var var) {
     using C = Gdn2WalkCfg<DK, DV>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -649,6 +679,15 @@ __device__ __forceinline__ void walk_run(Gdn2WalkSmem<DK, DV> &sm, const char *_
     hd.T = T;
     hd.row0 = (bh / H) * (long)T * H + (bh % H);
     hd.vcol0 = vt * C::BV;
+    if constexpr (VAR) {  // packed sequences: bh = n H + h walks sequence n's chunks
+        const int sn = (int)(bh / H), h = (int)(bh - (long)sn * H);
+        const int4 sq = var.seq[sn];
+        hd.ws = ws + ((long)h * var.NC + sq.z) * Gdn2Blk<DK>::BYTES;
+        hd.T = sq.y;
+        hd.row0 = (long)sq.x * H + h;
+        c0 = 0;
+        c1 = (sq.y + BT - 1) / BT;
+    }
     const long sbase = bh * (long)DK * DV;
 
     if (wave < 2) {
@@ -673,7 +712,7 @@ __device__ __forceinline__ void walk_run(Gdn2WalkSmem<DK, DV> &sm, const char *_
         // loaders: iteration c stores chunk c + 1 and fetches chunk c + 2
         const int lt = tid - 128;
         Gdn2Stage<DK> R;
-        stage_load<DK, DV>(R, hd, c0, lt);
+        if (!VAR || c0 < c1) stage_load<DK, DV>(R, hd, c0, lt);  // an empty sequence loads nothing
         __syncthreads();
         for (int c = c0 - 1; c < c1; ++c) {
             if (c + 1 < c1) {
@@ -688,16 +727,16 @@ __device__ __forceinline__ void walk_run(Gdn2WalkSmem<DK, DV> &sm, const char *_
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool VAR>
 __global__ __launch_bounds__(256, 1) void gdn2_walk_fused_kernel(const char *__restrict__ ws,
                                                                   const uint16_t *__restrict__ v,
                                                                   const uint16_t *__restrict__ wg,
                                                                   const float *__restrict__ h0, float *__restrict__ o,
                                                                   float *__restrict__ ht, int T, int H, int NT,
-                                                                  int c0, int c1, float scale) {
+                                                                  int c0, int c1, float scale, Gdn2Var var) {
     static_assert(sizeof(Gdn2WalkSmem<DK, DV>) <= 160 * 1024, "LDS budget");
     __shared__ Gdn2WalkSmem<DK, DV> sm;
-    walk_run<DK, DV>(sm, ws, v, wg, h0, o, ht, T, H, NT, scale, blockIdx.x, gridDim.x, c0, c1);
+    walk_run<DK, DV, VAR>(sm, ws, v, wg, h0, o, ht, T, H, NT, scale, blockIdx.x, gridDim.x, c0, c1, var);
 }
 
 // One launch of the pipelined forward: workgroups below nwalk walk chunks
@@ -724,9 +763,9 @@ __global__ __launch_bounds__(512, 1) void gdn2_pipe_kernel(const uint16_t *__res
     __shared__ Gdn2PipeSmem<DK, DV> sm;
     const int n = blockIdx.x;
     if (n < nwalk)
-        walk_run<DK, DV>(sm.walk, ws, v, wg, h0, o, ht, T, H, NT, scale, n, nwalk, wc0, wc1);
+        walk_run<DK, DV, false>(sm.walk, ws, v, wg, h0, o, ht, T, H, NT, scale, n, nwalk, wc0, wc1, Gdn2Var{});
     else
-        prep_run<DK>(sm.prep, q, k, la, bg, ws, T, H, NT, pc0, pnc, pidx, n - nwalk, gridDim.x - nwalk);
+        prep_run<DK, false>(sm.prep, q, k, la, bg, ws, T, H, NT, pc0, pnc, pidx, n - nwalk, gridDim.x - nwalk, Gdn2Var{});
 }
 
 // ----------------------------------------------------------------- launchers
@@ -771,8 +810,8 @@ static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float 
         const int nc = bound(1) - bound(0);
         const long nidx = (long)BH * nc;
         const long pgrid = nidx < ncu ? nidx : ncu;
-        hipLaunchKernelGGL((gdn2_prep_kernel<DK>), dim3((unsigned)pgrid), dim3(512), 0, st, q16, k16, la, b16,
-                           (char *)ws, T, H, NT, bound(0), nc, (int)nidx);
+        hipLaunchKernelGGL((gdn2_prep_kernel<DK, false>), dim3((unsigned)pgrid), dim3(512), 0, st, q16, k16, la, b16,
+                           (char *)ws, T, H, NT, bound(0), nc, (int)nidx, Gdn2Var{});
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -789,8 +828,9 @@ static hipError_t launch_gdn2_fused_t(const void *q, const void *k, const float 
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV>), dim3((unsigned)walk_grid), dim3(256), 0, st,
-                       (const char *)ws, v16, w16, K == 1 ? h0 : carry, o, ht, T, H, NT, bound(K - 1), NT, scale);
+    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV, false>), dim3((unsigned)walk_grid), dim3(256), 0, st,
+                       (const char *)ws, v16, w16, K == 1 ? h0 : carry, o, ht, T, H, NT, bound(K - 1), NT, scale,
+                       Gdn2Var{});
     return hipGetLastError();
 }
 
@@ -802,6 +842,130 @@ hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la,
     if (Dk == 128 && Dv == 64) return launch_gdn2_fused_t<128, 64>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
     if (Dk == 128 && Dv == 128)
         return launch_gdn2_fused_t<128, 128>(q, k, la, bg, v, wg, h0, o, ht, ws, B, T, H, scale, st);
+    return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------- packed sequences (varlen)
+// The sequence table from the offsets, in one workgroup: sequence n holds
+// tokens [s0, s1) with both offsets clamped into [0, total_T] and s1 >= s0, so
+// that malformed offsets never address out of range.  Its chunk numbers start
+// at the running sum of ceil(len / 64) over the earlier sequences, saturated
+// at NC; a sequence whose chunks would pass NC walks only the chunks that fit.
+__global__ __launch_bounds__(256) void gdn2_var_seq_kernel(const int *__restrict__ cu, int4 *__restrict__ seq, int N,
+                                                           int total_T, int NC) {
+    __shared__ long long part[256];
+    __shared__ long long carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + tid;
+        int s0 = 0, len = 0;
+        long long want = 0;
+        if (n < N) {
+            s0 = min(max(cu[n], 0), total_T);
+            const int s1 = min(max(cu[n + 1], s0), total_T);
+            len = s1 - s0;
+            want = (len + BT - 1) / BT;
+        }
+        part[tid] = want;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive scan over the workgroup
+            const long long add = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        const long long incl = carry + part[tid];
+        if (n < N) {
+            const long long cs = min(incl - want, (long long)NC), ce = min(incl, (long long)NC);
+            seq[n] = make_int4(s0, (int)min((long long)len, (ce - cs) * BT), (int)cs, 0);
+        }
+        __syncthreads();
+        if (tid == 255) carry = incl;
+        __syncthreads();
+    }
+    if (tid == 0) seq[N] = make_int4(0, 0, (int)min(carry, (long long)NC), 0);
+}
+
+// tab[g] for g < NC: the last sequence n < N whose first chunk number is <= g
+// (the numbers never decrease, so its range holds g), or N past the chunks in use.
+__global__ __launch_bounds__(256) void gdn2_var_tab_kernel(const int4 *__restrict__ seq, int *__restrict__ tab, int N,
+                                                           int NC) {
+    const long gi = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gi >= NC) return;
+    const int gc = (int)gi;
+    int n = N;
+    if (gc < seq[N].z) {
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seq[mid].z <= gc) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+    }
+    tab[gc] = n;
+}
+
+// Workspace of the packed form: blocks [H][NC], then seq [N + 1] and tab [NC].
+Gdn2VarWs gdn2_var_ws(int N, int total_T, int H, int Dk) {
+    Gdn2VarWs w;
+    w.NC = (long long)(total_T + BT - 1) / BT + N;
+    const size_t blocks = ((size_t)H * w.NC * gdn2_fused_block_bytes(Dk) + 255) / 256 * 256;
+    w.seq_off = blocks;
+    w.tab_off = w.seq_off + (((size_t)N + 1) * sizeof(int4) + 255) / 256 * 256;
+    w.total = w.tab_off + ((size_t)w.NC * sizeof(int) + 255) / 256 * 256;
+    return w;
+}
+
+template <int DK, int DV>
+static hipError_t launch_gdn2_varlen_t(const void *q, const void *k, const float *la, const void *bg, const void *v,
+                                       const void *wg, const int *cu, const float *h0, float *o, float *ht, void *ws,
+                                       int N, int total_T, int H, float scale, hipStream_t st) {
+    const Gdn2VarWs lay = gdn2_var_ws(N, total_T, H, DK);
+    const int NC = (int)lay.NC;
+    int4 *seq = (int4 *)((char *)ws + lay.seq_off);
+    int *tab = (int *)((char *)ws + lay.tab_off);
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu < 1) ncu = 1;
+    hipLaunchKernelGGL(gdn2_var_seq_kernel, dim3(1), dim3(256), 0, st, cu, seq, N, total_T, NC);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gdn2_var_tab_kernel, dim3((unsigned)((NC + 255) / 256)), dim3(256), 0, st,
+                       (const int4 *)seq, tab, N, NC);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const Gdn2Var var{seq, tab, N, NC};
+    // every (head, chunk number) block, unused numbers included (they read token 0)
+    const long nidx = (long)H * NC;
+    const long pgrid = nidx < ncu ? nidx : ncu;
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, true>), dim3((unsigned)pgrid), dim3(512), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, la, (const uint16_t *)bg, (char *)ws, total_T, H, NC, 0, NC, (int)nidx, var);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long walk_grid = (long)N * H * (DV / Gdn2WalkCfg<DK, DV>::BV);
+    hipLaunchKernelGGL((gdn2_walk_fused_kernel<DK, DV, true>), dim3((unsigned)walk_grid), dim3(256), 0, st,
+                       (const char *)ws, (const uint16_t *)v, (const uint16_t *)wg, h0, o, ht, total_T, H, NC, 0, 0,
+                       scale, var);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn2_fused_varlen_bf16(const void *q, const void *k, const float *la, const void *bg,
+                                         const void *v, const void *wg, const int *cu, const float *h0, float *o,
+                                         float *ht, void *ws, int N, int total_T, int H, int Dk, int Dv, float scale,
+                                         hipStream_t st) {
+#define GDN2_VAR(DKv, DVv)                                                                                       \
+    if (Dk == DKv && Dv == DVv)                                                                                  \
+    return launch_gdn2_varlen_t<DKv, DVv>(q, k, la, bg, v, wg, cu, h0, o, ht, ws, N, total_T, H, scale, st)
+    GDN2_VAR(64, 64);
+    GDN2_VAR(64, 128);
+    GDN2_VAR(128, 64);
+    GDN2_VAR(128, 128);
+#undef GDN2_VAR
     return hipErrorInvalidValue;
 }
 

@@ -291,6 +291,52 @@ gdn_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const flo
     return from_hip(gdn::launch_gdn2_walk(E, Qh, Kh, Gam, Tinv, P, D, v, w, h0, o, ht, B, T, H, Dk, Dv, bf, scale, st));
 }
 
+// Packed sequences for GDN-2: sizes the chunk numbering can hold (every
+// prep index h NC + g and every walk workgroup id fits in 32 bits).
+static bool var2_sizes_ok(int N, int total_T, int H, int Dv) {
+    if (N < 1 || total_T < 1 || H < 1) return false;
+    const long long NC = ((long long)total_T + kBT - 1) / kBT + N;
+    return (long long)H * NC < (1LL << 31) && (long long)N * H * (Dv / 32 > 0 ? Dv / 32 : 1) < (1LL << 31);
+}
+
+size_t gdn2_chunk_fwd_varlen_workspace(int N, int total_T, int H, int Dk, int Dv, gdn_dtype dtype) {
+    if (!var2_sizes_ok(N, total_T, H, Dv) || !head_ok(Dk) || !head_ok(Dv) || dtype != GDN_BF16) return 0;
+    return gdn::gdn2_var_ws(N, total_T, H, Dk).total;
+}
+
+gdn_status gdn2_chunk_fwd_varlen(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                                 const void *w, const int *cu_seqlens, const float *h0, float *o, float *ht, int N,
+                                 int total_T, int H, int Dk, int Dv, gdn_dtype dtype, float scale, void *ws,
+                                 size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !log_alpha || !b || !w || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+    if (!var2_sizes_ok(N, total_T, H, Dv)) return GDN_ERR_INVALID_ARG;
+    if (!head_ok(Dk) || !head_ok(Dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(b, 16) || !aligned(w, 16) ||
+        !aligned(o, 16))
+        return GDN_ERR_INVALID_ARG;
+    const size_t es = esize(dtype);
+    const size_t ntok = (size_t)total_T * H;
+    const size_t nstate = (size_t)N * H * Dk * Dv * sizeof(float);
+    const gdn::Gdn2VarWs lay = gdn::gdn2_var_ws(N, total_T, H, Dk);
+    const Range rq{q, ntok * Dk * es}, rk{k, ntok * Dk * es}, rv{v, ntok * Dv * es};
+    const Range rla{log_alpha, ntok * Dk * 4}, rb{b, ntok * Dk * es}, rw{w, ntok * Dv * es};
+    const Range rcu{cu_seqlens, (size_t)(N + 1) * sizeof(int)}, rh0{h0, h0 ? nstate : 0};
+    const Range ro{o, ntok * Dv * 4}, rht{ht, ht ? nstate : 0}, rws{ws, lay.total};
+    for (Range in : {rq, rk, rv, rla, rb, rw, rcu, rh0, rws})
+        if (overlap(ro, in)) return GDN_ERR_INVALID_ARG;
+    if (ht) {
+        if (overlap(rht, rh0) && ht != h0) return GDN_ERR_INVALID_ARG;
+        for (Range in : {rq, rk, rv, rla, rb, rw, rcu, ro, rws})
+            if (overlap(rht, in)) return GDN_ERR_INVALID_ARG;
+    }
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    for (Range in : {rq, rk, rv, rla, rb, rw, rcu, rh0})
+        if (overlap(rws, in)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_gdn2_fused_varlen_bf16(q, k, log_alpha, b, v, w, cu_seqlens, h0, o, ht, ws, N,
+                                                       total_T, H, Dk, Dv, scale, (hipStream_t)stream));
+}
+
 gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                               float *S, float *o, int B, int H, int Dk, int Dv, gdn_dtype dtype, float scale,
                               void *stream) {

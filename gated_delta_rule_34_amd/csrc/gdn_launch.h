@@ -65,6 +65,22 @@ hipError_t launch_gdn2_fused_bf16(const void *q, const void *k, const float *la,
                                   const void *wg, const float *h0, float *o, float *ht, void *ws, int B, int T,
                                   int H, int Dk, int Dv, float scale, hipStream_t st);
 
+// The same kernels over packed variable-length sequences (cu_seqlens on the
+// device, N + 1 offsets into total_T tokens): two small kernels number the
+// chunks of every sequence into NC = ceil(total_T / 64) + N chunk numbers,
+// the prep fills block (head, number) of each, and one walk workgroup per
+// (sequence, head, 32 value columns) carries the state.  ws layout in
+// Gdn2VarWs (total bytes, offsets of the sequence and chunk tables).
+struct Gdn2VarWs {
+    long long NC;
+    size_t seq_off, tab_off, total;
+};
+Gdn2VarWs gdn2_var_ws(int N, int total_T, int H, int Dk);
+hipError_t launch_gdn2_fused_varlen_bf16(const void *q, const void *k, const float *la, const void *bg,
+                                         const void *v, const void *wg, const int *cu, const float *h0, float *o,
+                                         float *ht, void *ws, int N, int total_T, int H, int Dk, int Dv, float scale,
+                                         hipStream_t st);
+
 hipError_t launch_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        float *S, float *o, int B, int H, int Dk, int Dv, bool bf16, float scale,
                        hipStream_t st);

@@ -43,7 +43,7 @@
  *     to fp16 (11 significant bits, largest finite value 65,504) for the
  *     matrix-core products: in gdn_chunk_fwd and gdn_chunk_fwd_varlen the
  *     chunk residuals R = beta (v - gamma K S), the new values, T - I and P;
- *     in gdn2_chunk_fwd also the decayed keys and queries and the state as
+ *     in gdn2_chunk_fwd and gdn2_chunk_fwd_varlen also the decayed keys and queries and the state as
  *     hi + lo parts.  With ||k_t|| <= 1, beta in [0, 1] and g <= 0 one has
  *     |T - I| <= 1, |P| <= scale, and for every value column c
  *       |R|, |new values| <= max_t |v_{t,c}| + sqrt(||h0[:, c]||^2 + sum_t beta_t v_{t,c}^2)
@@ -227,6 +227,34 @@ gdn_status gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, con
                                 const float *beta, const int *cu_seqlens, const float *h0,
                                 float *o, float *ht, int N, int total_T, int H, int Dk, int Dv,
                                 gdn_dtype dtype, float scale, void *stream);
+
+/* Bytes of workspace gdn2_chunk_fwd_varlen needs (256-byte aligned buffer);
+ * 0 for unsupported arguments (fp32, head sizes, sizes out of range). */
+size_t gdn2_chunk_fwd_varlen_workspace(int N, int total_T, int H, int Dk, int Dv, gdn_dtype dtype);
+
+/*
+ * gdn2_chunk_fwd_varlen -- gdn2_chunk_fwd on N packed sequences of different
+ * lengths (Gated DeltaNet-2 article, "Regla-2 del Delta cerrado", for the
+ * recurrence; each sequence is chunked from its own first token and carried
+ * on its own, exactly as a batch entry of gdn2_chunk_fwd).
+ *   q, k, b [total_T, H, Dk] and v, w [total_T, H, Dv] bf16, 16-byte aligned
+ *   log_alpha  [total_T, H, Dk] fp32
+ *   cu_seqlens device int32 [N + 1], as in gdn_chunk_fwd_varlen (offsets
+ *              clamped into [0, total_T]; an empty sequence passes its
+ *              initial state through)
+ *   h0, ht [N, H, Dk, Dv] fp32 (nullable; ht may alias h0);  o [total_T, H, Dv] fp32
+ *   ws  device, 256-byte aligned, >= gdn2_chunk_fwd_varlen_workspace(...)
+ *       bytes, owned by the caller: the per-chunk blocks of all sequences
+ *       (numbered into ceil(total_T / 64) + N chunk numbers per head) and two
+ *       small tables the call derives from cu_seqlens on the device.
+ * bf16 only (GDN_ERR_UNSUPPORTED for fp32).  Errors as gdn2_chunk_fwd, plus
+ * GDN_ERR_INVALID_ARG for a null cu_seqlens.  Asynchronous on `stream`.
+ */
+gdn_status gdn2_chunk_fwd_varlen(const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const void *b, const void *w,
+                                 const int *cu_seqlens, const float *h0, float *o, float *ht,
+                                 int N, int total_T, int H, int Dk, int Dv, gdn_dtype dtype,
+                                 float scale, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Backward of gdn_chunk_fwd (training): gradients of

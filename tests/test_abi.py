@@ -153,6 +153,39 @@ def test_varlen_rejects_bad_arguments():
     assert f(ptrs=p[:7] + [p[5]] + p[8:]) == 1      # o overlaps cu_seqlens
 
 
+def test_gdn2_varlen_workspace_and_validation():
+    lib = gdn.load()
+    N, total, H = 3, 300, 2
+    need = lib.gdn2_chunk_fwd_varlen_workspace(N, total, H, 128, 128, 1)
+    # chunk numbers ceil(300 / 64) + 3 = 8 per head, one block each, plus the two tables
+    blk = 66304
+    assert need >= H * 8 * blk and need % 256 == 0
+    assert lib.gdn2_chunk_fwd_varlen_workspace(N, total, H, 128, 128, 0) == 0   # fp32 unsupported
+    assert lib.gdn2_chunk_fwd_varlen_workspace(0, total, H, 128, 128, 1) == 0
+    assert lib.gdn2_chunk_fwd_varlen_workspace(N, total, H, 96, 128, 1) == 0
+    p = [FAKE + (i << 36) for i in range(10)]   # q k v log_alpha b w cu h0 o ht
+    ws = FAKE + (12 << 36)
+
+    def f(ptrs=p, N=N, total=total, Dk=128, dt=1, w=ws, nbytes=need):
+        return lib.gdn2_chunk_fwd_varlen(*[_p(x) for x in ptrs], N, total, H, Dk, 128, dt, 0.1, _p(w), nbytes, None)
+
+    assert f(ptrs=p[:6] + [None] + p[7:]) == 1      # no cu_seqlens
+    assert f(ptrs=p[:8] + [None] + p[9:]) == 1      # no o
+    assert f(N=0) == 1
+    assert f(total=0) == 1
+    assert f(dt=0) == 2                             # fp32: not supported on this path
+    assert f(Dk=96) == 2
+    assert f(w=None) == 3
+    assert f(w=ws + 8) == 3                         # misaligned workspace
+    assert f(nbytes=need - 1) == 3
+    assert f(ptrs=p[:8] + [p[0]] + p[9:]) == 1      # o overlaps q
+    assert f(ptrs=p[:8] + [p[6]] + p[9:]) == 1      # o overlaps cu_seqlens
+    assert f(ptrs=p[:9] + [p[8]]) == 1              # ht overlaps o
+    assert f(w=p[3]) == 1                           # workspace overlaps log_alpha
+    assert f(ptrs=[p[0] + 2] + p[1:]) == 1          # q not 16-byte aligned
+    assert f(ptrs=p[:5] + [p[5] + 8] + p[6:]) == 1  # w not 16-byte aligned
+
+
 def test_gdn2_bwd_workspace_and_validation():
     lib = gdn.load()
     assert lib.gdn2_chunk_bwd_workspace(2, 100, 3, 128, 128, 1) > 0
