@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ Hin, 
                                                        int T, int H, int NS, int L) {
     constexpr int CW = 32;
     __shared__ float sM[D * (D + 1)];
-    __shared__ float sS[D * CW];
+    __shared__ __align__(16) float sS[D * CW];
     const int tid = threadIdx.x;
     if (blockIdx.x == 0)
         for (int n = tid; n <= B * NS; n += 256) {
@@ -1040,18 +1040,51 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ Hin, 
     const long hs = (long)D * D;
     const int col = tid % CW, rg = tid / CW;  // 8 row groups of D / 8 rows
     constexpr int RPT = D / 8;
+    // Each thread requests all of its loads of a stage before its first
+    // store; the workspace sections move in float4 pieces (16-byte aligned
+    // rows), the caller's h0 element by element.
+    constexpr int SV = D * CW / 4 / 256, MV = D * D / 4 / 256;  // float4 per thread
     float *H0 = Hin + ((b * NS + 0) * H + h) * hs;
-    for (int idx = tid; idx < D * CW; idx += 256) {
-        const long off = (long)(idx / CW) * D + slice * CW + idx % CW;
-        H0[off] = h0 ? h0[bh * hs + off] : 0.f;
+    {
+        float hv[4 * SV];
+#pragma unroll
+        for (int x = 0; x < 4 * SV; ++x) {
+            const int idx = tid + 256 * x;
+            hv[x] = h0 ? h0[bh * hs + (long)(idx / CW) * D + slice * CW + idx % CW] : 0.f;
+        }
+#pragma unroll
+        for (int x = 0; x < 4 * SV; ++x) {
+            const int idx = tid + 256 * x;
+            H0[(long)(idx / CW) * D + slice * CW + idx % CW] = hv[x];
+        }
     }
     float *E1 = Hin + ((b * NS + 1) * H + h) * hs;
-    for (int idx = tid; idx < D * CW; idx += 256) sS[idx] = E1[(long)(idx / CW) * D + slice * CW + idx % CW];
+    {
+        float4 ev[SV];
+#pragma unroll
+        for (int x = 0; x < SV; ++x) {
+            const int idx = 4 * (tid + 256 * x);
+            ev[x] = *(const float4 *)(E1 + (long)(idx / CW) * D + slice * CW + idx % CW);
+        }
+#pragma unroll
+        for (int x = 0; x < SV; ++x) *(float4 *)&sS[4 * (tid + 256 * x)] = ev[x];
+    }
     for (int sgm = 1; sgm <= NS - 2; ++sgm) {
         const float *Ms = M + ((b * NS + sgm) * H + h) * hs;
         float *Es = Hin + ((b * NS + sgm + 1) * H + h) * hs;
+        float4 mv[MV];
+#pragma unroll
+        for (int x = 0; x < MV; ++x) mv[x] = *(const float4 *)(Ms + 4 * (tid + 256 * x));
         __syncthreads();
-        for (int idx = tid; idx < D * D; idx += 256) sM[(idx / D) * (D + 1) + idx % D] = Ms[idx];
+#pragma unroll
+        for (int x = 0; x < MV; ++x) {
+            const int idx = 4 * (tid + 256 * x), row = idx / D, c = idx % D;
+            float *d = &sM[row * (D + 1) + c];  // padded rows: four scalar stores
+            d[0] = mv[x].x;
+            d[1] = mv[x].y;
+            d[2] = mv[x].z;
+            d[3] = mv[x].w;
+        }
         __syncthreads();
         float acc[RPT];
 #pragma unroll
