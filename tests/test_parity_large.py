@@ -86,9 +86,19 @@ def _free():
     torch.cuda.empty_cache()
 
 
+def _need_gib(gib):
+    """Skip (not fail) when the device has less free memory than the case needs."""
+    torch = _torch()
+    _free()
+    free, _ = torch.cuda.mem_get_info()
+    if free < gib * 2 ** 30:
+        pytest.skip(f"needs about {gib} GiB of free device memory, {free / 2 ** 30:.0f} GiB free")
+
+
 def test_gdn_forward_past_2_31_elements():
     """gdn_chunk_fwd (bf16, the single fused kernel) over 4,160 heads."""
     torch = _torch()
+    _need_gib(40)
     x = gi.gdn_inputs(1, T, NV, D, D, seed=4801, dtype="bf16", h0=True)
     q, k, v = (_tile(x[n], B, H) for n in ("q", "k", "v"))
     g, beta = (_tile(x[n], B, H) for n in ("g", "beta"))
@@ -113,6 +123,7 @@ def test_gdn2_forward_past_2_31_elements():
     """gdn2_chunk_fwd (bf16, prep and walk kernels) over 4,160 heads; the
     workspace holds 17.6 GB of per-chunk blocks."""
     torch = _torch()
+    _need_gib(80)
     x = gi.gdn2_inputs(1, T, NV, D, D, seed=4802, dtype="bf16", h0=True)
     ins = [_tile(x[n], B, H) for n in ("q", "k", "v", "log_alpha", "b", "w")]
     h0 = _tile(x["h0"], B, H, time_axis=False)
@@ -139,6 +150,7 @@ def test_decode_step_state_past_2_31_elements(kind):
     """gdn_recurrent_step / gdn2_recurrent_step on an fp32 state of 2.18e9
     elements (8.7 GB), updated in place."""
     torch = _torch()
+    _need_gib(30)
     if kind == "gdn":
         x = gi.step_inputs(1, NV, D, D, seed=4803)
         names = ("q", "k", "v", "g", "beta")
@@ -169,6 +181,7 @@ def test_gdn_backward_past_2_31_elements():
     """gdn_chunk_bwd (bf16 inputs) over 4,160 heads, with h0 and a final-state
     gradient; every gradient to the full-size bars of the backward tests."""
     torch = _torch()
+    _need_gib(130)
     from tests.test_parity_bwd import GRADS, TOL_FULL
     x = gi.gdn_inputs(1, T, NV, D, D, seed=4805, dtype="bf16", h0=True)
     rng = np.random.default_rng(4806)
@@ -202,6 +215,7 @@ def test_gdn2_backward_past_2_31_elements():
     gradient and no h0 (the GDN-2 workload's setting); each gradient to the
     full-size bars of the GDN-2 backward tests."""
     torch = _torch()
+    _need_gib(200)
     from tests.test_parity_bwd2 import GRADS, NAMES, TOL_FULL
     x = gi.gdn2_inputs(1, T, NV, D, D, seed=4807, dtype="bf16")
     rng = np.random.default_rng(4808)
