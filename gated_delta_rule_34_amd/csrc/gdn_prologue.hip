@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk, const uint16_t *__restrict__ xv,
     const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ wq,
     const float *__restrict__ wk, const float *__restrict__ wv, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, const float *__restrict__ state_in, uint16_t *__restrict__ q,
-    uint16_t *__restrict__ k, uint16_t *__restrict__ v, float *__restrict__ g, float *__restrict__ beta, int B,
-    int T, int H) {
+    const float *__restrict__ dt_bias, const float *state_in, uint16_t *__restrict__ q,
+    uint16_t *__restrict__ k, uint16_t *__restrict__ v, float *__restrict__ g, float *__restrict__ beta,
+    float *state_out, int B, int T, int H) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // workgroup n runs on XCD n % 8: give each XCD a contiguous range of tokens
     // so the rows shared by neighbouring blocks stay in one L2
@@ -165,6 +165,17 @@ __global__ __launch_bounds__(256) void prologue_kernel(
             hist[1][c] = hist[2][c];
             hist[2][c] = cur[c];
         }
+        // after the last token the window is the new convolution state (rows
+        // T - 3 .. T - 1, cached values where those are negative); written
+        // here when it does not replace state_in, else by conv_state_kernel
+        if (state_out && t == T - 1 && live) {
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                float *sp = state_out + ((long)bb * 3 + r) * Ctot + coff + j * 8;  // 4-byte aligned
+#pragma unroll
+                for (int c = 0; c < 8; ++c) sp[c] = hist[r][c];
+            }
+        }
     }
 }
 
@@ -248,13 +259,19 @@ hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, const
                            float *beta, float *state_out, int B, int T, int H, int Dk, int Dv, hipStream_t st) {
     const long nblk = (long)B * ((T + kProTB - 1) / kProTB);
     const dim3 grid((unsigned)((nblk + 3) / 4), (unsigned)((H * (2 * Dk + Dv) / 8 + 63) / 64));
+    // A new state that does not replace the old one is written by the
+    // prologue kernel itself; in place (state_out == state_in) the blocks
+    // that read the old state could run after the one that writes the new
+    // state, so conv_state_kernel writes it after the prologue.
+    const bool fused_state = state_out && state_out != state_in;
 #define GDN_PRO(DKv, DVv)                                                                                        \
     if (Dk == DKv && Dv == DVv) {                                                                                \
         hipLaunchKernelGGL((prologue_kernel<DKv, DVv, kProTB>), grid, dim3(256), 0, st, (const uint16_t *)xq,     \
                            (const uint16_t *)xk, (const uint16_t *)xv, a, b, wq, wk, wv, A_log, dt_bias, state_in, \
-                           (uint16_t *)q, (uint16_t *)k, (uint16_t *)v, g, beta, B, T, H);                         \
+                           (uint16_t *)q, (uint16_t *)k, (uint16_t *)v, g, beta, fused_state ? state_out : nullptr, \
+                           B, T, H);                                                                               \
         hipError_t e = hipGetLastError();                                                                         \
-        if (e != hipSuccess || !state_out) return e;                                                              \
+        if (e != hipSuccess || !state_out || fused_state) return e;                                              \
         const long n = (long)B * H * (2 * DKv + DVv);                                                             \
         hipLaunchKernelGGL((conv_state_kernel<DKv, DVv>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,    \
                            (const uint16_t *)xq, (const uint16_t *)xk, (const uint16_t *)xv, state_in, state_out, \
